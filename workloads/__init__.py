@@ -1,0 +1,192 @@
+"""Seeded synthetic workloads shared by the tests, the bench and the oracle checks.
+
+This module only describes shapes and draws random inputs.  It performs none of
+the attention arithmetic: no masking, no score modification, no softmax.  Both
+the GPU path and the CPU oracle receive the exact bits drawn here.
+
+The five workloads follow the shapes the pages describe:
+
+* a tiny causal sliding window (the worked N=8, W=4 example of "FlexAttention:
+  from rules to fused kernels", section 2.2, Fig. 1, scaled up to N=512);
+* causal attention with tanh soft-capping ("FlexAttention: compiler optimization
+  of custom attention", section 2);
+* GQA with a document mask intersected with a sliding window and an ALiBi bias
+  ("FlexAttention: from rules to fused kernels", sections 1.1 and 1.2);
+* a 64K prefix-LM with a per-head relative-position table (same page, section
+  6.3 for prefix-LM, section 1.2 for the table; section 2.1 for the
+  262,144-block grid of a 64K sequence);
+* split-KV decode with a sliding window ending at the query position
+  ("FlexAttention: compiler optimization of custom attention", section 6).
+
+Mask specifications are plain nested tuples, independent of any binary layout:
+``("causal",)``, ``("swa", W)``, ``("doc",)``, ``("prefix", P)``,
+``("and", a, b)``, ``("or", a, b)``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Any, Optional, Tuple
+
+import numpy as np
+
+try:  # torch is only needed for the bf16 draws
+    import torch
+except Exception:  # pragma: no cover
+    torch = None
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    q_len: int
+    kv_len: int
+    d: int
+    block_q: int
+    block_kv: int
+    mask: Tuple[Any, ...]
+    score: str                      # identity | alibi | softcap | relpos
+    cap: float = 0.0                # soft-cap constant
+    relpos_radius: int = 0          # clip radius of the relative-position table
+    q_offset: int = 0               # global position of query row 0
+    seed: int = 0                   # torch seed for Q, K, V (drawn in that order)
+    aux_seed: int = 0               # numpy seed for the auxiliary tensors
+    doc_seed: Optional[int] = None  # numpy seed for the document lengths
+    doc_len_range: Tuple[int, int] = (256, 2048)
+    table_B: int = 1                # batch extent of the block tables (1 = broadcast)
+
+    @property
+    def g(self) -> int:
+        return self.Hq // self.Hkv
+
+
+WORKLOADS = {
+    "tiny_swa": Workload(
+        name="tiny_swa", B=1, Hq=2, Hkv=2, q_len=512, kv_len=512, d=64,
+        block_q=64, block_kv=64, mask=("swa", 128), score="identity",
+        seed=1001, aux_seed=1001),
+    "causal_softcap": Workload(
+        name="causal_softcap", B=2, Hq=16, Hkv=16, q_len=4096, kv_len=4096, d=128,
+        block_q=128, block_kv=128, mask=("causal",), score="softcap", cap=20.0,
+        seed=1002, aux_seed=1002),
+    "gqa_doc_swa_alibi": Workload(
+        name="gqa_doc_swa_alibi", B=1, Hq=32, Hkv=8, q_len=8192, kv_len=8192, d=128,
+        block_q=128, block_kv=128, mask=("and", ("doc",), ("swa", 1024)),
+        score="alibi", seed=1003, aux_seed=1003, doc_seed=0),
+    "prefix_relpos_64k": Workload(
+        name="prefix_relpos_64k", B=1, Hq=16, Hkv=2, q_len=65536, kv_len=65536, d=128,
+        block_q=128, block_kv=128, mask=("prefix", 4096), score="relpos",
+        relpos_radius=1024, seed=1004, aux_seed=1004),
+    "decode_swa_softcap": Workload(
+        name="decode_swa_softcap", B=64, Hq=32, Hkv=8, q_len=1, kv_len=32768, d=128,
+        block_q=128, block_kv=128, mask=("swa", 4096), score="softcap", cap=30.0,
+        q_offset=32767, seed=1005, aux_seed=1005),
+}
+
+# The N=8, W=4, 2x2-block classification case that goes with the tiny workload.
+WORKED_N8 = dict(q_len=8, kv_len=8, block_q=2, block_kv=2, mask=("swa", 4))
+
+
+def mask_uses_doc(spec) -> bool:
+    if spec[0] == "doc":
+        return True
+    if spec[0] in ("and", "or"):
+        return mask_uses_doc(spec[1]) or mask_uses_doc(spec[2])
+    return False
+
+
+def doc_lengths(total: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Document lengths drawn uniformly from [lo, hi] one at a time until they
+    cover ``total`` tokens; the last one is truncated to fit."""
+    rng = np.random.default_rng(seed)
+    out = []
+    acc = 0
+    while acc < total:
+        n = int(rng.integers(lo, hi + 1))
+        n = min(n, total - acc)
+        out.append(n)
+        acc += n
+    return np.asarray(out, dtype=np.int64)
+
+
+def doc_ids_from_lengths(lengths: np.ndarray) -> np.ndarray:
+    """Packed document IDs 0, 1, 2, ... (int32), one per token."""
+    return np.repeat(np.arange(len(lengths), dtype=np.int32), lengths)
+
+
+def alibi_slopes(Hq: int) -> np.ndarray:
+    """Per-query-head ALiBi slopes 2^(-8(h+1)/Hq) as float32 values."""
+    h = np.arange(Hq, dtype=np.float64)
+    return np.exp2(-8.0 * (h + 1.0) / Hq).astype(np.float32)
+
+
+def relpos_table(Hq: int, radius: int, seed: int, std: float = 0.1) -> np.ndarray:
+    """Per-query-head relative-position table, float32 [Hq, 2R+1], N(0, std^2)."""
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((Hq, 2 * radius + 1)) * std).astype(np.float32)
+
+
+def aux_inputs(w: Workload) -> dict:
+    """Document IDs, ALiBi slopes and relative-position table for a workload (numpy)."""
+    aux = {"doc_ids": None, "slopes": None, "table": None}
+    if mask_uses_doc(w.mask):
+        total = w.q_offset + max(w.q_len, w.kv_len)
+        seed = w.doc_seed if w.doc_seed is not None else w.aux_seed
+        lens = doc_lengths(total, w.doc_len_range[0], w.doc_len_range[1], seed)
+        aux["doc_lengths"] = lens
+        aux["doc_ids"] = doc_ids_from_lengths(lens)[None, :]   # [1, doc_len]
+    if w.score == "alibi":
+        aux["slopes"] = alibi_slopes(w.Hq)
+    if w.score == "relpos":
+        aux["table"] = relpos_table(w.Hq, w.relpos_radius, w.aux_seed)
+    return aux
+
+
+def randn_bf16(shape, seed: int, device="cpu", chunk_elems: int = 1 << 28):
+    """iid N(0,1) drawn in float32 from a seeded torch generator and rounded to
+    bfloat16 (round to nearest even).  Large tensors are drawn in chunks along
+    the leading dimension so that the float32 staging stays bounded."""
+    assert torch is not None
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    flat = out.view(-1)
+    n = flat.numel()
+    pos = 0
+    while pos < n:
+        m = min(chunk_elems, n - pos)
+        flat[pos:pos + m] = torch.randn(m, generator=gen, device=device,
+                                        dtype=torch.float32).to(torch.bfloat16)
+        pos += m
+    return out
+
+
+def qkv(w: Workload, device="cpu"):
+    """Q [B,Hq,q_len,d], K and V [B,Hkv,kv_len,d], bf16, drawn in that order
+    from one generator seeded with ``w.seed``."""
+    assert torch is not None
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed)
+    out = []
+    for shape in ((w.B, w.Hq, w.q_len, w.d), (w.B, w.Hkv, w.kv_len, w.d),
+                  (w.B, w.Hkv, w.kv_len, w.d)):
+        t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        flat = t.view(-1)
+        n = flat.numel()
+        pos = 0
+        chunk = 1 << 27
+        while pos < n:
+            m = min(chunk, n - pos)
+            flat[pos:pos + m] = torch.randn(m, generator=gen, device=device,
+                                            dtype=torch.float32).to(torch.bfloat16)
+            pos += m
+        out.append(t)
+    return tuple(out)
+
+
+def scaled(w: Workload, **kw) -> Workload:
+    """A copy of a workload with some fields replaced (for small parity cases)."""
+    return dataclasses.replace(w, **kw)
