@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+One step = fa_create_block_mask + fa_forward over one synthetic batch of the chosen
+workload (default: causal attention with tanh soft-cap, B=2, H=16, N=4096, d=128,
+128x128 blocks).  Inputs are resident in HBM before the timed region starts.
+
+Printed: ONE JSON line with the throughput over executed blocks (TFLOP/s for prefill
+workloads, GB/s for the decode workload), the roofline position of the dominant
+kernel (timed with HIP events on its own stream inside the timed region) and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn fwd TFLOP/s (executed blocks), % bf16 MFMA peak; decode GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_programmable_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per dispatch from the committed rocprofv3 counter summary, or None
+    if there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def accounting(w, tab):
+    """Executed blocks and algorithmic work of one step (tables built with B'=H'=1)."""
+    nf = int(tab["full_kv_ptr"][-1])
+    npart = int(tab["kv_ptr"][-1])
+    executed = nf + npart
+    heads = w.B * w.Hq
+    acc = {"full_blocks": nf, "partial_blocks": npart, "executed_blocks_per_head": executed}
+    if w.q_len == 1:
+        kv_bytes = w.B * w.Hkv * executed * w.block_kv * w.d * 2 * 2
+        q_bytes = w.B * w.Hq * w.q_len * w.d * 2
+        idx_bytes = 4 * (executed + 4)
+        acc["bytes"] = kv_bytes + 2 * q_bytes + w.B * w.Hq * w.q_len * 4 + idx_bytes
+        acc["flop"] = heads * executed * w.block_kv * 4 * w.d * w.q_len
+    else:
+        acc["flop"] = heads * executed * 4 * w.block_q * w.block_kv * w.d
+    return acc
+
+
+def cpu_baseline(w, aux, q, k, v, acc, budget_s):
+    """The oracle, as is, on a bounded sample: whole heads (prefill) or whole
+    batch entries (decode) until the time budget is used."""
+    import numpy as np
+    from oracle import attention as OA
+    from oracle import blockmask as OB
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    OB.tables(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset, aux["doc_ids"])
+    t_tab = time.perf_counter() - t0
+    kw = dict(cap=w.cap or None, slopes=aux["slopes"], table=aux["table"], radius=w.relpos_radius,
+              q_offset=w.q_offset, doc_ids=aux["doc_ids"])
+    done = 0
+    t_attn = 0.0
+    if w.q_len == 1:
+        units = w.B
+        per_unit = acc["bytes"] / w.B
+        while done < units and t_attn < budget_s:
+            b = done
+            qb, kb, vb = (t[b:b + 1].cpu() for t in (q, k, v))
+            t1 = time.perf_counter()
+            OA.attention(qb, kb, vb, w.mask, w.score, **kw)
+            t_attn += time.perf_counter() - t1
+            done += 1
+        rate = per_unit * done / (t_attn + t_tab) / 1e9
+        unit, sample = "GB/s", f"{done} of {units} requests (all {w.Hq} heads), plus the block tables"
+    else:
+        units = w.B * w.Hq
+        per_unit = acc["flop"] / units
+        kc = {}
+        while done < units and t_attn < budget_s:
+            b, h = divmod(done, w.Hq)
+            hkv = h // w.g
+            if (b, hkv) not in kc:
+                kc = {(b, hkv): (k[b:b + 1, hkv:hkv + 1].cpu(), v[b:b + 1, hkv:hkv + 1].cpu())}
+            kb, vb = kc[(b, hkv)]
+            qb = q[b:b + 1, h:h + 1].cpu()
+            sl = None if aux["slopes"] is None else aux["slopes"][h:h + 1]
+            tb = None if aux["table"] is None else aux["table"][h:h + 1]
+            t1 = time.perf_counter()
+            OA.attention(qb, kb, vb, w.mask, w.score, cap=w.cap or None, slopes=sl, table=tb,
+                         radius=w.relpos_radius, q_offset=w.q_offset, doc_ids=aux["doc_ids"])
+            t_attn += time.perf_counter() - t1
+            done += 1
+        rate = per_unit * done / (t_attn + t_tab * done / units) / 1e12
+        unit = "TFLOP/s"
+        sample = (f"{done} of {units} (batch, head) pairs, all {w.q_len} rows each, credited with "
+                  f"their executed-block FLOP; block tables timed once ({t_tab:.2f} s) and prorated")
+    return {"value": rate, "unit": unit, "cores": int(threads), "kind": "oracle", "sample": sample,
+            "seconds": round(t_attn + t_tab, 3)}
+
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import block_sparse_programmable_amd as fa
+    import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    aux = W.aux_inputs(w)
+    q, k, v = W.qkv(w, device=dev)
+    docT = None if aux["doc_ids"] is None else torch.as_tensor(aux["doc_ids"]).to(dev)
+    sl = None if aux["slopes"] is None else torch.as_tensor(aux["slopes"]).to(dev)
+    tb = None if aux["table"] is None else torch.as_tensor(aux["table"]).to(dev)
+
+    bm = fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset, docT)
+    tables = bm.tensors
+    bws = bm._keep[1]
+    out = torch.empty(w.B, w.Hq, w.q_len, w.d, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(w.B, w.Hq, w.q_len, dtype=torch.float32, device=dev)
+    fargs, _, _ = fa.forward_args(q, k, v, bm, w.score, w.cap, sl, tb, w.relpos_radius, None, out, lse)
+    fws_bytes = fa.forward_workspace_size(fargs)
+    fws = torch.empty(max(fws_bytes, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    acc = accounting(w, bm.compact())
+
+    def step(ev=None, i=0):
+        b = fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset,
+                                 docT, tables=tables, workspace=bws)
+        if ev is not None:
+            ev[0][i].record()
+        fa.forward(q, k, v, b, score=w.score, softcap=w.cap, alibi_slopes=sl, relpos=tb,
+                   relpos_radius=w.relpos_radius, out=out, lse=lse, workspace=fws)
+        if ev is not None:
+            ev[1][i].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = ([torch.cuda.Event(enable_timing=True) for _ in range(K)],
+          [torch.cuda.Event(enable_timing=True) for _ in range(K)])
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        step(ev, i)
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+    fwd_ms = [ev[0][i].elapsed_time(ev[1][i]) for i in range(K)]
+    fwd_avg = float(np.mean(fwd_ms))
+
+    decode = w.q_len == 1
+    if decode:
+        value = acc["bytes"] / (ms_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = acc["bytes"] / (fwd_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": read_traffic("decode", w.name)}
+    else:
+        value = acc["flop"] / (ms_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = acc["flop"] / (fwd_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": read_traffic("prefill", w.name)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, aux, q, k, v, acc, args.cpu_seconds)
+
+    cfg = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "q_len": w.q_len, "kv_len": w.kv_len,
+           "d": w.d, "block_q": w.block_q, "block_kv": w.block_kv, "mask": repr(w.mask),
+           "score_mod": w.score, "q_offset": w.q_offset, "seed": w.seed,
+           "full_blocks": acc["full_blocks"], "partial_blocks": acc["partial_blocks"]}
+    rec = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": K,
+           "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": cfg, "roofline": roof, "cpu_baseline": cpu,
+           "fwd_ms": fwd_avg, "fwd_ms_p10": float(np.percentile(fwd_ms, 10)),
+           "fwd_ms_p90": float(np.percentile(fwd_ms, 90)),
+           "algorithmic_flop": acc["flop"], "algorithmic_bytes": acc.get("bytes"),
+           "kernel_source_digest": kernel_source_digest(), "gpu": torch.cuda.get_device_name(0),
+           "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+    if decode:
+        rec["forward_workspace_bytes"] = fws_bytes
+    return rec
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="causal_softcap")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this library has no multi-GPU path "
+              f"(--gpus {args.gpus} requested); run with --gpus 1", file=sys.stderr)
+        return 2
+    rec = run(args)
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,80 @@
+"""Build libfa.so (gfx950) in-tree with hipcc.
+
+Usage: python -m block_sparse_programmable_amd.build [--verbose] [--resource-usage]
+
+Each csrc/*.hip file is compiled separately (in parallel) and linked into
+block_sparse_programmable_amd/libfa.so.  Packed-fp32 instructions are disabled for
+all device code.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libfa.so")
+ARCH = os.environ.get("FA_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc():
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def common_flags():
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-result"]
+
+
+def compile_one(src, verbose=False, resource_usage=False):
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [hipcc(), "-c", src, "-o", obj] + common_flags()
+    if resource_usage:
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = r.stdout + r.stderr
+    out = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out)
+    return obj
+
+
+def build(verbose=False, resource_usage=False, jobs=None):
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: compile_one(s, verbose, resource_usage), srcs))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-o", tmp] + objs + [f"--offload-arch={ARCH}", "-fPIC"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--resource-usage", action="store_true")
+    a = ap.parse_args(argv)
+    print(build(a.verbose, a.resource_usage))
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,330 @@
+// Host side of the C ABI declared in include/fa.h: argument validation, dispatch,
+// status strings and the thread-local last-error message.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "fa.h"
+#include "fa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+fa_status fail(fa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+fa_status ok() {
+  g_err.clear();
+  return FA_OK;
+}
+
+constexpr int64_t kMaxPos = 0x7fffffffLL;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool block_ok(int32_t b) { return b == 64 || b == 128; }
+
+// Validates the postfix program; fills the kernel-side copy.
+fa_status check_program(const fa_mask_desc& m, fa::MaskProg* out) {
+  if (m.n < 1 || m.n > FA_MASK_MAX_NODES)
+    return fail(FA_ERR_MASK_SPEC, "mask program must have 1..%d nodes (got %d)", FA_MASK_MAX_NODES, m.n);
+  int depth = 0;
+  int has_doc = 0;
+  for (int t = 0; t < m.n; ++t) {
+    const int op = m.node[t].op;
+    const int a = m.node[t].arg;
+    switch (op) {
+      case FA_M_CAUSAL:
+        depth++;
+        break;
+      case FA_M_SWA:
+        if (a < 1) return fail(FA_ERR_MASK_SPEC, "node %d: sliding window W must be >= 1 (got %d)", t, a);
+        depth++;
+        break;
+      case FA_M_DOC:
+        has_doc = 1;
+        depth++;
+        break;
+      case FA_M_PREFIX:
+        if (a < 0) return fail(FA_ERR_MASK_SPEC, "node %d: prefix length P must be >= 0 (got %d)", t, a);
+        depth++;
+        break;
+      case FA_M_AND:
+      case FA_M_OR:
+        if (depth < 2) return fail(FA_ERR_MASK_SPEC, "node %d: and/or needs two operands", t);
+        depth--;
+        break;
+      default:
+        return fail(FA_ERR_MASK_SPEC, "node %d: unknown mask op %d", t, op);
+    }
+  }
+  if (depth != 1) return fail(FA_ERR_MASK_SPEC, "mask program leaves %d values on the stack (expected 1)", depth);
+  if (out) {
+    out->n = m.n;
+    for (int t = 0; t < FA_MASK_MAX_NODES; ++t) {
+      out->op[t] = t < m.n ? m.node[t].op : 0;
+      out->arg[t] = t < m.n ? m.node[t].arg : 0;
+    }
+    out->has_doc = has_doc;
+  }
+  return FA_OK;
+}
+
+// Geometry and mask checks shared by the builder and the forward.
+fa_status check_mask_geometry(const fa_block_mask* bm, fa::MaskProg* prog) {
+  if (!block_ok(bm->block_q) || !block_ok(bm->block_kv))
+    return fail(FA_ERR_UNSUPPORTED, "block sizes must be 64 or 128 (got %d x %d)", bm->block_q, bm->block_kv);
+  if (bm->B < 1 || bm->H < 1) return fail(FA_ERR_SHAPE, "table extents B, H must be >= 1 (got %d, %d)", bm->B, bm->H);
+  if (bm->q_len < 0 || bm->kv_len < 0 || bm->q_offset < 0)
+    return fail(FA_ERR_SHAPE, "q_len, kv_len and q_offset must be >= 0");
+  if (bm->q_offset + bm->q_len > kMaxPos || bm->kv_len > kMaxPos)
+    return fail(FA_ERR_SHAPE, "positions must stay below 2^31");
+  fa_status s = check_program(bm->mask, prog);
+  if (s != FA_OK) return s;
+  if (prog->has_doc) {
+    const fa_mask_desc& m = bm->mask;
+    if (!m.doc_ids) return fail(FA_ERR_NULL, "document rule needs doc_ids");
+    if (m.doc_batch != 1 && m.doc_batch != bm->B)
+      return fail(FA_ERR_MASK_SPEC, "doc_batch (%d) must be 1 or equal to the table batch extent B (%d)", m.doc_batch,
+                  bm->B);
+    if (m.doc_len < bm->q_offset + bm->q_len || m.doc_len < bm->kv_len)
+      return fail(FA_ERR_SHAPE, "doc_len (%lld) must cover q_offset + q_len and kv_len", (long long)m.doc_len);
+  }
+  return FA_OK;
+}
+
+fa::DocRef doc_ref(const fa_block_mask* bm, const fa::MaskProg& prog) {
+  fa::DocRef d;
+  d.ids = prog.has_doc ? bm->mask.doc_ids : nullptr;
+  d.batch = bm->mask.doc_batch < 1 ? 1 : bm->mask.doc_batch;
+  d.len = bm->mask.doc_len;
+  return d;
+}
+
+int num_cus_of_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
+struct FwdPlan {
+  fa::FwdParams p;
+  bool decode;
+  size_t ws;
+};
+
+fa_status plan_forward(const fa_fwd_args* a, FwdPlan* plan) {
+  if (!a) return fail(FA_ERR_NULL, "args is NULL");
+  if (!a->q || !a->k || !a->v || !a->o || !a->lse) return fail(FA_ERR_NULL, "q, k, v, o and lse must be non-NULL");
+  if (!a->bm) return fail(FA_ERR_NULL, "bm (block tables) is NULL");
+  const fa_block_mask* bm = a->bm;
+  if (a->d != 64 && a->d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 64 or 128 (got %d)", a->d);
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1) return fail(FA_ERR_SHAPE, "B, Hq, Hkv must be >= 1");
+  if (a->Hq % a->Hkv != 0) return fail(FA_ERR_SHAPE, "Hq (%d) must be a multiple of Hkv (%d)", a->Hq, a->Hkv);
+  if (a->q_len < 0 || a->kv_len < 0) return fail(FA_ERR_SHAPE, "q_len and kv_len must be >= 0");
+  fa::MaskProg prog;
+  fa_status s = check_mask_geometry(bm, &prog);
+  if (s != FA_OK) return s;
+  if (bm->q_len != a->q_len || bm->kv_len != a->kv_len)
+    return fail(FA_ERR_MASK_MISMATCH, "block tables were built for q_len=%lld kv_len=%lld, forward has %lld, %lld",
+                (long long)bm->q_len, (long long)bm->kv_len, (long long)a->q_len, (long long)a->kv_len);
+  if (bm->B != 1 && bm->B != a->B)
+    return fail(FA_ERR_MASK_MISMATCH, "table batch extent %d is neither 1 nor B=%d", bm->B, a->B);
+  if (bm->H != 1 && bm->H != a->Hq)
+    return fail(FA_ERR_MASK_MISMATCH, "table head extent %d is neither 1 nor Hq=%d", bm->H, a->Hq);
+  if (prog.has_doc && bm->mask.doc_batch != 1 && bm->mask.doc_batch != a->B)
+    return fail(FA_ERR_MASK_MISMATCH, "doc_batch %d does not match B=%d", bm->mask.doc_batch, a->B);
+  if (!bm->kv_num || !bm->kv_ptr || !bm->kv_idx || !bm->full_kv_num || !bm->full_kv_ptr || !bm->full_kv_idx)
+    return fail(FA_ERR_NULL, "kv-side block tables must be non-NULL");
+  const fa_score_desc& sd = a->score;
+  switch (sd.kind) {
+    case FA_S_IDENTITY:
+      break;
+    case FA_S_ALIBI:
+      if (!sd.alibi_slopes) return fail(FA_ERR_NULL, "ALiBi needs alibi_slopes");
+      break;
+    case FA_S_SOFTCAP:
+      if (!(sd.softcap > 0.f) || !std::isfinite(sd.softcap))
+        return fail(FA_ERR_UNSUPPORTED, "softcap must be a finite value > 0");
+      break;
+    case FA_S_RELPOS:
+      if (!sd.relpos) return fail(FA_ERR_NULL, "relative-position bias needs its table");
+      if (sd.relpos_radius < 0) return fail(FA_ERR_UNSUPPORTED, "relpos_radius must be >= 0");
+      break;
+    default:
+      return fail(FA_ERR_UNSUPPORTED, "unknown score_mod kind %d", sd.kind);
+  }
+  float scale = a->scale;
+  if (std::isnan(scale) || std::isinf(scale)) return fail(FA_ERR_SHAPE, "scale must be finite");
+  if (scale <= 0.f) scale = 1.0f / std::sqrt((float)a->d);
+
+  fa::FwdParams& p = plan->p;
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.k = static_cast<const uint16_t*>(a->k);
+  p.v = static_cast<const uint16_t*>(a->v);
+  p.o = static_cast<uint16_t*>(a->o);
+  p.lse = a->lse;
+  p.B = a->B;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.g = a->Hq / a->Hkv;
+  p.d = a->d;
+  p.q_len = a->q_len;
+  p.kv_len = a->kv_len;
+  p.q_offset = bm->q_offset;
+  p.scale = scale;
+  p.score.kind = sd.kind;
+  p.score.softcap = sd.softcap;
+  p.score.slopes = sd.alibi_slopes;
+  p.score.table = sd.relpos;
+  p.score.radius = sd.relpos_radius;
+  p.prog = prog;
+  p.doc = doc_ref(bm, prog);
+  p.tab.num = bm->kv_num;
+  p.tab.ptr = bm->kv_ptr;
+  p.tab.idx = bm->kv_idx;
+  p.tab.fnum = bm->full_kv_num;
+  p.tab.fptr = bm->full_kv_ptr;
+  p.tab.fidx = bm->full_kv_idx;
+  p.tab.tB = bm->B;
+  p.tab.tH = bm->H;
+  p.tab.nqb = (int32_t)cdiv(a->q_len, bm->block_q);
+  p.tab.nkb = (int32_t)cdiv(a->kv_len, bm->block_kv);
+  p.tab.bq = bm->block_q;
+  p.tab.bk = bm->block_kv;
+  p.nsplit = 1;
+  p.ws = nullptr;
+  plan->decode = a->q_len > 0 && fa::decode_eligible(p);
+  plan->ws = 0;
+  if (plan->decode) {
+    p.nsplit = fa::decode_splits(p, num_cus_of_current_device());
+    plan->ws = fa::decode_workspace_bytes(p, p.nsplit);
+  }
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: inconsistent or unsupported sizes";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim, block size or score kind outside the menu";
+    case FA_ERR_MASK_SPEC: return "FA_ERR_MASK_SPEC: malformed mask program or parameter";
+    case FA_ERR_MASK_MISMATCH: return "FA_ERR_MASK_MISMATCH: block tables do not match the forward's shapes";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error";
+  }
+  return "unknown fa_status";
+}
+
+const char* fa_last_error_message(void) { return g_err.c_str(); }
+
+fa_status fa_block_mask_sizes(const fa_block_mask* bm, int64_t* rows, int64_t* cols, int64_t* idx_capacity,
+                              size_t* workspace_bytes) {
+  if (!bm) return fail(FA_ERR_NULL, "bm is NULL");
+  if (!block_ok(bm->block_q) || !block_ok(bm->block_kv))
+    return fail(FA_ERR_UNSUPPORTED, "block sizes must be 64 or 128 (got %d x %d)", bm->block_q, bm->block_kv);
+  if (bm->B < 1 || bm->H < 1) return fail(FA_ERR_SHAPE, "table extents B, H must be >= 1");
+  if (bm->q_len < 0 || bm->kv_len < 0 || bm->q_offset < 0) return fail(FA_ERR_SHAPE, "negative length or offset");
+  if (bm->q_offset + bm->q_len > kMaxPos || bm->kv_len > kMaxPos) return fail(FA_ERR_SHAPE, "positions must stay below 2^31");
+  const int64_t nqb = cdiv(bm->q_len, bm->block_q);
+  const int64_t nkb = cdiv(bm->kv_len, bm->block_kv);
+  if (rows) *rows = (int64_t)bm->B * bm->H * nqb;
+  if (cols) *cols = (int64_t)bm->B * bm->H * nkb;
+  if (idx_capacity) *idx_capacity = (int64_t)bm->B * bm->H * nqb * nkb;
+  if (workspace_bytes) *workspace_bytes = fa::build_workspace_bytes(bm->B, nqb, nkb);
+  return ok();
+}
+
+fa_status fa_create_block_mask(fa_block_mask* bm, void* workspace, size_t ws_bytes, fa_stream_t stream) {
+  if (!bm) return fail(FA_ERR_NULL, "bm is NULL");
+  fa::MaskProg prog;
+  fa_status s = check_mask_geometry(bm, &prog);
+  if (s != FA_OK) return s;
+  if (!bm->kv_num || !bm->kv_ptr || !bm->kv_idx || !bm->full_kv_num || !bm->full_kv_ptr || !bm->full_kv_idx ||
+      !bm->q_num || !bm->q_ptr || !bm->q_idx || !bm->full_q_num || !bm->full_q_ptr || !bm->full_q_idx)
+    return fail(FA_ERR_NULL, "all twelve table pointers must be non-NULL");
+  const int64_t nqb = cdiv(bm->q_len, bm->block_q);
+  const int64_t nkb = cdiv(bm->kv_len, bm->block_kv);
+  const size_t need = fa::build_workspace_bytes(bm->B, nqb, nkb);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(FA_ERR_WORKSPACE, "builder workspace needs %zu bytes (got %zu)", need, workspace ? ws_bytes : (size_t)0);
+  if (nqb > 0x7fffffff || nkb > 0x7fffffff) return fail(FA_ERR_SHAPE, "too many blocks");
+  fa::BuildParams p;
+  p.prog = prog;
+  p.doc = doc_ref(bm, prog);
+  p.tB = bm->B;
+  p.tH = bm->H;
+  p.q_len = bm->q_len;
+  p.kv_len = bm->kv_len;
+  p.q_offset = bm->q_offset;
+  p.bq = bm->block_q;
+  p.bk = bm->block_kv;
+  p.nqb = (int32_t)nqb;
+  p.nkb = (int32_t)nkb;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  p.grid = ws;
+  const size_t grid_bytes = (size_t)(bm->B * nqb * nkb + 255) & ~(size_t)255;
+  p.qstat = reinterpret_cast<int32_t*>(ws + grid_bytes);
+  p.kstat = p.qstat + (size_t)bm->B * nqb * 2;
+  p.kv_num = bm->kv_num;
+  p.kv_ptr = bm->kv_ptr;
+  p.kv_idx = bm->kv_idx;
+  p.full_kv_num = bm->full_kv_num;
+  p.full_kv_ptr = bm->full_kv_ptr;
+  p.full_kv_idx = bm->full_kv_idx;
+  p.q_num = bm->q_num;
+  p.q_ptr = bm->q_ptr;
+  p.q_idx = bm->q_idx;
+  p.full_q_num = bm->full_q_num;
+  p.full_q_ptr = bm->full_q_ptr;
+  p.full_q_idx = bm->full_q_idx;
+  hipError_t e = fa::launch_build(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "block-mask build launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+fa_status fa_forward_workspace_size(const fa_fwd_args* args, size_t* bytes) {
+  FwdPlan plan;
+  fa_status s = plan_forward(args, &plan);
+  if (s != FA_OK) return s;
+  if (!bytes) return fail(FA_ERR_NULL, "bytes is NULL");
+  *bytes = plan.ws;
+  return ok();
+}
+
+fa_status fa_forward(const fa_fwd_args* args, fa_stream_t stream) {
+  FwdPlan plan;
+  fa_status s = plan_forward(args, &plan);
+  if (s != FA_OK) return s;
+  if (plan.ws > 0) {
+    if (!args->workspace || args->ws_bytes < plan.ws)
+      return fail(FA_ERR_WORKSPACE, "forward workspace needs %zu bytes (got %zu)", plan.ws,
+                  args->workspace ? args->ws_bytes : (size_t)0);
+    plan.p.ws = static_cast<float*>(args->workspace);
+  }
+  if (args->q_len == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = plan.decode ? fa::launch_decode(plan.p, st) : fa::launch_prefill(plan.p, st);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

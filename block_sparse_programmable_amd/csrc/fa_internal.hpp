@@ -1,0 +1,83 @@
+// Internal parameter blocks and launchers shared by the host API and the kernels.
+// Nothing here is part of the public ABI (include/fa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace fa {
+
+// Mask program as passed to kernels (by value, in kernel arguments).
+struct MaskProg {
+  int32_t n;
+  int32_t op[FA_MASK_MAX_NODES];
+  int32_t arg[FA_MASK_MAX_NODES];
+  int32_t has_doc;
+};
+
+struct DocRef {
+  const int32_t* ids;  // [doc_batch, doc_len] or nullptr
+  int32_t batch;
+  int64_t len;
+};
+
+// ---------------------------------------------------------------- builder
+struct BuildParams {
+  MaskProg prog;
+  DocRef doc;
+  int32_t tB, tH;
+  int64_t q_len, kv_len, q_offset;
+  int32_t bq, bk;
+  int32_t nqb, nkb;
+  uint8_t* grid;      // [tB][nqb][nkb] classes
+  int32_t* qstat;     // [tB][nqb][2] doc min/max over the query block
+  int32_t* kstat;     // [tB][nkb][2] doc min/max over the KV block
+  int32_t *kv_num, *kv_ptr, *kv_idx, *full_kv_num, *full_kv_ptr, *full_kv_idx;
+  int32_t *q_num, *q_ptr, *q_idx, *full_q_num, *full_q_ptr, *full_q_idx;
+};
+
+size_t build_workspace_bytes(int64_t tB, int64_t nqb, int64_t nkb);
+hipError_t launch_build(const BuildParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------- forward
+struct ScoreParams {
+  int32_t kind;
+  float softcap;
+  const float* slopes;
+  const float* table;
+  int32_t radius;
+};
+
+struct TableRef {
+  const int32_t *num, *ptr, *idx;             // partial list
+  const int32_t *fnum, *fptr, *fidx;          // full list
+  int32_t tB, tH, nqb, nkb, bq, bk;
+};
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int32_t B, Hq, Hkv, g, d;
+  int64_t q_len, kv_len, q_offset;
+  float scale;
+  ScoreParams score;
+  MaskProg prog;
+  DocRef doc;
+  TableRef tab;
+  // split-KV decode
+  int32_t nsplit;
+  float* ws;  // partial states
+};
+
+bool decode_eligible(const FwdParams& p);
+int32_t decode_splits(const FwdParams& p, int num_cus);
+size_t decode_workspace_bytes(const FwdParams& p, int32_t nsplit);
+hipError_t launch_prefill(const FwdParams& p, hipStream_t s);
+hipError_t launch_decode(const FwdParams& p, hipStream_t s);
+
+}  // namespace fa

@@ -1,0 +1,193 @@
+/*
+ * fa.h -- C ABI of the block-sparse programmable attention library for MI355X (gfx950).
+ *
+ * Two operations, following the interface the pages state for FlexAttention
+ * ("FlexAttention: compiler optimization of custom attention", sections 2, 4 and 5;
+ * "FlexAttention: from rules to fused kernels", sections 1 and 2):
+ *
+ *   fa_create_block_mask  mask rule -> block tables (BCSR rows and their transposes)
+ *   fa_forward            O = softmax(mask(score_mod(Q K^T * scale))) V, plus LSE
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library never
+ *     allocates or frees device memory and keeps no state between calls, apart from
+ *     a thread-local copy of the last error message.
+ *   - All device work is enqueued on `stream` (a hipStream_t; NULL means the null
+ *     stream) without any host synchronisation.  Inputs must stay alive and
+ *     unmodified until that work has completed; this is the caller's duty.
+ *   - Every argument is validated before anything is launched.  On any error
+ *     nothing is written and no work is enqueued; the call returns a status code
+ *     and fa_last_error_message() describes the failure.
+ *   - Tensors are dense and contiguous, in the layouts stated per field.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* fa_stream_t; /* a hipStream_t */
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,          /* a required pointer is NULL                                */
+  FA_ERR_SHAPE = 2,         /* inconsistent or unsupported sizes                           */
+  FA_ERR_UNSUPPORTED = 3,   /* head dim, block size or score kind outside the menu         */
+  FA_ERR_MASK_SPEC = 4,     /* malformed mask program or parameter                         */
+  FA_ERR_MASK_MISMATCH = 5, /* block tables built for other lengths / block sizes          */
+  FA_ERR_WORKSPACE = 6,     /* workspace missing or smaller than required                  */
+  FA_ERR_HIP = 7            /* a HIP runtime call or kernel launch failed                  */
+} fa_status;
+
+/* ----------------------------------------------------------------------------------
+ * Mask rule: a postfix program over a fixed menu of element predicates M(b, i, j),
+ * with i = local query row + q_offset (global position) and j the key position.
+ *
+ *   FA_M_CAUSAL        j <= i
+ *   FA_M_SWA    (W)    j <= i and i - j < W, W >= 1; the window counts the current token
+ *                      ("FlexAttention: compiler optimization of custom attention", sec. 1-2)
+ *   FA_M_DOC           doc[b][i] == doc[b][j], doc IDs captured as an int32 tensor
+ *                      ("FlexAttention: from rules to fused kernels", sec. 1.1)
+ *   FA_M_PREFIX (P)    j < P or j <= i, P >= 0: bidirectional over the first P keys,
+ *                      causal after ("FlexAttention: from rules to fused kernels", sec. 6.3)
+ *   FA_M_AND, FA_M_OR  pop two values, push their intersection / union (and_masks/or_masks,
+ *                      "FlexAttention: from rules to fused kernels", sec. 1.1)
+ *
+ * A well-formed program has 1..16 nodes, never pops an empty stack and leaves exactly
+ * one value.  Decode uses q_offset so that rules see global positions
+ * ("FlexAttention: compiler optimization of custom attention", sec. 6).
+ * -------------------------------------------------------------------------------- */
+enum {
+  FA_M_CAUSAL = 1,
+  FA_M_SWA = 2,
+  FA_M_DOC = 3,
+  FA_M_PREFIX = 4,
+  FA_M_AND = 5,
+  FA_M_OR = 6
+};
+
+#define FA_MASK_MAX_NODES 16
+
+typedef struct {
+  int32_t op;  /* FA_M_* */
+  int32_t arg; /* W for FA_M_SWA, P for FA_M_PREFIX, ignored otherwise */
+} fa_mask_node;
+
+typedef struct {
+  int32_t n;                                /* number of nodes, 1..16                      */
+  fa_mask_node node[FA_MASK_MAX_NODES];     /* postfix order                               */
+  const int32_t* doc_ids;                   /* device int32 [doc_batch, doc_len]; required
+                                               iff the program contains FA_M_DOC           */
+  int32_t doc_batch;                        /* 1 (shared by all batch entries) or B         */
+  int64_t doc_len;                          /* >= q_offset + q_len and >= kv_len            */
+} fa_mask_desc;
+
+/* ----------------------------------------------------------------------------------
+ * Block tables ("BlockMask"): the query/key plane is cut into block_q x block_kv
+ * blocks; each block is EMPTY (no allowed pair), FULL (every in-range pair allowed)
+ * or PARTIAL (otherwise) -- "FlexAttention: from rules to fused kernels", sec. 2.1,
+ * 2.2 and 6.3.  Only in-range pairs (row < q_len, column < kv_len) are considered.
+ *
+ * Table extents B x H: B in {1, B_attn} and H in {1, Hq}; 1 broadcasts.  No rule of
+ * the menu depends on the head, so H > 1 repeats identical rows per head.  A
+ * document rule with doc_batch > 1 needs B == doc_batch.
+ *
+ * KV side (one row per query block, rows ordered (b', h', r), NQB = ceil(q_len/block_q)):
+ *   kv_num[rows]        number of PARTIAL blocks of the row
+ *   kv_ptr[rows + 1]    exclusive prefix sum of kv_num
+ *   kv_idx[...]         their KV block indices, ascending within each row
+ *   full_kv_num / full_kv_ptr / full_kv_idx   the same for FULL blocks
+ * Q side (one row per KV block, ordered (b', h', c), NKB = ceil(kv_len/block_kv)):
+ *   q_num / q_ptr / q_idx, full_q_num / full_q_ptr / full_q_idx  -- the exact
+ *   transposes (query block indices, ascending), used by a backward pass
+ *   ("Kernels: turning logical sparsity into real speed", sec. 4).
+ * Partial and full lists never share a block.  Entries past ptr[rows] are unspecified.
+ * All twelve arrays are caller-owned device int32 buffers sized by fa_block_mask_sizes.
+ * -------------------------------------------------------------------------------- */
+typedef struct {
+  fa_mask_desc mask;
+  int32_t B, H;                     /* table extents                                   */
+  int64_t q_len, kv_len, q_offset;  /* i_global = i + q_offset                          */
+  int32_t block_q, block_kv;        /* each 64 or 128                                   */
+  int32_t *kv_num, *kv_ptr, *kv_idx, *full_kv_num, *full_kv_ptr, *full_kv_idx;
+  int32_t *q_num, *q_ptr, *q_idx, *full_q_num, *full_q_ptr, *full_q_idx;
+} fa_block_mask;
+
+/* Sizes for a block mask: rows = B*H*NQB (length of kv_num; kv_ptr has rows+1),
+ * cols = B*H*NKB (length of q_num; q_ptr has cols+1), idx_capacity = B*H*NQB*NKB
+ * (length to allocate for each of the four idx arrays), workspace_bytes = scratch
+ * needed by fa_create_block_mask.  Reads only the geometry fields; pure host call. */
+fa_status fa_block_mask_sizes(const fa_block_mask* bm, int64_t* rows, int64_t* cols,
+                              int64_t* idx_capacity, size_t* workspace_bytes);
+
+/* Classify every block exactly and write all twelve arrays of *bm on `stream`.
+ * `workspace` is a device buffer of at least workspace_bytes (its contents on entry
+ * are ignored and on exit unspecified).  Deterministic: the same inputs always give
+ * the same tables bit for bit. */
+fa_status fa_create_block_mask(fa_block_mask* bm, void* workspace, size_t ws_bytes,
+                               fa_stream_t stream);
+
+/* ----------------------------------------------------------------------------------
+ * Score modification, applied to the scaled score s = (q . k) * scale of every pair
+ * in an executed block, before masking to -inf
+ * ("FlexAttention: compiler optimization of custom attention", sec. 2):
+ *   FA_S_IDENTITY  s
+ *   FA_S_ALIBI     s + slope[h_q] * (j - i)          (slopes: device fp32 [Hq])
+ *   FA_S_SOFTCAP   softcap * tanh(s / softcap)        (softcap > 0)
+ *   FA_S_RELPOS    s + table[h_q][clip(i - j, -R, R) + R]   (device fp32 [Hq, 2R+1], R >= 0)
+ * ALiBi and the relative-position table are indexed by the QUERY head
+ * ("FlexAttention: from rules to fused kernels", sec. 1.2); i and j are global positions.
+ * -------------------------------------------------------------------------------- */
+enum { FA_S_IDENTITY = 0, FA_S_ALIBI = 1, FA_S_SOFTCAP = 2, FA_S_RELPOS = 3 };
+
+typedef struct {
+  int32_t kind;
+  float softcap;
+  const float* alibi_slopes;
+  const float* relpos;
+  int32_t relpos_radius;
+} fa_score_desc;
+
+/* ----------------------------------------------------------------------------------
+ * Forward.  q: bf16 [B, Hq, q_len, d]; k, v: bf16 [B, Hkv, kv_len, d]; o: bf16
+ * [B, Hq, q_len, d]; lse: fp32 [B, Hq, q_len], natural-log log-sum-exp of the modified,
+ * masked row.  GQA/MQA: Hq % Hkv == 0 and query head h reads KV head h / (Hq/Hkv)
+ * ("FlexAttention: from rules to fused kernels", sec. 1.2).  d in {64, 128}.
+ * scale <= 0 selects 1/sqrt(d).  Only the KV blocks listed in *bm are visited; the
+ * mask rule is evaluated only on PARTIAL blocks (and on the ragged last block).
+ * A row with no allowed key gets O = 0 and LSE = -inf.
+ * bm must have been built for the same q_len, kv_len (and B/H extents compatible
+ * with B and Hq); q_offset is taken from bm.
+ * Short queries (one query block, (Hq/Hkv) * q_len <= 32, block_kv == 128) take a
+ * split-KV path that needs `workspace` of fa_forward_workspace_size bytes; every other
+ * shape needs none (workspace may then be NULL).
+ * -------------------------------------------------------------------------------- */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int32_t B, Hq, Hkv, d;
+  int64_t q_len, kv_len;
+  float scale;
+  fa_score_desc score;
+  const fa_block_mask* bm;
+  void* workspace;
+  size_t ws_bytes;
+} fa_fwd_args;
+
+fa_status fa_forward_workspace_size(const fa_fwd_args* args, size_t* bytes);
+fa_status fa_forward(const fa_fwd_args* args, fa_stream_t stream);
+
+const char* fa_status_string(fa_status s);
+const char* fa_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FA_H_ */

@@ -1,0 +1,187 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/fa.h declares, the ctypes structures match the C layout, and argument
+validation rejects bad inputs before any device work (no compute calls)."""
+import ctypes as C
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_sparse_programmable_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        from block_sparse_programmable_amd import build
+        build.build()
+    return L.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(fa_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    from block_sparse_programmable_amd import _lib as L
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+LAYOUT_C = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "fa.h"
+#define P(T, F) printf(#T "." #F " %zu\n", offsetof(T, F));
+int main(void) {
+  printf("fa_mask_desc %zu\nfa_block_mask %zu\nfa_score_desc %zu\nfa_fwd_args %zu\n",
+         sizeof(fa_mask_desc), sizeof(fa_block_mask), sizeof(fa_score_desc), sizeof(fa_fwd_args));
+  P(fa_mask_desc, doc_ids) P(fa_mask_desc, doc_batch) P(fa_mask_desc, doc_len)
+  P(fa_block_mask, B) P(fa_block_mask, q_len) P(fa_block_mask, q_offset) P(fa_block_mask, block_kv)
+  P(fa_block_mask, kv_num) P(fa_block_mask, full_q_idx)
+  P(fa_score_desc, softcap) P(fa_score_desc, relpos) P(fa_score_desc, relpos_radius)
+  P(fa_fwd_args, lse) P(fa_fwd_args, d) P(fa_fwd_args, q_len) P(fa_fwd_args, scale)
+  P(fa_fwd_args, score) P(fa_fwd_args, bm) P(fa_fwd_args, ws_bytes)
+  return 0;
+}
+"""
+
+
+def test_struct_layout_matches_header():
+    from block_sparse_programmable_amd import _lib as L
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(src, "w").write(LAYOUT_C)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), src, "-o", exe], check=True)
+        lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = dict(l.rsplit(" ", 1) for l in lines if l)
+    structs = {"fa_mask_desc": L.fa_mask_desc, "fa_block_mask": L.fa_block_mask,
+               "fa_score_desc": L.fa_score_desc, "fa_fwd_args": L.fa_fwd_args}
+    for k, v in got.items():
+        if "." in k:
+            s, f = k.split(".")
+            assert getattr(structs[s], f).offset == int(v), k
+        else:
+            assert C.sizeof(structs[k]) == int(v), k
+
+
+def _bm(L, **kw):
+    from block_sparse_programmable_amd.api import block_mask_desc
+    args = dict(mask=("causal",), B=1, H=1, q_len=256, kv_len=256, block_q=128, block_kv=128)
+    args.update(kw)
+    d, _ = block_mask_desc(**args)
+    return d
+
+
+def test_block_mask_sizes(lib):
+    from block_sparse_programmable_amd import _lib as L
+    from block_sparse_programmable_amd.api import block_mask_sizes
+    d = _bm(L, B=2, H=3, q_len=300, kv_len=1000, block_q=64, block_kv=128)
+    rows, cols, cap, ws = block_mask_sizes(d)
+    assert rows == 2 * 3 * 5 and cols == 2 * 3 * 8 and cap == 2 * 3 * 5 * 8 and ws > 0
+
+
+def _status(fn, *a):
+    return fn(*a)
+
+
+def test_validation_errors_before_any_launch(lib):
+    from block_sparse_programmable_amd import _lib as L
+    # builder: bad block size, bad program, missing doc IDs, missing tables, workspace
+    d = _bm(L, block_q=96)
+    assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_UNSUPPORTED
+    assert b"64 or 128" in lib.fa_last_error_message()
+    d = _bm(L)
+    d.mask.n = 2                                  # causal, causal: two values left
+    d.mask.node[1].op = L.FA_M_CAUSAL
+    assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_MASK_SPEC
+    d = _bm(L, mask=("swa", 0))
+    assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_MASK_SPEC
+    d = _bm(L, mask=("prefix", -1))
+    assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_MASK_SPEC
+    d = _bm(L)
+    d.mask.node[0].op = 99
+    assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_MASK_SPEC
+    d = _bm(L)
+    d.mask.n = 1
+    d.mask.node[0].op = L.FA_M_AND
+    assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_MASK_SPEC
+    d = _bm(L, mask=("doc",))
+    assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_NULL
+    d = _bm(L)
+    assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_NULL   # no tables
+    for name in ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx",
+                 "q_num", "q_ptr", "q_idx", "full_q_num", "full_q_ptr", "full_q_idx"):
+        setattr(d, name, 0x1000)                  # never dereferenced: rejected first
+    assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_WORKSPACE
+    assert lib.fa_create_block_mask(C.byref(d), C.c_void_p(0x2000), 1, None) == L.FA_ERR_WORKSPACE
+    d = _bm(L, q_len=-1)
+    assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_SHAPE
+    d = _bm(L, q_offset=2 ** 31 - 10, q_len=100)
+    assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_SHAPE
+
+
+def _fwd(L, bm, **kw):
+    a = L.fa_fwd_args()
+    a.q = a.k = a.v = a.o = a.lse = 0x1000
+    a.B, a.Hq, a.Hkv, a.d = 1, 4, 2, 128
+    a.q_len, a.kv_len = 256, 256
+    a.bm = C.pointer(bm)
+    for k, v in kw.items():
+        if k.startswith("score_"):
+            setattr(a.score, k[6:], v)
+        else:
+            setattr(a, k, v)
+    return a
+
+
+def test_forward_validation(lib):
+    from block_sparse_programmable_amd import _lib as L
+    bm = _bm(L)
+    for name in ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx"):
+        setattr(bm, name, 0x1000)
+    F = lambda a: lib.fa_forward(C.byref(a), None)
+    assert lib.fa_forward(None, None) == L.FA_ERR_NULL
+    assert F(_fwd(L, bm, q=None)) == L.FA_ERR_NULL
+    assert F(_fwd(L, bm, d=96)) == L.FA_ERR_UNSUPPORTED
+    assert F(_fwd(L, bm, Hkv=3)) == L.FA_ERR_SHAPE
+    assert F(_fwd(L, bm, q_len=128)) == L.FA_ERR_MASK_MISMATCH
+    assert F(_fwd(L, bm, kv_len=512)) == L.FA_ERR_MASK_MISMATCH
+    assert F(_fwd(L, bm, score_kind=7)) == L.FA_ERR_UNSUPPORTED
+    assert F(_fwd(L, bm, score_kind=L.FA_S_ALIBI)) == L.FA_ERR_NULL
+    assert F(_fwd(L, bm, score_kind=L.FA_S_SOFTCAP, score_softcap=0.0)) == L.FA_ERR_UNSUPPORTED
+    assert F(_fwd(L, bm, score_kind=L.FA_S_RELPOS)) == L.FA_ERR_NULL
+    assert F(_fwd(L, bm, score_kind=L.FA_S_RELPOS, score_relpos=0x1000,
+                  score_relpos_radius=-1)) == L.FA_ERR_UNSUPPORTED
+    assert F(_fwd(L, bm, scale=float("nan"))) == L.FA_ERR_SHAPE
+    bm2 = _bm(L, B=3)
+    for name in ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx"):
+        setattr(bm2, name, 0x1000)
+    assert F(_fwd(L, bm2)) == L.FA_ERR_MASK_MISMATCH
+    bm3 = _bm(L, H=2)
+    for name in ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx"):
+        setattr(bm3, name, 0x1000)
+    assert F(_fwd(L, bm3)) == L.FA_ERR_MASK_MISMATCH
+    bm.kv_idx = None
+    assert F(_fwd(L, bm)) == L.FA_ERR_NULL
+    for s in range(8):
+        assert lib.fa_status_string(s)
+
+
+def test_compile_mask_postfix():
+    from block_sparse_programmable_amd import _lib as L
+    from block_sparse_programmable_amd.api import compile_mask
+    prog = compile_mask(("and", ("doc",), ("or", ("swa", 7), ("prefix", 3))))
+    assert prog == [(L.FA_M_DOC, 0), (L.FA_M_SWA, 7), (L.FA_M_PREFIX, 3), (L.FA_M_OR, 0), (L.FA_M_AND, 0)]
