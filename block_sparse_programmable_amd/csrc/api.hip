@@ -2,6 +2,7 @@
 // status strings and the thread-local last-error message.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -77,6 +78,24 @@ fa_status check_program(const fa_mask_desc& m, fa::MaskProg* out) {
       out->arg[t] = t < m.n ? m.node[t].arg : 0;
     }
     out->has_doc = has_doc;
+    // An and-only tree of interval leaves is one key interval per row: causal and window
+    // bound it above by i, the window below by i - W + 1, prefixes above by max(P-1, i).
+    bool and_only = true;
+    int wmin = 0, hi_self = 0, pmin = -1;
+    for (int t = 0; t < m.n; ++t) {
+      const int op = m.node[t].op, a = m.node[t].arg;
+      if (op == FA_M_OR) and_only = false;
+      if (op == FA_M_CAUSAL) hi_self = 1;
+      if (op == FA_M_SWA) {
+        hi_self = 1;
+        wmin = wmin == 0 ? a : std::min(wmin, a);
+      }
+      if (op == FA_M_PREFIX) pmin = pmin < 0 ? a : std::min(pmin, a);
+    }
+    out->mk = and_only ? (has_doc ? fa::MK_INTERVAL_DOC : fa::MK_INTERVAL) : fa::MK_GENERIC;
+    out->wmin = wmin;
+    out->hi_self = hi_self;
+    out->pmin = pmin;
   }
   return FA_OK;
 }

@@ -9,12 +9,26 @@
 
 namespace fa {
 
+// How a kernel evaluates the element mask on partial blocks.
+enum MaskKind : int32_t {
+  MK_INTERVAL = 0,      // and-tree of causal / window / prefix: one key interval per row
+  MK_INTERVAL_DOC = 1,  // the same intersected with document equality
+  MK_GENERIC = 2        // anything with an or-node: postfix interpreter per element
+};
+
 // Mask program as passed to kernels (by value, in kernel arguments).
 struct MaskProg {
   int32_t n;
   int32_t op[FA_MASK_MAX_NODES];
   int32_t arg[FA_MASK_MAX_NODES];
   int32_t has_doc;
+  // interval form (MK_INTERVAL*): allowed keys of global row i are [lo(i), hi(i)] with
+  // lo = max(0, i - wmin + 1) if wmin > 0 else 0, hi = i if hi_self, else
+  // max(pmin - 1, i) if pmin >= 0, else unbounded
+  int32_t mk;
+  int32_t wmin;
+  int32_t hi_self;
+  int32_t pmin;
 };
 
 struct DocRef {
