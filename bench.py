@@ -225,6 +225,19 @@ def run(args):
     return rec
 
 
+def copy_calibration(mib):
+    """A plain device-to-device copy of known size (for scaling HBM byte counters)."""
+    import torch
+    torch.cuda.set_device(0)
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,7 +246,12 @@ def main(argv=None):
     ap.add_argument("--workload", default="causal_softcap")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args(argv)
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration(args.copy_calibration)))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this library has no multi-GPU path "
               f"(--gpus {args.gpus} requested); run with --gpus 1", file=sys.stderr)

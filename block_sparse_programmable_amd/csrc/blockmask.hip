@@ -24,13 +24,17 @@
 // pair with ballots (early exit once both an allowed and a disallowed pair are seen).
 // No conservative answer is ever emitted.
 //
-// Launches (all on the caller's stream, no host synchronisation):
+// Grids of at most 16384 blocks are built by one workgroup in a single launch with all
+// intermediates in LDS.  Larger grids use five launches (all on the caller's stream,
+// no host synchronisation):
 //   1. doc_stats   (only with a document rule) doc-ID min/max per query/KV block
 //   2. classify    one lane per block, then the wave resolves its undecided blocks
 //   3. count       one wave per row and per column: partial/full counts (ballot+popcount)
 //   4. scan        one workgroup: exclusive prefix sums of the four count arrays
 //   5. scatter     one wave per row and per column: ordered compaction (ballot+mbcnt)
-// Nothing uses atomics, so the tables are bit-for-bit deterministic.
+// No output position depends on an atomic or on scheduling order (the single-workgroup
+// path collects undecided blocks in an LDS list whose order does not matter), so the
+// tables are bit-for-bit deterministic.
 #include "device_common.hpp"
 #include "fa_internal.hpp"
 
@@ -70,7 +74,7 @@ __device__ __forceinline__ BlockGeom geom(const BuildParams& p, int r, int c) {
   return g;
 }
 
-__device__ int classify_bounds(const BuildParams& p, const BlockGeom& g, int tb, int r, int c) {
+__device__ int classify_bounds(const BuildParams& p, const BlockGeom& g, const int32_t* qs, const int32_t* ks) {
   int st[FA_MASK_MAX_NODES];
   int sp = 0;
   for (int t = 0; t < p.prog.n; ++t) {
@@ -87,8 +91,6 @@ __device__ int classify_bounds(const BuildParams& p, const BlockGeom& g, int tb,
       const int64_t hi_a = max(a - 1, g.a), hi_b = max(a - 1, g.bb);
       v = (g.c1 <= hi_a) ? VT : (g.c0 > hi_b ? VF : VM);
     } else if (op == FA_M_DOC) {
-      const int32_t* qs = p.qstat + ((int64_t)tb * p.nqb + r) * 2;
-      const int32_t* ks = p.kstat + ((int64_t)tb * p.nkb + c) * 2;
       const int qmin = qs[0], qmax = qs[1], kmin = ks[0], kmax = ks[1];
       if (qmin == qmax && kmin == kmax && qmin == kmin) v = VT;
       else if (qmax < kmin || kmax < qmin) v = VF;
@@ -96,13 +98,7 @@ __device__ int classify_bounds(const BuildParams& p, const BlockGeom& g, int tb,
     } else {
       sp -= 2;
       const int x = st[sp], y = st[sp + 1];
-      if (op == FA_M_AND) {
-        v = v_and(x, y);
-        if (v == VM && x == VM && y == VM) v = VU;
-      } else {
-        v = v_or(x, y);
-        if (v == VM && x == VM && y == VM) v = VU;
-      }
+      v = (op == FA_M_AND) ? v_and(x, y) : v_or(x, y);
     }
     st[sp++] = v;
   }
@@ -148,21 +144,68 @@ __global__ __launch_bounds__(256) void doc_stats_kernel(BuildParams p) {
   }
 }
 
+// Exact class of one block, decided by the whole wave: lanes cover the block's
+// columns, rows are walked in order with their document IDs held in registers and
+// broadcast by readlane; stops as soon as both an allowed and a disallowed in-range
+// pair have been seen.  And-only programs test each pair against the row's compiled
+// key interval plus the document compare; programs with an or-node use the interpreter.
+__device__ uint8_t exact_block(const BuildParams& p, int tb, int r, int c, int lane) {
+  const BlockGeom g = geom(p, r, c);
+  const int32_t* d = doc_row(p.doc, tb);
+  const int nrows = (int)(g.bb - g.a + 1);
+  const int ncols = (int)(g.c1 - g.c0 + 1);
+  const int a = (int)g.a;
+  const int j0 = (int)g.c0 + lane;
+  const int j1 = j0 + 64;
+  const bool ok0 = lane < ncols, ok1 = lane + 64 < ncols;
+  int dj0 = 0, dj1 = 0, dr0 = 0, dr1 = 0;
+  if (p.prog.has_doc) {
+    if (ok0) dj0 = d[j0];
+    if (ok1) dj1 = d[j1];
+    if (lane < nrows) dr0 = d[a + lane];
+    if (lane + 64 < nrows) dr1 = d[a + 64 + lane];
+  }
+  const bool interval_form = p.prog.mk != MK_GENERIC;
+  bool seen_t = false, seen_f = false;
+  for (int ri = 0; ri < nrows; ++ri) {
+    const int ii = a + ri;
+    const int di = p.prog.has_doc ? __builtin_amdgcn_readlane(ri < 64 ? dr0 : dr1, ri & 63) : 0;
+    bool m0, m1;
+    if (interval_form) {
+      // allowed keys of row ii: [lo, hi] (uniform across the wave)
+      const int lo = p.prog.wmin > 0 ? max(0, ii - p.prog.wmin + 1) : 0;
+      const int hi = p.prog.hi_self ? ii : (p.prog.pmin >= 0 ? max(p.prog.pmin - 1, ii) : 0x7fffffff);
+      m0 = ok0 && j0 >= lo && j0 <= hi && dj0 == di;
+      m1 = ok1 && j1 >= lo && j1 <= hi && dj1 == di;
+    } else {
+      m0 = ok0 && mask_allowed(p.prog, ii, j0, di, dj0);
+      m1 = ok1 && mask_allowed(p.prog, ii, j1, di, dj1);
+    }
+    seen_t = seen_t || (__ballot(m0 || m1) != 0);
+    seen_f = seen_f || (__ballot((ok0 && !m0) || (ok1 && !m1)) != 0);
+    if (seen_t && seen_f) break;
+  }
+  return seen_t ? (seen_f ? kPartial : kFull) : kEmpty;
+}
+
+constexpr int kClassifyPerWave = 16;   // blocks decided per wave (fast path on 16 lanes)
+
 __global__ __launch_bounds__(256) void classify_kernel(BuildParams p) {
   const int64_t total = (int64_t)p.tB * p.nqb * p.nkb;
-  const int64_t wave_base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;
+  const int64_t wave_base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kClassifyPerWave;
   const int lane = threadIdx.x & 63;
   if (wave_base >= total) return;
   const int64_t id = wave_base + lane;
   int val = VF;
   int tb = 0, r = 0, c = 0;
-  const bool valid = id < total;
+  const bool valid = lane < kClassifyPerWave && id < total;
   if (valid) {
     tb = (int)(id / ((int64_t)p.nqb * p.nkb));
     const int64_t rem = id - (int64_t)tb * p.nqb * p.nkb;
     r = (int)(rem / p.nkb);
     c = (int)(rem - (int64_t)r * p.nkb);
-    val = classify_bounds(p, geom(p, r, c), tb, r, c);
+    val = classify_bounds(p, geom(p, r, c), p.qstat + ((int64_t)tb * p.nqb + r) * 2,
+                          p.kstat + ((int64_t)tb * p.nkb + c) * 2);
     if (val != VU) p.grid[id] = val == VT ? kFull : (val == VF ? kEmpty : kPartial);
   }
   // exact evaluation of undecided blocks, one block at a time with the whole wave
@@ -171,28 +214,8 @@ __global__ __launch_bounds__(256) void classify_kernel(BuildParams p) {
     const int src = __builtin_ctzll(pending);
     pending &= pending - 1;
     const int ub = __shfl(tb, src), ur = __shfl(r, src), uc = __shfl(c, src);
-    const BlockGeom g = geom(p, ur, uc);
-    const int32_t* d = doc_row(p.doc, ub);
-    const int ncols = (int)(g.c1 - g.c0 + 1);
-    const int j0 = (int)g.c0 + lane;
-    const int j1 = j0 + 64;
-    const bool ok0 = lane < ncols, ok1 = lane + 64 < ncols;
-    const int dj0 = (p.prog.has_doc && ok0) ? d[j0] : 0;
-    const int dj1 = (p.prog.has_doc && ok1) ? d[j1] : 0;
-    bool seen_t = false, seen_f = false;
-    for (int64_t i = g.a; i <= g.bb; ++i) {
-      const int ii = (int)i;
-      const int di = p.prog.has_doc ? d[ii] : 0;
-      const bool m0 = ok0 && mask_allowed(p.prog, ii, j0, di, dj0);
-      const bool m1 = ok1 && mask_allowed(p.prog, ii, j1, di, dj1);
-      seen_t = seen_t || (__ballot(m0 || m1) != 0);
-      seen_f = seen_f || (__ballot((ok0 && !m0) || (ok1 && !m1)) != 0);
-      if (seen_t && seen_f) break;
-    }
-    if (lane == 0) {
-      const int64_t uid = ((int64_t)ub * p.nqb + ur) * p.nkb + uc;
-      p.grid[uid] = seen_t ? (seen_f ? kPartial : kFull) : kEmpty;
-    }
+    const uint8_t cls = exact_block(p, ub, ur, uc, lane);
+    if (lane == 0) p.grid[((int64_t)ub * p.nqb + ur) * p.nkb + uc] = cls;
   }
 }
 
@@ -299,6 +322,200 @@ __global__ __launch_bounds__(256) void scatter_kernel(BuildParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Small grids: the whole build in one workgroup of 16 waves, intermediates in LDS.
+// Same phases and the same per-block decisions as the multi-launch path.
+// ---------------------------------------------------------------------------------
+constexpr int kSmallMaxBlocks = 16384;  // tB * NQB * NKB
+constexpr int kSmallMaxLines = 2048;    // tB * (NQB + NKB)
+constexpr int kSmallMaxTB = 64;
+
+__global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
+  __shared__ uint8_t grid_s[kSmallMaxBlocks];
+  __shared__ int32_t stat_s[2 * kSmallMaxLines];   // doc min/max: query blocks, then KV blocks
+  __shared__ int32_t cnt_s[2 * kSmallMaxLines];    // partial/full counts: rows, then columns
+  __shared__ int32_t pre_s[2 * kSmallMaxLines];    // exclusive prefix of cnt_s within each tb
+  __shared__ int32_t tot_s[4 * kSmallMaxTB];       // per tb: rows partial/full, cols partial/full
+  __shared__ int32_t cum_s[4 * (kSmallMaxTB + 1)]; // prefix over tb of tH * tot_s
+  __shared__ int32_t list_s[kSmallMaxBlocks];      // undecided block ids
+  __shared__ int32_t n_undecided;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nq = p.tB * p.nqb, nk = p.tB * p.nkb, nl = nq + nk;
+  const int total = p.tB * p.nqb * p.nkb;
+
+  // phase 1: document-ID ranges per query block and per KV block
+  if (p.prog.has_doc) {
+    for (int line = wv; line < nl; line += 16) {
+      const bool qside = line < nq;
+      const int idx = qside ? line : line - nq;
+      const int tb = qside ? idx / p.nqb : idx / p.nkb;
+      const int blk = qside ? idx - tb * p.nqb : idx - tb * p.nkb;
+      const int32_t* d = doc_row(p.doc, tb);
+      int64_t lo, hi;
+      if (qside) {
+        lo = (int64_t)blk * p.bq + p.q_offset;
+        hi = min((int64_t)(blk + 1) * p.bq, p.q_len) + p.q_offset;
+      } else {
+        lo = (int64_t)blk * p.bk;
+        hi = min((int64_t)(blk + 1) * p.bk, p.kv_len);
+      }
+      int mn = 0x7fffffff, mx = (int)0x80000000;
+      for (int64_t x = lo + lane; x < hi; x += 64) {
+        const int v = d[x];
+        mn = min(mn, v);
+        mx = max(mx, v);
+      }
+      for (int off = 32; off > 0; off >>= 1) {
+        mn = min(mn, __shfl_xor(mn, off));
+        mx = max(mx, __shfl_xor(mx, off));
+      }
+      if (lane == 0) {
+        stat_s[2 * line] = mn;
+        stat_s[2 * line + 1] = mx;
+      }
+    }
+  }
+  __syncthreads();
+
+  // phase 2: bounds classification, one thread per block; undecided blocks go to a
+  // list (its order is irrelevant: each entry's class is decided on its own)
+  if (tid == 0) n_undecided = 0;
+  __syncthreads();
+  for (int id = tid; id < total; id += 1024) {
+    const int tb = id / (p.nqb * p.nkb);
+    const int rem = id - tb * p.nqb * p.nkb;
+    const int r = rem / p.nkb, c = rem - r * p.nkb;
+    const int v = classify_bounds(p, geom(p, r, c), stat_s + 2 * (tb * p.nqb + r), stat_s + 2 * (nq + tb * p.nkb + c));
+    grid_s[id] = v == VU ? kEmpty : (v == VT ? kFull : (v == VF ? kEmpty : kPartial));
+    if (v == VU) list_s[atomicAdd(&n_undecided, 1)] = id;
+  }
+  __syncthreads();
+
+  // phase 3: exact evaluation of the undecided blocks, spread over the 16 waves
+  const int nu = n_undecided;
+  for (int k = wv; k < nu; k += 16) {
+    const int uid = list_s[k];
+    const int tb = uid / (p.nqb * p.nkb);
+    const int rem = uid - tb * p.nqb * p.nkb;
+    const int r = rem / p.nkb, c = rem - r * p.nkb;
+    const uint8_t cls = exact_block(p, tb, r, c, lane);
+    if (lane == 0) grid_s[uid] = cls;
+  }
+  __syncthreads();
+
+  // phase 4: partial / full counts per row (tb, r) and per column (tb, c)
+  for (int line = wv; line < nl; line += 16) {
+    const bool rowside = line < nq;
+    const int idx = rowside ? line : line - nq;
+    const int tb = rowside ? idx / p.nqb : idx / p.nkb;
+    const int k = rowside ? idx - tb * p.nqb : idx - tb * p.nkb;
+    const int n = rowside ? p.nkb : p.nqb;
+    const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
+    int np = 0, nf = 0;
+    for (int x0 = 0; x0 < n; x0 += 64) {
+      const int x = x0 + lane;
+      uint8_t v = kEmpty;
+      if (x < n) v = rowside ? g[k * p.nkb + x] : g[x * p.nkb + k];
+      np += __popcll(__ballot(v == kPartial));
+      nf += __popcll(__ballot(v == kFull));
+    }
+    if (lane == 0) {
+      cnt_s[2 * line] = np;
+      cnt_s[2 * line + 1] = nf;
+    }
+  }
+  __syncthreads();
+
+  // phase 5: exclusive prefix within each tb; one wave per (tb, side, kind) sequence
+  for (int sq = wv; sq < 4 * p.tB; sq += 16) {
+    const int tb = sq >> 2, side = (sq >> 1) & 1, kind = sq & 1;
+    const int n = side == 0 ? p.nqb : p.nkb;
+    const int first = side == 0 ? tb * p.nqb : nq + tb * p.nkb;
+    int carry = 0;
+    for (int x0 = 0; x0 < n; x0 += 64) {
+      const int x = x0 + lane;
+      const int v = x < n ? cnt_s[2 * (first + x) + kind] : 0;
+      int incl = v;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      if (x < n) pre_s[2 * (first + x) + kind] = carry + incl - v;
+      carry += __shfl(incl, 63);
+    }
+    if (lane == 0) tot_s[4 * tb + 2 * side + kind] = carry;
+  }
+  __syncthreads();
+  if (tid < 4) {
+    int acc = 0;
+    for (int tb = 0; tb < p.tB; ++tb) {
+      cum_s[4 * tb + tid] = acc;
+      acc += p.tH * tot_s[4 * tb + tid];
+    }
+    cum_s[4 * p.tB + tid] = acc;
+  }
+  __syncthreads();
+
+  // phase 6: counts and pointers for every replicated head, then ordered scatter
+  const int rows = p.tB * p.tH * p.nqb, cols = p.tB * p.tH * p.nkb;
+  for (int x = tid; x < rows + cols; x += 1024) {
+    const bool rowside = x < rows;
+    const int idx = rowside ? x : x - rows;
+    const int per = rowside ? p.nqb : p.nkb;
+    const int bh = idx / per, k = idx - bh * per;
+    const int tb = bh / p.tH, h = bh - tb * p.tH;
+    const int line = rowside ? tb * p.nqb + k : nq + tb * p.nkb + k;
+    const int side = rowside ? 0 : 1;
+    const int np_ = cnt_s[2 * line], nf_ = cnt_s[2 * line + 1];
+    const int pp = cum_s[4 * tb + 2 * side] + h * tot_s[4 * tb + 2 * side] + pre_s[2 * line];
+    const int pf = cum_s[4 * tb + 2 * side + 1] + h * tot_s[4 * tb + 2 * side + 1] + pre_s[2 * line + 1];
+    if (rowside) {
+      p.kv_num[idx] = np_;
+      p.kv_ptr[idx] = pp;
+      p.full_kv_num[idx] = nf_;
+      p.full_kv_ptr[idx] = pf;
+    } else {
+      p.q_num[idx] = np_;
+      p.q_ptr[idx] = pp;
+      p.full_q_num[idx] = nf_;
+      p.full_q_ptr[idx] = pf;
+    }
+  }
+  if (tid == 0) {
+    p.kv_ptr[rows] = cum_s[4 * p.tB + 0];
+    p.full_kv_ptr[rows] = cum_s[4 * p.tB + 1];
+    p.q_ptr[cols] = cum_s[4 * p.tB + 2];
+    p.full_q_ptr[cols] = cum_s[4 * p.tB + 3];
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int x = wv; x < rows + cols; x += 16) {
+    const bool rowside = x < rows;
+    const int idx = rowside ? x : x - rows;
+    const int per = rowside ? p.nqb : p.nkb;
+    const int bh = idx / per, k = idx - bh * per;
+    const int tb = bh / p.tH, h = bh - tb * p.tH;
+    const int line = rowside ? tb * p.nqb + k : nq + tb * p.nkb + k;
+    const int side = rowside ? 0 : 1;
+    const int pp = cum_s[4 * tb + 2 * side] + h * tot_s[4 * tb + 2 * side] + pre_s[2 * line];
+    const int pf = cum_s[4 * tb + 2 * side + 1] + h * tot_s[4 * tb + 2 * side + 1] + pre_s[2 * line + 1];
+    int32_t* pout = (rowside ? p.kv_idx : p.q_idx) + pp;
+    int32_t* fout = (rowside ? p.full_kv_idx : p.full_q_idx) + pf;
+    const int n = rowside ? p.nkb : p.nqb;
+    const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
+    for (int x0 = 0; x0 < n; x0 += 64) {
+      const int y = x0 + lane;
+      uint8_t v = kEmpty;
+      if (y < n) v = rowside ? g[k * p.nkb + y] : g[y * p.nkb + k];
+      const uint64_t bp = __ballot(v == kPartial);
+      const uint64_t bf = __ballot(v == kFull);
+      if (v == kPartial) pout[__popcll(bp & below)] = y;
+      if (v == kFull) fout[__popcll(bf & below)] = y;
+      pout += __popcll(bp);
+      fout += __popcll(bf);
+    }
+  }
+}
+
 inline unsigned waves_to_blocks(int64_t waves) { return (unsigned)((waves + 3) / 4); }
 
 }  // namespace
@@ -312,10 +529,16 @@ size_t build_workspace_bytes(int64_t tB, int64_t nqb, int64_t nkb) {
 hipError_t launch_build(const BuildParams& p, hipStream_t s) {
   const int64_t total = (int64_t)p.tB * p.nqb * p.nkb;
   if (total == 0) return hipSuccess;
+  const int64_t lines = (int64_t)p.tB * (p.nqb + p.nkb);
+  const int64_t expanded = (int64_t)p.tB * p.tH * (p.nqb + p.nkb);
+  if (total <= kSmallMaxBlocks && lines <= kSmallMaxLines && p.tB <= kSmallMaxTB && expanded <= (1 << 20)) {
+    hipLaunchKernelGGL(build_small_kernel, dim3(1), dim3(1024), 0, s, p);
+    return hipGetLastError();
+  }
   if (p.prog.has_doc) {
     hipLaunchKernelGGL(doc_stats_kernel, dim3(waves_to_blocks((int64_t)p.tB * (p.nqb + p.nkb))), dim3(256), 0, s, p);
   }
-  hipLaunchKernelGGL(classify_kernel, dim3(waves_to_blocks((total + 63) / 64)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(classify_kernel, dim3(waves_to_blocks((total + kClassifyPerWave - 1) / kClassifyPerWave)), dim3(256), 0, s, p);
   hipLaunchKernelGGL(count_kernel, dim3(waves_to_blocks((int64_t)p.tB * (p.nqb + p.nkb))), dim3(256), 0, s, p);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, p);
   hipLaunchKernelGGL(scatter_kernel, dim3(waves_to_blocks((int64_t)p.tB * p.tH * (p.nqb + p.nkb))), dim3(256), 0, s, p);

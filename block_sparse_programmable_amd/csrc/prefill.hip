@@ -18,12 +18,16 @@
 //     the lane apart from one exchange between the two 32-lane halves.
 //   * O is accumulated transposed as well (O^T = V^T P^T): P^T in the MFMA output
 //     layout feeds the B operand directly once the key order inside each 16-key step
-//     is permuted; V^T is stored in LDS with the same permutation.
-//   * KV is staged in 64-key sub-tiles: K row-major and V transposed in LDS, 16-byte
-//     chunks XOR-swizzled by row so that ds_read_b128 fragment reads are bank-conflict
-//     free; global loads are 16 bytes per lane and cover whole 256-byte rows per
-//     quarter-wave.  Two LDS buffers plus register staging give one barrier per
-//     sub-tile with the next sub-tile's loads in flight during compute.
+//     is permuted the same way for the V^T operand; the exp work of each 16-key step
+//     is interleaved with the P V MFMAs of that step.
+//   * K and V are staged in 64-key sub-tiles, both row-major in LDS, copied HBM -> LDS
+//     with global_load_lds_dwordx4 (no staging registers, no VALU).  Each lane picks the
+//     global 16-byte chunk that its fixed LDS slot must hold, which realises the XOR
+//     swizzles: K 16-byte chunks by key & 7 (conflict-free ds_read_b128 fragments), V
+//     32-byte units by key & 7 (conflict-free transposing reads).  The P V operand (8
+//     keys of one head-dim index per lane) comes from two ds_read_b64_tr_b16 reads.
+//     Two LDS slots per operand: sub-tile s+1 is in flight while s is computed, one
+//     barrier per sub-tile.
 //   * softmax runs in base 2.  Where score_mod is monotone in the raw score (identity,
 //     soft-cap, a saturated relative-position bias) the row maximum is taken on the raw
 //     MFMA output and mapped once per row; the scale folds into the FMA feeding exp2.
@@ -48,18 +52,23 @@ constexpr float kRescaleThresh = 8.0f; // base-2 growth allowed before rescaling
 
 template <int D>
 struct Lds {
-  static constexpr int KROW = D * 2;          // bytes per K row
-  static constexpr int VROW = KT * 2;         // bytes per V^T row (one head-dim index)
-  static constexpr int KBYTES = KT * KROW;
-  static constexpr int VBYTES = D * VROW;
-  static constexpr int DOCBYTES = KT * 4;
-  static constexpr int BUF = KBYTES + VBYTES + DOCBYTES;
+  static constexpr int KROW = D * 2;          // bytes per K or V row
+  static constexpr int TILE = KT * KROW;      // one K or one V sub-tile
+  static constexpr int UNITS = D / 16;        // 32-byte units per V row
 };
 
-// physical 16-byte chunk of K row `key`, logical chunk `ch`
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+// K: physical 16-byte chunk of row `key` holding logical chunk `ch`
 __device__ __forceinline__ int k_off(int key, int ch, int krow) { return key * krow + ((ch ^ (key & 7)) << 4); }
-// V^T row d, physical chunk pc (8 keys)
-__device__ __forceinline__ int vt_off(int d, int pc) { return d * (KT * 2) + ((pc ^ (d & 7)) << 4); }
+// V: byte offset of V[key][d] (d a multiple of 4) with 32-byte units XOR-swizzled by key & 7
+template <int D>
+__device__ __forceinline__ int v_off(int key, int d) {
+  constexpr int UM = Lds<D>::UNITS - 1;
+  return key * (D * 2) + ((((d >> 4) ^ (key & 7)) & UM) << 5) + ((d & 15) << 1);
+}
 
 // key offset (within the 64-key sub-tile) held by S^T register rr of M-tile mt,
 // excluding the lane-half term 4*half
@@ -72,13 +81,20 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   constexpr int DCH = D / 8;     // 16-byte chunks per row
   constexpr int KSTEPS = D / 16; // k-steps of the QK^T product
   constexpr int DM = D / 32;     // 32-row tiles of O^T
-  constexpr int KCH = (KT * DCH + NT - 1) / NT;   // K chunks staged per thread
-  constexpr int NQUAD = 16 * DCH;                 // V units of 4 keys x 8 dims
-  constexpr int VQ = (NQUAD + NT - 1) / NT;
+  constexpr int KEYS_PER_KB = 1024 / (D * 2);     // keys covered by one 1 KB wave copy
+  constexpr int COPIES = KT / KEYS_PER_KB / NW;    // 1 KB copies per wave per operand
   constexpr bool kDoc = (MK == MK_INTERVAL_DOC);
   constexpr bool kRel = (SCORE == FA_S_RELPOS);
   using L = Lds<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * L::BUF];
+  // one LDS object per slot: the loop below is unrolled by two so that every access names
+  // a fixed object, which lets the compiler see that an in-flight copy into one slot does
+  // not alias reads of the other (no premature vmcnt waits)
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[L::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[L::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[L::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[L::TILE];
+  __shared__ __attribute__((aligned(256))) int32_t dbuf0[KT];
+  __shared__ __attribute__((aligned(256))) int32_t dbuf1[KT];
   __shared__ float rel_lds[kRel ? kRelposLdsMax : 1];
 
   const int tid = threadIdx.x;
@@ -163,77 +179,49 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
     }
   }
 
+  // the row's block list (full entries, then partial), 64 entries per register chunk;
+  // chunk k+1 is loaded when chunk k comes into use, entries are read with readlane
+  const int n_ent = nf + np;
+  auto load_chunk = [&](int base) -> int {
+    const int e = base + lane;
+    return e < nf ? flist[e] : (e < n_ent ? plist[e - nf] : 0);
+  };
+  int lst_cur = load_chunk(0);
+  int lst_nxt = n_ent > 64 ? load_chunk(64) : 0;
+  int lst_base = 0;
   auto sub_j0 = [&](int s, bool& partial) -> int {
     const int blk = s / spb;
     const int sub = s - blk * spb;
     partial = blk >= nf;
-    const int c = partial ? plist[blk - nf] : flist[blk];
-    return uniform(c) * p.tab.bk + sub * KT;
+    if (blk - lst_base >= 64) {
+      lst_base += 64;
+      lst_cur = lst_nxt;
+      if (lst_base + 64 < n_ent) lst_nxt = load_chunk(lst_base + 64);
+    }
+    const int c = __builtin_amdgcn_readlane(lst_cur, blk - lst_base);
+    return c * p.tab.bk + sub * KT;
   };
 
-  // ---- staging registers
-  u32x4 kreg[KCH];
-  u32x4 vreg[VQ][4];
-  int dreg = 0;
-  auto load_tile = [&](int j0) {
+  // ---- direct HBM -> LDS copies; rows past kv_len re-read the last row (they are masked)
+  auto copy_tile = [&](int j0, uint8_t* kdst, uint8_t* vdst, int32_t* ddst) {
 #pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int f = tid + NT * u;
-      const int key = f / DCH, ch = f % DCH;
-      const int j = j0 + key;
-      kreg[u] = (f < KT * DCH && (unsigned)j < (unsigned)kv_len) ? load16(kbase + (int64_t)j * D + ch * 8)
-                                                                  : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < VQ; ++u) {
-      const int qd = tid + NT * u;
-      const int kq = qd / DCH, dc = qd % DCH;
-      const int tq = kq >> 2, a = (kq >> 1) & 1, hh = kq & 1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + 16 * tq + 8 * a + 4 * hh + e;
-        vreg[u][e] = (qd < NQUAD && (unsigned)j < (unsigned)kv_len) ? load16(vbase + (int64_t)j * D + dc * 8)
-                                                                    : u32x4{0, 0, 0, 0};
-      }
+    for (int u = 0; u < COPIES; ++u) {
+      const int kb = (w * COPIES + u) * KEYS_PER_KB;
+      const int key = kb + lane / DCH;
+      const int pc = lane % DCH;                        // physical 16-byte chunk of the slot
+      const int j = min(j0 + key, kv_len - 1);
+      const int kch = pc ^ (key & 7);                   // K: logical chunk held there
+      const int vch = 2 * ((((pc >> 1) ^ (key & 7))) & (L::UNITS - 1)) + (pc & 1);   // V
+      __builtin_amdgcn_global_load_lds((gbl_void*)(kbase + (int64_t)j * D + kch * 8),
+                                       (lds_void*)(kdst + kb * L::KROW), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void*)(vbase + (int64_t)j * D + vch * 8),
+                                       (lds_void*)(vdst + kb * L::KROW), 16, 0, 0);
     }
     if constexpr (kDoc) {
-      if (tid < KT) {
-        const int j = j0 + tid;
-        dreg = (unsigned)j < (unsigned)kv_len ? docr[j] : -1;
+      if (w == 0) {
+        const int j = min(j0 + lane, kv_len - 1);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(docr + j), (lds_void*)ddst, 4, 0, 0);
       }
-    }
-  };
-  auto store_tile = [&](uint8_t* buf) {
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int f = tid + NT * u;
-      if (f < KT * DCH) {
-        const int key = f / DCH, ch = f % DCH;
-        *reinterpret_cast<u32x4*>(buf + k_off(key, ch, L::KROW)) = kreg[u];
-      }
-    }
-    uint8_t* vt = buf + L::KBYTES;
-#pragma unroll
-    for (int u = 0; u < VQ; ++u) {
-      const int qd = tid + NT * u;
-      if (qd < NQUAD) {
-        const int kq = qd / DCH, dc = qd % DCH;
-        const int tq = kq >> 2, a = (kq >> 1) & 1, hh = kq & 1;
-#pragma unroll
-        for (int dd = 0; dd < 8; dd += 2) {
-          // two head-dim indices per source dword: low halves -> dd, high halves -> dd+1
-          const uint32_t x0 = vreg[u][0][dd >> 1], x1 = vreg[u][1][dd >> 1];
-          const uint32_t x2 = vreg[u][2][dd >> 1], x3 = vreg[u][3][dd >> 1];
-          const u32x2 lo2 = {__builtin_amdgcn_perm(x1, x0, 0x05040100u), __builtin_amdgcn_perm(x3, x2, 0x05040100u)};
-          const u32x2 hi2 = {__builtin_amdgcn_perm(x1, x0, 0x07060302u), __builtin_amdgcn_perm(x3, x2, 0x07060302u)};
-          const int d = dc * 8 + dd;
-          *reinterpret_cast<u32x2*>(vt + vt_off(d, 2 * tq + hh) + 8 * a) = lo2;
-          *reinterpret_cast<u32x2*>(vt + vt_off(d + 1, 2 * tq + hh) + 8 * a) = hi2;
-        }
-      }
-    }
-    if constexpr (kDoc) {
-      if (tid < KT) reinterpret_cast<int32_t*>(buf + L::KBYTES + L::VBYTES)[tid] = dreg;
     }
   };
 
@@ -248,18 +236,20 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   int j0_cur = 0;
   if (nsub > 0) {
     j0_cur = sub_j0(0, part_cur);
-    load_tile(j0_cur);
+    copy_tile(j0_cur, kbuf0, vbuf0, dbuf0);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
-  for (int s = 0; s < nsub; ++s) {
-    uint8_t* buf = smem + (s & 1) * L::BUF;
-    store_tile(buf);
-    __syncthreads();
+  // one sub-tile: compute from (kcur, vcur, dcur) while the next one is copied into the
+  // other slot
+  auto tile = [&](int s, const uint8_t* buf, const uint8_t* vb, const int32_t* dl, uint8_t* knx,
+                  uint8_t* vnx, int32_t* dnx) {
     bool part_nxt = false;
     int j0_nxt = 0;
     if (s + 1 < nsub) {
       j0_nxt = sub_j0(s + 1, part_nxt);
-      load_tile(j0_nxt);
+      copy_tile(j0_nxt, knx, vnx, dnx);
     }
 
     // ---- S^T = K Q^T for the 64 keys of this sub-tile
@@ -291,7 +281,6 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
             sacc[mt][rr] = ok ? sacc[mt][rr] : kNegInf;
           }
       } else {
-        const int32_t* dl = reinterpret_cast<const int32_t*>(buf + L::KBYTES + L::VBYTES);
         // keys outside [lo, hi] (hi already clipped to kv_len - 1) are masked; when only
         // the ragged tail needs masking the same interval test applies with the tail
         // bound alone
@@ -394,51 +383,61 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
     }
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
 
-    // ---- weights P (bf16) and their row sum (fp32, before rounding)
-    bf16x8 pb[4];
-    float psum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4 pk;
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        float pv[2];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const float x = sacc[t >> 1][8 * (t & 1) + 2 * e2 + h2];
-          float arg;
-          if constexpr (SCORE == FA_S_SOFTCAP) {
-            const float rr = fast_rcp(fast_exp2(x * sc.capk) + 1.f);
-            arg = __builtin_fmaf(-2.f * sc.cap2, rr, sc.cap2 - m_use);
-            if (masked) arg = (x == kNegInf) ? kNegInf : arg;
-          } else if constexpr (SCORE == FA_S_IDENTITY) {
-            arg = __builtin_fmaf(x, sc.c2, -m_use);
-          } else {
-            arg = raw_mode ? __builtin_fmaf(x, sc.c2, bias2 - m_use) : x - m_use;
-          }
-          pv[h2] = fast_exp2(arg);
-        }
-        pk[e2] = pack_bf16x2(pv[0], pv[1]);
-        psum += pv[0] + pv[1];
-      }
-      pb[t] = __builtin_bit_cast(bf16x8, pk);
-    }
-    l_run += psum;
-
-    // ---- O^T += V^T P^T
-    const uint8_t* vt = buf + L::KBYTES;
-#pragma unroll
-    for (int dm = 0; dm < DM; ++dm) {
-      const int d = 32 * dm + col;
+    // ---- weights P (bf16), row sum and O^T += V^T P^T, one 16-key step at a time
+    {
+      const int g16 = lane >> 4, li = lane & 15;
+      float psum = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const u32x4 vv = *reinterpret_cast<const u32x4*>(vt + vt_off(d, 2 * t + half));
-        oacc[dm] = mfma32(__builtin_bit_cast(bf16x8, vv), pb[t], oacc[dm]);
+        u32x4 pk;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          float pv[2];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const float x = sacc[t >> 1][8 * (t & 1) + 2 * e2 + h2];
+            float arg;
+            if constexpr (SCORE == FA_S_SOFTCAP) {
+              const float rr = fast_rcp(fast_exp2(x * sc.capk) + 1.f);
+              arg = __builtin_fmaf(-2.f * sc.cap2, rr, sc.cap2 - m_use);
+              if (masked) arg = (x == kNegInf) ? kNegInf : arg;
+            } else if constexpr (SCORE == FA_S_IDENTITY) {
+              arg = __builtin_fmaf(x, sc.c2, -m_use);
+            } else {
+              arg = raw_mode ? __builtin_fmaf(x, sc.c2, bias2 - m_use) : x - m_use;
+            }
+            pv[h2] = fast_exp2(arg);
+          }
+          pk[e2] = pack_bf16x2(pv[0], pv[1]);
+          psum += pv[0] + pv[1];
+        }
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
+        // V^T fragment rows d = 32 dm + (lane & 31), keys of this step in the slot order
+        // of P^T: two transposing reads of 4 keys x 16 head-dim indices per 16-lane group
+        const int key = 16 * t + 4 * half + (li >> 2);
+#pragma unroll
+        for (int dm = 0; dm < DM; ++dm) {
+          const int d0 = 32 * dm + 16 * (g16 & 1) + 4 * (li & 3);
+          const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vb + v_off<D>(key, d0)));
+          const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vb + v_off<D>(key + 8, d0)));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[dm] = mfma32(a, pb, oacc[dm]);
+        }
       }
+      l_run += psum;
     }
 
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     part_cur = part_nxt;
     j0_cur = j0_nxt;
+  };
+
+  for (int s = 0; s < nsub; s += 2) {
+    tile(s, kbuf0, vbuf0, dbuf0, kbuf1, vbuf1, dbuf1);
+    if (s + 1 < nsub) tile(s + 1, kbuf1, vbuf1, dbuf1, kbuf0, vbuf0, dbuf0);
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)

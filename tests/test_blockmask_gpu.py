@@ -89,3 +89,17 @@ def test_workload_tables(name):
     expected = {"tiny_swa": (7, 14), "causal_softcap": (496, 32), "gqa_doc_swa_alibi": (175, 160),
                 "prefix_relpos_64k": (131344, 480), "decode_swa_softcap": (32, 0)}[name]
     assert (nf, npart) == expected
+
+
+@pytest.mark.parametrize("spec", [("and", ("doc",), ("swa", 700)), ("or", ("doc",), ("prefix", 300)),
+                                  ("causal",), ("and", ("prefix", 1000), ("doc",))],
+                         ids=["doc&swa", "doc|prefix", "causal", "prefix&doc"])
+def test_large_grid_multi_launch_path(spec):
+    # more than 16384 blocks: the five-launch build path (the small grids above use the
+    # single-workgroup path); per-batch documents, replicated heads, ragged tail
+    n = 64 * 130 + 17
+    doc = np.stack([docs_for(n, "packed", 11), docs_for(n, "nonmono", 12)])
+    if W.mask_uses_doc(spec):
+        check_tables(spec, 2, 2, n, n, 64, 64, 0, doc)
+    else:
+        check_tables(spec, 1, 3, n, n, 64, 64, 0, None)
