@@ -39,6 +39,9 @@
 //     compare against IDs staged in LDS; other programs use the generic interpreter.
 //   * grid order: longest rows first (query block index descending), and heads
 //     grouped so that consecutive workgroups of one XCD share a KV head.
+#include <type_traits>
+#include <utility>
+
 #include "device_common.hpp"
 #include "fa_internal.hpp"
 
@@ -59,7 +62,8 @@ struct Lds {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void gbl_void;
+
+constexpr int kListCap = 512;   // block-list entries staged in LDS per pass over the row
 
 // K: physical 16-byte chunk of row `key` holding logical chunk `ch`
 __device__ __forceinline__ int k_off(int key, int ch, int krow) { return key * krow + ((ch ^ (key & 7)) << 4); }
@@ -74,6 +78,60 @@ __device__ __forceinline__ int v_off(int key, int d) {
 // excluding the lane-half term 4*half
 __device__ __forceinline__ constexpr int key_of(int mt, int rr) { return 32 * mt + 8 * (rr >> 2) + (rr & 3); }
 
+template <int... U, typename F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, U...>, F&& f) {
+  (f(std::integral_constant<int, U>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+// LDS byte address of a __shared__ object (the M0 operand of the LDS-DMA loads)
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
+  return (uint32_t)(uintptr_t)(const lds_void*)ptr;
+}
+
+// HBM -> LDS loads that bypass VGPRs (global_load_lds).  Lane l writes LDS bytes
+// [m0 + IMM + 16 l, +16); the immediate offset applies to the global and the LDS side
+// alike.  Issued from inline assembly so that every address is a scalar base plus one
+// precomputed per-lane offset; the caller waits (vmcnt) before the barrier that
+// publishes the tile.  One wait state separates the M0 write from the load that reads
+// it.
+// wave-uniform value in scalar registers (the "s" operands below)
+__device__ __forceinline__ uint32_t sreg(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ const void* sreg(const void* ptr) {
+  const uint64_t v = (uint64_t)(uintptr_t)ptr;
+  const uint64_t lo = sreg((uint32_t)v), hi = sreg((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(lo | (hi << 32));
+}
+
+template <int IMM>
+__device__ __forceinline__ void dma16_s(uint32_t m0, const void* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3"
+               :: "s"(sreg(m0)), "v"(voff), "s"(sreg(sbase)), "i"(IMM) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_v(uint32_t m0, const void* gaddr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(sreg(m0)), "v"(gaddr) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_s(uint32_t m0, const void* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(sreg(m0)), "v"(voff), "s"(sreg(sbase)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_v(uint32_t m0, const void* gaddr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(sreg(m0)), "v"(gaddr) : "memory", "m0");
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// round-to-nearest-even pair conversion into one dword (v_cvt_pk_bf16_f32), low = a
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 template <int D, int NW, int SCORE, int MK>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   constexpr int NT = NW * 64;
@@ -81,20 +139,18 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   constexpr int DCH = D / 8;     // 16-byte chunks per row
   constexpr int KSTEPS = D / 16; // k-steps of the QK^T product
   constexpr int DM = D / 32;     // 32-row tiles of O^T
-  constexpr int KEYS_PER_KB = 1024 / (D * 2);     // keys covered by one 1 KB wave copy
-  constexpr int COPIES = KT / KEYS_PER_KB / NW;    // 1 KB copies per wave per operand
+  constexpr int KPK = 1024 / (D * 2);       // keys covered by one 1 KB wave copy
+  constexpr int COPIES = KT / KPK / NW;     // 1 KB copies per wave per operand
+  constexpr int VAR = KPK >= 8 ? 1 : 8 / KPK;  // distinct swizzle patterns over the copies
   constexpr bool kDoc = (MK == MK_INTERVAL_DOC);
   constexpr bool kRel = (SCORE == FA_S_RELPOS);
   using L = Lds<D>;
-  // one LDS object per slot: the loop below is unrolled by two so that every access names
-  // a fixed object, which lets the compiler see that an in-flight copy into one slot does
-  // not alias reads of the other (no premature vmcnt waits)
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[L::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[L::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[L::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[L::TILE];
-  __shared__ __attribute__((aligned(256))) int32_t dbuf0[KT];
-  __shared__ __attribute__((aligned(256))) int32_t dbuf1[KT];
+  static_assert(L::KROW * KPK == 1024, "one copy moves 1 KB");
+  static_assert((COPIES * KPK) % 8 == 0, "wave slices start at a multiple of 8 keys");
+  // K slot 0 | K slot 1 | V slot 0 | V slot 1 | doc IDs slot 0 | slot 1.  The loop below is
+  // unrolled by two, so every LDS read is a per-lane base plus an immediate offset.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * L::TILE + 2 * KT * 4];
+  __shared__ int32_t list_s[kListCap];
   __shared__ float rel_lds[kRel ? kRelposLdsMax : 1];
 
   const int tid = threadIdx.x;
@@ -136,6 +192,10 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       u32x4 v = row_ok ? load16(qrow + 16 * t + 8 * half) : u32x4{0, 0, 0, 0};
       qf[t] = __builtin_bit_cast(bf16x8, v);
     }
+    // consume the loads here: the block loop's HBM -> LDS copies are invisible to the
+    // compiler's wait counting, which would otherwise wait for all memory at every tile
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) asm volatile("" : "+v"(qf[t]));
   }
 
   // ---- block-table row
@@ -146,8 +206,9 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   const int np = uniform(p.tab.num[row]);
   const int32_t* flist = p.tab.fidx + uniform(p.tab.fptr[row]);
   const int32_t* plist = p.tab.idx + uniform(p.tab.ptr[row]);
-  const int spb = p.tab.bk / KT;
-  const int nsub = (nf + np) * spb;
+  const int bk = p.tab.bk;
+  const int spb_sh = bk == 2 * KT ? 1 : 0;   // sub-tiles per block = 1 << spb_sh
+  const int n_ent = nf + np;
 
   const uint16_t* kbase = p.k + (int64_t)(b * p.Hkv + hkv) * p.kv_len * D;
   const uint16_t* vbase = p.v + (int64_t)(b * p.Hkv + hkv) * p.kv_len * D;
@@ -170,60 +231,77 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
     }
   }
 
-  // relative-position table of this query head, pre-multiplied by log2(e)
+  // relative-position table of this query head, pre-multiplied by log2(e); the two
+  // saturated entries are kept in registers
   const int R = p.score.radius;
   const bool rel_in_lds = kRel && (2 * R + 1) <= kRelposLdsMax;
+  float bias_far2 = 0.f, bias_ahead2 = 0.f;   // rel >= R and rel <= -R
   if constexpr (kRel) {
     if (rel_in_lds) {
       for (int x = tid; x < 2 * R + 1; x += NT) rel_lds[x] = sc.tab[x] * kLog2e;
     }
+    bias_far2 = sc.tab[2 * R] * kLog2e;
+    bias_ahead2 = sc.tab[0] * kLog2e;
   }
 
-  // the row's block list (full entries, then partial), 64 entries per register chunk;
-  // chunk k+1 is loaded when chunk k comes into use, entries are read with readlane
-  const int n_ent = nf + np;
-  auto load_chunk = [&](int base) -> int {
-    const int e = base + lane;
-    return e < nf ? flist[e] : (e < n_ent ? plist[e - nf] : 0);
-  };
-  int lst_cur = load_chunk(0);
-  int lst_nxt = n_ent > 64 ? load_chunk(64) : 0;
-  int lst_base = 0;
-  auto sub_j0 = [&](int s, bool& partial) -> int {
-    const int blk = s / spb;
-    const int sub = s - blk * spb;
-    partial = blk >= nf;
-    if (blk - lst_base >= 64) {
-      lst_base += 64;
-      lst_cur = lst_nxt;
-      if (lst_base + 64 < n_ent) lst_nxt = load_chunk(lst_base + 64);
-    }
-    const int c = __builtin_amdgcn_readlane(lst_cur, blk - lst_base);
-    return c * p.tab.bk + sub * KT;
-  };
-
-  // ---- direct HBM -> LDS copies; rows past kv_len re-read the last row (they are masked)
-  auto copy_tile = [&](int j0, uint8_t* kdst, uint8_t* vdst, int32_t* ddst) {
+  // ---- per-lane offsets of the HBM -> LDS copies.  Wave w fills keys
+  // [w COPIES KPK, (w+1) COPIES KPK) of a sub-tile, 1 KB (KPK keys) per copy; LDS slots are
+  // linear, and each lane fetches the global chunk its slot must hold under the swizzle.
+  const int wu = uniform(w);
+  const int wave_key0 = wu * COPIES * KPK;
+  uint32_t koff[VAR], voff[VAR];
 #pragma unroll
-    for (int u = 0; u < COPIES; ++u) {
-      const int kb = (w * COPIES + u) * KEYS_PER_KB;
-      const int key = kb + lane / DCH;
-      const int pc = lane % DCH;                        // physical 16-byte chunk of the slot
-      const int j = min(j0 + key, kv_len - 1);
-      const int kch = pc ^ (key & 7);                   // K: logical chunk held there
-      const int vch = 2 * ((((pc >> 1) ^ (key & 7))) & (L::UNITS - 1)) + (pc & 1);   // V
-      __builtin_amdgcn_global_load_lds((gbl_void*)(kbase + (int64_t)j * D + kch * 8),
-                                       (lds_void*)(kdst + kb * L::KROW), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gbl_void*)(vbase + (int64_t)j * D + vch * 8),
-                                       (lds_void*)(vdst + kb * L::KROW), 16, 0, 0);
-    }
-    if constexpr (kDoc) {
-      if (w == 0) {
-        const int j = min(j0 + lane, kv_len - 1);
-        __builtin_amdgcn_global_load_lds((gbl_void*)(docr + j), (lds_void*)ddst, 4, 0, 0);
+  for (int var = 0; var < VAR; ++var) {
+    const int key_in = lane / DCH;
+    const int pc = lane % DCH;
+    const int key7 = (var * KPK + key_in) & 7;
+    koff[var] = (uint32_t)(key_in * L::KROW + ((pc ^ key7) << 4));
+    voff[var] = (uint32_t)(key_in * L::KROW + ((2 * (((pc >> 1) ^ key7) & (L::UNITS - 1)) + (pc & 1)) << 4));
+  }
+
+  auto copy_tile = [&](int j0, auto slot_c) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    const uint32_t mk = lds_addr(smem + SLOT * L::TILE) + wave_key0 * L::KROW;
+    const uint32_t mv = lds_addr(smem + (2 + SLOT) * L::TILE) + wave_key0 * L::KROW;
+    const uint32_t md = lds_addr(smem + 4 * L::TILE + SLOT * KT * 4);
+    if (j0 + KT <= kv_len) {
+      const char* kg = (const char*)kbase + ((int64_t)j0 + wave_key0) * L::KROW;
+      const char* vg = (const char*)vbase + ((int64_t)j0 + wave_key0) * L::KROW;
+      static_for<COPIES>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        constexpr int grp = (u / 4) * 4096;   // immediate offsets stay below 4 KB
+        dma16_s<(u % 4) * 1024>(mk + grp, kg + grp, koff[u % VAR]);
+        dma16_s<(u % 4) * 1024>(mv + grp, vg + grp, voff[u % VAR]);
+      });
+      if constexpr (kDoc) {
+        if (wu == 0) dma4_s(md, docr + j0, (uint32_t)lane * 4);
+      }
+    } else {
+      // ragged tail: keys past kv_len re-read the last key (they are masked)
+      static_for<COPIES>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        const int key = wave_key0 + u * KPK + lane / DCH;
+        const int64_t j = min(j0 + key, kv_len - 1);
+        dma16_v(mk + u * 1024, (const char*)kbase + j * L::KROW + (koff[u % VAR] & (L::KROW - 1)));
+        dma16_v(mv + u * 1024, (const char*)vbase + j * L::KROW + (voff[u % VAR] & (L::KROW - 1)));
+      });
+      if constexpr (kDoc) {
+        if (wu == 0) dma4_v(md, docr + min(j0 + lane, kv_len - 1));
       }
     }
   };
+
+  // ---- per-lane LDS read bases.  K fragment (mt, t): key 32 mt + col, logical chunk
+  // 2t + half at physical chunk (2t + half) ^ (key & 7); t = 4q + t' adds q * 128 bytes.
+  // V^T fragment (t, dm, hl): keys 16 t + 8 hl + 4 half + (li >> 2), head-dim d0 =
+  // 32 dm + 16 (g16 & 1) + 4 (li & 3); t and hl add whole rows.
+  const int g16 = lane >> 4, li = lane & 15;
+  uint32_t kaddr[4], vaddr[DM];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) kaddr[t] = (uint32_t)k_off(col, 2 * t + half, L::KROW);
+#pragma unroll
+  for (int dm = 0; dm < DM; ++dm)
+    vaddr[dm] = (uint32_t)v_off<D>(4 * half + (li >> 2), 32 * dm + 16 * (g16 & 1) + 4 * (li & 3));
 
   // ---- online softmax state (per lane: one query row; halves share m)
   float m_run = kNegInf;
@@ -232,43 +310,26 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
 #pragma unroll
   for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
 
-  bool part_cur = false;
-  int j0_cur = 0;
-  if (nsub > 0) {
-    j0_cur = sub_j0(0, part_cur);
-    copy_tile(j0_cur, kbuf0, vbuf0, dbuf0);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  // one sub-tile: compute from (kcur, vcur, dcur) while the next one is copied into the
-  // other slot
-  auto tile = [&](int s, const uint8_t* buf, const uint8_t* vb, const int32_t* dl, uint8_t* knx,
-                  uint8_t* vnx, int32_t* dnx) {
-    bool part_nxt = false;
-    int j0_nxt = 0;
-    if (s + 1 < nsub) {
-      j0_nxt = sub_j0(s + 1, part_nxt);
-      copy_tile(j0_nxt, knx, vnx, dnx);
-    }
-
-    // ---- S^T = K Q^T for the 64 keys of this sub-tile
+  // ---- one 64-key sub-tile from LDS (buf, vb, dl); MASKED: partial block or ragged tail
+  auto compute = [&](auto slot_c, bool masked, bool part, int j0) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    const uint8_t* kb = smem + SLOT * L::TILE;
+    const uint8_t* vb = smem + (2 + SLOT) * L::TILE;
+    const int32_t* dl = reinterpret_cast<const int32_t*>(smem + 4 * L::TILE + SLOT * KT * 4);
+    // S^T = K Q^T
     f32x16 sacc[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       sacc[mt] = f32x16{};
-      const int key = 32 * mt + col;
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(buf + k_off(key, 2 * t + half, L::KROW));
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + kaddr[t & 3] + (t >> 2) * 128 + mt * 32 * L::KROW);
         sacc[mt] = mfma32(__builtin_bit_cast(bf16x8, kv), qf[t], sacc[mt]);
       }
     }
+    const int jl = j0 + 4 * half;   // key of element (mt=0, rr=0) in this lane
 
-    const bool masked = part_cur || (j0_cur + KT > kv_len);
-    const int jl = j0_cur + 4 * half;   // key of element (mt=0, rr=0) in this lane
-
-    // ---- element mask (partial / ragged sub-tiles only): x = -inf where disallowed
+    // element mask: x = -inf where disallowed
     if (masked) {
       if constexpr (MK == MK_GENERIC) {
 #pragma unroll
@@ -277,15 +338,14 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
           for (int rr = 0; rr < 16; ++rr) {
             const int j = jl + key_of(mt, rr);
             bool ok = (unsigned)j < (unsigned)kv_len;
-            if (part_cur && ok) ok = mask_allowed(p.prog, i_g, j, doc_i, p.prog.has_doc ? docr[j] : 0);
+            if (part && ok) ok = mask_allowed(p.prog, i_g, j, doc_i, p.prog.has_doc ? docr[j] : 0);
             sacc[mt][rr] = ok ? sacc[mt][rr] : kNegInf;
           }
       } else {
         // keys outside [lo, hi] (hi already clipped to kv_len - 1) are masked; when only
-        // the ragged tail needs masking the same interval test applies with the tail
-        // bound alone
+        // the ragged tail needs masking the same test applies with the tail bound alone
         uint32_t lo_t = lo_u, span_t = span;
-        if (!part_cur) {
+        if (!part) {
           lo_t = 0;
           span_t = (uint32_t)(kv_len - 1);
         }
@@ -295,7 +355,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
           for (int g4 = 0; g4 < 4; ++g4) {
             int dq[4] = {doc_i, doc_i, doc_i, doc_i};
             if constexpr (kDoc) {
-              if (part_cur) {
+              if (part) {
                 const u32x4 dv = *reinterpret_cast<const u32x4*>(dl + 32 * mt + 8 * g4 + 4 * half);
                 dq[0] = (int)dv[0];
                 dq[1] = (int)dv[1];
@@ -314,18 +374,18 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       }
     }
 
-    // ---- score_mod to the base-2 domain and the tile maximum
-    // Monotone kinds keep the raw score in sacc (tile maximum mapped once); the others
-    // store t = log2(e) * score_mod(s * scale) in sacc.
+    // score_mod to the base-2 domain and the tile maximum.  Monotone kinds keep the raw
+    // score in sacc (tile maximum mapped once); the others store
+    // t = log2(e) * score_mod(s * scale) in sacc.
     bool raw_mode;
     float bias2 = 0.f;  // constant base-2 bias of a saturated relative-position tile
     if constexpr (SCORE == FA_S_IDENTITY || SCORE == FA_S_SOFTCAP) {
       raw_mode = true;
     } else if constexpr (SCORE == FA_S_RELPOS) {
-      const int dmin = i_wave0 - (j0_cur + KT - 1);
-      const int dmax = i_wave0 + 31 - j0_cur;
+      const int dmin = i_wave0 - (j0 + KT - 1);
+      const int dmax = i_wave0 + 31 - j0;
       raw_mode = dmin >= R || dmax <= -R;
-      if (raw_mode) bias2 = sc.tab[dmin >= R ? 2 * R : 0] * kLog2e;
+      bias2 = dmin >= R ? bias_far2 : bias_ahead2;
     } else {
       raw_mode = false;
     }
@@ -371,7 +431,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       }
     }
 
-    // ---- lazy online-softmax rescale (wave-uniform branch)
+    // lazy online-softmax rescale (wave-uniform branch)
     const bool grow = m_cand > m_run + kRescaleThresh;
     if (__ballot(grow) != 0) {
       const float m_new = grow ? m_cand : m_run;
@@ -382,62 +442,100 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
     }
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    const float softcap_c = sc.cap2 - m_use;
+    const float raw_c = bias2 - m_use;
 
-    // ---- weights P (bf16), row sum and O^T += V^T P^T, one 16-key step at a time
-    {
-      const int g16 = lane >> 4, li = lane & 15;
-      float psum = 0.f;
+    // weights P (bf16), row sum and O^T += V^T P^T, one 16-key step at a time
+    float psum = 0.f;
+    // P for the 8 elements of 16-key step t (packed bf16 pairs); CHECK re-applies the
+    // mask where the soft-cap would map a -inf score to a finite value
+    auto p_step = [&](int t, u32x4& pk, auto check_c) {
+      constexpr bool CHECK = decltype(check_c)::value;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        u32x4 pk;
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float pv[2];
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          float pv[2];
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const float x = sacc[t >> 1][8 * (t & 1) + 2 * e2 + h2];
-            float arg;
-            if constexpr (SCORE == FA_S_SOFTCAP) {
-              const float rr = fast_rcp(fast_exp2(x * sc.capk) + 1.f);
-              arg = __builtin_fmaf(-2.f * sc.cap2, rr, sc.cap2 - m_use);
-              if (masked) arg = (x == kNegInf) ? kNegInf : arg;
-            } else if constexpr (SCORE == FA_S_IDENTITY) {
-              arg = __builtin_fmaf(x, sc.c2, -m_use);
-            } else {
-              arg = raw_mode ? __builtin_fmaf(x, sc.c2, bias2 - m_use) : x - m_use;
-            }
-            pv[h2] = fast_exp2(arg);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const float x = sacc[t >> 1][8 * (t & 1) + 2 * e2 + h2];
+          float arg;
+          if constexpr (SCORE == FA_S_SOFTCAP) {
+            const float rr = fast_rcp(fast_exp2(x * sc.capk) + 1.f);
+            arg = __builtin_fmaf(-2.f * sc.cap2, rr, softcap_c);
+            if constexpr (CHECK) arg = (x == kNegInf) ? kNegInf : arg;
+          } else if constexpr (SCORE == FA_S_IDENTITY) {
+            arg = __builtin_fmaf(x, sc.c2, -m_use);
+          } else {
+            arg = raw_mode ? __builtin_fmaf(x, sc.c2, raw_c) : x - m_use;
           }
-          pk[e2] = pack_bf16x2(pv[0], pv[1]);
-          psum += pv[0] + pv[1];
+          pv[h2] = fast_exp2(arg);
         }
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
-        // V^T fragment rows d = 32 dm + (lane & 31), keys of this step in the slot order
-        // of P^T: two transposing reads of 4 keys x 16 head-dim indices per 16-lane group
-        const int key = 16 * t + 4 * half + (li >> 2);
-#pragma unroll
-        for (int dm = 0; dm < DM; ++dm) {
-          const int d0 = 32 * dm + 16 * (g16 & 1) + 4 * (li & 3);
-          const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vb + v_off<D>(key, d0)));
-          const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vb + v_off<D>(key + 8, d0)));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[dm] = mfma32(a, pb, oacc[dm]);
-        }
+        pk[e2] = cvt_pk_bf16(pv[0], pv[1]);
+        psum += pv[0] + pv[1];
       }
-      l_run += psum;
+    };
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      u32x4 pk;
+      if (SCORE == FA_S_SOFTCAP && masked) {
+        p_step(t, pk, std::true_type{});
+      } else {
+        p_step(t, pk, std::false_type{});
+      }
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
+      // V^T fragment rows d = 32 dm + (lane & 31), keys of this step in the slot order
+      // of P^T: two transposing reads of 4 keys x 16 head-dim indices per 16-lane group
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm) {
+        const uint8_t* va = vb + vaddr[dm] + 16 * t * L::KROW;
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(va + 8 * L::KROW));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[dm] = mfma32(a, pb, oacc[dm]);
+      }
     }
-
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    part_cur = part_nxt;
-    j0_cur = j0_nxt;
+    l_run += psum;
   };
 
-  for (int s = 0; s < nsub; s += 2) {
-    tile(s, kbuf0, vbuf0, dbuf0, kbuf1, vbuf1, dbuf1);
-    if (s + 1 < nsub) tile(s + 1, kbuf1, vbuf1, dbuf1, kbuf0, vbuf0, dbuf0);
+  // ---- the row's block list (full entries, then partial) in passes of kListCap entries
+  for (int c0 = 0; c0 < n_ent; c0 += kListCap) {
+    const int cnt = min(kListCap, n_ent - c0);
+    for (int e = tid; e < cnt; e += NT) {
+      const int ge = c0 + e;
+      list_s[e] = ge < nf ? flist[ge] : plist[ge - nf];
+    }
+    __syncthreads();
+    const int nsub = cnt << spb_sh;
+    auto sub_j0 = [&](int s, bool& part) -> int {
+      const int blk = s >> spb_sh;
+      part = c0 + blk >= nf;
+      return uniform(list_s[blk]) * bk + (s & spb_sh) * KT;
+    };
+    bool part_cur = false;
+    int j0_cur = sub_j0(0, part_cur);
+    copy_tile(j0_cur, std::integral_constant<int, 0>{});
+    wait_dma();
+    __syncthreads();
+
+    // sub-tile s from one slot while s+1 is copied into the other
+    auto step = [&](int s, auto slot_c) {
+      constexpr int SLOT = decltype(slot_c)::value;
+      bool part_nxt = false;
+      int j0_nxt = 0;
+      if (s + 1 < nsub) {
+        j0_nxt = sub_j0(s + 1, part_nxt);
+        copy_tile(j0_nxt, std::integral_constant<int, 1 - SLOT>{});
+      }
+      compute(slot_c, part_cur || j0_cur + KT > kv_len, part_cur, j0_cur);
+      wait_dma();
+      __syncthreads();
+      part_cur = part_nxt;
+      j0_cur = j0_nxt;
+    };
+    for (int s = 0; s < nsub; s += 2) {
+      step(s, std::integral_constant<int, 0>{});
+      if (s + 1 < nsub) step(s + 1, std::integral_constant<int, 1>{});
+    }
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
@@ -451,8 +549,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       for (int gq = 0; gq < 4; ++gq) {
         const int d0 = 32 * dm + 8 * gq + 4 * half;
         u32x2 o2;
-        o2[0] = pack_bf16x2(oacc[dm][4 * gq + 0] * inv, oacc[dm][4 * gq + 1] * inv);
-        o2[1] = pack_bf16x2(oacc[dm][4 * gq + 2] * inv, oacc[dm][4 * gq + 3] * inv);
+        o2[0] = cvt_pk_bf16(oacc[dm][4 * gq + 0] * inv, oacc[dm][4 * gq + 1] * inv);
+        o2[1] = cvt_pk_bf16(oacc[dm][4 * gq + 2] * inv, oacc[dm][4 * gq + 3] * inv);
         *reinterpret_cast<u32x2*>(orow + d0) = o2;
       }
     }
