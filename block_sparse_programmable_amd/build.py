@@ -38,9 +38,13 @@ def common_flags():
             "-Wno-unused-result"]
 
 
+# per-file device code generation options
+FILE_FLAGS = {}
+
+
 def compile_one(src, verbose=False, resource_usage=False):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-c", src, "-o", obj] + common_flags()
+    cmd = [hipcc(), "-c", src, "-o", obj] + common_flags() + FILE_FLAGS.get(os.path.basename(src), [])
     if resource_usage:
         cmd.append("-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)

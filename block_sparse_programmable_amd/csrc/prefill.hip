@@ -39,98 +39,13 @@
 //     compare against IDs staged in LDS; other programs use the generic interpreter.
 //   * grid order: longest rows first (query block index descending), and heads
 //     grouped so that consecutive workgroups of one XCD share a KV head.
-#include <type_traits>
-#include <utility>
-
 #include "device_common.hpp"
 #include "fa_internal.hpp"
+#include "prefill_common.hpp"
 
 namespace fa {
 
 namespace {
-
-constexpr int KT = 64;                 // keys per sub-tile
-constexpr int kRelposLdsMax = 3073;    // table entries staged in LDS (2R+1 <= this)
-constexpr float kRescaleThresh = 8.0f; // base-2 growth allowed before rescaling O
-
-template <int D>
-struct Lds {
-  static constexpr int KROW = D * 2;          // bytes per K or V row
-  static constexpr int TILE = KT * KROW;      // one K or one V sub-tile
-  static constexpr int UNITS = D / 16;        // 32-byte units per V row
-};
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr int kListCap = 512;   // block-list entries staged in LDS per pass over the row
-
-// K: physical 16-byte chunk of row `key` holding logical chunk `ch`
-__device__ __forceinline__ int k_off(int key, int ch, int krow) { return key * krow + ((ch ^ (key & 7)) << 4); }
-// V: byte offset of V[key][d] (d a multiple of 4) with 32-byte units XOR-swizzled by key & 7
-template <int D>
-__device__ __forceinline__ int v_off(int key, int d) {
-  constexpr int UM = Lds<D>::UNITS - 1;
-  return key * (D * 2) + ((((d >> 4) ^ (key & 7)) & UM) << 5) + ((d & 15) << 1);
-}
-
-// key offset (within the 64-key sub-tile) held by S^T register rr of M-tile mt,
-// excluding the lane-half term 4*half
-__device__ __forceinline__ constexpr int key_of(int mt, int rr) { return 32 * mt + 8 * (rr >> 2) + (rr & 3); }
-
-template <int... U, typename F>
-__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, U...>, F&& f) {
-  (f(std::integral_constant<int, U>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(std::make_integer_sequence<int, N>{}, f);
-}
-
-// LDS byte address of a __shared__ object (the M0 operand of the LDS-DMA loads)
-__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
-  return (uint32_t)(uintptr_t)(const lds_void*)ptr;
-}
-
-// HBM -> LDS loads that bypass VGPRs (global_load_lds).  Lane l writes LDS bytes
-// [m0 + IMM + 16 l, +16); the immediate offset applies to the global and the LDS side
-// alike.  Issued from inline assembly so that every address is a scalar base plus one
-// precomputed per-lane offset; the caller waits (vmcnt) before the barrier that
-// publishes the tile.  One wait state separates the M0 write from the load that reads
-// it.
-// wave-uniform value in scalar registers (the "s" operands below)
-__device__ __forceinline__ uint32_t sreg(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ const void* sreg(const void* ptr) {
-  const uint64_t v = (uint64_t)(uintptr_t)ptr;
-  const uint64_t lo = sreg((uint32_t)v), hi = sreg((uint32_t)(v >> 32));
-  return (const void*)(uintptr_t)(lo | (hi << 32));
-}
-
-template <int IMM>
-__device__ __forceinline__ void dma16_s(uint32_t m0, const void* sbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3"
-               :: "s"(sreg(m0)), "v"(voff), "s"(sreg(sbase)), "i"(IMM) : "memory", "m0");
-}
-__device__ __forceinline__ void dma16_v(uint32_t m0, const void* gaddr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(sreg(m0)), "v"(gaddr) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4_s(uint32_t m0, const void* sbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-               :: "s"(sreg(m0)), "v"(voff), "s"(sreg(sbase)) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4_v(uint32_t m0, const void* gaddr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(sreg(m0)), "v"(gaddr) : "memory", "m0");
-}
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// round-to-nearest-even pair conversion into one dword (v_cvt_pk_bf16_f32), low = a
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  const f32x2_t v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 
 template <int D, int NW, int SCORE, int MK>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
@@ -147,8 +62,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   using L = Lds<D>;
   static_assert(L::KROW * KPK == 1024, "one copy moves 1 KB");
   static_assert((COPIES * KPK) % 8 == 0, "wave slices start at a multiple of 8 keys");
-  // K slot 0 | K slot 1 | V slot 0 | V slot 1 | doc IDs slot 0 | slot 1.  The loop below is
-  // unrolled by two, so every LDS read is a per-lane base plus an immediate offset.
+  // K slot 0 | K slot 1 | V slot 0 | V slot 1 | doc IDs slot 0 | slot 1 (doc IDs travel
+  // with K).  Every LDS read is a per-lane base plus an immediate offset.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * L::TILE + 2 * KT * 4];
   __shared__ int32_t list_s[kListCap];
   __shared__ float rel_lds[kRel ? kRelposLdsMax : 1];
@@ -259,21 +174,22 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
     voff[var] = (uint32_t)(key_in * L::KROW + ((2 * (((pc >> 1) ^ key7) & (L::UNITS - 1)) + (pc & 1)) << 4));
   }
 
-  auto copy_tile = [&](int j0, auto slot_c) {
+  // copy of one operand (K with its doc IDs, or V) of the sub-tile at key j0 into a slot
+  auto copy_op = [&](int j0, auto isv_c, auto slot_c) {
+    constexpr bool ISV = decltype(isv_c)::value;
     constexpr int SLOT = decltype(slot_c)::value;
-    const uint32_t mk = lds_addr(smem + SLOT * L::TILE) + wave_key0 * L::KROW;
-    const uint32_t mv = lds_addr(smem + (2 + SLOT) * L::TILE) + wave_key0 * L::KROW;
+    const uint16_t* gb = ISV ? vbase : kbase;
+    const uint32_t m = lds_addr(smem + ((ISV ? 2 : 0) + SLOT) * L::TILE) + wave_key0 * L::KROW;
     const uint32_t md = lds_addr(smem + 4 * L::TILE + SLOT * KT * 4);
+    const uint32_t* off = ISV ? voff : koff;
     if (j0 + KT <= kv_len) {
-      const char* kg = (const char*)kbase + ((int64_t)j0 + wave_key0) * L::KROW;
-      const char* vg = (const char*)vbase + ((int64_t)j0 + wave_key0) * L::KROW;
+      const char* g = (const char*)gb + ((int64_t)j0 + wave_key0) * L::KROW;
       static_for<COPIES>([&](auto uc) {
         constexpr int u = decltype(uc)::value;
         constexpr int grp = (u / 4) * 4096;   // immediate offsets stay below 4 KB
-        dma16_s<(u % 4) * 1024>(mk + grp, kg + grp, koff[u % VAR]);
-        dma16_s<(u % 4) * 1024>(mv + grp, vg + grp, voff[u % VAR]);
+        dma16_s<(u % 4) * 1024>(m + grp, g + grp, off[u % VAR]);
       });
-      if constexpr (kDoc) {
+      if constexpr (kDoc && !ISV) {
         if (wu == 0) dma4_s(md, docr + j0, (uint32_t)lane * 4);
       }
     } else {
@@ -282,10 +198,9 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
         constexpr int u = decltype(uc)::value;
         const int key = wave_key0 + u * KPK + lane / DCH;
         const int64_t j = min(j0 + key, kv_len - 1);
-        dma16_v(mk + u * 1024, (const char*)kbase + j * L::KROW + (koff[u % VAR] & (L::KROW - 1)));
-        dma16_v(mv + u * 1024, (const char*)vbase + j * L::KROW + (voff[u % VAR] & (L::KROW - 1)));
+        dma16_v(m + u * 1024, (const char*)gb + j * L::KROW + (off[u % VAR] & (L::KROW - 1)));
       });
-      if constexpr (kDoc) {
+      if constexpr (kDoc && !ISV) {
         if (wu == 0) dma4_v(md, docr + min(j0 + lane, kv_len - 1));
       }
     }
@@ -310,26 +225,27 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
 #pragma unroll
   for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
 
-  // ---- one 64-key sub-tile from LDS (buf, vb, dl); MASKED: partial block or ragged tail
-  auto compute = [&](auto slot_c, bool masked, bool part, int j0) {
+  // ---- S^T = K Q^T for the sub-tile in K slot SLOT
+  auto qk = [&](auto slot_c, f32x16 (&s)[2]) {
     constexpr int SLOT = decltype(slot_c)::value;
     const uint8_t* kb = smem + SLOT * L::TILE;
-    const uint8_t* vb = smem + (2 + SLOT) * L::TILE;
-    const int32_t* dl = reinterpret_cast<const int32_t*>(smem + 4 * L::TILE + SLOT * KT * 4);
-    // S^T = K Q^T
-    f32x16 sacc[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      sacc[mt] = f32x16{};
+      s[mt] = f32x16{};
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t) {
         const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + kaddr[t & 3] + (t >> 2) * 128 + mt * 32 * L::KROW);
-        sacc[mt] = mfma32(__builtin_bit_cast(bf16x8, kv), qf[t], sacc[mt]);
+        s[mt] = mfma32(__builtin_bit_cast(bf16x8, kv), qf[t], s[mt]);
       }
     }
-    const int jl = j0 + 4 * half;   // key of element (mt=0, rr=0) in this lane
+  };
 
-    // element mask: x = -inf where disallowed
+  // ---- mask (partial / ragged sub-tiles), score_mod, tile maximum and the lazy
+  // online-softmax rescale; returns how the weights of the tile are formed
+  auto prep = [&](f32x16 (&s)[2], bool part, bool masked, int j0, auto dslot_c) -> TileMode {
+    constexpr int DSLOT = decltype(dslot_c)::value;
+    const int32_t* dl = reinterpret_cast<const int32_t*>(smem + 4 * L::TILE + DSLOT * KT * 4);
+    const int jl = j0 + 4 * half;   // key of element (mt=0, rr=0) in this lane
     if (masked) {
       if constexpr (MK == MK_GENERIC) {
 #pragma unroll
@@ -339,7 +255,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
             const int j = jl + key_of(mt, rr);
             bool ok = (unsigned)j < (unsigned)kv_len;
             if (part && ok) ok = mask_allowed(p.prog, i_g, j, doc_i, p.prog.has_doc ? docr[j] : 0);
-            sacc[mt][rr] = ok ? sacc[mt][rr] : kNegInf;
+            s[mt][rr] = ok ? s[mt][rr] : kNegInf;
           }
       } else {
         // keys outside [lo, hi] (hi already clipped to kv_len - 1) are masked; when only
@@ -368,45 +284,26 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
               const int rr = 4 * g4 + e;
               const uint32_t j = (uint32_t)(jl + key_of(mt, rr));
               const bool ok = (j - lo_t) <= span_t && dq[e] == doc_i;
-              sacc[mt][rr] = ok ? sacc[mt][rr] : kNegInf;
+              s[mt][rr] = ok ? s[mt][rr] : kNegInf;
             }
           }
       }
     }
 
-    // score_mod to the base-2 domain and the tile maximum.  Monotone kinds keep the raw
-    // score in sacc (tile maximum mapped once); the others store
-    // t = log2(e) * score_mod(s * scale) in sacc.
-    bool raw_mode;
+    // Monotone kinds keep the raw score (the tile maximum is mapped once); the others
+    // store t = log2(e) * score_mod(s * scale) (-inf stays -inf).
+    bool raw;
     float bias2 = 0.f;  // constant base-2 bias of a saturated relative-position tile
-    if constexpr (SCORE == FA_S_IDENTITY || SCORE == FA_S_SOFTCAP) {
-      raw_mode = true;
+    if constexpr (SCORE == FA_S_IDENTITY) {
+      raw = true;
+    } else if constexpr (SCORE == FA_S_SOFTCAP) {
+      raw = true;   // monotone: the maximum is taken on raw scores
     } else if constexpr (SCORE == FA_S_RELPOS) {
       const int dmin = i_wave0 - (j0 + KT - 1);
       const int dmax = i_wave0 + 31 - j0;
-      raw_mode = dmin >= R || dmax <= -R;
+      raw = dmin >= R || dmax <= -R;
       bias2 = dmin >= R ? bias_far2 : bias_ahead2;
-    } else {
-      raw_mode = false;
-    }
-    float tmax = kNegInf;
-    if (raw_mode) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, sacc[mt][rr]);
-    } else {
-      if constexpr (SCORE == FA_S_ALIBI) {
-        const float base = sc.slope2 * (float)(jl - i_g);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const float t = __builtin_fmaf(sacc[mt][rr], sc.c2, __builtin_fmaf(sc.slope2, (float)key_of(mt, rr), base));
-            sacc[mt][rr] = t;
-            tmax = fmaxf(tmax, t);
-          }
-      } else if constexpr (SCORE == FA_S_RELPOS) {
+      if (!raw) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -414,24 +311,35 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
             int rel = i_g - (jl + key_of(mt, rr));
             rel = rel < -R ? -R : (rel > R ? R : rel);
             const float bb = rel_in_lds ? rel_lds[rel + R] : sc.tab[rel + R] * kLog2e;
-            const float t = __builtin_fmaf(sacc[mt][rr], sc.c2, bb);
-            sacc[mt][rr] = t;
-            tmax = fmaxf(tmax, t);
+            s[mt][rr] = __builtin_fmaf(s[mt][rr], sc.c2, bb);
           }
       }
+    } else {
+      raw = false;
+      const float base = sc.slope2 * (float)(jl - i_g);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+          s[mt][rr] = __builtin_fmaf(s[mt][rr], sc.c2, __builtin_fmaf(sc.slope2, (float)key_of(mt, rr), base));
     }
+    float tmax = kNegInf;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, s[mt][rr]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     // map a raw-score maximum into the base-2 domain
     float m_cand = tmax;
-    if (raw_mode && tmax != kNegInf) {
+    if (raw && tmax != kNegInf) {
       if constexpr (SCORE == FA_S_SOFTCAP) {
         m_cand = sc.cap2 - 2.f * sc.cap2 * fast_rcp(fast_exp2(tmax * sc.capk) + 1.f);
       } else {
         m_cand = __builtin_fmaf(tmax, sc.c2, bias2);
       }
     }
-
-    // lazy online-softmax rescale (wave-uniform branch)
+    // lazy rescale (wave-uniform branch): the reference moves only when a row's tile
+    // maximum exceeds it by more than kRescaleThresh
     const bool grow = m_cand > m_run + kRescaleThresh;
     if (__ballot(grow) != 0) {
       const float m_new = grow ? m_cand : m_run;
@@ -442,62 +350,118 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
     }
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-    const float softcap_c = sc.cap2 - m_use;
-    const float raw_c = bias2 - m_use;
-
-    // weights P (bf16), row sum and O^T += V^T P^T, one 16-key step at a time
-    float psum = 0.f;
-    // P for the 8 elements of 16-key step t (packed bf16 pairs); CHECK re-applies the
-    // mask where the soft-cap would map a -inf score to a finite value
-    auto p_step = [&](int t, u32x4& pk, auto check_c) {
-      constexpr bool CHECK = decltype(check_c)::value;
+    TileMode md;
+    md.one = 1.f;
+    if constexpr (SCORE == FA_S_SOFTCAP) {
+      md.mul = 0.f;
+      md.add = sc.cap2 - m_use;
+      if (masked) {
+        // y = log2(exp2(s capk) + 1) / capk keeps -inf and reproduces the weight with one = 0
+        const float inv_k = 1.f / sc.capk;
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        float pv[2];
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const float x = sacc[t >> 1][8 * (t & 1) + 2 * e2 + h2];
-          float arg;
-          if constexpr (SCORE == FA_S_SOFTCAP) {
-            const float rr = fast_rcp(fast_exp2(x * sc.capk) + 1.f);
-            arg = __builtin_fmaf(-2.f * sc.cap2, rr, softcap_c);
-            if constexpr (CHECK) arg = (x == kNegInf) ? kNegInf : arg;
-          } else if constexpr (SCORE == FA_S_IDENTITY) {
-            arg = __builtin_fmaf(x, sc.c2, -m_use);
-          } else {
-            arg = raw_mode ? __builtin_fmaf(x, sc.c2, raw_c) : x - m_use;
+          for (int rr = 0; rr < 16; ++rr) {
+            const float x = s[mt][rr];
+            const float y = fast_log2(fast_exp2(x * sc.capk) + 1.f) * inv_k;
+            s[mt][rr] = (x == kNegInf) ? kNegInf : y;
           }
-          pv[h2] = fast_exp2(arg);
-        }
-        pk[e2] = cvt_pk_bf16(pv[0], pv[1]);
-        psum += pv[0] + pv[1];
+        md.one = 0.f;
+      }
+    } else if (raw) {
+      md.mul = sc.c2;
+      md.add = bias2 - m_use;
+    } else {
+      md.mul = 1.f;
+      md.add = -m_use;
+    }
+    return md;
+  };
+
+  // ---- one pipelined step: the weights P of the tile in s (bf16 pairs), O^T += V^T P^T
+  // with V from V slot VS, and (QK) the scores of the next tile into sn from K slot KS.
+  // Five groups, fenced for the scheduler: group g reads V of 16-key step g-1 and K of
+  // quarter g of the next QK product, forms P of step g (VALU that covers the LDS
+  // latency), then multiplies P of step g-1 with V and runs QK quarter g; no MFMA of a
+  // group waits on VALU of the same group.
+  auto fused = [&](auto vs_c, auto ks_c, const f32x16 (&s)[2], f32x16 (&sn)[2],
+                   const TileMode& md) -> float {
+    constexpr int VS = decltype(vs_c)::value;
+    constexpr int KS = decltype(ks_c)::value;
+    constexpr bool QK = true;
+    constexpr int KQ = KSTEPS / 2;   // k-steps per quarter of the QK product
+    const uint8_t* vb = smem + (2 + VS) * L::TILE;
+    const uint8_t* kb = smem + KS * L::TILE;
+    float psum = 0.f;
+    u32x4 kf[KQ];
+    bf16x8 vf[DM];
+    u32x4 pk[2];
+    auto read_k = [&](auto q_c, u32x4 (&dst)[KQ]) {
+      constexpr int q = decltype(q_c)::value;
+#pragma unroll
+      for (int i = 0; i < KQ; ++i) {
+        const int t = (q & 1) * KQ + i;
+        dst[i] = *reinterpret_cast<const u32x4*>(kb + kaddr[t & 3] + (t >> 2) * 128 + (q >> 1) * 32 * L::KROW);
       }
     };
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4 pk;
-      if (SCORE == FA_S_SOFTCAP && masked) {
-        p_step(t, pk, std::true_type{});
-      } else {
-        p_step(t, pk, std::false_type{});
-      }
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
-      // V^T fragment rows d = 32 dm + (lane & 31), keys of this step in the slot order
-      // of P^T: two transposing reads of 4 keys x 16 head-dim indices per 16-lane group
+    auto read_v = [&](auto t_c, bf16x8 (&dst)[DM]) {
+      constexpr int t = decltype(t_c)::value;
 #pragma unroll
       for (int dm = 0; dm < DM; ++dm) {
         const uint8_t* va = vb + vaddr[dm] + 16 * t * L::KROW;
         const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va));
         const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(va + 8 * L::KROW));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[dm] = mfma32(a, pb, oacc[dm]);
+        dst[dm] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-    }
-    l_run += psum;
+    };
+    auto p_step = [&](auto t_c, u32x4& dst) {
+      constexpr int t = decltype(t_c)::value;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float pv2[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const float x = s[t >> 1][8 * (t & 1) + 2 * e2 + h2];
+          float arg;
+          if constexpr (SCORE == FA_S_SOFTCAP) {
+            const float rr = fast_rcp(fast_exp2(x * sc.capk) + md.one);
+            arg = __builtin_fmaf(-2.f * sc.cap2, rr, md.add);
+          } else {
+            arg = __builtin_fmaf(x, md.mul, md.add);
+          }
+          pv2[h2] = fast_exp2(arg);
+        }
+        dst[e2] = cvt_pk_bf16(pv2[0], pv2[1]);
+        psum += pv2[0] + pv2[1];
+      }
+    };
+    static_for<5>([&](auto g_c) {
+      constexpr int g = decltype(g_c)::value;
+      if constexpr (g >= 1) read_v(std::integral_constant<int, g - 1>{}, vf);
+      if constexpr (QK && g < 4) read_k(g_c, kf);
+      if constexpr (g < 4) p_step(g_c, pk[g & 1]);
+      if constexpr (g >= 1) {
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[(g - 1) & 1]);
+#pragma unroll
+        for (int dm = 0; dm < DM; ++dm) oacc[dm] = mfma32(vf[dm], pb, oacc[dm]);
+      }
+      if constexpr (QK && g < 4) {
+        constexpr int mt = g >> 1;
+        if constexpr ((g & 1) == 0) sn[mt] = f32x16{};
+#pragma unroll
+        for (int i = 0; i < KQ; ++i)
+          sn[mt] = mfma32(__builtin_bit_cast(bf16x8, kf[i]), qf[(g & 1) * KQ + i], sn[mt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    return psum;
   };
 
-  // ---- the row's block list (full entries, then partial) in passes of kListCap entries
+  // ---- the row's block list (full entries, then partial) in passes of kListCap entries.
+  // Software pipeline over sub-tiles: while the weights of sub-tile s are formed and
+  // multiplied with V_s, the scores of s+1 are computed from K_{s+1}; K runs one sub-tile
+  // ahead of V in the copies (K_{s+2} and V_{s+1} are in flight during step s).
   for (int c0 = 0; c0 < n_ent; c0 += kListCap) {
     const int cnt = min(kListCap, n_ent - c0);
     for (int e = tid; e < cnt; e += NT) {
@@ -506,35 +470,45 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
     }
     __syncthreads();
     const int nsub = cnt << spb_sh;
-    auto sub_j0 = [&](int s, bool& part) -> int {
-      const int blk = s >> spb_sh;
-      part = c0 + blk >= nf;
-      return uniform(list_s[blk]) * bk + (s & spb_sh) * KT;
-    };
-    bool part_cur = false;
-    int j0_cur = sub_j0(0, part_cur);
-    copy_tile(j0_cur, std::integral_constant<int, 0>{});
+    auto sub_j0 = [&](int s) -> int { return uniform(list_s[s >> spb_sh]) * bk + (s & spb_sh) * KT; };
+    auto sub_part = [&](int s) -> bool { return c0 + (s >> spb_sh) >= nf; };
+
+    // prologue: K_0, V_0 (and K_1) resident, scores of sub-tile 0 prepared
+    int j0_a = sub_j0(0);                       // sub-tile s
+    int j0_b = nsub > 1 ? sub_j0(1) : 0;        // sub-tile s + 1
+    copy_op(j0_a, std::false_type{}, std::integral_constant<int, 0>{});
+    copy_op(j0_a, std::true_type{}, std::integral_constant<int, 0>{});
+    if (nsub > 1) copy_op(j0_b, std::false_type{}, std::integral_constant<int, 1>{});
     wait_dma();
     __syncthreads();
+    f32x16 sa[2], sb[2];
+    qk(std::integral_constant<int, 0>{}, sa);
+    TileMode md = prep(sa, sub_part(0), sub_part(0) || j0_a + KT > kv_len, j0_a, std::integral_constant<int, 0>{});
 
-    // sub-tile s from one slot while s+1 is copied into the other
-    auto step = [&](int s, auto slot_c) {
-      constexpr int SLOT = decltype(slot_c)::value;
-      bool part_nxt = false;
-      int j0_nxt = 0;
-      if (s + 1 < nsub) {
-        j0_nxt = sub_j0(s + 1, part_nxt);
-        copy_tile(j0_nxt, std::integral_constant<int, 1 - SLOT>{});
+    // step s (slot parity P = s & 1): V_s in V slot P, K_{s+1} in K slot 1-P; copies of
+    // K_{s+2} into K slot P and V_{s+1} into V slot 1-P
+    auto step = [&](int s, auto par_c, f32x16 (&scur)[2], f32x16 (&snxt)[2]) {
+      constexpr int P = decltype(par_c)::value;
+      using SP = std::integral_constant<int, P>;
+      using SQ = std::integral_constant<int, 1 - P>;
+      const bool more = s + 1 < nsub;
+      if (s + 2 < nsub) copy_op(sub_j0(s + 2), std::false_type{}, SP{});
+      if (more) copy_op(j0_b, std::true_type{}, SQ{});
+      // the last step of a pass also multiplies the (stale) other K slot: its scores are
+      // discarded, and one code path keeps the register allocation of the loop intact
+      l_run += fused(SP{}, SQ{}, scur, snxt, md);
+      if (more) {
+        const bool part = sub_part(s + 1);
+        md = prep(snxt, part, part || j0_b + KT > kv_len, j0_b, SQ{});
+        j0_a = j0_b;
+        j0_b = s + 2 < nsub ? sub_j0(s + 2) : 0;
       }
-      compute(slot_c, part_cur || j0_cur + KT > kv_len, part_cur, j0_cur);
       wait_dma();
       __syncthreads();
-      part_cur = part_nxt;
-      j0_cur = j0_nxt;
     };
     for (int s = 0; s < nsub; s += 2) {
-      step(s, std::integral_constant<int, 0>{});
-      if (s + 1 < nsub) step(s + 1, std::integral_constant<int, 1>{});
+      step(s, std::integral_constant<int, 0>{}, sa, sb);
+      if (s + 1 < nsub) step(s + 1, std::integral_constant<int, 1>{}, sb, sa);
     }
   }
 
