@@ -38,8 +38,9 @@ def common_flags():
             "-Wno-unused-result"]
 
 
-# per-file device code generation options
-FILE_FLAGS = {}
+# per-file device code generation options: decode keeps MFMA results in VGPRs (its
+# softmax reads every score)
+FILE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def compile_one(src, verbose=False, resource_usage=False):

@@ -9,59 +9,68 @@
 // would be wrong.  The merge law itself is "Kernels: turning logical sparsity into real
 // speed", section 3.
 //
-// gfx950 mapping
-//   * one workgroup (4 waves) per (b, h_kv, split); the g = Hq/Hkv query heads that share
-//     a KV head, times q_len positions, form the 32 columns of one MFMA tile, so every
-//     K/V byte is read from HBM once per (b, h_kv).
-//   * a split is a contiguous range of the row's listed blocks with equal block counts.
-//     Each iteration stages one 128-key block (K row-major, V transposed, both
-//     XOR-swizzled) into LDS with 16-byte coalesced loads; the next block's loads are in
-//     flight in registers while the current one is computed.  Wave w takes keys
-//     32w .. 32w+31 of the block and keeps its own online-softmax state.
-//   * the four wave states are merged through LDS at the end of the split and written
-//     as (m, l, o) partials; a second small kernel merges the splits.
+// gfx950 mapping (the kernel is bound by HBM bandwidth, so the design maximises the
+// bytes in flight per CU):
+//   * a work unit is (b, h_kv, split); the g = Hq/Hkv query heads that share the KV head,
+//     times q_len positions, form the columns of one 32-column MFMA tile, so every K/V
+//     byte is read from HBM once per (b, h_kv).  A split is a contiguous range of the
+//     row's listed blocks with equal block counts.
+//   * each wave runs one unit on its own: no barriers.  It streams 32-key stages
+//     HBM -> LDS with global_load_lds_dwordx4 (no staging registers) into a private ring
+//     of kStages slots and keeps kStages - 1 stages in flight while it computes one;
+//     a vmcnt wait per stage is the only synchronisation.  The ring of two waves fills
+//     most of the LDS, so up to ~96 KB per CU are in flight.
+//   * K and V of a stage are row-major in LDS with the XOR swizzles of the prefill
+//     kernels (K 16-byte chunks by key & 7, V 32-byte units by key & 7): scores from
+//     ds_read_b128 fragments, the P V operand from ds_read_b64_tr_b16.
+//   * with one split the wave writes O and LSE itself; otherwise it writes its
+//     (m, l, o) partial and a second small kernel merges the splits.
 #include "device_common.hpp"
 #include "fa_internal.hpp"
+#include "prefill_common.hpp"
 
 namespace fa {
 
 namespace {
 
-constexpr int DKT = 128;  // keys per decode iteration (one 128-key block)
+constexpr int DKT = 128;     // block size of the block table rows decoded here
+constexpr int SK = 32;       // keys per stage
+constexpr int kStages = 4;   // LDS ring slots per wave
+constexpr int kDecWaves = 2; // independent waves (units) per workgroup
 
 template <int D>
 struct DLds {
-  static constexpr int KROW = D * 2;
-  static constexpr int VROW = DKT * 2;
-  static constexpr int KBYTES = DKT * KROW;
-  static constexpr int VBYTES = D * VROW;
-  static constexpr int BUF = KBYTES + VBYTES;
+  static constexpr int KROW = D * 2;            // bytes per K or V row
+  static constexpr int HALF = SK * KROW;        // K (or V) part of a stage
+  static constexpr int STAGE = 2 * HALF;        // K then V
+  static constexpr int WAVE = kStages * STAGE;  // one wave's ring
+  static constexpr int UNITS = D / 16;          // 32-byte units per V row
 };
 
-__device__ __forceinline__ int dk_off(int key, int ch, int krow) { return key * krow + ((ch ^ (key & 7)) << 4); }
-__device__ __forceinline__ int dvt_off(int d, int pc) { return d * (DKT * 2) + ((pc ^ (d & 7)) << 4); }
-
 template <int D, int SCORE>
-__global__ __launch_bounds__(256, 1) void decode_kernel(FwdParams p) {
-  constexpr int NT = 256;
+__global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) {
   constexpr int DCH = D / 8;
   constexpr int KSTEPS = D / 16;
   constexpr int DM = D / 32;
-  constexpr int KCH = DKT * DCH / NT;     // K chunks per thread
-  constexpr int NQUAD = 32 * DCH;         // V units of 4 keys x 8 dims
-  constexpr int VQ = NQUAD / NT;
+  constexpr int KPK = 1024 / (D * 2);          // keys per 1 KB copy
+  constexpr int CPO = SK / KPK;                // copies per operand per stage
+  constexpr int CPS = 2 * CPO;                 // copies per stage
+  constexpr int VAR = KPK >= 8 ? 1 : 8 / KPK;
   using L = DLds<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * L::BUF];
+  static_assert(CPS * (kStages - 1) <= 63, "outstanding copies must fit the vmcnt counter");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kDecWaves * L::WAVE];
 
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int lane = tid & 63;
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
 
   const int ns = p.nsplit;
-  const int s_id = blockIdx.x % ns;
-  const int bk_id = blockIdx.x / ns;       // b * Hkv + h_kv
+  const int64_t unit = (int64_t)blockIdx.x * kDecWaves + w;
+  const int64_t units = (int64_t)p.B * p.Hkv * ns;
+  if (unit >= units) return;   // wave-uniform: no barrier follows
+  const int s_id = (int)(unit % ns);
+  const int bk_id = (int)(unit / ns);      // b * Hkv + h_kv
   const int b = bk_id / p.Hkv;
   const int hkv = bk_id - b * p.Hkv;
   const int q_len = (int)p.q_len;
@@ -97,6 +106,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(FwdParams p) {
   const int n_ent = nf + np;
   const int e_begin = (int)(((int64_t)s_id * n_ent) / ns);
   const int e_end = (int)(((int64_t)(s_id + 1) * n_ent) / ns);
+  const int nst = (e_end - e_begin) * (DKT / SK);
 
   const uint16_t* kbase = p.k + (int64_t)bk_id * p.kv_len * D;
   const uint16_t* vbase = p.v + (int64_t)bk_id * p.kv_len * D;
@@ -104,60 +114,77 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(FwdParams p) {
   const int doc_i = (p.prog.has_doc && col_ok) ? docr[i_g] : 0;
   const ScoreCtx sc = make_score_ctx(p.score, p.scale, hq);
 
-  auto ent_j0 = [&](int e, bool& partial) -> int {
-    partial = e >= nf;
-    const int c = partial ? plist[e - nf] : flist[e];
-    return uniform(c) * DKT;
+  // the unit's block list, 64 entries per register (lane e holds entry base + e)
+  int lst_base = 0;
+  auto load_list = [&](int base) -> int {
+    const int e = e_begin + base + lane;
+    return e < e_end ? (e < nf ? flist[e] : plist[e - nf]) : 0;
+  };
+  int lst = load_list(0);
+#pragma unroll
+  for (int t = 0; t < KSTEPS; ++t) asm volatile("" : "+v"(qf[t]));
+  asm volatile("" : "+v"(lst));   // loads complete before the copies start
+  auto stage_j0 = [&](int s) -> int {
+    const int e = s / (DKT / SK);
+    if (e - lst_base >= 64) {   // rare: next 64 entries (waits for all copies in flight)
+      lst_base += 64;
+      lst = load_list(lst_base);
+    }
+    return __builtin_amdgcn_readlane(lst, e - lst_base) * DKT + (s % (DKT / SK)) * SK;
+  };
+  auto stage_part = [&](int s) -> bool { return e_begin + s / (DKT / SK) >= nf; };
+
+  // per-lane copy offsets (swizzles as in the prefill kernels)
+  uint32_t koff[VAR], voff[VAR];
+#pragma unroll
+  for (int var = 0; var < VAR; ++var) {
+    const int key_in = lane / DCH;
+    const int pc = lane % DCH;
+    const int key7 = (var * KPK + key_in) & 7;
+    koff[var] = (uint32_t)(key_in * L::KROW + ((pc ^ key7) << 4));
+    voff[var] = (uint32_t)(key_in * L::KROW + ((2 * (((pc >> 1) ^ key7) & (L::UNITS - 1)) + (pc & 1)) << 4));
+  }
+  uint8_t* ring = smem + w * L::WAVE;
+  const uint32_t ring_lds = lds_addr(ring);
+
+  // one stage (32 keys from j0) into ring slot `slot`
+  auto copy_stage = [&](int j0, int slot) {
+    const uint32_t mk = sreg(ring_lds + (uint32_t)slot * L::STAGE);
+    const uint32_t mv = mk + L::HALF;
+    if (j0 + SK <= kv_len) {
+      const char* kg = (const char*)kbase + (int64_t)j0 * L::KROW;
+      const char* vg = (const char*)vbase + (int64_t)j0 * L::KROW;
+      static_for<CPO>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        constexpr int grp = (u / 4) * 4096;   // immediate offsets stay below 4 KB
+        dma16_s<(u % 4) * 1024>(mk + grp, kg + grp, koff[u % VAR]);
+        dma16_s<(u % 4) * 1024>(mv + grp, vg + grp, voff[u % VAR]);
+      });
+    } else {
+      // ragged tail: keys past kv_len re-read the last key (they are masked); offsets
+      // from jb = min(j0, kv_len - 1) stay non-negative
+      const int jb = min(j0, kv_len - 1);
+      const char* kg = (const char*)kbase + (int64_t)jb * L::KROW;
+      const char* vg = (const char*)vbase + (int64_t)jb * L::KROW;
+      static_for<CPO>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        const int key = u * KPK + lane / DCH;
+        const uint32_t rowoff = (uint32_t)(min(j0 + key, kv_len - 1) - jb) * L::KROW;
+        dma16_s<0>(mk + u * 1024, kg, rowoff + (koff[u % VAR] & (L::KROW - 1)));
+        dma16_s<0>(mv + u * 1024, vg, rowoff + (voff[u % VAR] & (L::KROW - 1)));
+      });
+    }
   };
 
-  u32x4 kreg[KCH];
-  u32x4 vreg[VQ][4];
-  auto load_tile = [&](int j0) {
+  // per-lane LDS read bases: K fragment t (key col, chunk 2t + half), V^T fragment of
+  // head-dim tile dm (keys 4 half + (li >> 2) (+8, +16 per k-step), d0 = 32 dm + ...)
+  const int g16 = lane >> 4, li = lane & 15;
+  uint32_t kaddr[4], vaddr[DM];
 #pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int f = tid + NT * u;
-      const int key = f / DCH, ch = f % DCH;
-      const int j = j0 + key;
-      kreg[u] = (unsigned)j < (unsigned)kv_len ? load16(kbase + (int64_t)j * D + ch * 8) : u32x4{0, 0, 0, 0};
-    }
+  for (int t = 0; t < 4; ++t) kaddr[t] = (uint32_t)k_off(col, 2 * t + half, L::KROW);
 #pragma unroll
-    for (int u = 0; u < VQ; ++u) {
-      const int qd = tid + NT * u;
-      const int kq = qd / DCH, dc = qd % DCH;
-      const int ww = kq >> 3, tq = (kq >> 2) & 1, a = (kq >> 1) & 1, h2 = kq & 1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + 32 * ww + 16 * tq + 8 * a + 4 * h2 + e;
-        vreg[u][e] = (unsigned)j < (unsigned)kv_len ? load16(vbase + (int64_t)j * D + dc * 8) : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](uint8_t* buf) {
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int f = tid + NT * u;
-      const int key = f / DCH, ch = f % DCH;
-      *reinterpret_cast<u32x4*>(buf + dk_off(key, ch, L::KROW)) = kreg[u];
-    }
-    uint8_t* vt = buf + L::KBYTES;
-#pragma unroll
-    for (int u = 0; u < VQ; ++u) {
-      const int qd = tid + NT * u;
-      const int kq = qd / DCH, dc = qd % DCH;
-      const int ww = kq >> 3, tq = (kq >> 2) & 1, a = (kq >> 1) & 1, h2 = kq & 1;
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int sh = (dd & 1) * 16;
-        const uint32_t e0 = (vreg[u][0][dd >> 1] >> sh) & 0xffffu;
-        const uint32_t e1 = (vreg[u][1][dd >> 1] >> sh) & 0xffffu;
-        const uint32_t e2 = (vreg[u][2][dd >> 1] >> sh) & 0xffffu;
-        const uint32_t e3 = (vreg[u][3][dd >> 1] >> sh) & 0xffffu;
-        const int d = dc * 8 + dd;
-        *reinterpret_cast<u32x2*>(vt + dvt_off(d, 4 * ww + 2 * tq + h2) + 8 * a) =
-            u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
-      }
-    }
-  };
+  for (int dm = 0; dm < DM; ++dm)
+    vaddr[dm] = (uint32_t)v_off<D>(4 * half + (li >> 2), 32 * dm + 16 * (g16 & 1) + 4 * (li & 3));
 
   float m_run = kNegInf;
   float l_run = 0.f;
@@ -165,138 +192,141 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(FwdParams p) {
 #pragma unroll
   for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
 
-  bool part_cur = false;
-  int j0_cur = 0;
-  if (e_begin < e_end) {
-    j0_cur = ent_j0(e_begin, part_cur);
-    load_tile(j0_cur);
-  }
-  for (int e = e_begin; e < e_end; ++e) {
-    uint8_t* buf = smem + ((e - e_begin) & 1) * L::BUF;
-    store_tile(buf);
-    __syncthreads();
-    bool part_nxt = false;
-    int j0_nxt = 0;
-    if (e + 1 < e_end) {
-      j0_nxt = ent_j0(e + 1, part_nxt);
-      load_tile(j0_nxt);
+  // prologue: fill the ring
+  int issued = 0;
+  int j0_of[kStages];
+#pragma unroll
+  for (int k = 0; k < kStages; ++k) {
+    if (k < nst) {
+      j0_of[k] = stage_j0(k);
+      copy_stage(j0_of[k], k);
+      ++issued;
     }
+  }
 
-    // S^T for keys 32w .. 32w+31 of the block
+  for (int s = 0; s < nst; ++s) {
+    const int slot = s % kStages;
+    // stage s has landed once at most (issued - s - 1) stages of copies are outstanding
+    switch (issued - s - 1) {
+      case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+      case 1: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(CPS) : "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(2 * CPS) : "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(3 * CPS) : "memory"); break;
+    }
+    int j0 = 0;
+#pragma unroll
+    for (int k = 0; k < kStages; ++k)
+      if (k == slot) j0 = j0_of[k];
+    const bool part = stage_part(s);
+    const uint8_t* kb = ring + slot * L::STAGE;
+    const uint8_t* vb = kb + L::HALF;
+
+    // S^T for the 32 keys of the stage
     f32x16 sacc = f32x16{};
-    const int key = 32 * w + col;
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(buf + dk_off(key, 2 * t + half, L::KROW));
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + kaddr[t & 3] + (t >> 2) * 128);
       sacc = mfma32(__builtin_bit_cast(bf16x8, kv), qf[t], sacc);
     }
 
-    const bool ragged = j0_cur + DKT > kv_len;
+    // score_mod first, then the mask (-inf) on partial and ragged stages only
+    const int jl = j0 + 4 * half;   // key of register 0 in this lane
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) sacc[rr] = score_log2<SCORE>(sacc[rr], sc, i_g, jl + key_of(0, rr));
+    if (part || j0 + SK > kv_len) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int j = jl + key_of(0, rr);
+        bool ok = (unsigned)j < (unsigned)kv_len;
+        if (part && ok) ok = mask_allowed(p.prog, i_g, j, doc_i, p.prog.has_doc ? docr[j] : 0);
+        sacc[rr] = ok ? sacc[rr] : kNegInf;
+      }
+    }
     float tmax = kNegInf;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int j = j0_cur + 32 * w + 8 * (rr >> 2) + 4 * half + (rr & 3);
-      float t = score_log2<SCORE>(sacc[rr], sc, i_g, j);
-      if (ragged || part_cur) {
-        bool ok = (unsigned)j < (unsigned)kv_len;
-        if (part_cur && ok) {
-          const int doc_j = p.prog.has_doc ? docr[j] : 0;
-          ok = mask_allowed(p.prog, i_g, j, doc_i, doc_j);
-        }
-        t = ok ? t : kNegInf;
-      }
-      sacc[rr] = t;
-      tmax = fmaxf(tmax, t);
-    }
+    for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, sacc[rr]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    l_run *= alpha;
+    if (m_new > m_run) {
+      const float alpha = fast_exp2(m_run - m_use);   // 0 when m_run = -inf
+      l_run *= alpha;
 #pragma unroll
-    for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
+      for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
+    }
+    m_run = m_new;
 
-    bf16x8 pb[2];
     float psum = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t2 = 0; t2 < 2; ++t2) {
       u32x4 pk;
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        const float p0 = fast_exp2(sacc[8 * t + 2 * e2] - m_use);
-        const float p1 = fast_exp2(sacc[8 * t + 2 * e2 + 1] - m_use);
+        const float p0 = fast_exp2(sacc[8 * t2 + 2 * e2] - m_use);
+        const float p1 = fast_exp2(sacc[8 * t2 + 2 * e2 + 1] - m_use);
         psum += p0 + p1;
-        pk[e2] = pack_bf16x2(p0, p1);
+        pk[e2] = cvt_pk_bf16(p0, p1);
       }
-      pb[t] = __builtin_bit_cast(bf16x8, pk);
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
+#pragma unroll
+      for (int dm = 0; dm < DM; ++dm) {
+        const uint8_t* va = vb + vaddr[dm] + 16 * t2 * L::KROW;
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(va + 8 * L::KROW));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[dm] = mfma32(a, pb, oacc[dm]);
+      }
     }
     l_run += psum;
 
-    const uint8_t* vt = buf + L::KBYTES;
+    // refill this slot with stage s + kStages once its reads have completed
+    if (s + kStages < nst) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int jn = stage_j0(s + kStages);
 #pragma unroll
-    for (int dm = 0; dm < DM; ++dm) {
-      const int d = 32 * dm + col;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 vv = *reinterpret_cast<const u32x4*>(vt + dvt_off(d, 4 * w + 2 * t + half));
-        oacc[dm] = mfma32(__builtin_bit_cast(bf16x8, vv), pb[t], oacc[dm]);
-      }
+      for (int k = 0; k < kStages; ++k)
+        if (k == slot) j0_of[k] = jn;
+      copy_stage(jn, slot);
+      ++issued;
     }
-    part_cur = part_nxt;
-    j0_cur = j0_nxt;
   }
 
-  // ---- merge the four wave states through LDS, write this split's partial
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);            // [4][32] m, [4][32] l, [4][D][32] o
-  float* red_m = red;
-  float* red_l = red + 4 * 32;
-  float* red_o = red + 8 * 32;
+  // ---- results: final O and LSE (one split) or this split's (m, l, o) partial
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (half == 0) {
-    red_m[w * 32 + col] = m_run;
-    red_l[w * 32 + col] = l_tot;
-  }
+  if (!col_ok) return;
+  if (ns == 1) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* o = p.o + orow * D;
 #pragma unroll
-  for (int dm = 0; dm < DM; ++dm) {
+    for (int dm = 0; dm < DM; ++dm) {
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int d = 32 * dm + 8 * (rr >> 2) + 4 * half + (rr & 3);
-      red_o[(w * D + d) * 32 + col] = oacc[dm][rr];
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = 32 * dm + 8 * gq + 4 * half;
+        u32x2 o2;
+        o2[0] = cvt_pk_bf16(oacc[dm][4 * gq + 0] * inv, oacc[dm][4 * gq + 1] * inv);
+        o2[1] = cvt_pk_bf16(oacc[dm][4 * gq + 2] * inv, oacc[dm][4 * gq + 3] * inv);
+        *reinterpret_cast<u32x2*>(o + d0) = o2;
+      }
     }
-  }
-  __syncthreads();
-  // thread t: column c = t % 32, dims (t / 32) + 8k
-  {
-    const int c = tid & 31;
-    if (c < ncols) {
-      float M = kNegInf;
+    if (half == 0) p.lse[orow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+  } else {
+    const int64_t rows = (int64_t)p.B * p.Hq * p.q_len;
+    const int64_t prow = orow * ns + s_id;
+    float* ws_m = p.ws;
+    float* ws_l = p.ws + rows * ns;
+    float* ws_o = p.ws + 2 * rows * ns;
+    if (half == 0) {
+      ws_m[prow] = m_run;
+      ws_l[prow] = l_tot;
+    }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) M = fmaxf(M, red_m[q * 32 + c]);
-      float wq[4];
-      float lsum = 0.f;
+    for (int dm = 0; dm < DM; ++dm) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float mq = red_m[q * 32 + c];
-        wq[q] = (mq == kNegInf) ? 0.f : fast_exp2(mq - M);
-        lsum += wq[q] * red_l[q * 32 + c];
-      }
-      const int hh2 = c / q_len;
-      const int ip2 = c - hh2 * q_len;
-      const int64_t prow = (((int64_t)(b * p.Hq + hkv * p.g + hh2)) * p.q_len + ip2) * ns + s_id;
-      float* ws_m = p.ws;
-      float* ws_l = p.ws + (int64_t)p.B * p.Hq * p.q_len * ns;
-      float* ws_o = p.ws + 2 * (int64_t)p.B * p.Hq * p.q_len * ns;
-      if ((tid >> 5) == 0) {
-        ws_m[prow] = M;
-        ws_l[prow] = lsum;
-      }
-      for (int d = tid >> 5; d < D; d += 8) {
-        float acc = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc += wq[q] * red_o[(q * D + d) * 32 + c];
-        ws_o[prow * D + d] = acc;
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = 32 * dm + 8 * gq + 4 * half;
+        f32x4 v4 = {oacc[dm][4 * gq + 0], oacc[dm][4 * gq + 1], oacc[dm][4 * gq + 2], oacc[dm][4 * gq + 3]};
+        *reinterpret_cast<f32x4*>(ws_o + prow * D + d0) = v4;
       }
     }
   }
@@ -330,9 +360,9 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   uint16_t* o = p.o + rowi * D + lane * PER;
   if constexpr (PER == 2) {
-    *reinterpret_cast<uint32_t*>(o) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    *reinterpret_cast<uint32_t*>(o) = cvt_pk_bf16(acc[0] * inv, acc[1] * inv);
   } else {
-    const uint32_t pk = pack_bf16x2(acc[0] * inv, 0.f);
+    const uint32_t pk = cvt_pk_bf16(acc[0] * inv, 0.f);
     o[0] = (uint16_t)(pk & 0xffffu);
   }
   if (lane == 0) p.lse[rowi] = lsum > 0.f ? (M + fast_log2(lsum)) * kLn2 : kNegInf;
@@ -344,9 +374,12 @@ bool decode_eligible(const FwdParams& p) {
   return p.tab.nqb == 1 && p.tab.bk == DKT && (int64_t)p.g * p.q_len <= 32 && p.q_len >= 1;
 }
 
+// splits per (b, h_kv): enough units for one wave per SIMD pair slot (kDecWaves waves per
+// CU, one workgroup per CU), capped by the listed block count of a row
 int32_t decode_splits(const FwdParams& p, int num_cus) {
   const int64_t items = (int64_t)p.B * p.Hkv;
-  int64_t ns = (4 * (int64_t)num_cus + items - 1) / items;
+  const int64_t slots = (int64_t)kDecWaves * num_cus;
+  int64_t ns = (slots + items - 1) / items;
   if (ns > p.tab.nkb) ns = p.tab.nkb;
   if (ns > 64) ns = 64;
   if (ns < 1) ns = 1;
@@ -354,13 +387,15 @@ int32_t decode_splits(const FwdParams& p, int num_cus) {
 }
 
 size_t decode_workspace_bytes(const FwdParams& p, int32_t nsplit) {
+  if (nsplit <= 1) return 0;   // one split writes O and LSE directly
   const size_t rows = (size_t)p.B * p.Hq * p.q_len;
   return rows * nsplit * (2 + (size_t)p.d) * sizeof(float);
 }
 
 hipError_t launch_decode(const FwdParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.nsplit));
-  const dim3 block(256);
+  const int64_t units = (int64_t)p.B * p.Hkv * p.nsplit;
+  const dim3 grid((unsigned)((units + kDecWaves - 1) / kDecWaves));
+  const dim3 block(64 * kDecWaves);
 #define FA_DEC(DD, SS) hipLaunchKernelGGL((decode_kernel<DD, SS>), grid, block, 0, s, p)
   if (p.d == 128) {
     switch (p.score.kind) {
@@ -379,11 +414,11 @@ hipError_t launch_decode(const FwdParams& p, hipStream_t s) {
   }
 #undef FA_DEC
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.nsplit <= 1) return e;
   const int64_t rows = (int64_t)p.B * p.Hq * p.q_len;
   const dim3 cgrid((unsigned)((rows + 3) / 4));
-  if (p.d == 128) hipLaunchKernelGGL((combine_kernel<128>), cgrid, block, 0, s, p);
-  else hipLaunchKernelGGL((combine_kernel<64>), cgrid, block, 0, s, p);
+  if (p.d == 128) hipLaunchKernelGGL((combine_kernel<128>), cgrid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((combine_kernel<64>), cgrid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
