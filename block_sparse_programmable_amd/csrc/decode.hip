@@ -9,22 +9,23 @@
 // would be wrong.  The merge law itself is "Kernels: turning logical sparsity into real
 // speed", section 3.
 //
-// gfx950 mapping (the kernel is bound by HBM bandwidth, so the design maximises the
-// bytes in flight per CU):
+// gfx950 mapping (the kernel is bound by HBM bandwidth, so the design keeps many bytes
+// in flight per CU and little work per byte):
 //   * a work unit is (b, h_kv, split); the g = Hq/Hkv query heads that share the KV head,
-//     times q_len positions, form the columns of one 32-column MFMA tile, so every K/V
-//     byte is read from HBM once per (b, h_kv).  A split is a contiguous range of the
-//     row's listed blocks with equal block counts.
-//   * each wave runs one unit on its own: no barriers.  It streams 32-key stages
-//     HBM -> LDS with global_load_lds_dwordx4 (no staging registers) into a private ring
-//     of kStages slots and keeps kStages - 1 stages in flight while it computes one;
-//     a vmcnt wait per stage is the only synchronisation.  The ring of two waves fills
-//     most of the LDS, so up to ~96 KB per CU are in flight.
+//     times q_len positions (at most 16), form the columns of 16x16x32 MFMA tiles, so
+//     every K/V byte is read from HBM once per (b, h_kv).  A split is a contiguous range
+//     of the row's listed blocks with equal block counts.
+//   * each wave runs one unit on its own: no barriers.  It streams 16-key stages
+//     HBM -> LDS with global_load_lds_dwordx4 (no staging registers) into a private
+//     five-slot ring and keeps four stages in flight while it computes one; a vmcnt
+//     wait per stage is the only synchronisation.  Four waves per CU fill the 160 KB
+//     of LDS.
 //   * K and V of a stage are row-major in LDS with the XOR swizzles of the prefill
 //     kernels (K 16-byte chunks by key & 7, V 32-byte units by key & 7): scores from
 //     ds_read_b128 fragments, the P V operand from ds_read_b64_tr_b16.
-//   * with one split the wave writes O and LSE itself; otherwise it writes its
-//     (m, l, o) partial and a second small kernel merges the splits.
+//   * with one split the wave writes O and LSE itself; when the splits of a (b, h_kv)
+//     share a workgroup they are merged through LDS after the stream; otherwise each
+//     wave writes its (m, l, o) partial and a second small kernel merges the splits.
 #include "device_common.hpp"
 #include "fa_internal.hpp"
 #include "prefill_common.hpp"
@@ -34,9 +35,10 @@ namespace fa {
 namespace {
 
 constexpr int DKT = 128;     // block size of the block table rows decoded here
-constexpr int SK = 32;       // keys per stage
-constexpr int kStages = 4;   // LDS ring slots per wave
-constexpr int kDecWaves = 2; // independent waves (units) per workgroup
+constexpr int SK = 16;       // keys per stage
+constexpr int kStages = 5;   // LDS ring slots per wave
+constexpr int kDecWaves = 4; // independent waves (units) per workgroup
+constexpr int kDecCols = 16; // query columns (heads sharing a KV head x positions)
 
 template <int D>
 struct DLds {
@@ -47,28 +49,50 @@ struct DLds {
   static constexpr int UNITS = D / 16;          // 32-byte units per V row
 };
 
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  // D[i][n] += sum_k A[i][k] B[k][n]; lane l holds A[l%16][8(l/16)..+8] and
+  // B[8(l/16)..+8][l%16]; D: lane l, register r -> row 4(l/16) + r, column l%16.
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16k16(const s16x4& a, const s16x4& b, const f32x4& c) {
+  // as above with a 16-deep contraction: lane l holds A[l%16][4(l/16)..+4] and
+  // B[4(l/16)..+4][l%16]
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Scores S^T (keys x columns) of a 16-key stage on 16x16x32 MFMAs (contraction over the
+// head dim), O^T (head-dim x columns) on 16x16x16 MFMAs (contraction over the stage's
+// keys).  In lane l (group g = l/16, column l%16) S^T register r holds key 4g + r,
+// which is exactly the P^T operand of the P V product; the V^T operand of lane l
+// (d = 16 dt + l%16, keys 4g .. 4g+3) is one transposing LDS read.
 template <int D, int SCORE>
 __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) {
   constexpr int DCH = D / 8;
-  constexpr int KSTEPS = D / 16;
-  constexpr int DM = D / 32;
+  constexpr int KT4 = D / 32;                  // k-steps of the QK product
+  constexpr int DT = D / 16;                   // 16-row tiles of O^T
   constexpr int KPK = 1024 / (D * 2);          // keys per 1 KB copy
   constexpr int CPO = SK / KPK;                // copies per operand per stage
   constexpr int CPS = 2 * CPO;                 // copies per stage
   constexpr int VAR = KPK >= 8 ? 1 : 8 / KPK;
   using L = DLds<D>;
   static_assert(CPS * (kStages - 1) <= 63, "outstanding copies must fit the vmcnt counter");
+  static_assert(kStages == 5, "the wait below spells out up to four stages in flight");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kDecWaves * L::WAVE];
 
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int col = lane & 31;
-  const int half = lane >> 5;
+  const int col = lane & 15;
+  const int g4 = lane >> 4;
 
   const int ns = p.nsplit;
-  const int64_t unit = (int64_t)blockIdx.x * kDecWaves + w;
+  // splits of one (b, h_kv) sit in one workgroup when ns divides kDecWaves: they are
+  // merged through LDS at the end (no second kernel, no global partials)
+  const bool local_merge = ns > 1 && kDecWaves % ns == 0;
   const int64_t units = (int64_t)p.B * p.Hkv * ns;
-  if (unit >= units) return;   // wave-uniform: no barrier follows
+  const int64_t unit_raw = (int64_t)blockIdx.x * kDecWaves + w;
+  const bool live = unit_raw < units;   // a trailing wave idles but still meets the barriers
+  if (!live && !local_merge) return;    // wave-uniform; no barrier follows in this case
+  const int64_t unit = live ? unit_raw : units - 1;
   const int s_id = (int)(unit % ns);
   const int bk_id = (int)(unit / ns);      // b * Hkv + h_kv
   const int b = bk_id / p.Hkv;
@@ -85,12 +109,13 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
   const int i_g = ip + (int)p.q_offset;
   const int64_t orow = ((int64_t)(b * p.Hq + hq)) * p.q_len + ip;
 
-  bf16x8 qf[KSTEPS];
+  // Q^T operand: lane holds Q[column][32 t + 8 g .. +8]
+  bf16x8 qf[KT4];
   {
     const uint16_t* qrow = p.q + orow * D;
 #pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) {
-      u32x4 v = col_ok ? load16(qrow + 16 * t + 8 * half) : u32x4{0, 0, 0, 0};
+    for (int t = 0; t < KT4; ++t) {
+      u32x4 v = col_ok ? load16(qrow + 32 * t + 8 * g4) : u32x4{0, 0, 0, 0};
       qf[t] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -106,7 +131,12 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
   const int n_ent = nf + np;
   const int e_begin = (int)(((int64_t)s_id * n_ent) / ns);
   const int e_end = (int)(((int64_t)(s_id + 1) * n_ent) / ns);
-  const int nst = (e_end - e_begin) * (DKT / SK);
+  const int nst = live ? (e_end - e_begin) * (DKT / SK) : 0;
+  // Each unit walks its stages starting at a unit-dependent rotation: units start at
+  // the same offset of equally sized KV rows otherwise, and thousands of streams in
+  // lockstep crowd the same HBM channels.  The online softmax is order-free.
+  const int rot = nst > 0 ? (int)((unit * 37) % nst) : 0;
+  auto rs = [&](int s) { const int t = s + rot; return t >= nst ? t - nst : t; };
 
   const uint16_t* kbase = p.k + (int64_t)bk_id * p.kv_len * D;
   const uint16_t* vbase = p.v + (int64_t)bk_id * p.kv_len * D;
@@ -121,13 +151,15 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
     return e < e_end ? (e < nf ? flist[e] : plist[e - nf]) : 0;
   };
   int lst = load_list(0);
+  // consume the loads here: the copies below are invisible to the compiler's wait
+  // counting, which would otherwise wait for all memory at every use
 #pragma unroll
-  for (int t = 0; t < KSTEPS; ++t) asm volatile("" : "+v"(qf[t]));
-  asm volatile("" : "+v"(lst));   // loads complete before the copies start
+  for (int t = 0; t < KT4; ++t) asm volatile("" : "+v"(qf[t]));
+  asm volatile("" : "+v"(lst));
   auto stage_j0 = [&](int s) -> int {
     const int e = s / (DKT / SK);
-    if (e - lst_base >= 64) {   // rare: next 64 entries (waits for all copies in flight)
-      lst_base += 64;
+    if (e - lst_base >= 64 || e < lst_base) {   // rare: other 64 entries (waits for all
+      lst_base = e & ~63;                       // copies in flight)
       lst = load_list(lst_base);
     }
     return __builtin_amdgcn_readlane(lst, e - lst_base) * DKT + (s % (DKT / SK)) * SK;
@@ -147,7 +179,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
   uint8_t* ring = smem + w * L::WAVE;
   const uint32_t ring_lds = lds_addr(ring);
 
-  // one stage (32 keys from j0) into ring slot `slot`
+  // one stage (SK keys from j0) into ring slot `slot`
   auto copy_stage = [&](int j0, int slot) {
     const uint32_t mk = sreg(ring_lds + (uint32_t)slot * L::STAGE);
     const uint32_t mv = mk + L::HALF;
@@ -176,75 +208,46 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
     }
   };
 
-  // per-lane LDS read bases: K fragment t (key col, chunk 2t + half), V^T fragment of
-  // head-dim tile dm (keys 4 half + (li >> 2) (+8, +16 per k-step), d0 = 32 dm + ...)
-  const int g16 = lane >> 4, li = lane & 15;
-  uint32_t kaddr[4], vaddr[DM];
+  // per-lane LDS read bases.  K fragment t: key col, logical chunk 4t + g; t and t + 2
+  // differ by 128 bytes.  V^T fragment dt: source row 4g + (col >> 2), head-dim
+  // 16 dt + 4 (col & 3).
+  uint32_t kaddr[2], vaddr[DT];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) kaddr[t] = (uint32_t)k_off(col, 2 * t + half, L::KROW);
+  for (int t = 0; t < 2; ++t) kaddr[t] = (uint32_t)k_off(col, 4 * t + g4, L::KROW);
 #pragma unroll
-  for (int dm = 0; dm < DM; ++dm)
-    vaddr[dm] = (uint32_t)v_off<D>(4 * half + (li >> 2), 32 * dm + 16 * (g16 & 1) + 4 * (li & 3));
+  for (int dt = 0; dt < DT; ++dt) vaddr[dt] = (uint32_t)v_off<D>(4 * g4 + (col >> 2), 16 * dt + 4 * (col & 3));
 
   float m_run = kNegInf;
-  float l_run = 0.f;
-  f32x16 oacc[DM];
+  float l_run = 0.f;   // this lane's share; the four lane groups are summed at the end
+  f32x4 oacc[DT];
 #pragma unroll
-  for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: fill the ring
-  int issued = 0;
-  int j0_of[kStages];
-#pragma unroll
-  for (int k = 0; k < kStages; ++k) {
-    if (k < nst) {
-      j0_of[k] = stage_j0(k);
-      copy_stage(j0_of[k], k);
-      ++issued;
-    }
-  }
-
-  for (int s = 0; s < nst; ++s) {
-    const int slot = s % kStages;
-    // stage s has landed once at most (issued - s - 1) stages of copies are outstanding
-    switch (issued - s - 1) {
-      case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-      case 1: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(CPS) : "memory"); break;
-      case 2: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(2 * CPS) : "memory"); break;
-      default: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(3 * CPS) : "memory"); break;
-    }
-    int j0 = 0;
-#pragma unroll
-    for (int k = 0; k < kStages; ++k)
-      if (k == slot) j0 = j0_of[k];
-    const bool part = stage_part(s);
-    const uint8_t* kb = ring + slot * L::STAGE;
+  auto compute = [&](int j0, bool part, int slot) {
+    const uint32_t so = (uint32_t)slot * L::STAGE;
+    const uint8_t* kb = ring + so;
     const uint8_t* vb = kb + L::HALF;
-
-    // S^T for the 32 keys of the stage
-    f32x16 sacc = f32x16{};
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) {
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + kaddr[t & 3] + (t >> 2) * 128);
-      sacc = mfma32(__builtin_bit_cast(bf16x8, kv), qf[t], sacc);
+    for (int t = 0; t < KT4; ++t) {
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + kaddr[t & 1] + (t >> 1) * 128);
+      sacc = mfma16(__builtin_bit_cast(bf16x8, kv), qf[t], sacc);
     }
-
-    // score_mod first, then the mask (-inf) on partial and ragged stages only
-    const int jl = j0 + 4 * half;   // key of register 0 in this lane
+    // score_mod, then the mask (-inf) on partial and ragged stages only
+    const int jl = j0 + 4 * g4;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) sacc[rr] = score_log2<SCORE>(sacc[rr], sc, i_g, jl + key_of(0, rr));
+    for (int r = 0; r < 4; ++r) sacc[r] = score_log2<SCORE>(sacc[r], sc, i_g, jl + r);
     if (part || j0 + SK > kv_len) {
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int j = jl + key_of(0, rr);
+      for (int r = 0; r < 4; ++r) {
+        const int j = jl + r;
         bool ok = (unsigned)j < (unsigned)kv_len;
         if (part && ok) ok = mask_allowed(p.prog, i_g, j, doc_i, p.prog.has_doc ? docr[j] : 0);
-        sacc[rr] = ok ? sacc[rr] : kNegInf;
+        sacc[r] = ok ? sacc[r] : kNegInf;
       }
     }
-    float tmax = kNegInf;
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, sacc[rr]);
+    float tmax = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
@@ -252,83 +255,135 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
       const float alpha = fast_exp2(m_run - m_use);   // 0 when m_run = -inf
       l_run *= alpha;
 #pragma unroll
-      for (int dm = 0; dm < DM; ++dm) oacc[dm] *= alpha;
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
     }
     m_run = m_new;
-
-    float psum = 0.f;
+    const float p0 = fast_exp2(sacc[0] - m_use);
+    const float p1 = fast_exp2(sacc[1] - m_use);
+    const float p2 = fast_exp2(sacc[2] - m_use);
+    const float p3 = fast_exp2(sacc[3] - m_use);
+    l_run += (p0 + p1) + (p2 + p3);
+    const u32x2 pk = {cvt_pk_bf16(p0, p1), cvt_pk_bf16(p2, p3)};
+    const s16x4 pb = __builtin_bit_cast(s16x4, pk);
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      u32x4 pk;
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const float p0 = fast_exp2(sacc[8 * t2 + 2 * e2] - m_use);
-        const float p1 = fast_exp2(sacc[8 * t2 + 2 * e2 + 1] - m_use);
-        psum += p0 + p1;
-        pk[e2] = cvt_pk_bf16(p0, p1);
-      }
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
-#pragma unroll
-      for (int dm = 0; dm < DM; ++dm) {
-        const uint8_t* va = vb + vaddr[dm] + 16 * t2 * L::KROW;
-        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va));
-        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(va + 8 * L::KROW));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[dm] = mfma32(a, pb, oacc[dm]);
-      }
+    for (int dt = 0; dt < DT; ++dt) {
+      const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vb + vaddr[dt]));
+      oacc[dt] = mfma16k16(a, pb, oacc[dt]);
     }
-    l_run += psum;
+  };
 
-    // refill this slot with stage s + kStages once its reads have completed
+  // ring of kStages slots: stage s in slot s % kStages, the next kStages - 1 in flight
+  int issued = 0;
+  int j0_of[kStages];
+#pragma unroll
+  for (int k = 0; k < kStages; ++k) {
+    j0_of[k] = 0;
+    if (k < nst) {
+      j0_of[k] = stage_j0(rs(k));
+      copy_stage(j0_of[k], k);
+      ++issued;
+    }
+  }
+  int slot = 0;
+  for (int s = 0; s < nst; ++s) {
+    // stage s has landed once at most (issued - s - 1) stages of copies are outstanding
+    switch (issued - s - 1) {
+      case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+      case 1: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(CPS) : "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(2 * CPS) : "memory"); break;
+      case 3: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(3 * CPS) : "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(4 * CPS) : "memory"); break;
+    }
+    int j0 = 0;
+#pragma unroll
+    for (int k = 0; k < kStages; ++k)
+      if (k == slot) j0 = j0_of[k];
+    compute(j0, stage_part(rs(s)), slot);
     if (s + kStages < nst) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      const int jn = stage_j0(s + kStages);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads of this slot are done
+      const int jn = stage_j0(rs(s + kStages));
 #pragma unroll
       for (int k = 0; k < kStages; ++k)
         if (k == slot) j0_of[k] = jn;
       copy_stage(jn, slot);
       ++issued;
     }
+    slot = slot + 1 == kStages ? 0 : slot + 1;
   }
 
-  // ---- results: final O and LSE (one split) or this split's (m, l, o) partial
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // ---- results: final O and LSE (one split, or splits merged in LDS), or this
+  // split's (m, l, o) partial for the merge kernel
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (local_merge) {
+    // per wave: m[16], l[16], o[16][D] (columns x head dim), over the finished rings
+    constexpr int RW = 32 + 16 * D;
+    float* red = reinterpret_cast<float*>(smem);
+    __syncthreads();
+    float* mine = red + w * RW;
+    if (g4 == 0) {
+      mine[col] = m_run;
+      mine[16 + col] = l_tot;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4*>(mine + 32 + col * D + 16 * dt + 4 * g4) = oacc[dt];
+    __syncthreads();
+    if (!live || s_id != 0 || !col_ok) return;
+    float M = kNegInf;
+    for (int q = 0; q < ns; ++q) M = fmaxf(M, red[(w + q) * RW + col]);
+    float wq[kDecWaves];
+    float lsum = 0.f;
+#pragma unroll
+    for (int q = 0; q < kDecWaves; ++q) {
+      wq[q] = 0.f;
+      if (q < ns) {
+        const float mq = red[(w + q) * RW + col];
+        wq[q] = (mq == kNegInf) ? 0.f : fast_exp2(mq - M);
+        lsum += wq[q] * red[(w + q) * RW + 16 + col];
+      }
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    uint16_t* o = p.o + orow * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < kDecWaves; ++q)
+        if (q < ns) acc += wq[q] * *reinterpret_cast<const f32x4*>(red + (w + q) * RW + 32 + col * D + 16 * dt + 4 * g4);
+      u32x2 o2;
+      o2[0] = cvt_pk_bf16(acc[0] * inv, acc[1] * inv);
+      o2[1] = cvt_pk_bf16(acc[2] * inv, acc[3] * inv);
+      *reinterpret_cast<u32x2*>(o + 16 * dt + 4 * g4) = o2;
+    }
+    if (g4 == 0) p.lse[orow] = lsum > 0.f ? (M + fast_log2(lsum)) * kLn2 : kNegInf;
+    return;
+  }
   if (!col_ok) return;
   if (ns == 1) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* o = p.o + orow * D;
 #pragma unroll
-    for (int dm = 0; dm < DM; ++dm) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d0 = 32 * dm + 8 * gq + 4 * half;
-        u32x2 o2;
-        o2[0] = cvt_pk_bf16(oacc[dm][4 * gq + 0] * inv, oacc[dm][4 * gq + 1] * inv);
-        o2[1] = cvt_pk_bf16(oacc[dm][4 * gq + 2] * inv, oacc[dm][4 * gq + 3] * inv);
-        *reinterpret_cast<u32x2*>(o + d0) = o2;
-      }
+    for (int dt = 0; dt < DT; ++dt) {
+      u32x2 o2;
+      o2[0] = cvt_pk_bf16(oacc[dt][0] * inv, oacc[dt][1] * inv);
+      o2[1] = cvt_pk_bf16(oacc[dt][2] * inv, oacc[dt][3] * inv);
+      *reinterpret_cast<u32x2*>(o + 16 * dt + 4 * g4) = o2;
     }
-    if (half == 0) p.lse[orow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+    if (g4 == 0) p.lse[orow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
   } else {
     const int64_t rows = (int64_t)p.B * p.Hq * p.q_len;
     const int64_t prow = orow * ns + s_id;
     float* ws_m = p.ws;
     float* ws_l = p.ws + rows * ns;
     float* ws_o = p.ws + 2 * rows * ns;
-    if (half == 0) {
+    if (g4 == 0) {
       ws_m[prow] = m_run;
       ws_l[prow] = l_tot;
     }
 #pragma unroll
-    for (int dm = 0; dm < DM; ++dm) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d0 = 32 * dm + 8 * gq + 4 * half;
-        f32x4 v4 = {oacc[dm][4 * gq + 0], oacc[dm][4 * gq + 1], oacc[dm][4 * gq + 2], oacc[dm][4 * gq + 3]};
-        *reinterpret_cast<f32x4*>(ws_o + prow * D + d0) = v4;
-      }
-    }
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(ws_o + prow * D + 16 * dt + 4 * g4) = oacc[dt];
   }
 }
 
@@ -371,11 +426,11 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
 }  // namespace
 
 bool decode_eligible(const FwdParams& p) {
-  return p.tab.nqb == 1 && p.tab.bk == DKT && (int64_t)p.g * p.q_len <= 32 && p.q_len >= 1;
+  return p.tab.nqb == 1 && p.tab.bk == DKT && (int64_t)p.g * p.q_len <= kDecCols && p.q_len >= 1;
 }
 
-// splits per (b, h_kv): enough units for one wave per SIMD pair slot (kDecWaves waves per
-// CU, one workgroup per CU), capped by the listed block count of a row
+// splits per (b, h_kv): enough units for every wave slot (kDecWaves waves per CU, one
+// workgroup per CU), capped by the listed block count of a row
 int32_t decode_splits(const FwdParams& p, int num_cus) {
   const int64_t items = (int64_t)p.B * p.Hkv;
   const int64_t slots = (int64_t)kDecWaves * num_cus;
@@ -387,7 +442,8 @@ int32_t decode_splits(const FwdParams& p, int num_cus) {
 }
 
 size_t decode_workspace_bytes(const FwdParams& p, int32_t nsplit) {
-  if (nsplit <= 1) return 0;   // one split writes O and LSE directly
+  // one split, or splits merged inside a workgroup, write O and LSE directly
+  if (nsplit <= 1 || kDecWaves % nsplit == 0) return 0;
   const size_t rows = (size_t)p.B * p.Hq * p.q_len;
   return rows * nsplit * (2 + (size_t)p.d) * sizeof(float);
 }
@@ -414,7 +470,7 @@ hipError_t launch_decode(const FwdParams& p, hipStream_t s) {
   }
 #undef FA_DEC
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.nsplit <= 1) return e;
+  if (e != hipSuccess || p.nsplit <= 1 || kDecWaves % p.nsplit == 0) return e;
   const int64_t rows = (int64_t)p.B * p.Hq * p.q_len;
   const dim3 cgrid((unsigned)((rows + 3) / 4));
   if (p.d == 128) hipLaunchKernelGGL((combine_kernel<128>), cgrid, dim3(256), 0, s, p);

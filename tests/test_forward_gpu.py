@@ -163,15 +163,39 @@ def test_gqa_matches_expanded_kv():
 @pytest.mark.parametrize("score", ["identity", "softcap", "alibi", "relpos"])
 def test_decode_shapes(score):
     # single query (and a few) against long KV through the split-KV path
-    for (B, Hq, Hkv, q_len, kv_len, mask) in (
-            (3, 8, 2, 1, 2000, ("swa", 700)),
-            (2, 4, 4, 1, 1024, ("causal",)),
-            (2, 8, 1, 4, 900, ("causal",)),
-            (1, 32, 8, 1, 4096, ("swa", 4096)),
-            (2, 4, 2, 3, 513, ("prefix", 100))):
-        q, k, v = qkv(B, Hq, Hkv, q_len, kv_len, 128, seed=20 + kv_len)
+    # (g * q_len columns: up to 16 take the split-KV kernel, 32 the prefill kernel)
+    for (B, Hq, Hkv, q_len, kv_len, mask, d) in (
+            (3, 8, 2, 1, 2000, ("swa", 700), 128),
+            (2, 4, 4, 1, 1024, ("causal",), 128),
+            (2, 8, 1, 4, 900, ("causal",), 128),
+            (1, 32, 8, 1, 4096, ("swa", 4096), 128),
+            (2, 4, 2, 3, 513, ("prefix", 100), 128),
+            (1, 16, 1, 1, 3000, ("swa", 1500), 128),
+            (2, 8, 1, 2, 1500, ("causal",), 128),
+            (3, 8, 2, 1, 1100, ("swa", 600), 64)):
+        q, k, v = qkv(B, Hq, Hkv, q_len, kv_len, d, seed=20 + kv_len)
         check(q, k, v, mask, 128, 128, score, q_offset=kv_len - q_len,
-              ctx=f"decode {B}x{Hq}/{Hkv} q{q_len} kv{kv_len} {mask} {score}", **score_kw(score, Hq))
+              ctx=f"decode {B}x{Hq}/{Hkv} q{q_len} kv{kv_len} d{d} {mask} {score}", **score_kw(score, Hq))
+
+
+@pytest.mark.parametrize("B,Hkv,kv_len", [(128, 8, 700), (64, 4, 1100), (16, 2, 1500)],
+                         ids=["one_split", "splits_in_workgroup", "split_merge_kernel"])
+def test_decode_split_paths(B, Hkv, kv_len):
+    # enough (batch, KV head) pairs for one split per unit, splits merged in LDS, and
+    # splits merged by the second kernel (on a 256-CU device: 1, 4 and 12 splits)
+    Hq = 2 * Hkv
+    q, k, v = qkv(B, Hq, Hkv, 1, kv_len, 128, seed=40 + B)
+    check(q, k, v, ("swa", 600), 128, 128, "softcap", q_offset=kv_len - 1,
+          ctx=f"decode split path B{B} Hkv{Hkv} kv{kv_len}", **score_kw("softcap", Hq))
+
+
+def test_decode_long_rows():
+    # one (batch, KV head) pair over 4200 listed blocks: 64 splits of 65-66 blocks, so a
+    # split's block list spans more than one 64-entry register chunk (with the rotated
+    # stage order the chunk is reloaded going forward and back)
+    kv_len = 128 * 4200
+    q, k, v = qkv(1, 2, 1, 1, kv_len, 128, seed=50)
+    check(q, k, v, ("causal",), 128, 128, "identity", q_offset=kv_len - 1, ctx="decode long rows")
 
 
 def test_decode_empty_and_offsets():
