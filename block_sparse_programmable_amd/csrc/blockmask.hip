@@ -144,28 +144,108 @@ __global__ __launch_bounds__(256) void doc_stats_kernel(BuildParams p) {
   }
 }
 
-// Exact class of one block, decided by the whole wave: lanes cover the block's
-// columns, rows are walked in order with their document IDs held in registers and
-// broadcast by readlane; stops as soon as both an allowed and a disallowed in-range
-// pair have been seen.  And-only programs test each pair against the row's compiled
-// key interval plus the document compare; programs with an or-node use the interpreter.
-__device__ uint8_t exact_block(const BuildParams& p, int tb, int r, int c, int lane) {
+// Exact class of one block, decided by the whole wave.
+//
+// Fast form (and-only programs whose KV block holds non-decreasing document IDs in at
+// most eight runs): the keys of the block that share row i's document are one
+// contiguous range, read off the runs (start column and ID, wave-uniform); with the
+// row's compiled key interval that gives the row's allowed keys as one interval, so each
+// lane decides two rows outright ("FlexAttention: from rules to fused kernels",
+// section 6.3: document rules have boundary structure too).
+//
+// General form: lanes cover the block's columns, rows are walked in order with their
+// document IDs held in registers and broadcast by readlane; stops as soon as both an
+// allowed and a disallowed in-range pair have been seen.  And-only programs test each
+// pair against the row's compiled key interval plus the document compare; programs
+// with an or-node use the interpreter.
+// document IDs of a block's columns (j0, j0 + 64) and rows (a, a + 64) for this lane
+struct BlockDocs {
+  int dj0, dj1, dr0, dr1;
+};
+
+__device__ __forceinline__ BlockDocs load_block_docs(const BuildParams& p, int tb, int r, int c, int lane) {
+  BlockDocs bd = {0, 0, 0, 0};
+  if (!p.prog.has_doc) return bd;
   const BlockGeom g = geom(p, r, c);
   const int32_t* d = doc_row(p.doc, tb);
+  const int nrows = (int)(g.bb - g.a + 1);
+  const int ncols = (int)(g.c1 - g.c0 + 1);
+  if (lane < ncols) bd.dj0 = d[g.c0 + lane];
+  if (lane + 64 < ncols) bd.dj1 = d[g.c0 + 64 + lane];
+  if (lane < nrows) bd.dr0 = d[g.a + lane];
+  if (lane + 64 < nrows) bd.dr1 = d[g.a + 64 + lane];
+  return bd;
+}
+
+__device__ uint8_t exact_block(const BuildParams& p, int tb, int r, int c, int lane, const BlockDocs& bd) {
+  const BlockGeom g = geom(p, r, c);
   const int nrows = (int)(g.bb - g.a + 1);
   const int ncols = (int)(g.c1 - g.c0 + 1);
   const int a = (int)g.a;
   const int j0 = (int)g.c0 + lane;
   const int j1 = j0 + 64;
   const bool ok0 = lane < ncols, ok1 = lane + 64 < ncols;
-  int dj0 = 0, dj1 = 0, dr0 = 0, dr1 = 0;
-  if (p.prog.has_doc) {
-    if (ok0) dj0 = d[j0];
-    if (ok1) dj1 = d[j1];
-    if (lane < nrows) dr0 = d[a + lane];
-    if (lane + 64 < nrows) dr1 = d[a + 64 + lane];
-  }
+  const int dj0 = bd.dj0, dj1 = bd.dj1, dr0 = bd.dr0, dr1 = bd.dr1;
   const bool interval_form = p.prog.mk != MK_GENERIC;
+  if (interval_form && p.prog.has_doc) {
+    // the block's columns as runs of equal document IDs: a run starts where the ID
+    // differs from the previous column; IDs must not decrease across the block
+    const int last0 = __shfl(dj0, 63);
+    const int prev0 = __shfl(dj0, lane > 0 ? lane - 1 : 0);
+    const int prev1 = lane > 0 ? __shfl(dj1, lane - 1) : last0;
+    const bool desc = (ok0 && lane > 0 && dj0 < prev0) || (ok1 && dj1 < prev1);
+    uint64_t m0 = __ballot(ok0 && (lane == 0 || dj0 != prev0));
+    uint64_t m1 = __ballot(ok1 && dj1 != prev1);
+    constexpr int kRuns = 8;
+    if (__ballot(desc) == 0 && __popcll(m0) + __popcll(m1) <= kRuns) {
+      // run k: first column rs[k], ID rv[k] (wave-uniform); unused runs keep rs = ncols
+      int rs[kRuns], rv[kRuns];
+#pragma unroll
+      for (int k = 0; k < kRuns; ++k) {
+        rs[k] = ncols;
+        rv[k] = 0x7fffffff;
+        if (m0) {
+          const int pos = __builtin_ctzll(m0);
+          m0 &= m0 - 1;
+          rs[k] = pos;
+          rv[k] = __builtin_amdgcn_readlane(dj0, pos);
+        } else if (m1) {
+          const int pos = __builtin_ctzll(m1);
+          m1 &= m1 - 1;
+          rs[k] = 64 + pos;
+          rv[k] = __builtin_amdgcn_readlane(dj1, pos);
+        }
+      }
+      bool not_full = false, not_empty = false;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int ri = lane + 64 * q;
+        if (ri < nrows) {
+          const int ii = a + ri;
+          const int di = q == 0 ? dr0 : dr1;
+          // columns with ID == di: [first run with ID >= di, first run with ID > di)
+          int lb = ncols, ub = ncols;
+#pragma unroll
+          for (int k = kRuns - 1; k >= 0; --k) {
+            if (rv[k] >= di) lb = rs[k];
+            if (rv[k] > di) ub = rs[k];
+          }
+          int lo = p.prog.wmin > 0 ? max(0, ii - p.prog.wmin + 1) : 0;
+          int hi = p.prog.hi_self ? ii : (p.prog.pmin >= 0 ? max(p.prog.pmin - 1, ii) : 0x7fffffff);
+          const int c0 = (int)g.c0, c1 = (int)g.c1;
+          lo = max(lo, c0 + lb);
+          hi = min(hi, c0 + ub - 1);
+          const bool full = lo <= c0 && hi >= c1;
+          const bool empty = max(lo, c0) > min(hi, c1);
+          not_full = not_full || !full;
+          not_empty = not_empty || !empty;
+        }
+      }
+      const bool all_full = __ballot(not_full) == 0;
+      const bool all_empty = __ballot(not_empty) == 0;
+      return all_full ? kFull : (all_empty ? kEmpty : kPartial);
+    }
+  }
   bool seen_t = false, seen_f = false;
   for (int ri = 0; ri < nrows; ++ri) {
     const int ii = a + ri;
@@ -214,7 +294,7 @@ __global__ __launch_bounds__(256) void classify_kernel(BuildParams p) {
     const int src = __builtin_ctzll(pending);
     pending &= pending - 1;
     const int ub = __shfl(tb, src), ur = __shfl(r, src), uc = __shfl(c, src);
-    const uint8_t cls = exact_block(p, ub, ur, uc, lane);
+    const uint8_t cls = exact_block(p, ub, ur, uc, lane, load_block_docs(p, ub, ur, uc, lane));
     if (lane == 0) p.grid[((int64_t)ub * p.nqb + ur) * p.nkb + uc] = cls;
   }
 }
@@ -343,35 +423,57 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
   const int nq = p.tB * p.nqb, nk = p.tB * p.nkb, nl = nq + nk;
   const int total = p.tB * p.nqb * p.nkb;
 
-  // phase 1: document-ID ranges per query block and per KV block
+  // phase 1: document-ID ranges per query block and per KV block.  A wave takes four
+  // lines at a time (at most 128 IDs each: two per lane) and issues all their loads
+  // before reducing, so the HBM latency is paid once per four lines.
   if (p.prog.has_doc) {
-    for (int line = wv; line < nl; line += 16) {
-      const bool qside = line < nq;
-      const int idx = qside ? line : line - nq;
-      const int tb = qside ? idx / p.nqb : idx / p.nkb;
-      const int blk = qside ? idx - tb * p.nqb : idx - tb * p.nkb;
-      const int32_t* d = doc_row(p.doc, tb);
-      int64_t lo, hi;
-      if (qside) {
-        lo = (int64_t)blk * p.bq + p.q_offset;
-        hi = min((int64_t)(blk + 1) * p.bq, p.q_len) + p.q_offset;
-      } else {
-        lo = (int64_t)blk * p.bk;
-        hi = min((int64_t)(blk + 1) * p.bk, p.kv_len);
+    constexpr int G = 4;
+    for (int l0 = wv * G; l0 < nl; l0 += 16 * G) {
+      int v[G][2];
+      bool in[G][2];
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int line = l0 + u;
+        int64_t lo = 0, hi = 0;
+        const int32_t* d = nullptr;
+        if (line < nl) {
+          const bool qside = line < nq;
+          const int idx = qside ? line : line - nq;
+          const int tb = qside ? idx / p.nqb : idx / p.nkb;
+          const int blk = qside ? idx - tb * p.nqb : idx - tb * p.nkb;
+          d = doc_row(p.doc, tb);
+          if (qside) {
+            lo = (int64_t)blk * p.bq + p.q_offset;
+            hi = min((int64_t)(blk + 1) * p.bq, p.q_len) + p.q_offset;
+          } else {
+            lo = (int64_t)blk * p.bk;
+            hi = min((int64_t)(blk + 1) * p.bk, p.kv_len);
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t x = lo + lane + 64 * h;
+          in[u][h] = x < hi;
+          v[u][h] = in[u][h] ? d[x] : 0;
+        }
       }
-      int mn = 0x7fffffff, mx = (int)0x80000000;
-      for (int64_t x = lo + lane; x < hi; x += 64) {
-        const int v = d[x];
-        mn = min(mn, v);
-        mx = max(mx, v);
-      }
-      for (int off = 32; off > 0; off >>= 1) {
-        mn = min(mn, __shfl_xor(mn, off));
-        mx = max(mx, __shfl_xor(mx, off));
-      }
-      if (lane == 0) {
-        stat_s[2 * line] = mn;
-        stat_s[2 * line + 1] = mx;
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        int mn = 0x7fffffff, mx = (int)0x80000000;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (in[u][h]) {
+            mn = min(mn, v[u][h]);
+            mx = max(mx, v[u][h]);
+          }
+        for (int off = 32; off > 0; off >>= 1) {
+          mn = min(mn, __shfl_xor(mn, off));
+          mx = max(mx, __shfl_xor(mx, off));
+        }
+        if (lane == 0 && l0 + u < nl) {
+          stat_s[2 * (l0 + u)] = mn;
+          stat_s[2 * (l0 + u) + 1] = mx;
+        }
       }
     }
   }
@@ -391,31 +493,59 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
   }
   __syncthreads();
 
-  // phase 3: exact evaluation of the undecided blocks, spread over the 16 waves
+  // phase 3: exact evaluation of the undecided blocks, spread over the 16 waves; the
+  // document IDs of a wave's next block are loaded while the current one is decided
   const int nu = n_undecided;
-  for (int k = wv; k < nu; k += 16) {
-    const int uid = list_s[k];
-    const int tb = uid / (p.nqb * p.nkb);
+  auto decode_id = [&](int uid, int& tb, int& r, int& c) {
+    tb = uid / (p.nqb * p.nkb);
     const int rem = uid - tb * p.nqb * p.nkb;
-    const int r = rem / p.nkb, c = rem - r * p.nkb;
-    const uint8_t cls = exact_block(p, tb, r, c, lane);
-    if (lane == 0) grid_s[uid] = cls;
+    r = rem / p.nkb;
+    c = rem - r * p.nkb;
+  };
+  if (wv < nu) {
+    int tb, r, c;
+    decode_id(list_s[wv], tb, r, c);
+    BlockDocs cur = load_block_docs(p, tb, r, c, lane);
+    for (int k = wv; k < nu; k += 16) {
+      const int uid = list_s[k];
+      decode_id(uid, tb, r, c);
+      BlockDocs nxt = {0, 0, 0, 0};
+      if (k + 16 < nu) {
+        int tb2, r2, c2;
+        decode_id(list_s[k + 16], tb2, r2, c2);
+        nxt = load_block_docs(p, tb2, r2, c2, lane);
+      }
+      const uint8_t cls = exact_block(p, tb, r, c, lane, cur);
+      if (lane == 0) grid_s[uid] = cls;
+      cur = nxt;
+    }
   }
   __syncthreads();
 
-  // phase 4: partial / full counts per row (tb, r) and per column (tb, c)
-  for (int line = wv; line < nl; line += 16) {
-    const bool rowside = line < nq;
+  // phase 4: partial / full counts per row (tb, r) and per column (tb, c).  A side whose
+  // lines are very short (at most kShort entries, e.g. the query side of a decode grid)
+  // takes one thread per line, otherwise one wave per line (ballot counts).
+  constexpr int kShort = 8;
+  auto line_geom = [&](int line, int& tb, int& k, int& n, bool& rowside) {
+    rowside = line < nq;
     const int idx = rowside ? line : line - nq;
-    const int tb = rowside ? idx / p.nqb : idx / p.nkb;
-    const int k = rowside ? idx - tb * p.nqb : idx - tb * p.nkb;
-    const int n = rowside ? p.nkb : p.nqb;
+    tb = rowside ? idx / p.nqb : idx / p.nkb;
+    k = rowside ? idx - tb * p.nqb : idx - tb * p.nkb;
+    n = rowside ? p.nkb : p.nqb;
+  };
+  auto entry = [&](const uint8_t* g, bool rowside, int k, int x) -> uint8_t {
+    return rowside ? g[k * p.nkb + x] : g[x * p.nkb + k];
+  };
+  for (int line = wv; line < nl; line += 16) {
+    int tb, k, n;
+    bool rowside;
+    line_geom(line, tb, k, n, rowside);
+    if (n <= kShort) continue;
     const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
     int np = 0, nf = 0;
     for (int x0 = 0; x0 < n; x0 += 64) {
       const int x = x0 + lane;
-      uint8_t v = kEmpty;
-      if (x < n) v = rowside ? g[k * p.nkb + x] : g[x * p.nkb + k];
+      const uint8_t v = x < n ? entry(g, rowside, k, x) : kEmpty;
       np += __popcll(__ballot(v == kPartial));
       nf += __popcll(__ballot(v == kFull));
     }
@@ -423,6 +553,21 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
       cnt_s[2 * line] = np;
       cnt_s[2 * line + 1] = nf;
     }
+  }
+  for (int line = tid; line < nl; line += 1024) {
+    int tb, k, n;
+    bool rowside;
+    line_geom(line, tb, k, n, rowside);
+    if (n > kShort) continue;
+    const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
+    int np = 0, nf = 0;
+    for (int x = 0; x < n; ++x) {
+      const uint8_t v = entry(g, rowside, k, x);
+      np += v == kPartial;
+      nf += v == kFull;
+    }
+    cnt_s[2 * line] = np;
+    cnt_s[2 * line + 1] = nf;
   }
   __syncthreads();
 
@@ -487,31 +632,53 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
     p.q_ptr[cols] = cum_s[4 * p.tB + 2];
     p.full_q_ptr[cols] = cum_s[4 * p.tB + 3];
   }
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int x = wv; x < rows + cols; x += 16) {
-    const bool rowside = x < rows;
+  // ordered scatter: short lines one thread each, long lines one wave each
+  auto out_line = [&](int x, int& k, int& tb, int& n, bool& rowside, int32_t*& pout, int32_t*& fout) {
+    rowside = x < rows;
     const int idx = rowside ? x : x - rows;
     const int per = rowside ? p.nqb : p.nkb;
-    const int bh = idx / per, k = idx - bh * per;
-    const int tb = bh / p.tH, h = bh - tb * p.tH;
+    const int bh = idx / per;
+    k = idx - bh * per;
+    tb = bh / p.tH;
+    const int h = bh - tb * p.tH;
     const int line = rowside ? tb * p.nqb + k : nq + tb * p.nkb + k;
     const int side = rowside ? 0 : 1;
     const int pp = cum_s[4 * tb + 2 * side] + h * tot_s[4 * tb + 2 * side] + pre_s[2 * line];
     const int pf = cum_s[4 * tb + 2 * side + 1] + h * tot_s[4 * tb + 2 * side + 1] + pre_s[2 * line + 1];
-    int32_t* pout = (rowside ? p.kv_idx : p.q_idx) + pp;
-    int32_t* fout = (rowside ? p.full_kv_idx : p.full_q_idx) + pf;
-    const int n = rowside ? p.nkb : p.nqb;
+    pout = (rowside ? p.kv_idx : p.q_idx) + pp;
+    fout = (rowside ? p.full_kv_idx : p.full_q_idx) + pf;
+    n = rowside ? p.nkb : p.nqb;
+  };
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int x = wv; x < rows + cols; x += 16) {
+    int k, tb, n;
+    bool rowside;
+    int32_t *pout, *fout;
+    out_line(x, k, tb, n, rowside, pout, fout);
+    if (n <= kShort) continue;
     const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
     for (int x0 = 0; x0 < n; x0 += 64) {
       const int y = x0 + lane;
-      uint8_t v = kEmpty;
-      if (y < n) v = rowside ? g[k * p.nkb + y] : g[y * p.nkb + k];
+      const uint8_t v = y < n ? entry(g, rowside, k, y) : kEmpty;
       const uint64_t bp = __ballot(v == kPartial);
       const uint64_t bf = __ballot(v == kFull);
       if (v == kPartial) pout[__popcll(bp & below)] = y;
       if (v == kFull) fout[__popcll(bf & below)] = y;
       pout += __popcll(bp);
       fout += __popcll(bf);
+    }
+  }
+  for (int x = tid; x < rows + cols; x += 1024) {
+    int k, tb, n;
+    bool rowside;
+    int32_t *pout, *fout;
+    out_line(x, k, tb, n, rowside, pout, fout);
+    if (n > kShort) continue;
+    const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
+    for (int y = 0; y < n; ++y) {
+      const uint8_t v = entry(g, rowside, k, y);
+      if (v == kPartial) *pout++ = y;
+      if (v == kFull) *fout++ = y;
     }
   }
 }
