@@ -30,14 +30,21 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_digest():
+KERNEL_SOURCES = {
+    "prefill": ("prefill.hip", "prefill_common.hpp", "device_common.hpp", "fa_internal.hpp"),
+    "decode": ("decode.hip", "prefill_common.hpp", "device_common.hpp", "fa_internal.hpp"),
+}
+
+
+def kernel_source_digest(kernel):
+    """Digest of the source files a kernel is built from (a counter summary taken on
+    other sources no longer describes it)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_sparse_programmable_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode())
-                h.update(f.read())
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -52,7 +59,7 @@ def read_traffic(kernel, workload):
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_digest") != kernel_source_digest():
+    if kv.get("source_digest") != kernel_source_digest(kernel):
         return None
     try:
         return float(kv["hbm_bytes_per_dispatch"])
@@ -218,7 +225,8 @@ def run(args):
            "fwd_ms": fwd_avg, "fwd_ms_p10": float(np.percentile(fwd_ms, 10)),
            "fwd_ms_p90": float(np.percentile(fwd_ms, 90)),
            "algorithmic_flop": acc["flop"], "algorithmic_bytes": acc.get("bytes"),
-           "kernel_source_digest": kernel_source_digest(), "gpu": torch.cuda.get_device_name(0),
+           "kernel_source_digest": kernel_source_digest("decode" if decode else "prefill"),
+           "gpu": torch.cuda.get_device_name(0),
            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
     if decode:
         rec["forward_workspace_bytes"] = fws_bytes
