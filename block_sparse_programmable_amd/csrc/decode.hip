@@ -21,8 +21,8 @@
 //     wait per stage is the only synchronisation.  Four waves per CU fill the 160 KB
 //     of LDS.
 //   * K and V of a stage are row-major in LDS with the XOR swizzles of the prefill
-//     kernels (K 16-byte chunks by key & 7, V 32-byte units by key & 7): scores from
-//     ds_read_b128 fragments, the P V operand from ds_read_b64_tr_b16.
+//     kernels (conflict-free on the 64-bank LDS): scores from ds_read_b128 fragments,
+//     the P V operand from ds_read_b64_tr_b16.
 //   * with one split the wave writes O and LSE itself; when the splits of a (b, h_kv)
 //     share a workgroup they are merged through LDS after the stream; otherwise each
 //     wave writes its (m, l, o) partial and a second small kernel merges the splits.
@@ -73,7 +73,8 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
   constexpr int KPK = 1024 / (D * 2);          // keys per 1 KB copy
   constexpr int CPO = SK / KPK;                // copies per operand per stage
   constexpr int CPS = 2 * CPO;                 // copies per stage
-  constexpr int VAR = KPK >= 8 ? 1 : 8 / KPK;
+  constexpr int KVAR = KPK >= kSwzKeys ? 1 : kSwzKeys / KPK;   // K swizzle patterns per stage
+  constexpr int VVAR = KPK >= 8 ? 1 : 8 / KPK;                  // V pattern repeats every 8 keys
   using L = DLds<D>;
   static_assert(CPS * (kStages - 1) <= 63, "outstanding copies must fit the vmcnt counter");
   static_assert(kStages == 5, "the wait below spells out up to four stages in flight");
@@ -167,14 +168,15 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
   auto stage_part = [&](int s) -> bool { return e_begin + s / (DKT / SK) >= nf; };
 
   // per-lane copy offsets (swizzles as in the prefill kernels)
-  uint32_t koff[VAR], voff[VAR];
+  uint32_t koff[KVAR], voff[VVAR];
 #pragma unroll
-  for (int var = 0; var < VAR; ++var) {
+  for (int var = 0; var < KVAR; ++var) {
     const int key_in = lane / DCH;
     const int pc = lane % DCH;
-    const int key7 = (var * KPK + key_in) & 7;
-    koff[var] = (uint32_t)(key_in * L::KROW + ((pc ^ key7) << 4));
-    voff[var] = (uint32_t)(key_in * L::KROW + ((2 * (((pc >> 1) ^ key7) & (L::UNITS - 1)) + (pc & 1)) << 4));
+    const int key = var * KPK + key_in;   // key within the swizzle period
+    koff[var] = (uint32_t)(key_in * L::KROW + ((pc ^ k_swz<D>(key)) << 4));
+    if (var < VVAR)
+      voff[var] = (uint32_t)(key_in * L::KROW + ((2 * (((pc >> 1) ^ v_swz<D>(key)) & (L::UNITS - 1)) + (pc & 1)) << 4));
   }
   uint8_t* ring = smem + w * L::WAVE;
   const uint32_t ring_lds = lds_addr(ring);
@@ -189,8 +191,8 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
       static_for<CPO>([&](auto uc) {
         constexpr int u = decltype(uc)::value;
         constexpr int grp = (u / 4) * 4096;   // immediate offsets stay below 4 KB
-        dma16_s<(u % 4) * 1024>(mk + grp, kg + grp, koff[u % VAR]);
-        dma16_s<(u % 4) * 1024>(mv + grp, vg + grp, voff[u % VAR]);
+        dma16_s<(u % 4) * 1024>(mk + grp, kg + grp, koff[u % KVAR]);
+        dma16_s<(u % 4) * 1024>(mv + grp, vg + grp, voff[u % VVAR]);
       });
     } else {
       // ragged tail: keys past kv_len re-read the last key (they are masked); offsets
@@ -202,18 +204,17 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
         constexpr int u = decltype(uc)::value;
         const int key = u * KPK + lane / DCH;
         const uint32_t rowoff = (uint32_t)(min(j0 + key, kv_len - 1) - jb) * L::KROW;
-        dma16_s<0>(mk + u * 1024, kg, rowoff + (koff[u % VAR] & (L::KROW - 1)));
-        dma16_s<0>(mv + u * 1024, vg, rowoff + (voff[u % VAR] & (L::KROW - 1)));
+        dma16_s<0>(mk + u * 1024, kg, rowoff + (koff[u % KVAR] & (L::KROW - 1)));
+        dma16_s<0>(mv + u * 1024, vg, rowoff + (voff[u % VVAR] & (L::KROW - 1)));
       });
     }
   };
 
-  // per-lane LDS read bases.  K fragment t: key col, logical chunk 4t + g; t and t + 2
-  // differ by 128 bytes.  V^T fragment dt: source row 4g + (col >> 2), head-dim
-  // 16 dt + 4 (col & 3).
-  uint32_t kaddr[2], vaddr[DT];
+  // per-lane LDS read bases.  K fragment t: key col, logical chunk 4t + g.  V^T
+  // fragment dt: source row 4g + (col >> 2), head-dim 16 dt + 4 (col & 3).
+  uint32_t kaddr[KT4], vaddr[DT];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) kaddr[t] = (uint32_t)k_off(col, 4 * t + g4, L::KROW);
+  for (int t = 0; t < KT4; ++t) kaddr[t] = (uint32_t)k_off<D>(col, 4 * t + g4);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) vaddr[dt] = (uint32_t)v_off<D>(4 * g4 + (col >> 2), 16 * dt + 4 * (col & 3));
 
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < KT4; ++t) {
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + kaddr[t & 1] + (t >> 1) * 128);
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + kaddr[t]);
       sacc = mfma16(__builtin_bit_cast(bf16x8, kv), qf[t], sacc);
     }
     // score_mod, then the mask (-inf) on partial and ragged stages only

@@ -23,8 +23,9 @@
 //   * K and V are staged in 64-key sub-tiles, both row-major in LDS, copied HBM -> LDS
 //     with global_load_lds_dwordx4 (no staging registers, no VALU).  Each lane picks the
 //     global 16-byte chunk that its fixed LDS slot must hold, which realises the XOR
-//     swizzles: K 16-byte chunks by key & 7 (conflict-free ds_read_b128 fragments), V
-//     32-byte units by key & 7 (conflict-free transposing reads).  The P V operand (8
+//     swizzles of K 16-byte chunks and V 32-byte units, chosen for the 64-bank LDS so
+//     that the ds_read_b128 fragments and the transposing reads are free of bank
+//     conflicts (an XOR by key & 7 leaves a 2-way conflict).  The P V operand (8
 //     keys of one head-dim index per lane) comes from two ds_read_b64_tr_b16 reads.
 //     Two LDS slots per operand: sub-tile s+1 is in flight while s is computed, one
 //     barrier per sub-tile.
@@ -56,12 +57,13 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   constexpr int DM = D / 32;     // 32-row tiles of O^T
   constexpr int KPK = 1024 / (D * 2);       // keys covered by one 1 KB wave copy
   constexpr int COPIES = KT / KPK / NW;     // 1 KB copies per wave per operand
-  constexpr int VAR = KPK >= 8 ? 1 : 8 / KPK;  // distinct swizzle patterns over the copies
+  constexpr int KVAR = KPK >= kSwzKeys ? 1 : kSwzKeys / KPK;  // K swizzle patterns over the copies
+  constexpr int VVAR = KPK >= 8 ? 1 : 8 / KPK;                 // V pattern repeats every 8 keys
   constexpr bool kDoc = (MK == MK_INTERVAL_DOC);
   constexpr bool kRel = (SCORE == FA_S_RELPOS);
   using L = Lds<D>;
   static_assert(L::KROW * KPK == 1024, "one copy moves 1 KB");
-  static_assert((COPIES * KPK) % 8 == 0, "wave slices start at a multiple of 8 keys");
+  static_assert((COPIES * KPK) % kSwzKeys == 0, "wave slices start at a swizzle period");
   // K slot 0 | K slot 1 | V slot 0 | V slot 1 | doc IDs slot 0 | slot 1 (doc IDs travel
   // with K).  Every LDS read is a per-lane base plus an immediate offset.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * L::TILE + 2 * KT * 4];
@@ -164,15 +166,30 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   // linear, and each lane fetches the global chunk its slot must hold under the swizzle.
   const int wu = uniform(w);
   const int wave_key0 = wu * COPIES * KPK;
-  uint32_t koff[VAR], voff[VAR];
-#pragma unroll
-  for (int var = 0; var < VAR; ++var) {
+  // Both swizzles are XOR-linear in the key and a copy's first key is a multiple of
+  // KPK, so the offsets of later copies in a period are the first copy's offsets XOR a
+  // constant (flipped next to each copy, which keeps one live register per operand).
+  uint32_t koff0, voff0;
+  {
     const int key_in = lane / DCH;
     const int pc = lane % DCH;
-    const int key7 = (var * KPK + key_in) & 7;
-    koff[var] = (uint32_t)(key_in * L::KROW + ((pc ^ key7) << 4));
-    voff[var] = (uint32_t)(key_in * L::KROW + ((2 * (((pc >> 1) ^ key7) & (L::UNITS - 1)) + (pc & 1)) << 4));
+    koff0 = (uint32_t)(key_in * L::KROW + ((pc ^ k_swz<D>(key_in)) << 4));
+    voff0 = (uint32_t)(key_in * L::KROW + ((2 * (((pc >> 1) ^ v_swz<D>(key_in)) & (L::UNITS - 1)) + (pc & 1)) << 4));
   }
+  auto copy_off = [&](auto isv_c, auto u_c) -> uint32_t {
+    constexpr bool ISV = decltype(isv_c)::value;
+    constexpr int u = decltype(u_c)::value;
+    constexpr uint32_t flip = ISV ? (uint32_t)(v_swz<D>((u % VVAR) * KPK) << 5)
+                                  : (uint32_t)(k_swz<D>((u % KVAR) * KPK) << 4);
+    const uint32_t base = ISV ? voff0 : koff0;
+    if constexpr (flip == 0) {
+      return base;
+    } else {
+      uint32_t o;
+      asm volatile("v_xor_b32 %0, %1, %2" : "=v"(o) : "i"(flip), "v"(base));
+      return o;
+    }
+  };
 
   // copy of one operand (K with its doc IDs, or V) of the sub-tile at key j0 into a slot
   auto copy_op = [&](int j0, auto isv_c, auto slot_c) {
@@ -181,13 +198,13 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
     const uint16_t* gb = ISV ? vbase : kbase;
     const uint32_t m = lds_addr(smem + ((ISV ? 2 : 0) + SLOT) * L::TILE) + wave_key0 * L::KROW;
     const uint32_t md = lds_addr(smem + 4 * L::TILE + SLOT * KT * 4);
-    const uint32_t* off = ISV ? voff : koff;
+
     if (j0 + KT <= kv_len) {
       const char* g = (const char*)gb + ((int64_t)j0 + wave_key0) * L::KROW;
       static_for<COPIES>([&](auto uc) {
         constexpr int u = decltype(uc)::value;
         constexpr int grp = (u / 4) * 4096;   // immediate offsets stay below 4 KB
-        dma16_s<(u % 4) * 1024>(m + grp, g + grp, off[u % VAR]);
+        dma16_s<(u % 4) * 1024>(m + grp, g + grp, copy_off(isv_c, uc));
       });
       if constexpr (kDoc && !ISV) {
         if (wu == 0) dma4_s(md, docr + j0, (uint32_t)lane * 4);
@@ -198,7 +215,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
         constexpr int u = decltype(uc)::value;
         const int key = wave_key0 + u * KPK + lane / DCH;
         const int64_t j = min(j0 + key, kv_len - 1);
-        dma16_v(m + u * 1024, (const char*)gb + j * L::KROW + (off[u % VAR] & (L::KROW - 1)));
+        const uint32_t o = copy_off(isv_c, uc);
+        dma16_v(m + u * 1024, (const char*)gb + j * L::KROW + (o & (L::KROW - 1)));
       });
       if constexpr (kDoc && !ISV) {
         if (wu == 0) dma4_v(md, docr + min(j0 + lane, kv_len - 1));
@@ -207,13 +225,22 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   };
 
   // ---- per-lane LDS read bases.  K fragment (mt, t): key 32 mt + col, logical chunk
-  // 2t + half at physical chunk (2t + half) ^ (key & 7); t = 4q + t' adds q * 128 bytes.
+  // 2t + half at physical chunk (2t + half) ^ k_swz(key); mt adds whole rows.
   // V^T fragment (t, dm, hl): keys 16 t + 8 hl + 4 half + (li >> 2), head-dim d0 =
   // 32 dm + 16 (g16 & 1) + 4 (li & 3); t and hl add whole rows.
   const int g16 = lane >> 4, li = lane & 15;
+  // Chunks 8..15 of a 256-byte row sit at the address of chunk - 8 with bit 7 flipped;
+  // that XOR is issued next to each read (volatile, so it is not hoisted into 4 more
+  // live registers).
   uint32_t kaddr[4], vaddr[DM];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) kaddr[t] = (uint32_t)k_off(col, 2 * t + half, L::KROW);
+  for (int t = 0; t < 4; ++t) kaddr[t] = (uint32_t)k_off<D>(col, 2 * t + half);
+  auto kfrag = [&](int t) -> uint32_t {
+    if (t < 4) return kaddr[t];
+    uint32_t a;
+    asm volatile("v_xor_b32 %0, 0x80, %1" : "=v"(a) : "v"(kaddr[t & 3]));
+    return a;
+  };
 #pragma unroll
   for (int dm = 0; dm < DM; ++dm)
     vaddr[dm] = (uint32_t)v_off<D>(4 * half + (li >> 2), 32 * dm + 16 * (g16 & 1) + 4 * (li & 3));
@@ -234,7 +261,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       s[mt] = f32x16{};
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + kaddr[t & 3] + (t >> 2) * 128 + mt * 32 * L::KROW);
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + kfrag(t) + mt * 32 * L::KROW);
         s[mt] = mfma32(__builtin_bit_cast(bf16x8, kv), qf[t], s[mt]);
       }
     }
@@ -401,7 +428,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < KQ; ++i) {
         const int t = (q & 1) * KQ + i;
-        dst[i] = *reinterpret_cast<const u32x4*>(kb + kaddr[t & 3] + (t >> 2) * 128 + (q >> 1) * 32 * L::KROW);
+        dst[i] = *reinterpret_cast<const u32x4*>(kb + kfrag(t) + (q >> 1) * 32 * L::KROW);
       }
     };
     auto read_v = [&](auto t_c, bf16x8 (&dst)[DM]) {

@@ -26,13 +26,32 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kListCap = 512;   // block-list entries staged in LDS per pass over the row
 
-// K: physical 16-byte chunk of row `key` holding logical chunk `ch`
-__device__ __forceinline__ int k_off(int key, int ch, int krow) { return key * krow + ((ch ^ (key & 7)) << 4); }
-// V: byte offset of V[key][d] (d a multiple of 4) with 32-byte units XOR-swizzled by key & 7
+// LDS swizzles.  The LDS serves 256 bytes (64 banks of 4 bytes) per cycle; a
+// ds_read_b128 is served 16 lanes at a time, so the 16 keys that lanes 0-15 (or 16-31)
+// read at one logical chunk must land on 16 distinct 16-byte bank groups.  Both
+// patterns repeat every kSwzKeys keys.
+constexpr int kSwzKeys = 16;
+// K: XOR of the 16-byte chunk index.  256-byte rows (D = 128): key & 15 over the 16
+// chunks of a row; 128-byte rows (D = 64, two rows per bank window): (key >> 1) & 7.
+template <int D>
+__device__ __forceinline__ constexpr int k_swz(int key) {
+  return D == 128 ? (key & 15) : ((key >> 1) & 7);
+}
+// V: XOR of the 32-byte unit index.  The transposing reads of one instruction cover 8
+// keys (4 per lane half) at two neighbouring units; for 256-byte rows the pattern
+// 2 (key & 3) + ((key >> 2) & 1) puts those 16 (key, unit) pairs on distinct units.
+template <int D>
+__device__ __forceinline__ constexpr int v_swz(int key) {
+  return D == 128 ? (((key & 3) << 1) | ((key >> 2) & 1)) : (key & 7);
+}
+// K: byte offset of physical 16-byte chunk of row `key` holding logical chunk `ch`
+template <int D>
+__device__ __forceinline__ int k_off(int key, int ch) { return key * (D * 2) + ((ch ^ k_swz<D>(key)) << 4); }
+// V: byte offset of V[key][d] (d a multiple of 4)
 template <int D>
 __device__ __forceinline__ int v_off(int key, int d) {
   constexpr int UM = Lds<D>::UNITS - 1;
-  return key * (D * 2) + ((((d >> 4) ^ (key & 7)) & UM) << 5) + ((d & 15) << 1);
+  return key * (D * 2) + ((((d >> 4) ^ v_swz<D>(key)) & UM) << 5) + ((d & 15) << 1);
 }
 
 // key offset (within the 64-key sub-tile) held by S^T register rr of M-tile mt,

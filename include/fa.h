@@ -162,7 +162,7 @@ typedef struct {
  * A row with no allowed key gets O = 0 and LSE = -inf.
  * bm must have been built for the same q_len, kv_len (and B/H extents compatible
  * with B and Hq); q_offset is taken from bm.
- * Short queries (one query block, (Hq/Hkv) * q_len <= 32, block_kv == 128) take a
+ * Short queries (one query block, (Hq/Hkv) * q_len <= 16, block_kv == 128) take a
  * split-KV path that needs `workspace` of fa_forward_workspace_size bytes; every other
  * shape needs none (workspace may then be NULL).
  * -------------------------------------------------------------------------------- */
