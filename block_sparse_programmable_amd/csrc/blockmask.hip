@@ -42,6 +42,10 @@ namespace fa {
 
 namespace {
 
+// wave-wide exclusive prefix sum (DPP), from the device library that also provides the
+// wave reductions used below
+extern "C" __device__ int __ockl_wfscan_add_i32(int, bool);
+
 constexpr uint8_t kEmpty = 0, kPartial = 1, kFull = 2;
 enum : int { VT = 0, VF = 1, VM = 2, VU = 3 };
 
@@ -74,7 +78,46 @@ __device__ __forceinline__ BlockGeom geom(const BuildParams& p, int r, int c) {
   return g;
 }
 
-__device__ int classify_bounds(const BuildParams& p, const BlockGeom& g, const int32_t* qs, const int32_t* ks) {
+// Document part from the per-block ID ranges.  When the IDs are non-decreasing over
+// every position either side reads (docs_sorted), the IDs present in a block are all the
+// present IDs between its min and max, so two blocks share an ID iff their ranges
+// overlap: overlapping ranges that are not one common ID make a known partial block.
+__device__ __forceinline__ int classify_doc(const int32_t* qs, const int32_t* ks, bool docs_sorted) {
+  const int qmin = qs[0], qmax = qs[1], kmin = ks[0], kmax = ks[1];
+  if (qmin == qmax && kmin == kmax && qmin == kmin) return VT;
+  if (qmax < kmin || kmax < qmin) return VF;
+  return docs_sorted ? VM : VU;
+}
+
+// And-only programs (interval form): the allowed keys of row i are [lo(i), hi(i)] with
+// both ends non-decreasing in i and lo(i) <= i <= hi(i), so the block is FULL iff
+// lo(last row) <= c0 and hi(first row) >= c1, and EMPTY iff no row reaches the block:
+// the first row i1 with hi(i1) >= c0 has the smallest lo among the rows that do, so the
+// block is empty iff there is no such row or lo(i1) > c1.  Otherwise it is partial.
+__device__ int classify_interval(const BuildParams& p, const BlockGeom& g, const int32_t* qs, const int32_t* ks,
+                                 bool docs_sorted) {
+  const MaskProg& m = p.prog;
+  auto lo_of = [&](int64_t i) -> int64_t { return m.wmin > 0 ? max((int64_t)0, i - m.wmin + 1) : (int64_t)0; };
+  auto hi_of = [&](int64_t i) -> int64_t {
+    return m.hi_self ? i : (m.pmin >= 0 ? max((int64_t)m.pmin - 1, i) : (int64_t)0x7fffffffffffffffLL);
+  };
+  int v;
+  if (lo_of(g.bb) <= g.c0 && hi_of(g.a) >= g.c1) {
+    v = VT;
+  } else {
+    int64_t i1;
+    if (m.hi_self) i1 = max(g.a, g.c0);
+    else if (m.pmin >= 0) i1 = (int64_t)m.pmin - 1 >= g.c0 ? g.a : max(g.a, g.c0);
+    else i1 = g.a;
+    v = (i1 > g.bb || lo_of(i1) > g.c1) ? VF : VM;
+  }
+  if (m.has_doc) v = v_and(v, classify_doc(qs, ks, docs_sorted));
+  return v;
+}
+
+__device__ int classify_bounds(const BuildParams& p, const BlockGeom& g, const int32_t* qs, const int32_t* ks,
+                               bool docs_sorted = false) {
+  if (p.prog.mk != MK_GENERIC) return classify_interval(p, g, qs, ks, docs_sorted);
   int st[FA_MASK_MAX_NODES];
   int sp = 0;
   for (int t = 0; t < p.prog.n; ++t) {
@@ -91,10 +134,7 @@ __device__ int classify_bounds(const BuildParams& p, const BlockGeom& g, const i
       const int64_t hi_a = max(a - 1, g.a), hi_b = max(a - 1, g.bb);
       v = (g.c1 <= hi_a) ? VT : (g.c0 > hi_b ? VF : VM);
     } else if (op == FA_M_DOC) {
-      const int qmin = qs[0], qmax = qs[1], kmin = ks[0], kmax = ks[1];
-      if (qmin == qmax && kmin == kmax && qmin == kmin) v = VT;
-      else if (qmax < kmin || kmax < qmin) v = VF;
-      else v = VU;
+      v = classify_doc(qs, ks, docs_sorted);
     } else {
       sp -= 2;
       const int x = st[sp], y = st[sp + 1];
@@ -419,23 +459,28 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
   __shared__ int32_t cum_s[4 * (kSmallMaxTB + 1)]; // prefix over tb of tH * tot_s
   __shared__ int32_t list_s[kSmallMaxBlocks];      // undecided block ids
   __shared__ int32_t n_undecided;
+  __shared__ int32_t unsorted_s;   // some document ID decreases along the positions read
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nq = p.tB * p.nqb, nk = p.tB * p.nkb, nl = nq + nk;
   const int total = p.tB * p.nqb * p.nkb;
+  if (tid == 0) unsorted_s = 0;
+  __syncthreads();
 
-  // phase 1: document-ID ranges per query block and per KV block.  A wave takes four
-  // lines at a time (at most 128 IDs each: two per lane) and issues all their loads
-  // before reducing, so the HBM latency is paid once per four lines.
+  // phase 1: document-ID ranges per query block and per KV block, and whether the IDs
+  // are non-decreasing inside each block.  A wave takes eight lines at a time (at most
+  // 128 IDs each: two per lane, plus the ID after each for the order test) and issues
+  // all their loads before reducing, so the HBM latency is paid once per eight lines;
+  // the reductions are wave-wide DPP reductions.
   if (p.prog.has_doc) {
-    constexpr int G = 4;
+    constexpr int G = 8;
     for (int l0 = wv * G; l0 < nl; l0 += 16 * G) {
       int v[G][2];
-      bool in[G][2];
+      bool in[G][2], inn[G][2];
 #pragma unroll
       for (int u = 0; u < G; ++u) {
         const int line = l0 + u;
-        int64_t lo = 0, hi = 0;
-        const int32_t* d = nullptr;
+        int64_t lo = 0, hi = 1;   // lines past the end read ID 0 of batch 0 and use nothing
+        const int32_t* d = doc_row(p.doc, 0);
         if (line < nl) {
           const bool qside = line < nq;
           const int idx = qside ? line : line - nq;
@@ -450,46 +495,101 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
             hi = min((int64_t)(blk + 1) * p.bk, p.kv_len);
           }
         }
+        // unconditional loads at clamped positions keep all of them in flight at once
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int64_t x = lo + lane + 64 * h;
-          in[u][h] = x < hi;
-          v[u][h] = in[u][h] ? d[x] : 0;
+          in[u][h] = line < nl && x < hi;
+          inn[u][h] = line < nl && x + 1 < hi;
+          v[u][h] = d[min(x, hi - 1)];
         }
       }
+      bool any_desc = false;
 #pragma unroll
       for (int u = 0; u < G; ++u) {
-        int mn = 0x7fffffff, mx = (int)0x80000000;
+        // the ID one position on: the next lane's (DPP wave shift left by one lane); for
+        // lane 63 of the first half, lane 0 of the second
+        const int nx0 = __builtin_amdgcn_update_dpp(__builtin_amdgcn_readlane(v[u][1], 0), v[u][0], 0x130, 0xf, 0xf, false);
+        const int nx1 = __builtin_amdgcn_update_dpp(v[u][1], v[u][1], 0x130, 0xf, 0xf, false);
+        const bool desc = (inn[u][0] && nx0 < v[u][0]) || (inn[u][1] && nx1 < v[u][1]);
+        int mn, mx;
+        if (__ballot(desc) == 0) {
+          // non-decreasing line: first and last ID (last at offset nin - 1)
+          const int nin = __popcll(__ballot(in[u][0])) + __popcll(__ballot(in[u][1]));
+          const int last = nin > 0 ? nin - 1 : 0;
+          mn = __builtin_amdgcn_readlane(v[u][0], 0);
+          mx = last < 64 ? __builtin_amdgcn_readlane(v[u][0], last) : __builtin_amdgcn_readlane(v[u][1], last - 64);
+        } else {
+          any_desc = true;
+          mn = 0x7fffffff;
+          mx = (int)0x80000000;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          if (in[u][h]) {
-            mn = min(mn, v[u][h]);
-            mx = max(mx, v[u][h]);
-          }
-        for (int off = 32; off > 0; off >>= 1) {
-          mn = min(mn, __shfl_xor(mn, off));
-          mx = max(mx, __shfl_xor(mx, off));
+          for (int h = 0; h < 2; ++h)
+            if (in[u][h]) {
+              mn = min(mn, v[u][h]);
+              mx = max(mx, v[u][h]);
+            }
+          mn = __ockl_wfred_min_i32(mn);
+          mx = __ockl_wfred_max_i32(mx);
         }
         if (lane == 0 && l0 + u < nl) {
           stat_s[2 * (l0 + u)] = mn;
           stat_s[2 * (l0 + u) + 1] = mx;
         }
       }
+      if (any_desc && lane == 0) unsorted_s = 1;
     }
   }
   __syncthreads();
 
+  // order across lines: each line's IDs must not be below the previous line's on the same
+  // side, and when the query positions start at or after the last key the query side
+  // must not be below the key side (otherwise the two ranges overlap and each being
+  // ordered orders their union)
+  if (p.prog.has_doc) {
+    for (int line = tid; line < nl; line += 1024) {
+      const bool qside = line < nq;
+      const int idx = qside ? line : line - nq;
+      const int per = qside ? p.nqb : p.nkb;
+      const int blk = idx % per;
+      bool bad = blk > 0 && stat_s[2 * line] < stat_s[2 * (line - 1) + 1];
+      if (qside && blk == 0 && p.q_offset >= p.kv_len) {
+        const int tb = idx / per;
+        bad = bad || stat_s[2 * line] < stat_s[2 * (nq + tb * p.nkb + p.nkb - 1) + 1];
+      }
+      if (bad) unsorted_s = 1;
+    }
+  }
   // phase 2: bounds classification, one thread per block; undecided blocks go to a
   // list (its order is irrelevant: each entry's class is decided on its own)
   if (tid == 0) n_undecided = 0;
   __syncthreads();
-  for (int id = tid; id < total; id += 1024) {
-    const int tb = id / (p.nqb * p.nkb);
-    const int rem = id - tb * p.nqb * p.nkb;
-    const int r = rem / p.nkb, c = rem - r * p.nkb;
-    const int v = classify_bounds(p, geom(p, r, c), stat_s + 2 * (tb * p.nqb + r), stat_s + 2 * (nq + tb * p.nkb + c));
-    grid_s[id] = v == VU ? kEmpty : (v == VT ? kFull : (v == VF ? kEmpty : kPartial));
-    if (v == VU) list_s[atomicAdd(&n_undecided, 1)] = id;
+  const bool docs_sorted = p.prog.has_doc && unsorted_s == 0;
+  {
+    // (tb, r, c) of block id, advanced by 1024 ids per step without dividing
+    const int nblk = p.nqb * p.nkb;
+    int tb = tid / nblk;
+    int r = (tid - tb * nblk) / p.nkb;
+    int c = tid - tb * nblk - r * p.nkb;
+    const int st_tb = 1024 / nblk, st_rem = 1024 - st_tb * nblk;
+    const int st_r = st_rem / p.nkb, st_c = st_rem - st_r * p.nkb;
+    for (int id = tid; id < total; id += 1024) {
+      const int v = classify_bounds(p, geom(p, r, c), stat_s + 2 * (tb * p.nqb + r),
+                                    stat_s + 2 * (nq + tb * p.nkb + c), docs_sorted);
+      grid_s[id] = v == VU ? kEmpty : (v == VT ? kFull : (v == VF ? kEmpty : kPartial));
+      if (v == VU) list_s[atomicAdd(&n_undecided, 1)] = id;
+      c += st_c;
+      r += st_r;
+      tb += st_tb;
+      if (c >= p.nkb) {
+        c -= p.nkb;
+        ++r;
+      }
+      if (r >= p.nqb) {
+        r -= p.nqb;
+        ++tb;
+      }
+    }
   }
   __syncthreads();
 
@@ -522,10 +622,14 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
   }
   __syncthreads();
 
-  // phase 4: partial / full counts per row (tb, r) and per column (tb, c).  A side whose
-  // lines are very short (at most kShort entries, e.g. the query side of a decode grid)
-  // takes one thread per line, otherwise one wave per line (ballot counts).
+  // phase 4: partial / full counts per row (tb, r) and per column (tb, c).  Every line
+  // of a side has the same length; a side of short lines (at most kShort entries, e.g.
+  // the query side of a decode grid) takes one thread per line, the other one wave per
+  // line (ballot counts).  Lines are [rows | columns], so each kind is one range.
   constexpr int kShort = 8;
+  const bool rows_long = p.nkb > kShort, cols_long = p.nqb > kShort;
+  const int lw0 = rows_long ? 0 : nq, lw1 = cols_long ? nl : nq;   // long lines
+  const int ls0 = rows_long ? nq : 0, ls1 = cols_long ? nq : nl;   // short lines
   auto line_geom = [&](int line, int& tb, int& k, int& n, bool& rowside) {
     rowside = line < nq;
     const int idx = rowside ? line : line - nq;
@@ -536,11 +640,10 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
   auto entry = [&](const uint8_t* g, bool rowside, int k, int x) -> uint8_t {
     return rowside ? g[k * p.nkb + x] : g[x * p.nkb + k];
   };
-  for (int line = wv; line < nl; line += 16) {
+  for (int line = lw0 + wv; line < lw1; line += 16) {
     int tb, k, n;
     bool rowside;
     line_geom(line, tb, k, n, rowside);
-    if (n <= kShort) continue;
     const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
     int np = 0, nf = 0;
     for (int x0 = 0; x0 < n; x0 += 64) {
@@ -554,11 +657,10 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
       cnt_s[2 * line + 1] = nf;
     }
   }
-  for (int line = tid; line < nl; line += 1024) {
+  for (int line = ls0 + tid; line < ls1; line += 1024) {
     int tb, k, n;
     bool rowside;
     line_geom(line, tb, k, n, rowside);
-    if (n > kShort) continue;
     const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
     int np = 0, nf = 0;
     for (int x = 0; x < n; ++x) {
@@ -580,13 +682,9 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
     for (int x0 = 0; x0 < n; x0 += 64) {
       const int x = x0 + lane;
       const int v = x < n ? cnt_s[2 * (first + x) + kind] : 0;
-      int incl = v;
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      if (x < n) pre_s[2 * (first + x) + kind] = carry + incl - v;
-      carry += __shfl(incl, 63);
+      const int excl = __ockl_wfscan_add_i32(v, false);   // DPP wave scan
+      if (x < n) pre_s[2 * (first + x) + kind] = carry + excl;
+      carry += __builtin_amdgcn_readlane(excl + v, 63);
     }
     if (lane == 0) tot_s[4 * tb + 2 * side + kind] = carry;
   }
@@ -632,53 +730,55 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
     p.q_ptr[cols] = cum_s[4 * p.tB + 2];
     p.full_q_ptr[cols] = cum_s[4 * p.tB + 3];
   }
-  // ordered scatter: short lines one thread each, long lines one wave each
-  auto out_line = [&](int x, int& k, int& tb, int& n, bool& rowside, int32_t*& pout, int32_t*& fout) {
-    rowside = x < rows;
-    const int idx = rowside ? x : x - rows;
-    const int per = rowside ? p.nqb : p.nkb;
-    const int bh = idx / per;
-    k = idx - bh * per;
-    tb = bh / p.tH;
-    const int h = bh - tb * p.tH;
-    const int line = rowside ? tb * p.nqb + k : nq + tb * p.nkb + k;
+  // ordered scatter, per base line and then for every replicated head (head h of tb
+  // starts h * tot after head 0): long lines one wave each (ballot compaction), short
+  // lines one thread each
+  auto line_out = [&](int line, bool rowside, int tb, int& pp0, int& pf0, int& tp, int& tf) {
     const int side = rowside ? 0 : 1;
-    const int pp = cum_s[4 * tb + 2 * side] + h * tot_s[4 * tb + 2 * side] + pre_s[2 * line];
-    const int pf = cum_s[4 * tb + 2 * side + 1] + h * tot_s[4 * tb + 2 * side + 1] + pre_s[2 * line + 1];
-    pout = (rowside ? p.kv_idx : p.q_idx) + pp;
-    fout = (rowside ? p.full_kv_idx : p.full_q_idx) + pf;
-    n = rowside ? p.nkb : p.nqb;
+    tp = tot_s[4 * tb + 2 * side];
+    tf = tot_s[4 * tb + 2 * side + 1];
+    pp0 = cum_s[4 * tb + 2 * side] + pre_s[2 * line];
+    pf0 = cum_s[4 * tb + 2 * side + 1] + pre_s[2 * line + 1];
   };
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int x = wv; x < rows + cols; x += 16) {
-    int k, tb, n;
+  for (int line = lw0 + wv; line < lw1; line += 16) {
+    int tb, k, n, pp0, pf0, tp, tf;
     bool rowside;
-    int32_t *pout, *fout;
-    out_line(x, k, tb, n, rowside, pout, fout);
-    if (n <= kShort) continue;
+    line_geom(line, tb, k, n, rowside);
+    line_out(line, rowside, tb, pp0, pf0, tp, tf);
+    int32_t* pidx = rowside ? p.kv_idx : p.q_idx;
+    int32_t* fidx = rowside ? p.full_kv_idx : p.full_q_idx;
     const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
     for (int x0 = 0; x0 < n; x0 += 64) {
       const int y = x0 + lane;
       const uint8_t v = y < n ? entry(g, rowside, k, y) : kEmpty;
       const uint64_t bp = __ballot(v == kPartial);
       const uint64_t bf = __ballot(v == kFull);
-      if (v == kPartial) pout[__popcll(bp & below)] = y;
-      if (v == kFull) fout[__popcll(bf & below)] = y;
-      pout += __popcll(bp);
-      fout += __popcll(bf);
+      const int ip = pp0 + __popcll(bp & below), jf = pf0 + __popcll(bf & below);
+      for (int h = 0; h < p.tH; ++h) {
+        if (v == kPartial) pidx[ip + h * tp] = y;
+        if (v == kFull) fidx[jf + h * tf] = y;
+      }
+      pp0 += __popcll(bp);
+      pf0 += __popcll(bf);
     }
   }
-  for (int x = tid; x < rows + cols; x += 1024) {
-    int k, tb, n;
+  for (int line = ls0 + tid; line < ls1; line += 1024) {
+    int tb, k, n, pp0, pf0, tp, tf;
     bool rowside;
-    int32_t *pout, *fout;
-    out_line(x, k, tb, n, rowside, pout, fout);
-    if (n > kShort) continue;
+    line_geom(line, tb, k, n, rowside);
+    line_out(line, rowside, tb, pp0, pf0, tp, tf);
+    int32_t* pidx = rowside ? p.kv_idx : p.q_idx;
+    int32_t* fidx = rowside ? p.full_kv_idx : p.full_q_idx;
     const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
     for (int y = 0; y < n; ++y) {
       const uint8_t v = entry(g, rowside, k, y);
-      if (v == kPartial) *pout++ = y;
-      if (v == kFull) *fout++ = y;
+      for (int h = 0; h < p.tH; ++h) {
+        if (v == kPartial) pidx[pp0 + h * tp] = y;
+        if (v == kFull) fidx[pf0 + h * tf] = y;
+      }
+      pp0 += v == kPartial;
+      pf0 += v == kFull;
     }
   }
 }
