@@ -196,6 +196,36 @@ def run(args):
     fwd_ms = [ev[0][i].elapsed_time(ev[1][i]) for i in range(K)]
     fwd_avg = float(np.mean(fwd_ms))
 
+    # the builder and the forward alone, each with caches flushed before every
+    # repetition (a 1 GiB read that is not timed; a read leaves clean lines, where a
+    # write would leave dirty ones for the timed kernel to write back): the step loop
+    # above runs back to back, where inputs that fit the last-level cache stay warm
+    cold = {}
+    if args.cold_reps > 0:
+        flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        sink = torch.empty(2, dtype=torch.uint8, device=dev)
+        e = [[torch.cuda.Event(enable_timing=True) for _ in range(args.cold_reps)] for _ in range(4)]
+        for i in range(args.cold_reps):
+            torch.amax(flush, dim=0, out=sink[0])
+            e[0][i].record()
+            b = fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset,
+                                     docT, tables=tables, workspace=bws)
+            e[1][i].record()
+            torch.amax(flush, dim=0, out=sink[1])
+            e[2][i].record()
+            fa.forward(q, k, v, b, score=w.score, softcap=w.cap, alibi_slopes=sl, relpos=tb,
+                       relpos_radius=w.relpos_radius, out=out, lse=lse, workspace=fws)
+            e[3][i].record()
+        torch.cuda.synchronize()
+        bt = [e[0][i].elapsed_time(e[1][i]) for i in range(args.cold_reps)]
+        ft = [e[2][i].elapsed_time(e[3][i]) for i in range(args.cold_reps)]
+        cold = {"reps": args.cold_reps,
+                "build_ms_median": float(np.median(bt)), "build_ms_p10": float(np.percentile(bt, 10)),
+                "build_ms_p90": float(np.percentile(bt, 90)),
+                "fwd_ms_median": float(np.median(ft)), "fwd_ms_p10": float(np.percentile(ft, 10)),
+                "fwd_ms_p90": float(np.percentile(ft, 90))}
+        del flush, sink
+
     decode = w.q_len == 1
     if decode:
         value = acc["bytes"] / (ms_step * 1e-3) / 1e9
@@ -225,6 +255,7 @@ def run(args):
            "fwd_ms": fwd_avg, "fwd_ms_p10": float(np.percentile(fwd_ms, 10)),
            "fwd_ms_p90": float(np.percentile(fwd_ms, 90)),
            "algorithmic_flop": acc["flop"], "algorithmic_bytes": acc.get("bytes"),
+           "cold_cache": cold or None,
            "kernel_source_digest": kernel_source_digest("decode" if decode else "prefill"),
            "gpu": torch.cuda.get_device_name(0),
            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
@@ -254,6 +285,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="causal_softcap")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="repetitions of the separately timed build and forward with flushed caches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args(argv)
