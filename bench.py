@@ -78,6 +78,8 @@ def accounting(w, tab):
         kv_bytes = w.B * w.Hkv * executed * w.block_kv * w.d * 2 * 2
         q_bytes = w.B * w.Hq * w.q_len * w.d * 2
         idx_bytes = 4 * (executed + 4)
+        if w.page_size:   # page-table entries of the executed blocks, per request
+            idx_bytes += 4 * w.B * executed * (w.block_kv // w.page_size)
         acc["bytes"] = kv_bytes + 2 * q_bytes + w.B * w.Hq * w.q_len * 4 + idx_bytes
         acc["flop"] = heads * executed * w.block_kv * 4 * w.d * w.q_len
     else:
@@ -165,16 +167,28 @@ def run(args):
     fargs, _, _ = fa.forward_args(q, k, v, bm, w.score, w.cap, sl, tb, w.relpos_radius, None, out, lse)
     fws_bytes = fa.forward_workspace_size(fargs)
     fws = torch.empty(max(fws_bytes, 1), dtype=torch.uint8, device=dev)
+    if w.page_size:
+        # paged caches holding the same logical K/V through a fragmented page table
+        pt_np = W.page_table(w)
+        kc, vc = W.paged_caches(w, k, v, pt_np)
+        ptT = torch.as_tensor(pt_np).to(dev)
     torch.cuda.synchronize()
     acc = accounting(w, bm.compact())
+
+    def fwd(b):
+        if w.page_size:
+            fa.forward_paged(q, kc, vc, ptT, w.kv_len, b, score=w.score, softcap=w.cap, alibi_slopes=sl,
+                             relpos=tb, relpos_radius=w.relpos_radius, out=out, lse=lse, workspace=fws)
+        else:
+            fa.forward(q, k, v, b, score=w.score, softcap=w.cap, alibi_slopes=sl, relpos=tb,
+                       relpos_radius=w.relpos_radius, out=out, lse=lse, workspace=fws)
 
     def step(ev=None, i=0):
         b = fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset,
                                  docT, tables=tables, workspace=bws)
         if ev is not None:
             ev[0][i].record()
-        fa.forward(q, k, v, b, score=w.score, softcap=w.cap, alibi_slopes=sl, relpos=tb,
-                   relpos_radius=w.relpos_radius, out=out, lse=lse, workspace=fws)
+        fwd(b)
         if ev is not None:
             ev[1][i].record()
 
@@ -213,8 +227,7 @@ def run(args):
             e[1][i].record()
             torch.amax(flush, dim=0, out=sink[1])
             e[2][i].record()
-            fa.forward(q, k, v, b, score=w.score, softcap=w.cap, alibi_slopes=sl, relpos=tb,
-                       relpos_radius=w.relpos_radius, out=out, lse=lse, workspace=fws)
+            fwd(b)
             e[3][i].record()
         torch.cuda.synchronize()
         bt = [e[0][i].elapsed_time(e[1][i]) for i in range(args.cold_reps)]
@@ -246,7 +259,7 @@ def run(args):
 
     cfg = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "q_len": w.q_len, "kv_len": w.kv_len,
            "d": w.d, "block_q": w.block_q, "block_kv": w.block_kv, "mask": repr(w.mask),
-           "score_mod": w.score, "q_offset": w.q_offset, "seed": w.seed,
+           "score_mod": w.score, "q_offset": w.q_offset, "seed": w.seed, "page_size": w.page_size or None,
            "full_blocks": acc["full_blocks"], "partial_blocks": acc["partial_blocks"]}
     rec = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": K,
            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,

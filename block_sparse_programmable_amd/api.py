@@ -146,9 +146,10 @@ def create_block_mask(mask, B, H, q_len, kv_len, block_q=128, block_kv=128, q_of
 
 def forward_args(q, k, v, block_mask: BlockMask, score="identity", softcap=0.0,
                  alibi_slopes=None, relpos=None, relpos_radius=0, scale=None, out=None,
-                 lse=None):
+                 lse=None, kv_len=None):
     B, Hq, q_len, d = q.shape
-    Hkv, kv_len = k.shape[1], k.shape[2]
+    Hkv = k.shape[1]
+    kv_len = k.shape[2] if kv_len is None else int(kv_len)
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
@@ -175,6 +176,35 @@ def forward_workspace_size(args) -> int:
     n = C.c_size_t()
     L.check(lib.fa_forward_workspace_size(C.byref(args), C.byref(n)))
     return n.value
+
+
+def forward_paged(q, k_cache, v_cache, page_table, kv_len, block_mask: BlockMask, score="identity",
+                  softcap=0.0, alibi_slopes=None, relpos=None, relpos_radius=0, scale=None, out=None,
+                  lse=None, workspace=None, stream=None):
+    """Short-query forward over paged caches k_cache/v_cache bf16 [num_pages, Hkv, page_size, d]
+    with page_table int32 [B, pt_stride] (logical page -> physical page) and logical length
+    kv_len.  Returns O [B,Hq,q_len,d] bf16 and LSE [B,Hq,q_len] fp32."""
+    lib = L.load()
+    num_pages, _, page_size, _ = k_cache.shape
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or not page_table.is_contiguous():
+        raise ValueError("page_table must be a contiguous int32 [B, pt_stride] tensor")
+    a, out, lse = forward_args(q, k_cache, v_cache, block_mask, score, softcap, alibi_slopes, relpos,
+                               relpos_radius, scale, out, lse, kv_len=kv_len)
+    kv = L.fa_paged_kv()
+    kv.page_table = page_table.data_ptr()
+    kv.pt_stride = page_table.shape[1]
+    kv.page_size = page_size
+    kv.num_pages = num_pages
+    need = forward_workspace_size(a)
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        a.workspace = workspace.data_ptr()
+        a.ws_bytes = workspace.numel() * workspace.element_size()
+    L.check(lib.fa_forward_paged(C.byref(a), C.byref(kv), _stream(stream)))
+    return out, lse
 
 
 def forward(q, k, v, block_mask: BlockMask, score="identity", softcap=0.0, alibi_slopes=None,

@@ -226,6 +226,10 @@ fa_status plan_forward(const fa_fwd_args* a, FwdPlan* plan) {
   p.tab.bk = bm->block_kv;
   p.nsplit = 1;
   p.ws = nullptr;
+  p.pt = nullptr;
+  p.pt_stride = 0;
+  p.page_shift = 0;
+  p.num_pages = 0;
   plan->decode = a->q_len > 0 && fa::decode_eligible(p);
   plan->ws = 0;
   if (plan->decode) {
@@ -330,9 +334,32 @@ fa_status fa_forward_workspace_size(const fa_fwd_args* args, size_t* bytes) {
 }
 
 fa_status fa_forward(const fa_fwd_args* args, fa_stream_t stream) {
+  return fa_forward_paged(args, nullptr, stream);
+}
+
+fa_status fa_forward_paged(const fa_fwd_args* args, const fa_paged_kv* kv, fa_stream_t stream) {
   FwdPlan plan;
   fa_status s = plan_forward(args, &plan);
   if (s != FA_OK) return s;
+  if (kv) {
+    if (!kv->page_table) return fail(FA_ERR_NULL, "page_table is NULL");
+    const int32_t ps = kv->page_size;
+    if (ps < 16 || ps > 65536 || (ps & (ps - 1)) != 0)
+      return fail(FA_ERR_UNSUPPORTED, "page_size must be a power of two in [16, 65536] (got %d)", ps);
+    const int64_t pages = (args->kv_len + ps - 1) / ps;
+    if (kv->pt_stride < pages)
+      return fail(FA_ERR_SHAPE, "pt_stride %lld is below the %lld pages of kv_len", (long long)kv->pt_stride,
+                  (long long)pages);
+    if (kv->num_pages < 1 || kv->num_pages > 0x7fffffffLL)
+      return fail(FA_ERR_SHAPE, "num_pages must be in [1, 2^31 - 1]");
+    if (args->q_len > 0 && !plan.decode)
+      return fail(FA_ERR_UNSUPPORTED, "a paged KV cache is read by the short-query path only: "
+                  "(Hq/Hkv) * q_len <= 16, one query block and block_kv == 128");
+    plan.p.pt = kv->page_table;
+    plan.p.pt_stride = kv->pt_stride;
+    plan.p.page_shift = __builtin_ctz((unsigned)ps);
+    plan.p.num_pages = kv->num_pages;
+  }
   if (plan.ws > 0) {
     if (!args->workspace || args->ws_bytes < plan.ws)
       return fail(FA_ERR_WORKSPACE, "forward workspace needs %zu bytes (got %zu)", plan.ws,

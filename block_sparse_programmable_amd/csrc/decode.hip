@@ -65,7 +65,7 @@ __device__ __forceinline__ f32x4 mfma16k16(const s16x4& a, const s16x4& b, const
 // keys).  In lane l (group g = l/16, column l%16) S^T register r holds key 4g + r,
 // which is exactly the P^T operand of the P V product; the V^T operand of lane l
 // (d = 16 dt + l%16, keys 4g .. 4g+3) is one transposing LDS read.
-template <int D, int SCORE>
+template <int D, int SCORE, bool PAGED>
 __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) {
   constexpr int DCH = D / 8;
   constexpr int KT4 = D / 32;                  // k-steps of the QK product
@@ -139,8 +139,23 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
   const int rot = nst > 0 ? (int)((unit * 37) % nst) : 0;
   auto rs = [&](int s) { const int t = s + rot; return t >= nst ? t - nst : t; };
 
-  const uint16_t* kbase = p.k + (int64_t)bk_id * p.kv_len * D;
-  const uint16_t* vbase = p.v + (int64_t)bk_id * p.kv_len * D;
+  // first K/V row of this (b, h_kv) (contiguous layout), or the request's page-table
+  // row (paged layout: logical key j lives in page pt_row[j >> page_shift], row
+  // (page * Hkv + h_kv) * page_size + (j & (page_size - 1)) of the cache)
+  const int64_t krow0 = (int64_t)bk_id * p.kv_len;
+  const int32_t* pt_row = PAGED ? p.pt + (int64_t)b * p.pt_stride : nullptr;
+  const int pshift = PAGED ? p.page_shift : 0;
+  const int pmask = (1 << pshift) - 1;
+  const int last_page = PAGED ? (int)(p.num_pages - 1) : 0;
+  auto page_of = [&](int jb) -> int {
+    // physical page of logical key jb, clamped into the cache (scalar load)
+    const int pg = pt_row[jb >> pshift];
+    return min(max(pg, 0), last_page);
+  };
+  auto row_of = [&](int jb, int pg) -> int64_t {
+    if constexpr (PAGED) return ((int64_t)pg * p.Hkv + hkv) * (pmask + 1) + (jb & pmask);
+    return krow0 + jb;
+  };
   const int32_t* docr = doc_row(p.doc, b);
   const int doc_i = (p.prog.has_doc && col_ok) ? docr[i_g] : 0;
   const ScoreCtx sc = make_score_ctx(p.score, p.scale, hq);
@@ -181,13 +196,16 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
   uint8_t* ring = smem + w * L::WAVE;
   const uint32_t ring_lds = lds_addr(ring);
 
-  // one stage (SK keys from j0) into ring slot `slot`
-  auto copy_stage = [&](int j0, int slot) {
+  // one stage (SK keys from j0) into ring slot `slot`; pg is the physical page of key
+  // min(j0, kv_len - 1) (paged layout: a stage never crosses a page, and a ragged stage
+  // only reads keys from that one up to kv_len - 1, inside the same page)
+  auto copy_stage = [&](int j0, int pg, int slot) {
     const uint32_t mk = sreg(ring_lds + (uint32_t)slot * L::STAGE);
     const uint32_t mv = mk + L::HALF;
     if (j0 + SK <= kv_len) {
-      const char* kg = (const char*)kbase + (int64_t)j0 * L::KROW;
-      const char* vg = (const char*)vbase + (int64_t)j0 * L::KROW;
+      const int64_t r0 = row_of(j0, pg);
+      const char* kg = (const char*)p.k + r0 * L::KROW;
+      const char* vg = (const char*)p.v + r0 * L::KROW;
       static_for<CPO>([&](auto uc) {
         constexpr int u = decltype(uc)::value;
         constexpr int grp = (u / 4) * 4096;   // immediate offsets stay below 4 KB
@@ -198,8 +216,9 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
       // ragged tail: keys past kv_len re-read the last key (they are masked); offsets
       // from jb = min(j0, kv_len - 1) stay non-negative
       const int jb = min(j0, kv_len - 1);
-      const char* kg = (const char*)kbase + (int64_t)jb * L::KROW;
-      const char* vg = (const char*)vbase + (int64_t)jb * L::KROW;
+      const int64_t rb = row_of(jb, pg);
+      const char* kg = (const char*)p.k + rb * L::KROW;
+      const char* vg = (const char*)p.v + rb * L::KROW;
       static_for<CPO>([&](auto uc) {
         constexpr int u = decltype(uc)::value;
         const int key = u * KPK + lane / DCH;
@@ -282,7 +301,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
     j0_of[k] = 0;
     if (k < nst) {
       j0_of[k] = stage_j0(rs(k));
-      copy_stage(j0_of[k], k);
+      copy_stage(j0_of[k], PAGED ? page_of(min(j0_of[k], kv_len - 1)) : 0, k);
       ++issued;
     }
   }
@@ -300,14 +319,18 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
 #pragma unroll
     for (int k = 0; k < kStages; ++k)
       if (k == slot) j0 = j0_of[k];
+    // the next stage's position (and its page, a scalar load that lands during the
+    // compute below)
+    const bool more = s + kStages < nst;
+    const int jn = more ? stage_j0(rs(s + kStages)) : 0;
+    const int pgn = (PAGED && more) ? page_of(min(jn, kv_len - 1)) : 0;
     compute(j0, stage_part(rs(s)), slot);
-    if (s + kStages < nst) {
+    if (more) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads of this slot are done
-      const int jn = stage_j0(rs(s + kStages));
 #pragma unroll
       for (int k = 0; k < kStages; ++k)
         if (k == slot) j0_of[k] = jn;
-      copy_stage(jn, slot);
+      copy_stage(jn, pgn, slot);
       ++issued;
     }
     slot = slot + 1 == kStages ? 0 : slot + 1;
@@ -449,11 +472,11 @@ size_t decode_workspace_bytes(const FwdParams& p, int32_t nsplit) {
   return rows * nsplit * (2 + (size_t)p.d) * sizeof(float);
 }
 
-hipError_t launch_decode(const FwdParams& p, hipStream_t s) {
-  const int64_t units = (int64_t)p.B * p.Hkv * p.nsplit;
-  const dim3 grid((unsigned)((units + kDecWaves - 1) / kDecWaves));
-  const dim3 block(64 * kDecWaves);
-#define FA_DEC(DD, SS) hipLaunchKernelGGL((decode_kernel<DD, SS>), grid, block, 0, s, p)
+namespace {
+
+template <bool PAGED>
+void launch_decode_kernel(const FwdParams& p, hipStream_t s, dim3 grid, dim3 block) {
+#define FA_DEC(DD, SS) hipLaunchKernelGGL((decode_kernel<DD, SS, PAGED>), grid, block, 0, s, p)
   if (p.d == 128) {
     switch (p.score.kind) {
       case FA_S_IDENTITY: FA_DEC(128, FA_S_IDENTITY); break;
@@ -470,6 +493,19 @@ hipError_t launch_decode(const FwdParams& p, hipStream_t s) {
     }
   }
 #undef FA_DEC
+}
+
+}  // namespace
+
+hipError_t launch_decode(const FwdParams& p, hipStream_t s) {
+  const int64_t units = (int64_t)p.B * p.Hkv * p.nsplit;
+  const dim3 grid((unsigned)((units + kDecWaves - 1) / kDecWaves));
+  const dim3 block(64 * kDecWaves);
+  if (p.pt) {
+    launch_decode_kernel<true>(p, s, grid, block);
+  } else {
+    launch_decode_kernel<false>(p, s, grid, block);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit <= 1 || kDecWaves % p.nsplit == 0) return e;
   const int64_t rows = (int64_t)p.B * p.Hq * p.q_len;

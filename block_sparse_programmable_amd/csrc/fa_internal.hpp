@@ -86,6 +86,12 @@ struct FwdParams {
   // split-KV decode
   int32_t nsplit;
   float* ws;  // partial states
+  // paged K/V (decode path): k and v are [num_pages, Hkv, page_size, d]; pt == nullptr
+  // for contiguous K/V
+  const int32_t* pt;
+  int64_t pt_stride;
+  int32_t page_shift;   // log2(page_size)
+  int64_t num_pages;
 };
 
 bool decode_eligible(const FwdParams& p);

@@ -7,6 +7,7 @@
  *
  *   fa_create_block_mask  mask rule -> block tables (BCSR rows and their transposes)
  *   fa_forward            O = softmax(mask(score_mod(Q K^T * scale))) V, plus LSE
+ *   fa_forward_paged      the same over a paged KV cache (short-query path)
  *
  * Conventions shared by every entry point
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library never
@@ -183,6 +184,40 @@ typedef struct {
 
 fa_status fa_forward_workspace_size(const fa_fwd_args* args, size_t* bytes);
 fa_status fa_forward(const fa_fwd_args* args, fa_stream_t stream);
+
+/* ----------------------------------------------------------------------------------
+ * Paged KV cache ("FlexAttention: from rules to fused kernels", sec. 5: a per-request
+ * page table maps logical KV block j to a physical cache block; the attention rules,
+ * score_mod positions and the BlockMask stay in logical positions, and the kernel
+ * follows the table while it streams K/V instead of gathering a contiguous copy).
+ *
+ *   page_table  device int32 [B, pt_stride]: physical page of logical page p of
+ *               request b is page_table[b * pt_stride + p]; logical page p holds the
+ *               logical keys [p * page_size, (p + 1) * page_size).  Entries may repeat
+ *               (requests sharing a prefix share pages).
+ *   page_size   keys per page: a power of two, 16 <= page_size <= 65536.
+ *   pt_stride   >= ceil(kv_len / page_size) (entries past that count are never read).
+ *   num_pages   pages in each cache; every entry read must lie in [0, num_pages).  An
+ *               entry outside that range is clamped into it (so every access stays
+ *               inside the caches) and the rows that use it get unspecified values.
+ *
+ * fa_forward_paged takes the same arguments as fa_forward, except that args->k and
+ * args->v are the paged caches, bf16 [num_pages, Hkv, page_size, d] each (one
+ * contiguous page_size x d slab per page and KV head), and args->kv_len is the
+ * logical KV length.  Only the short-query split-KV path is paged: the shape must
+ * satisfy the conditions stated for it above ((Hq/Hkv) * q_len <= 16, one query
+ * block, block_kv == 128), otherwise FA_ERR_UNSUPPORTED.  The workspace is the one
+ * fa_forward_workspace_size reports for `args`.  Results equal fa_forward on the
+ * logical (gathered) K and V bit for bit.
+ * -------------------------------------------------------------------------------- */
+typedef struct {
+  const int32_t* page_table;
+  int64_t pt_stride;
+  int32_t page_size;
+  int64_t num_pages;
+} fa_paged_kv;
+
+fa_status fa_forward_paged(const fa_fwd_args* args, const fa_paged_kv* kv, fa_stream_t stream);
 
 const char* fa_status_string(fa_status s);
 const char* fa_last_error_message(void);

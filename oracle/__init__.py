@@ -17,9 +17,11 @@ What it computes, in plain numpy float64:
                    of values, log-sum-exp; no online softmax, no tiling.
 * ``merge``     -- the merge law of partial softmax states, used only to pin the
                    split-KV combination.
+* ``paged``     -- the logical K/V of a paged cache (page-table gather), so that
+                   paged attention is checked against dense attention on it.
 
 Parity status of every function is stated in its docstring; each is pinned by
 the tests in ``tests/test_oracle_pins.py`` against values and identities that
 the pages and elementary mathematics fix.
 """
-from . import masks, blockmask, attention, merge  # noqa: F401
+from . import masks, blockmask, attention, merge, paged  # noqa: F401

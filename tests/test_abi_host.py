@@ -174,6 +174,20 @@ def test_forward_validation(lib):
     for name in ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx"):
         setattr(bm3, name, 0x1000)
     assert F(_fwd(L, bm3)) == L.FA_ERR_MASK_MISMATCH
+    # paged caches: argument checks, and the paged cache is only read by the short-query path
+    P = lambda a, kv: lib.fa_forward_paged(C.byref(a), C.byref(kv), None)
+    kv = L.fa_paged_kv(page_table=0x1000, pt_stride=16, page_size=16, num_pages=4)
+    assert lib.fa_forward_paged(None, C.byref(kv), None) == L.FA_ERR_NULL
+    assert P(_fwd(L, bm), L.fa_paged_kv(page_table=None, pt_stride=16, page_size=16, num_pages=4)) == L.FA_ERR_NULL
+    for ps in (8, 24, 1 << 17):
+        assert P(_fwd(L, bm), L.fa_paged_kv(page_table=0x1000, pt_stride=64, page_size=ps,
+                                            num_pages=4)) == L.FA_ERR_UNSUPPORTED
+    assert P(_fwd(L, bm), L.fa_paged_kv(page_table=0x1000, pt_stride=15, page_size=16,
+                                        num_pages=4)) == L.FA_ERR_SHAPE      # 256 keys need 16
+    assert P(_fwd(L, bm), L.fa_paged_kv(page_table=0x1000, pt_stride=16, page_size=16,
+                                        num_pages=0)) == L.FA_ERR_SHAPE
+    assert P(_fwd(L, bm), kv) == L.FA_ERR_UNSUPPORTED                          # prefill shape
+    assert b"short-query" in lib.fa_last_error_message()
     bm.kv_idx = None
     assert F(_fwd(L, bm)) == L.FA_ERR_NULL
     for s in range(8):

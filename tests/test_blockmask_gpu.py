@@ -87,7 +87,8 @@ def test_workload_tables(name):
     nf = int(got["full_kv_ptr"][-1])
     npart = int(got["kv_ptr"][-1])
     expected = {"tiny_swa": (7, 14), "causal_softcap": (496, 32), "gqa_doc_swa_alibi": (175, 160),
-                "prefix_relpos_64k": (131344, 480), "decode_swa_softcap": (32, 0)}[name]
+                "prefix_relpos_64k": (131344, 480), "decode_swa_softcap": (32, 0),
+                "decode_paged_swa_softcap": (32, 0)}[name]
     assert (nf, npart) == expected
 
 

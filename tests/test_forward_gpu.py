@@ -224,9 +224,19 @@ def test_workload_full_size_sampled(name):
     bm = fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset, docT)
     sl = None if aux["slopes"] is None else torch.as_tensor(aux["slopes"]).cuda()
     tb = None if aux["table"] is None else torch.as_tensor(aux["table"]).cuda()
-    o, lse = fa.forward(q, k, v, bm, score=w.score, softcap=w.cap, alibi_slopes=sl, relpos=tb,
-                        relpos_radius=w.relpos_radius)
-    torch.cuda.synchronize()
+    if w.page_size:
+        # the same logical K/V through the workload's fragmented page table
+        pt = W.page_table(w)
+        kcache, vcache = W.paged_caches(w, k, v, pt)
+        o, lse = fa.forward_paged(q, kcache, vcache, torch.as_tensor(pt).cuda(), w.kv_len, bm,
+                                  score=w.score, softcap=w.cap, alibi_slopes=sl, relpos=tb,
+                                  relpos_radius=w.relpos_radius)
+        torch.cuda.synchronize()
+        del kcache, vcache
+    else:
+        o, lse = fa.forward(q, k, v, bm, score=w.score, softcap=w.cap, alibi_slopes=sl, relpos=tb,
+                            relpos_radius=w.relpos_radius)
+        torch.cuda.synchronize()
     if w.q_len == 1:
         batches = [0, w.B // 2, w.B - 1]
         heads = list(range(w.Hq))

@@ -508,3 +508,42 @@ def test_oracle_matches_torch_cpu_flexattention(case):
     Ot, Lt = _torch_flex(q, k, v, case["spec"], case["kind"], doc=doc, **kw)
     assert np.abs(O - Ot).max() < 1e-10
     assert np.abs(L - Lt).max() < 1e-10
+
+
+# ---- paged KV gather ("FlexAttention: from rules to fused kernels", section 5)
+
+def test_paged_gather_worked_example():
+    from oracle import paged as OP
+    # two requests, page size 2, one KV head of width 1; physical pages hold the values
+    # 10+p, 20+p (rows 0 and 1 of page p)
+    cache = np.array([[[[10 + p], [20 + p]]] for p in range(4)], dtype=np.float64)
+    table = np.array([[3, 0, 2], [1, 1, 0]], dtype=np.int32)
+    got = OP.gather_logical_kv(cache, table, kv_len=5)
+    want0 = [13, 23, 10, 20, 12]       # pages 3, 0, 2 (the last page holds one key)
+    want1 = [11, 21, 11, 21, 10]       # page 1 twice: a shared page read twice
+    assert got.shape == (2, 1, 5, 1)
+    assert got[0, 0, :, 0].tolist() == want0
+    assert got[1, 0, :, 0].tolist() == want1
+
+
+def test_paged_gather_identity_table_and_shared_prefix():
+    from oracle import paged as OP
+    rng = np.random.default_rng(5)
+    B, H, T, d, ps = 3, 2, 50, 4, 16
+    k = rng.standard_normal((B, H, T, d))
+    npg = -(-T // ps)
+    cache = np.zeros((B * npg, H, ps, d))
+    for b in range(B):
+        for lp in range(npg):
+            n = min(ps, T - lp * ps)
+            cache[b * npg + lp, :, :n] = k[b, :, lp * ps:lp * ps + n]
+    ident = np.arange(B * npg, dtype=np.int32).reshape(B, npg)
+    assert np.array_equal(OP.gather_logical_kv(cache, ident, T), k)
+    # request 2 reuses request 0's first two pages: its first 32 keys become request 0's
+    shared = ident.copy()
+    shared[2, :2] = shared[0, :2]
+    g = OP.gather_logical_kv(cache, shared, T)
+    assert np.array_equal(g[2, :, :32], k[0, :, :32])
+    assert np.array_equal(g[2, :, 32:], k[2, :, 32:])
+    with pytest.raises(ValueError):
+        OP.gather_logical_kv(cache, np.full((1, npg), B * npg, dtype=np.int32), T)

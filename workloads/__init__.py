@@ -16,7 +16,8 @@ The five workloads follow the shapes the pages describe:
   6.3 for prefix-LM, section 1.2 for the table; section 2.1 for the
   262,144-block grid of a 64K sequence);
 * split-KV decode with a sliding window ending at the query position
-  ("FlexAttention: compiler optimization of custom attention", section 6).
+  ("FlexAttention: compiler optimization of custom attention", section 6), also
+  over a paged KV cache ("FlexAttention: from rules to fused kernels", section 5).
 
 Mask specifications are plain nested tuples, independent of any binary layout:
 ``("causal",)``, ``("swa", W)``, ``("doc",)``, ``("prefix", P)``,
@@ -57,6 +58,7 @@ class Workload:
     doc_seed: Optional[int] = None  # numpy seed for the document lengths
     doc_len_range: Tuple[int, int] = (256, 2048)
     table_B: int = 1                # batch extent of the block tables (1 = broadcast)
+    page_size: int = 0              # > 0: K/V live in a paged cache with this page size
 
     @property
     def g(self) -> int:
@@ -84,6 +86,12 @@ WORKLOADS = {
         name="decode_swa_softcap", B=64, Hq=32, Hkv=8, q_len=1, kv_len=32768, d=128,
         block_q=128, block_kv=128, mask=("swa", 4096), score="softcap", cap=30.0,
         q_offset=32767, seed=1005, aux_seed=1005),
+    # the same decode over a paged KV cache: 16-key pages placed by a random
+    # permutation ("FlexAttention: from rules to fused kernels", section 5)
+    "decode_paged_swa_softcap": Workload(
+        name="decode_paged_swa_softcap", B=64, Hq=32, Hkv=8, q_len=1, kv_len=32768, d=128,
+        block_q=128, block_kv=128, mask=("swa", 4096), score="softcap", cap=30.0,
+        q_offset=32767, seed=1005, aux_seed=1006, page_size=16),
 }
 
 # The N=8, W=4, 2x2-block classification case that goes with the tiny workload.
@@ -190,3 +198,30 @@ def qkv(w: Workload, device="cpu"):
 def scaled(w: Workload, **kw) -> Workload:
     """A copy of a workload with some fields replaced (for small parity cases)."""
     return dataclasses.replace(w, **kw)
+
+
+def page_table(w: Workload) -> np.ndarray:
+    """Page table int32 [B, ceil(kv_len / page_size)] of a paged workload: the B * pages
+    logical pages take the physical pages of one random permutation (numpy seed
+    ``w.aux_seed``), so consecutive logical pages are scattered over the cache."""
+    npg = -(-w.kv_len // w.page_size)
+    rng = np.random.default_rng(w.aux_seed)
+    return rng.permutation(w.B * npg).astype(np.int32).reshape(w.B, npg)
+
+
+def paged_caches(w: Workload, k, v, table):
+    """K/V caches [B * pages, Hkv, page_size, d] holding the logical K and V
+    [B, Hkv, kv_len, d] at the pages ``table`` names (unused tail rows are zero)."""
+    assert torch is not None
+    ps = w.page_size
+    npg = table.shape[1]
+    pad = npg * ps - w.kv_len
+    out = []
+    for t in (k, v):
+        cache = torch.zeros((w.B * npg, w.Hkv, ps, w.d), dtype=t.dtype, device=t.device)
+        src = t if pad == 0 else torch.nn.functional.pad(t, (0, 0, 0, pad))
+        src = src.view(w.B, w.Hkv, npg, ps, w.d).permute(0, 2, 1, 3, 4).reshape(w.B * npg, w.Hkv, ps, w.d)
+        idx = torch.as_tensor(table.reshape(-1), dtype=torch.long, device=t.device)
+        cache.index_copy_(0, idx, src)
+        out.append(cache)
+    return tuple(out)
