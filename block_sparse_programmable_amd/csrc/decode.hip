@@ -143,7 +143,9 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
   // row (paged layout: logical key j lives in page pt_row[j >> page_shift], row
   // (page * Hkv + h_kv) * page_size + (j & (page_size - 1)) of the cache)
   const int64_t krow0 = (int64_t)bk_id * p.kv_len;
-  const int32_t* pt_row = PAGED ? p.pt + (int64_t)b * p.pt_stride : nullptr;
+  // (wave-uniform, held in scalar registers so that the per-stage table read is a
+  // scalar load, tracked apart from the vector-memory copies)
+  const int32_t* pt_row = PAGED ? static_cast<const int32_t*>(sreg(p.pt + (int64_t)b * p.pt_stride)) : nullptr;
   const int pshift = PAGED ? p.page_shift : 0;
   const int pmask = (1 << pshift) - 1;
   const int last_page = PAGED ? (int)(p.num_pages - 1) : 0;
