@@ -19,9 +19,10 @@ What it computes, in plain numpy float64:
                    split-KV combination.
 * ``paged``     -- the logical K/V of a paged cache (page-table gather), so that
                    paged attention is checked against dense attention on it.
+* ``backward``  -- dQ, dK, dV of the dense definition by float64 autograd.
 
 Parity status of every function is stated in its docstring; each is pinned by
 the tests in ``tests/test_oracle_pins.py`` against values and identities that
 the pages and elementary mathematics fix.
 """
-from . import masks, blockmask, attention, merge, paged  # noqa: F401
+from . import masks, blockmask, attention, merge, paged, backward  # noqa: F401

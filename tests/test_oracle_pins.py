@@ -547,3 +547,53 @@ def test_paged_gather_identity_table_and_shared_prefix():
     assert np.array_equal(g[2, :, 32:], k[2, :, 32:])
     with pytest.raises(ValueError):
         OP.gather_logical_kv(cache, np.full((1, npg), B * npg, dtype=np.int32), T)
+
+
+# ---- backward: gradients of the dense definition ("FlexAttention: from rules to fused
+# kernels", section 4), pinned by finite differences of the forward oracle
+
+@pytest.mark.parametrize("kind", ["identity", "softcap", "alibi", "relpos"])
+def test_backward_matches_finite_differences(kind):
+    from oracle import backward as OBW
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, ql, kl, d = 1, 2, 1, 5, 7, 3
+    q = rng.standard_normal((B, Hq, ql, d))
+    k = rng.standard_normal((B, Hkv, kl, d))
+    v = rng.standard_normal((B, Hkv, kl, d))
+    do = rng.standard_normal((B, Hq, ql, d))
+    # causal with q_offset=-... : row 0 sees key 0 only; a window rule leaves one row empty
+    spec = ("and", ("causal",), ("swa", 3))
+    kw = dict(cap=0.7, slopes=[0.5, 0.25], table=rng.standard_normal((Hq, 5)), radius=2)
+    kw = {"identity": {}, "softcap": dict(cap=kw["cap"]), "alibi": dict(slopes=kw["slopes"]),
+          "relpos": dict(table=kw["table"], radius=kw["radius"])}[kind]
+    dq, dk, dv = OBW.attention_grads(q, k, v, do, spec, kind, q_offset=1, **kw)
+
+    def loss(q_, k_, v_):
+        O, _ = OA.attention(q_, k_, v_, spec, kind, q_offset=1, **kw)
+        return float((O * do).sum())
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in [tuple(rng.integers(0, n) for n in x.shape) for _ in range(6)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - g[idx]) < 1e-6 * max(1.0, abs(fd)), (kind, name, idx, fd, g[idx])
+
+
+def test_backward_matches_sdpa_causal():
+    from oracle import backward as OBW
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((1, 2, 9, 4))
+    k = rng.standard_normal((1, 2, 9, 4))
+    v = rng.standard_normal((1, 2, 9, 4))
+    do = rng.standard_normal((1, 2, 9, 4))
+    dq, dk, dv = OBW.attention_grads(q, k, v, do, ("causal",))
+    Q, K, V = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    O = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True)
+    (O * torch.tensor(do)).sum().backward()
+    for a, b in ((dq, Q.grad), (dk, K.grad), (dv, V.grad)):
+        assert np.abs(a - b.numpy()).max() < 1e-12
