@@ -20,7 +20,8 @@ FA_S_IDENTITY, FA_S_ALIBI, FA_S_SOFTCAP, FA_S_RELPOS = 0, 1, 2, 3
 
 # names declared in include/fa.h (checked against the header by the tests)
 EXPORTS = ("fa_block_mask_sizes", "fa_create_block_mask", "fa_forward_workspace_size",
-           "fa_forward", "fa_forward_paged", "fa_status_string", "fa_last_error_message")
+           "fa_forward", "fa_forward_paged", "fa_backward_workspace_size", "fa_backward",
+           "fa_status_string", "fa_last_error_message")
 
 
 class fa_mask_node(C.Structure):
@@ -62,6 +63,12 @@ class fa_fwd_args(C.Structure):
                 ("workspace", C.c_void_p), ("ws_bytes", C.c_size_t)]
 
 
+class fa_bwd_args(C.Structure):
+    _fields_ = [("fwd", C.POINTER(fa_fwd_args)), ("dout", C.c_void_p), ("dq", C.c_void_p),
+                ("dk", C.c_void_p), ("dv", C.c_void_p), ("workspace", C.c_void_p),
+                ("ws_bytes", C.c_size_t)]
+
+
 class fa_paged_kv(C.Structure):
     _fields_ = [("page_table", C.c_void_p), ("pt_stride", C.c_int64), ("page_size", C.c_int32),
                 ("num_pages", C.c_int64)]
@@ -92,6 +99,10 @@ def load(path: str = LIB_PATH):
     lib.fa_forward.restype = C.c_int
     lib.fa_forward_paged.argtypes = [C.POINTER(fa_fwd_args), C.POINTER(fa_paged_kv), C.c_void_p]
     lib.fa_forward_paged.restype = C.c_int
+    lib.fa_backward_workspace_size.argtypes = [C.POINTER(fa_bwd_args), C.POINTER(C.c_size_t)]
+    lib.fa_backward_workspace_size.restype = C.c_int
+    lib.fa_backward.argtypes = [C.POINTER(fa_bwd_args), C.c_void_p]
+    lib.fa_backward.restype = C.c_int
     lib.fa_status_string.argtypes = [C.c_int]
     lib.fa_status_string.restype = C.c_char_p
     lib.fa_last_error_message.argtypes = []

@@ -178,6 +178,40 @@ def forward_workspace_size(args) -> int:
     return n.value
 
 
+def backward(q, k, v, out, lse, dout, block_mask: BlockMask, score="identity", softcap=0.0,
+             alibi_slopes=None, relpos=None, relpos_radius=0, scale=None, dq=None, dk=None, dv=None,
+             workspace=None, stream=None):
+    """dQ [B,Hq,q_len,d], dK and dV [B,Hkv,kv_len,d] (fp32) of the forward that produced
+    out and lse, for the output gradient dout (bf16, same shape as out)."""
+    lib = L.load()
+    if dout.dtype != torch.bfloat16 or not dout.is_contiguous() or dout.shape != out.shape:
+        raise ValueError("dout must be a contiguous bfloat16 tensor shaped like out")
+    a, _, _ = forward_args(q, k, v, block_mask, score, softcap, alibi_slopes, relpos, relpos_radius,
+                           scale, out, lse)
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.shape != ref.shape:
+            raise ValueError(f"{name} must be a contiguous float32 tensor shaped like its input")
+    ba = L.fa_bwd_args()
+    ba.fwd = C.pointer(a)
+    ba.dout = dout.data_ptr()
+    ba.dq, ba.dk, ba.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    n = C.c_size_t()
+    L.check(lib.fa_backward_workspace_size(C.byref(ba), C.byref(n)))
+    if n.value > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < n.value:
+            workspace = torch.empty(n.value, dtype=torch.uint8, device=q.device)
+        ba.workspace = workspace.data_ptr()
+        ba.ws_bytes = workspace.numel() * workspace.element_size()
+    L.check(lib.fa_backward(C.byref(ba), _stream(stream)))
+    return dq, dk, dv
+
+
 def forward_paged(q, k_cache, v_cache, page_table, kv_len, block_mask: BlockMask, score="identity",
                   softcap=0.0, alibi_slopes=None, relpos=None, relpos_radius=0, scale=None, out=None,
                   lse=None, workspace=None, stream=None):

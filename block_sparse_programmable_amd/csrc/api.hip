@@ -218,6 +218,12 @@ fa_status plan_forward(const fa_fwd_args* a, FwdPlan* plan) {
   p.tab.fnum = bm->full_kv_num;
   p.tab.fptr = bm->full_kv_ptr;
   p.tab.fidx = bm->full_kv_idx;
+  p.tab.qnum = bm->q_num;
+  p.tab.qptr = bm->q_ptr;
+  p.tab.qidx = bm->q_idx;
+  p.tab.qfnum = bm->full_q_num;
+  p.tab.qfptr = bm->full_q_ptr;
+  p.tab.qfidx = bm->full_q_idx;
   p.tab.tB = bm->B;
   p.tab.tH = bm->H;
   p.tab.nqb = (int32_t)cdiv(a->q_len, bm->block_q);
@@ -335,6 +341,57 @@ fa_status fa_forward_workspace_size(const fa_fwd_args* args, size_t* bytes) {
 
 fa_status fa_forward(const fa_fwd_args* args, fa_stream_t stream) {
   return fa_forward_paged(args, nullptr, stream);
+}
+
+namespace {
+
+fa_status plan_backward(const fa_bwd_args* a, fa::BwdParams* bp, size_t* ws) {
+  if (!a) return fail(FA_ERR_NULL, "args is NULL");
+  FwdPlan plan;
+  fa_status s = plan_forward(a->fwd, &plan);
+  if (s != FA_OK) return s;
+  const fa_block_mask* bm = a->fwd->bm;
+  if (!bm->q_num || !bm->q_ptr || !bm->q_idx || !bm->full_q_num || !bm->full_q_ptr || !bm->full_q_idx)
+    return fail(FA_ERR_NULL, "the backward needs the q-side block tables");
+  if (!a->dout || !a->dq || !a->dk || !a->dv) return fail(FA_ERR_NULL, "dout, dq, dk and dv must be non-NULL");
+  bp->f = plan.p;
+  bp->dout = static_cast<const uint16_t*>(a->dout);
+  bp->dq = a->dq;
+  bp->dk = a->dk;
+  bp->dv = a->dv;
+  bp->delta = nullptr;
+  *ws = fa::backward_workspace_bytes(plan.p);
+  return FA_OK;
+}
+
+}  // namespace
+
+fa_status fa_backward_workspace_size(const fa_bwd_args* args, size_t* bytes) {
+  fa::BwdParams bp;
+  size_t ws = 0;
+  fa_status s = plan_backward(args, &bp, &ws);
+  if (s != FA_OK) return s;
+  if (!bytes) return fail(FA_ERR_NULL, "bytes is NULL");
+  *bytes = ws;
+  return ok();
+}
+
+fa_status fa_backward(const fa_bwd_args* args, fa_stream_t stream) {
+  fa::BwdParams bp;
+  size_t ws = 0;
+  fa_status s = plan_backward(args, &bp, &ws);
+  if (s != FA_OK) return s;
+  if (ws > 0) {
+    if (!args->workspace || args->ws_bytes < ws)
+      return fail(FA_ERR_WORKSPACE, "backward workspace needs %zu bytes (got %zu)", ws,
+                  args->workspace ? args->ws_bytes : (size_t)0);
+    if (((uintptr_t)args->workspace & 255) != 0)
+      return fail(FA_ERR_WORKSPACE, "backward workspace must be 256-byte aligned");
+    bp.delta = static_cast<float*>(args->workspace);
+  }
+  hipError_t e = fa::launch_backward(bp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 fa_status fa_forward_paged(const fa_fwd_args* args, const fa_paged_kv* kv, fa_stream_t stream) {

@@ -1,0 +1,351 @@
+// Block-sparse attention backward for gfx950: dQ, dK, dV of the forward
+// O = softmax(mask(score_mod(Q K^T * scale))) V.
+//
+// What is computed ("FlexAttention: from rules to fused kernels", section 4: the
+// backward recomputes each executed block's scores from the saved row log-sum-exp,
+// differentiates score_mod, and walks the same block tables -- a query row's KV list
+// for dQ, a KV column's query list for dK and dV, so no atomics are needed):
+//   P = exp(score_mod(s) - LSE) on allowed pairs (0 elsewhere), s = (q . k) * scale
+//   dV = P^T dO,   dP = dO V^T,   delta_i = sum_d dO_id O_id
+//   dS = P * (dP - delta) * d score_mod / d (q . k)
+//   dQ = dS K,     dK = dS^T Q
+// with d score_mod / d(q . k) = scale (identity, ALiBi, relative position) or
+// scale * (1 - tanh^2) (soft-cap).  Gradients are accumulated in fp32 and written
+// in fp32; P and dS enter the MFMAs as bf16 (round to nearest even).
+//
+// gfx950 mapping (16x16 MFMA tiles, wave64):
+//   * bwd_dkdv_kernel: one workgroup per (b, h_kv, KV block, 64-key sub-tile), a
+//     wave per 16 keys.  K and V of the wave's keys stay in registers as the B
+//     operands of S = Q K^T and dP = dO V^T (v_mfma_f32_16x16x32_bf16); the query
+//     rows of each listed block (for every query head of the group) are staged in
+//     LDS, and dV^T += dO^T P, dK^T += Q^T dS take their A operands from transposing
+//     LDS reads (ds_read_b64_tr_b16) and P, dS straight from the accumulator layout
+//     (v_mfma_f32_16x16x16_bf16).
+//   * bwd_dq_kernel: one workgroup per (b, h_q, query block), a wave per 16 rows;
+//     Q and dO of the wave's rows stay in registers, the K and V tiles of each
+//     listed block are staged in LDS, and S^T = K Q^T, dP^T = V dO^T,
+//     dQ^T += K^T dS^T mirror the first kernel.
+//   * bwd_delta_kernel: delta = rowsum(dO * O), one wave per row.
+// Partial blocks and ragged tails apply the mask rule per element (interpreter).
+#include "device_common.hpp"
+#include "fa_internal.hpp"
+#include "prefill_common.hpp"
+
+namespace fa {
+
+namespace {
+
+__device__ __forceinline__ f32x4 mma_k32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_k16(const s16x4& a, const s16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ s16x4 tr_read(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+__device__ __forceinline__ s16x4 pack4(float a, float b, float c, float d) {
+  const u32x2 v = {cvt_pk_bf16(a, b), cvt_pk_bf16(c, d)};
+  return __builtin_bit_cast(s16x4, v);
+}
+
+// LDS row pitch: D bf16 plus 16 bytes, so the 16 rows a ds_read_b128 pass touches at one
+// column fall on distinct bank groups
+template <int D>
+struct Pitch {
+  static constexpr int RS = D * 2 + 16;
+};
+
+// stage rows [r0, r0 + n) of a [rows_total, D] bf16 matrix into LDS (zeros past the end)
+template <int D, int NT>
+__device__ __forceinline__ void stage_rows(uint8_t* dst, const uint16_t* src, int r0, int n, int rows_total) {
+  constexpr int CH = D / 8;
+  for (int x = threadIdx.x; x < n * CH; x += NT) {
+    const int row = x / CH, ch = x - row * CH;
+    const int gr = r0 + row;
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (gr < rows_total) v = load16(src + (int64_t)gr * D + ch * 8);
+    *reinterpret_cast<u32x4*>(dst + row * Pitch<D>::RS + ch * 16) = v;
+  }
+}
+
+// weight and score gradient of one element: P = exp2(t - lse2); dS = P (dP - delta) dmod
+template <int SCORE>
+__device__ __forceinline__ void grad_elem(float s, float dp, float lse2, float delta, bool ok,
+                                          const ScoreCtx& sc, float scale, int ig, int j, float& pv,
+                                          float& ds) {
+  const float t = score_log2<SCORE>(s, sc, ig, j);
+  float dmod = scale;
+  if constexpr (SCORE == FA_S_SOFTCAP) {
+    const float th = t / sc.cap2;   // tanh of the scaled score over the cap
+    dmod = scale * (1.f - th * th);
+  }
+  pv = ok ? fast_exp2(t - lse2) : 0.f;
+  ds = ok ? pv * (dp - delta) * dmod : 0.f;
+}
+
+// ---- delta = rowsum(dO * O), one wave per row
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams bp) {
+  const FwdParams& p = bp.f;
+  const int64_t rows = (int64_t)p.B * p.Hq * p.q_len;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float acc = 0.f;
+  constexpr int PER = D / 64;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int64_t x = row * D + lane * PER + k;
+    const float o = __builtin_bit_cast(float, (uint32_t)p.o[x] << 16);
+    const float g = __builtin_bit_cast(float, (uint32_t)bp.dout[x] << 16);
+    acc += o * g;
+  }
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) bp.delta[row] = acc;
+}
+
+// ---- dK, dV: one workgroup per (b, h_kv, KV block, 64-key sub-tile), 4 waves x 16 keys
+template <int D, int SCORE>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams bp) {
+  const FwdParams& p = bp.f;
+  constexpr int RS = Pitch<D>::RS;
+  constexpr int KS = D / 32;   // k-steps of the 16x16x32 products over the head dim
+  constexpr int DT = D / 16;   // 16-row tiles of dK^T and dV^T
+  constexpr int BQM = 128;     // largest query block
+  __shared__ __attribute__((aligned(16))) uint8_t qs[BQM * RS];   // Q rows of one (head, block)
+  __shared__ __attribute__((aligned(16))) uint8_t gs[BQM * RS];   // dO rows
+  __shared__ float lse_s[BQM], del_s[BQM];
+
+  const int nsub = p.tab.bk / 64;
+  int item = blockIdx.x;
+  const int sub = item % nsub;
+  item /= nsub;
+  const int c = item % p.tab.nkb;
+  item /= p.tab.nkb;
+  const int hkv = item % p.Hkv;
+  const int b = item / p.Hkv;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, g4 = lane >> 4;
+  const int q_len = (int)p.q_len, kv_len = (int)p.kv_len, bq = p.tab.bq;
+  const int key0 = c * p.tab.bk + sub * 64 + w * 16;   // first key of this wave
+  const int j = key0 + col;                            // this lane's key (S column)
+
+  // B operands: lane holds K[j][32 t + 8 g4 .. +8] and V[j][...] (rows past kv_len are
+  // read clamped and masked)
+  bf16x8 kf[KS], vf[KS];
+  {
+    const int jr = min(j, max(kv_len - 1, 0));
+    const int64_t base = ((int64_t)(b * p.Hkv + hkv) * kv_len + jr) * D;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      kf[t] = __builtin_bit_cast(bf16x8, kv_len > 0 ? load16(p.k + base + 32 * t + 8 * g4) : u32x4{0, 0, 0, 0});
+      vf[t] = __builtin_bit_cast(bf16x8, kv_len > 0 ? load16(p.v + base + 32 * t + 8 * g4) : u32x4{0, 0, 0, 0});
+    }
+  }
+  f32x4 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int32_t* docr = doc_row(p.doc, b);
+  const int doc_j = (p.prog.has_doc && j < kv_len) ? docr[j] : 0;
+  const int tb = p.tab.tB == 1 ? 0 : b;
+
+  for (int hh = 0; hh < p.g; ++hh) {
+    const int hq = hkv * p.g + hh;
+    const ScoreCtx sc = make_score_ctx(p.score, p.scale, hq);
+    const int th = p.tab.tH == 1 ? 0 : hq;
+    const int line = (tb * p.tab.tH + th) * p.tab.nkb + c;   // q-side line of column c
+    const int nf = uniform(p.tab.qfnum[line]);
+    const int np = uniform(p.tab.qnum[line]);
+    const int32_t* fl = p.tab.qfidx + uniform(p.tab.qfptr[line]);
+    const int32_t* pl = p.tab.qidx + uniform(p.tab.qptr[line]);
+    const int64_t bh = (int64_t)b * p.Hq + hq;
+    for (int e = 0; e < nf + np; ++e) {
+      const bool part = e >= nf;
+      const int r = uniform(part ? pl[e - nf] : fl[e]);
+      const int r0 = r * bq;
+      __syncthreads();   // the previous block's rows are consumed
+      stage_rows<D, 256>(qs, p.q + bh * q_len * D, r0, bq, q_len);
+      stage_rows<D, 256>(gs, bp.dout + bh * q_len * D, r0, bq, q_len);
+      for (int x = threadIdx.x; x < bq; x += 256) {
+        const int i = r0 + x;
+        lse_s[x] = i < q_len ? p.lse[bh * q_len + i] * kLog2e : 0.f;
+        del_s[x] = i < q_len ? bp.delta[bh * q_len + i] : 0.f;
+      }
+      __syncthreads();
+      for (int q0 = 0; q0 < bq; q0 += 16) {
+        // S (16 rows x 16 keys) and dP on 16x16x32 tiles
+        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+          const int off = (q0 + col) * RS + (32 * t + 8 * g4) * 2;
+          s = mma_k32(*reinterpret_cast<const bf16x8*>(qs + off), kf[t], s);
+          dp = mma_k32(*reinterpret_cast<const bf16x8*>(gs + off), vf[t], dp);
+        }
+        // lane: rows q0 + 4 g4 + rr, key j
+        float pv[4], ds[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int xr = q0 + 4 * g4 + rr;
+          const int i = r0 + xr;
+          const int ig = i + (int)p.q_offset;
+          bool ok = i < q_len && j < kv_len;
+          if (part && ok) ok = mask_allowed(p.prog, ig, j, p.prog.has_doc ? docr[ig] : 0, doc_j);
+          grad_elem<SCORE>(s[rr], dp[rr], lse_s[xr], del_s[xr], ok, sc, p.scale, ig, j, pv[rr], ds[rr]);
+        }
+        const s16x4 pb = pack4(pv[0], pv[1], pv[2], pv[3]);
+        const s16x4 db = pack4(ds[0], ds[1], ds[2], ds[3]);
+        // dV^T += dO^T P and dK^T += Q^T dS (A: head-dim x 16 rows, transposing reads)
+        const int toff = (q0 + 4 * g4 + (col >> 2)) * RS + 4 * (col & 3) * 2;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          dv[dt] = mma_k16(tr_read(gs + toff + 32 * dt), pb, dv[dt]);
+          dk[dt] = mma_k16(tr_read(qs + toff + 32 * dt), db, dk[dt]);
+        }
+      }
+    }
+  }
+  // lane holds key j, head dims 16 dt + 4 g4 .. +4
+  if (j < kv_len) {
+    const int64_t base = ((int64_t)(b * p.Hkv + hkv) * kv_len + j) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      *reinterpret_cast<f32x4*>(bp.dk + base + 16 * dt + 4 * g4) = dk[dt];
+      *reinterpret_cast<f32x4*>(bp.dv + base + 16 * dt + 4 * g4) = dv[dt];
+    }
+  }
+}
+
+// ---- dQ: one workgroup per (b, h_q, query block), NW waves x 16 rows
+template <int D, int SCORE, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
+  const FwdParams& p = bp.f;
+  constexpr int NT = NW * 64;
+  constexpr int RS = Pitch<D>::RS;
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int BKM = 128;
+  __shared__ __attribute__((aligned(16))) uint8_t ks[BKM * RS];
+  __shared__ __attribute__((aligned(16))) uint8_t vs[BKM * RS];
+
+  const int nqb = p.tab.nqb;
+  const int r = blockIdx.x % nqb;
+  const int bh = blockIdx.x / nqb;   // b * Hq + h_q
+  const int b = bh / p.Hq, hq = bh - b * p.Hq, hkv = hq / p.g;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, g4 = lane >> 4;
+  const int q_len = (int)p.q_len, kv_len = (int)p.kv_len, bk = p.tab.bk;
+  const int i = r * p.tab.bq + w * 16 + col;   // this lane's row (S^T column)
+  const bool row_ok = i < q_len;
+  const int ig = i + (int)p.q_offset;
+
+  // B operands: Q[i][32 t + 8 g4 .. +8] and dO[i][...]
+  bf16x8 qf[KS], gf[KS];
+  {
+    const int ir = min(i, q_len - 1);
+    const int64_t base = ((int64_t)bh * q_len + ir) * D;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      qf[t] = __builtin_bit_cast(bf16x8, load16(p.q + base + 32 * t + 8 * g4));
+      gf[t] = __builtin_bit_cast(bf16x8, load16(bp.dout + base + 32 * t + 8 * g4));
+    }
+  }
+  const float lse2 = row_ok ? p.lse[(int64_t)bh * q_len + i] * kLog2e : 0.f;
+  const float delta = row_ok ? bp.delta[(int64_t)bh * q_len + i] : 0.f;
+  const ScoreCtx sc = make_score_ctx(p.score, p.scale, hq);
+  const int32_t* docr = doc_row(p.doc, b);
+  const int doc_i = (p.prog.has_doc && row_ok) ? docr[ig] : 0;
+  f32x4 dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int tb = p.tab.tB == 1 ? 0 : b;
+  const int th = p.tab.tH == 1 ? 0 : hq;
+  const int row = (tb * p.tab.tH + th) * nqb + r;
+  const int nf = uniform(p.tab.fnum[row]);
+  const int np = uniform(p.tab.num[row]);
+  const int32_t* fl = p.tab.fidx + uniform(p.tab.fptr[row]);
+  const int32_t* pl = p.tab.idx + uniform(p.tab.ptr[row]);
+  const int64_t kvh = (int64_t)(b * p.Hkv + hkv) * kv_len;
+  for (int e = 0; e < nf + np; ++e) {
+    const bool part = e >= nf;
+    const int c = uniform(part ? pl[e - nf] : fl[e]);
+    const int j0 = c * bk;
+    __syncthreads();
+    stage_rows<D, NT>(ks, p.k + kvh * D, j0, bk, kv_len);
+    stage_rows<D, NT>(vs, p.v + kvh * D, j0, bk, kv_len);
+    __syncthreads();
+    for (int k0 = 0; k0 < bk; k0 += 16) {
+      // S^T (16 keys x 16 rows) = K Q^T and dP^T = V dO^T
+      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        const int off = (k0 + col) * RS + (32 * t + 8 * g4) * 2;
+        s = mma_k32(*reinterpret_cast<const bf16x8*>(ks + off), qf[t], s);
+        dp = mma_k32(*reinterpret_cast<const bf16x8*>(vs + off), gf[t], dp);
+      }
+      // lane: keys j0 + k0 + 4 g4 + rr, row i
+      float pv[4], ds[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int jj = j0 + k0 + 4 * g4 + rr;
+        bool ok = row_ok && jj < kv_len;
+        if (part && ok) ok = mask_allowed(p.prog, ig, jj, doc_i, p.prog.has_doc ? docr[jj] : 0);
+        grad_elem<SCORE>(s[rr], dp[rr], lse2, delta, ok, sc, p.scale, ig, jj, pv[rr], ds[rr]);
+      }
+      (void)pv;
+      const s16x4 db = pack4(ds[0], ds[1], ds[2], ds[3]);
+      // dQ^T += K^T dS^T (A: head-dim x 16 keys, transposing reads)
+      const int toff = (k0 + 4 * g4 + (col >> 2)) * RS + 4 * (col & 3) * 2;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dq[dt] = mma_k16(tr_read(ks + toff + 32 * dt), db, dq[dt]);
+    }
+  }
+  if (row_ok) {
+    float* out = bp.dq + ((int64_t)bh * q_len + i) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(out + 16 * dt + 4 * g4) = dq[dt];
+  }
+}
+
+template <int D, int SCORE>
+hipError_t launch_bwd_score(const BwdParams& bp, hipStream_t s) {
+  const FwdParams& p = bp.f;
+  const int64_t items = (int64_t)p.B * p.Hkv * p.tab.nkb * (p.tab.bk / 64);
+  if (items > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<D, SCORE>), dim3((unsigned)items), dim3(256), 0, s, bp);
+  const int64_t qitems = (int64_t)p.B * p.Hq * p.tab.nqb;
+  if (qitems > 0) {
+    if (p.tab.bq == 128) {
+      hipLaunchKernelGGL((bwd_dq_kernel<D, SCORE, 8>), dim3((unsigned)qitems), dim3(512), 0, s, bp);
+    } else {
+      hipLaunchKernelGGL((bwd_dq_kernel<D, SCORE, 4>), dim3((unsigned)qitems), dim3(256), 0, s, bp);
+    }
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdParams& bp, hipStream_t s) {
+  const FwdParams& p = bp.f;
+  const int64_t rows = (int64_t)p.B * p.Hq * p.q_len;
+  if (rows > 0) hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, bp);
+  switch (p.score.kind) {
+    case FA_S_IDENTITY: return launch_bwd_score<D, FA_S_IDENTITY>(bp, s);
+    case FA_S_ALIBI: return launch_bwd_score<D, FA_S_ALIBI>(bp, s);
+    case FA_S_SOFTCAP: return launch_bwd_score<D, FA_S_SOFTCAP>(bp, s);
+    default: return launch_bwd_score<D, FA_S_RELPOS>(bp, s);
+  }
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(const FwdParams& p) {
+  return ((size_t)p.B * p.Hq * p.q_len * sizeof(float) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_backward(const BwdParams& bp, hipStream_t s) {
+  return bp.f.d == 128 ? launch_bwd_d<128>(bp, s) : launch_bwd_d<64>(bp, s);
+}
+
+}  // namespace fa

@@ -67,6 +67,8 @@ struct ScoreParams {
 struct TableRef {
   const int32_t *num, *ptr, *idx;             // partial list
   const int32_t *fnum, *fptr, *fidx;          // full list
+  const int32_t *qnum, *qptr, *qidx;          // q side (columns): partial list
+  const int32_t *qfnum, *qfptr, *qfidx;       // q side: full list
   int32_t tB, tH, nqb, nkb, bq, bk;
 };
 
@@ -98,6 +100,18 @@ bool decode_eligible(const FwdParams& p);
 int32_t decode_splits(const FwdParams& p, int num_cus);
 size_t decode_workspace_bytes(const FwdParams& p, int32_t nsplit);
 hipError_t launch_prefill(const FwdParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------- backward
+struct BwdParams {
+  FwdParams f;            // the forward's inputs, O and LSE (from the forward)
+  const uint16_t* dout;   // bf16 [B, Hq, q_len, d]
+  float* dq;              // fp32 [B, Hq, q_len, d]
+  float* dk;              // fp32 [B, Hkv, kv_len, d]
+  float* dv;              // fp32 [B, Hkv, kv_len, d]
+  float* delta;           // fp32 [B, Hq, q_len] workspace: rowsum(dO * O)
+};
+size_t backward_workspace_bytes(const FwdParams& p);
+hipError_t launch_backward(const BwdParams& p, hipStream_t s);
 hipError_t launch_decode(const FwdParams& p, hipStream_t s);
 
 }  // namespace fa

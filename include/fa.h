@@ -8,6 +8,7 @@
  *   fa_create_block_mask  mask rule -> block tables (BCSR rows and their transposes)
  *   fa_forward            O = softmax(mask(score_mod(Q K^T * scale))) V, plus LSE
  *   fa_forward_paged      the same over a paged KV cache (short-query path)
+ *   fa_backward           dQ, dK, dV of fa_forward
  *
  * Conventions shared by every entry point
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library never
@@ -210,6 +211,38 @@ fa_status fa_forward(const fa_fwd_args* args, fa_stream_t stream);
  * fa_forward_workspace_size reports for `args`.  Results equal fa_forward on the
  * logical (gathered) K and V bit for bit.
  * -------------------------------------------------------------------------------- */
+/* ----------------------------------------------------------------------------------
+ * Backward ("FlexAttention: from rules to fused kernels", section 4: the scores of each
+ * executed block are recomputed from the saved LSE, score_mod is differentiated, and
+ * the block tables are walked per query row for dQ and per KV column -- the q-side
+ * tables -- for dK and dV).
+ *
+ *   fwd        the arguments of the forward call whose gradients are wanted, with
+ *              fwd->o and fwd->lse holding that call's results; fwd->bm must carry the
+ *              q-side tables (fa_create_block_mask fills them).  The forward's
+ *              workspace fields are ignored.
+ *   dout       bf16 [B, Hq, q_len, d]: gradient of the loss with respect to O.
+ *   dq         fp32 [B, Hq, q_len, d]; dk, dv fp32 [B, Hkv, kv_len, d]: written (not
+ *              accumulated); GQA heads' contributions are summed into their KV head.
+ *   workspace  device buffer of fa_backward_workspace_size bytes (fp32 row sums
+ *              dO . O), 256-byte aligned, contents on entry irrelevant.
+ * Gradients flow to Q, K and V only (not to ALiBi slopes or the position table).
+ * Rows with no allowed key contribute nothing.  Errors as for fa_forward, plus
+ * FA_ERR_NULL for missing q-side tables, dout or gradient buffers.
+ * -------------------------------------------------------------------------------- */
+typedef struct {
+  const fa_fwd_args* fwd;
+  const void* dout;
+  float* dq;
+  float* dk;
+  float* dv;
+  void* workspace;
+  size_t ws_bytes;
+} fa_bwd_args;
+
+fa_status fa_backward_workspace_size(const fa_bwd_args* args, size_t* bytes);
+fa_status fa_backward(const fa_bwd_args* args, fa_stream_t stream);
+
 typedef struct {
   const int32_t* page_table;
   int64_t pt_stride;
