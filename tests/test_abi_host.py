@@ -188,6 +188,28 @@ def test_forward_validation(lib):
                                         num_pages=0)) == L.FA_ERR_SHAPE
     assert P(_fwd(L, bm), kv) == L.FA_ERR_UNSUPPORTED                          # prefill shape
     assert b"short-query" in lib.fa_last_error_message()
+    # backward: needs dout, the gradient buffers and the q-side tables; workspace rules
+    fwd = _fwd(L, bm)
+    Bk = lambda **kw: L.fa_bwd_args(fwd=C.pointer(fwd), **kw)
+    assert lib.fa_backward(None, None) == L.FA_ERR_NULL
+    assert lib.fa_backward(C.byref(Bk(dout=0x1000, dq=0x1000, dk=0x1000)), None) == L.FA_ERR_NULL
+    for name in ("q_num", "full_q_idx"):
+        saved = getattr(bm, name)
+        setattr(bm, name, None)
+        assert lib.fa_backward(C.byref(Bk(dout=0x1000, dq=0x1000, dk=0x1000, dv=0x1000)), None) == L.FA_ERR_NULL
+        setattr(bm, name, saved)
+    for name in ("q_num", "q_ptr", "q_idx", "full_q_num", "full_q_ptr", "full_q_idx"):
+        setattr(bm, name, 0x1000)
+    ok = Bk(dout=0x1000, dq=0x1000, dk=0x1000, dv=0x1000)
+    n = C.c_size_t(0)
+    assert lib.fa_backward_workspace_size(C.byref(ok), C.byref(n)) == L.FA_OK
+    assert n.value == 1 * 4 * 256 * 4                                 # fp32 row sums
+    assert lib.fa_backward(C.byref(ok), None) == L.FA_ERR_WORKSPACE
+    ok.workspace, ok.ws_bytes = 0x1010, n.value
+    assert lib.fa_backward(C.byref(ok), None) == L.FA_ERR_WORKSPACE    # misaligned
+    bad = _fwd(L, bm, d=96)                                           # forward checks apply
+    assert lib.fa_backward(C.byref(L.fa_bwd_args(fwd=C.pointer(bad), dout=0x1000, dq=0x1000, dk=0x1000,
+                                                 dv=0x1000)), None) == L.FA_ERR_UNSUPPORTED
     bm.kv_idx = None
     assert F(_fwd(L, bm)) == L.FA_ERR_NULL
     for s in range(8):
