@@ -239,6 +239,34 @@ def run(args):
                 "fwd_ms_p90": float(np.percentile(ft, 90))}
         del flush, sink
 
+    # backward of the same step's forward (prefill workloads): dQ, dK, dV over the
+    # block tables, credited with 5 products of 2 Bq Bk d FLOP per executed block
+    bwd = None
+    if args.backward and w.q_len > 1:
+        dout = W.randn_bf16(tuple(out.shape), w.seed + 7, device=dev)
+        fwd(bm)
+        gq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        gk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+        gv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+        bkw = dict(score=w.score, softcap=w.cap, alibi_slopes=sl, relpos=tb, relpos_radius=w.relpos_radius,
+                   dq=gq, dk=gk, dv=gv)
+        for _ in range(3):
+            fa.backward(q, k, v, out, lse, dout, bm, **bkw)
+        torch.cuda.synchronize()
+        nb = max(3, K // 2)
+        e = [[torch.cuda.Event(enable_timing=True) for _ in range(nb)] for _ in range(2)]
+        for i in range(nb):
+            e[0][i].record()
+            fa.backward(q, k, v, out, lse, dout, bm, **bkw)
+            e[1][i].record()
+        torch.cuda.synchronize()
+        bt = [e[0][i].elapsed_time(e[1][i]) for i in range(nb)]
+        bflop = acc["flop"] * 5 // 2
+        bwd = {"reps": nb, "ms_mean": float(np.mean(bt)), "ms_p10": float(np.percentile(bt, 10)),
+               "ms_p90": float(np.percentile(bt, 90)), "algorithmic_flop": bflop,
+               "tflops": bflop / (float(np.mean(bt)) * 1e-3) / 1e12,
+               "frac_bf16_peak": bflop / (float(np.mean(bt)) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
     decode = w.q_len == 1
     if decode:
         value = acc["bytes"] / (ms_step * 1e-3) / 1e9
@@ -269,6 +297,7 @@ def run(args):
            "fwd_ms_p90": float(np.percentile(fwd_ms, 90)),
            "algorithmic_flop": acc["flop"], "algorithmic_bytes": acc.get("bytes"),
            "cold_cache": cold or None,
+           "backward": bwd,
            "kernel_source_digest": kernel_source_digest("decode" if decode else "prefill"),
            "gpu": torch.cuda.get_device_name(0),
            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
@@ -298,6 +327,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="causal_softcap")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the backward of the forward (prefill workloads)")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="repetitions of the separately timed build and forward with flushed caches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

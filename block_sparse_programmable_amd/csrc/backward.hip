@@ -56,18 +56,32 @@ struct Pitch {
   static constexpr int RS = D * 2 + 16;
 };
 
-// stage rows [r0, r0 + n) of a [rows_total, D] bf16 matrix into LDS (zeros past the end)
+// Rows [r0, r0 + n) (n <= 128) of a [rows_total, D] bf16 matrix, staged through
+// registers: fetch() issues the global loads (zeros past the end) and put() stores them
+// to LDS later, so a tile's loads are in flight while the previous tile is computed.
 template <int D, int NT>
-__device__ __forceinline__ void stage_rows(uint8_t* dst, const uint16_t* src, int r0, int n, int rows_total) {
-  constexpr int CH = D / 8;
-  for (int x = threadIdx.x; x < n * CH; x += NT) {
-    const int row = x / CH, ch = x - row * CH;
-    const int gr = r0 + row;
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (gr < rows_total) v = load16(src + (int64_t)gr * D + ch * 8);
-    *reinterpret_cast<u32x4*>(dst + row * Pitch<D>::RS + ch * 16) = v;
+struct RowStage {
+  static constexpr int CH = D / 8;                 // 16-byte chunks per row
+  static constexpr int PER = 128 * CH / NT;        // chunks per thread for 128 rows
+  u32x4 r[PER];
+  __device__ __forceinline__ void fetch(const uint16_t* src, int r0, int n, int rows_total) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int x = threadIdx.x + u * NT;
+      const int row = x / CH, ch = x - row * CH;
+      const int gr = r0 + row;
+      r[u] = (row < n && gr < rows_total) ? load16(src + (int64_t)gr * D + ch * 8) : u32x4{0, 0, 0, 0};
+    }
   }
-}
+  __device__ __forceinline__ void put(uint8_t* dst, int n) const {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int x = threadIdx.x + u * NT;
+      const int row = x / CH, ch = x - row * CH;
+      if (row < n) *reinterpret_cast<u32x4*>(dst + row * Pitch<D>::RS + ch * 16) = r[u];
+    }
+  }
+};
 
 // weight and score gradient of one element: P = exp2(t - lse2); dS = P (dP - delta) dmod
 template <int SCORE>
@@ -162,19 +176,42 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams bp) {
     const int32_t* fl = p.tab.qfidx + uniform(p.tab.qfptr[line]);
     const int32_t* pl = p.tab.qidx + uniform(p.tab.qptr[line]);
     const int64_t bh = (int64_t)b * p.Hq + hq;
-    for (int e = 0; e < nf + np; ++e) {
+    const uint16_t* qsrc = p.q + bh * q_len * D;
+    const uint16_t* gsrc = bp.dout + bh * q_len * D;
+    const int n_ent = nf + np;
+    // query block of list entry e and its row statistics (one per thread, bq <= 256)
+    auto block_of = [&](int e) -> int { return uniform(e >= nf ? pl[e - nf] : fl[e]); };
+    auto stats = [&](int r0, float& l2, float& dl) {
+      const int i = r0 + (int)threadIdx.x;
+      const bool ok = (int)threadIdx.x < bq && i < q_len;
+      l2 = ok ? p.lse[bh * q_len + i] * kLog2e : 0.f;
+      dl = ok ? bp.delta[bh * q_len + i] : 0.f;
+    };
+    RowStage<D, 256> sq, sg;
+    float nl2 = 0.f, ndl = 0.f;
+    if (n_ent > 0) {
+      const int r0n = block_of(0) * bq;
+      sq.fetch(qsrc, r0n, bq, q_len);
+      sg.fetch(gsrc, r0n, bq, q_len);
+      stats(r0n, nl2, ndl);
+    }
+    for (int e = 0; e < n_ent; ++e) {
       const bool part = e >= nf;
-      const int r = uniform(part ? pl[e - nf] : fl[e]);
-      const int r0 = r * bq;
+      const int r0 = block_of(e) * bq;
       __syncthreads();   // the previous block's rows are consumed
-      stage_rows<D, 256>(qs, p.q + bh * q_len * D, r0, bq, q_len);
-      stage_rows<D, 256>(gs, bp.dout + bh * q_len * D, r0, bq, q_len);
-      for (int x = threadIdx.x; x < bq; x += 256) {
-        const int i = r0 + x;
-        lse_s[x] = i < q_len ? p.lse[bh * q_len + i] * kLog2e : 0.f;
-        del_s[x] = i < q_len ? bp.delta[bh * q_len + i] : 0.f;
+      sq.put(qs, bq);
+      sg.put(gs, bq);
+      if ((int)threadIdx.x < bq) {
+        lse_s[threadIdx.x] = nl2;
+        del_s[threadIdx.x] = ndl;
       }
       __syncthreads();
+      if (e + 1 < n_ent) {   // next block's rows travel while this one is computed
+        const int r0n = block_of(e + 1) * bq;
+        sq.fetch(qsrc, r0n, bq, q_len);
+        sg.fetch(gsrc, r0n, bq, q_len);
+        stats(r0n, nl2, ndl);
+      }
       for (int q0 = 0; q0 < bq; q0 += 16) {
         // S (16 rows x 16 keys) and dP on 16x16x32 tiles
         f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -268,14 +305,24 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
   const int32_t* fl = p.tab.fidx + uniform(p.tab.fptr[row]);
   const int32_t* pl = p.tab.idx + uniform(p.tab.ptr[row]);
   const int64_t kvh = (int64_t)(b * p.Hkv + hkv) * kv_len;
-  for (int e = 0; e < nf + np; ++e) {
+  const int n_ent = nf + np;
+  auto block_of = [&](int e) -> int { return uniform(e >= nf ? pl[e - nf] : fl[e]); };
+  RowStage<D, NT> sk, sv;
+  if (n_ent > 0) {
+    sk.fetch(p.k + kvh * D, block_of(0) * bk, bk, kv_len);
+    sv.fetch(p.v + kvh * D, block_of(0) * bk, bk, kv_len);
+  }
+  for (int e = 0; e < n_ent; ++e) {
     const bool part = e >= nf;
-    const int c = uniform(part ? pl[e - nf] : fl[e]);
-    const int j0 = c * bk;
+    const int j0 = block_of(e) * bk;
     __syncthreads();
-    stage_rows<D, NT>(ks, p.k + kvh * D, j0, bk, kv_len);
-    stage_rows<D, NT>(vs, p.v + kvh * D, j0, bk, kv_len);
+    sk.put(ks, bk);
+    sv.put(vs, bk);
     __syncthreads();
+    if (e + 1 < n_ent) {   // next block's K and V travel while this one is computed
+      sk.fetch(p.k + kvh * D, block_of(e + 1) * bk, bk, kv_len);
+      sv.fetch(p.v + kvh * D, block_of(e + 1) * bk, bk, kv_len);
+    }
     for (int k0 = 0; k0 < bk; k0 += 16) {
       // S^T (16 keys x 16 rows) = K Q^T and dP^T = V dO^T
       f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
