@@ -267,7 +267,49 @@ def run(args):
                "tflops": bflop / (float(np.mean(bt)) * 1e-3) / 1e12,
                "frac_bf16_peak": bflop / (float(np.mean(bt)) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
+    # decode from tables prebuilt once for the whole context: per step, slice the query
+    # block of the current position (kv side only) instead of rebuilding; the forward
+    # over the slice is timed beside the forward over rebuilt tables
+    pre = None
     decode = w.q_len == 1
+    if args.prebuilt and decode:
+        Lmax = w.kv_len
+        eb = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        eb[0].record()
+        src = fa.create_block_mask(w.mask, 1, 1, Lmax, Lmax, w.block_q, w.block_kv, 0, docT)
+        eb[1].record()
+        torch.cuda.synchronize()
+        sl_bm = fa.slice_block_mask(src, w.q_len, w.kv_len, w.q_offset, q_side=False)
+        R = max(20, K)
+        e = [[torch.cuda.Event(enable_timing=True) for _ in range(R)] for _ in range(6)]
+        for i in range(R):
+            e[0][i].record()
+            fa.slice_block_mask(src, w.q_len, w.kv_len, w.q_offset, q_side=False, tables=sl_bm.tensors,
+                                workspace=sl_bm._keep[1])
+            e[1][i].record()
+            fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset,
+                                 docT, tables=tables, workspace=bws)
+            e[2][i].record()
+        for i in range(R):
+            e[3][i].record()
+            fwd(sl_bm)
+            e[4][i].record()
+        torch.cuda.synchronize()
+        o_slice = out.float().clone()
+        fwd(bm)
+        torch.cuda.synchronize()
+        st = [e[0][i].elapsed_time(e[1][i]) for i in range(R)]
+        rt = [e[1][i].elapsed_time(e[2][i]) for i in range(R)]
+        ft = [e[3][i].elapsed_time(e[4][i]) for i in range(R)]
+        sc = sl_bm.compact()
+        pre = {"lmax": Lmax, "prebuild_ms": eb[0].elapsed_time(eb[1]), "reps": R,
+               "slice_ms_median": float(np.median(st)), "rebuild_ms_median": float(np.median(rt)),
+               "fwd_over_slice_ms_mean": float(np.mean(ft)), "fwd_over_rebuilt_ms_mean": fwd_avg,
+               "slice_blocks": int(sc["kv_ptr"][-1] + sc["full_kv_ptr"][-1]),
+               "rebuilt_blocks": acc["full_blocks"] + acc["partial_blocks"],
+               "max_abs_o_diff": float((o_slice - out.float()).abs().max())}
+        del src, sl_bm
+
     if decode:
         value = acc["bytes"] / (ms_step * 1e-3) / 1e9
         unit = "GB/s"
@@ -298,6 +340,7 @@ def run(args):
            "algorithmic_flop": acc["flop"], "algorithmic_bytes": acc.get("bytes"),
            "cold_cache": cold or None,
            "backward": bwd,
+           "prebuilt": pre,
            "kernel_source_digest": kernel_source_digest("decode" if decode else "prefill"),
            "gpu": torch.cuda.get_device_name(0),
            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
@@ -329,6 +372,8 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward of the forward (prefill workloads)")
+    ap.add_argument("--prebuilt", action="store_true",
+                    help="decode workloads: also time slicing tables prebuilt for the whole context")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="repetitions of the separately timed build and forward with flushed caches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

@@ -81,8 +81,10 @@ class BlockMask:
         """Host copies of the tables trimmed to their used length (numpy int32)."""
         out = {}
         for side in ("kv", "full_kv", "q", "full_q"):
-            num = self.tensors[f"{side}_num"].cpu().numpy()
+            if f"{side}_num" not in self.tensors:
+                continue
             ptr = self.tensors[f"{side}_ptr"].cpu().numpy()
+            num = self.tensors[f"{side}_num"][: len(ptr) - 1].cpu().numpy()   # allocated >= 1
             idx = self.tensors[f"{side}_idx"][: int(ptr[-1])].cpu().numpy()
             out[f"{side}_num"], out[f"{side}_ptr"], out[f"{side}_idx"] = num, ptr, idx
         return out
@@ -142,6 +144,31 @@ def create_block_mask(mask, B, H, q_len, kv_len, block_q=128, block_kv=128, q_of
     L.check(lib.fa_create_block_mask(C.byref(d), C.c_void_p(workspace.data_ptr()),
                                      workspace.numel(), _stream(stream)))
     return BlockMask(d, tables, (doc_ids, workspace))
+
+
+def slice_block_mask(src: BlockMask, q_len, kv_len, q_offset, q_side=True, stream=None, tables=None,
+                     workspace=None):
+    """Tables for rows [q_offset, q_offset + q_len) and keys [0, kv_len) cut out of the
+    prebuilt ``src`` (fa_block_mask_slice); ``q_side=False`` writes only the kv side."""
+    lib = L.load()
+    d = L.fa_block_mask.from_buffer_copy(src.desc)
+    d.q_len, d.kv_len, d.q_offset = int(q_len), int(kv_len), int(q_offset)
+    rows, cols, cap, ws = block_mask_sizes(d)
+    device = src.tensors["kv_num"].device
+    sides = (("kv", rows), ("full_kv", rows)) + ((("q", cols), ("full_q", cols)) if q_side else ())
+    if tables is None:
+        tables = {}
+        for side, n in sides:
+            tables[f"{side}_num"] = torch.empty(max(n, 1), dtype=torch.int32, device=device)
+            tables[f"{side}_ptr"] = torch.empty(n + 1, dtype=torch.int32, device=device)
+            tables[f"{side}_idx"] = torch.empty(max(cap, 1), dtype=torch.int32, device=device)
+    for name in TABLE_NAMES:
+        setattr(d, name, tables[name].data_ptr() if name in tables else None)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+    L.check(lib.fa_block_mask_slice(C.byref(src.desc), C.byref(d), C.c_void_p(workspace.data_ptr()),
+                                    workspace.numel(), _stream(stream)))
+    return BlockMask(d, tables, (src._keep[0], workspace))
 
 
 def forward_args(q, k, v, block_mask: BlockMask, score="identity", softcap=0.0,

@@ -278,7 +278,9 @@ fa_status fa_block_mask_sizes(const fa_block_mask* bm, int64_t* rows, int64_t* c
   if (rows) *rows = (int64_t)bm->B * bm->H * nqb;
   if (cols) *cols = (int64_t)bm->B * bm->H * nkb;
   if (idx_capacity) *idx_capacity = (int64_t)bm->B * bm->H * nqb * nkb;
-  if (workspace_bytes) *workspace_bytes = fa::build_workspace_bytes(bm->B, nqb, nkb);
+  if (workspace_bytes)
+    *workspace_bytes = std::max(fa::build_workspace_bytes(bm->B, nqb, nkb),
+                                fa::slice_workspace_bytes((int64_t)bm->B * bm->H, nqb, nkb));
   return ok();
 }
 
@@ -427,6 +429,102 @@ fa_status fa_forward_paged(const fa_fwd_args* args, const fa_paged_kv* kv, fa_st
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = plan.decode ? fa::launch_decode(plan.p, st) : fa::launch_prefill(plan.p, st);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+fa_status fa_block_mask_slice(const fa_block_mask* src, fa_block_mask* dst, void* workspace, size_t ws_bytes,
+                              fa_stream_t stream) {
+  if (!src || !dst) return fail(FA_ERR_NULL, "src and dst must be non-NULL");
+  fa::MaskProg prog;
+  fa_status s = check_mask_geometry(src, &prog);
+  if (s != FA_OK) return s;
+  fa::MaskProg prog_dst;
+  s = check_mask_geometry(dst, &prog_dst);
+  if (s != FA_OK) return s;
+  const fa_mask_desc &ms = src->mask, &md = dst->mask;
+  bool same = ms.n == md.n &&
+              (!prog.has_doc || (ms.doc_ids == md.doc_ids && ms.doc_batch == md.doc_batch && ms.doc_len == md.doc_len));
+  for (int t = 0; same && t < ms.n; ++t)
+    same = ms.node[t].op == md.node[t].op &&
+           ((ms.node[t].op != FA_M_SWA && ms.node[t].op != FA_M_PREFIX) || ms.node[t].arg == md.node[t].arg);
+  if (!same) return fail(FA_ERR_MASK_MISMATCH, "dst must carry the same mask rule (program and document IDs) as src");
+  if (src->B != dst->B || src->H != dst->H || src->block_q != dst->block_q || src->block_kv != dst->block_kv)
+    return fail(FA_ERR_MASK_MISMATCH, "dst must have the table extents and block sizes of src");
+  if (dst->kv_len > src->kv_len || dst->q_offset < src->q_offset ||
+      dst->q_offset + dst->q_len > src->q_offset + src->q_len)
+    return fail(FA_ERR_SHAPE,
+                "slice rows [%lld, %lld) x keys [0, %lld) leave the prebuilt rows [%lld, %lld) x keys [0, %lld); "
+                "a longer context needs tables built for it",
+                (long long)dst->q_offset, (long long)(dst->q_offset + dst->q_len), (long long)dst->kv_len,
+                (long long)src->q_offset, (long long)(src->q_offset + src->q_len), (long long)src->kv_len);
+  const int64_t delta = dst->q_offset - src->q_offset;
+  const int64_t nqb = cdiv(dst->q_len, dst->block_q), nkb = cdiv(dst->kv_len, dst->block_kv);
+  const int64_t nqb_src = cdiv(src->q_len, src->block_q), nkb_src = cdiv(src->kv_len, src->block_kv);
+  const bool aligned = delta % dst->block_q == 0;
+  const bool inside_one = nqb == 1 && delta / dst->block_q == (delta + dst->q_len - 1) / dst->block_q;
+  if (nqb > 0 && !aligned && !inside_one)
+    return fail(FA_ERR_SHAPE,
+                "each new query block must be one prebuilt query block or lie inside one: q_offset - src.q_offset "
+                "(%lld) must be a multiple of block_q, or the rows must fit in one prebuilt block",
+                (long long)delta);
+  if ((int64_t)src->B * src->H * nqb_src * nkb_src > 0x7fffffffLL ||
+      (int64_t)src->B * src->H * (nqb_src + nkb_src) > 0x7fffffffLL)
+    return fail(FA_ERR_SHAPE, "prebuilt tables too large for 32-bit indices");
+  if (!src->kv_num || !src->kv_ptr || !src->kv_idx || !src->full_kv_num || !src->full_kv_ptr || !src->full_kv_idx)
+    return fail(FA_ERR_NULL, "src kv-side tables must be non-NULL");
+  if (!dst->kv_num || !dst->kv_ptr || !dst->kv_idx || !dst->full_kv_num || !dst->full_kv_ptr || !dst->full_kv_idx)
+    return fail(FA_ERR_NULL, "dst kv-side tables must be non-NULL");
+  const int nq_set = (dst->q_num != nullptr) + (dst->q_ptr != nullptr) + (dst->q_idx != nullptr) +
+                     (dst->full_q_num != nullptr) + (dst->full_q_ptr != nullptr) + (dst->full_q_idx != nullptr);
+  if (nq_set != 0 && nq_set != 6)
+    return fail(FA_ERR_NULL, "dst q-side tables must be all set or all NULL");
+  const bool qside = nq_set == 6;
+  const size_t need = fa::slice_workspace_bytes((int64_t)dst->B * dst->H, nqb, nkb);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(FA_ERR_WORKSPACE, "slice workspace needs %zu bytes (got %zu)", need, workspace ? ws_bytes : (size_t)0);
+  if (((uintptr_t)workspace & 15) != 0) return fail(FA_ERR_WORKSPACE, "slice workspace must be 16-byte aligned");
+  fa::SliceParams sp;
+  fa::BuildParams& p = sp.d;
+  p.prog = prog;
+  p.doc = doc_ref(dst, prog);
+  p.tB = src->B * src->H;
+  p.tH = 1;
+  p.q_len = dst->q_len;
+  p.kv_len = dst->kv_len;
+  p.q_offset = dst->q_offset;
+  p.bq = dst->block_q;
+  p.bk = dst->block_kv;
+  p.nqb = (int32_t)nqb;
+  p.nkb = (int32_t)nkb;
+  p.grid = static_cast<uint8_t*>(workspace);
+  p.qstat = p.kstat = nullptr;
+  p.kv_num = dst->kv_num;
+  p.kv_ptr = dst->kv_ptr;
+  p.kv_idx = dst->kv_idx;
+  p.full_kv_num = dst->full_kv_num;
+  p.full_kv_ptr = dst->full_kv_ptr;
+  p.full_kv_idx = dst->full_kv_idx;
+  p.q_num = qside ? dst->q_num : nullptr;
+  p.q_ptr = qside ? dst->q_ptr : nullptr;
+  p.q_idx = qside ? dst->q_idx : nullptr;
+  p.full_q_num = qside ? dst->full_q_num : nullptr;
+  p.full_q_ptr = qside ? dst->full_q_ptr : nullptr;
+  p.full_q_idx = qside ? dst->full_q_idx : nullptr;
+  sp.s_num[0] = src->kv_num;
+  sp.s_ptr[0] = src->kv_ptr;
+  sp.s_idx[0] = src->kv_idx;
+  sp.s_num[1] = src->full_kv_num;
+  sp.s_ptr[1] = src->full_kv_ptr;
+  sp.s_idx[1] = src->full_kv_idx;
+  sp.nqb_src = (int32_t)nqb_src;
+  sp.nkb_src = (int32_t)nkb_src;
+  sp.r_base = (int32_t)(delta / dst->block_q);
+  sp.H = src->H;
+  sp.src_q_offset = src->q_offset;
+  sp.src_q_len = src->q_len;
+  sp.src_kv_len = src->kv_len;
+  hipError_t e = fa::launch_slice(sp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "block-mask slice launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

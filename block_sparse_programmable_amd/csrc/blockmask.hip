@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void count_kernel(BuildParams p) {
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int nr = p.tB * p.nqb;
-  const int nc = p.tB * p.nkb;
+  const int nc = p.q_num ? p.tB * p.nkb : 0;   // query side not requested: rows only
   if (wave >= nr + nc) return;
   const bool rowside = wave < nr;
   const int idx = rowside ? wave : wave - nr;
@@ -385,6 +385,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(BuildParams p) {
     const int32_t* num = which == 0 ? p.kv_num : which == 1 ? p.full_kv_num : which == 2 ? p.q_num : p.full_q_num;
     int32_t* ptr = which == 0 ? p.kv_ptr : which == 1 ? p.full_kv_ptr : which == 2 ? p.q_ptr : p.full_q_ptr;
     const int64_t n = (which < 2) ? (int64_t)p.tB * p.tH * p.nqb : (int64_t)p.tB * p.tH * p.nkb;
+    if (num == nullptr) continue;   // query side not requested (kernel argument: uniform)
     if (tid == 0) carry_s = 0;
     __syncthreads();
     for (int64_t base = 0; base < n; base += 1024) {
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(BuildParams p) {
   const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int64_t nr = (int64_t)p.tB * p.tH * p.nqb;
-  const int64_t nc = (int64_t)p.tB * p.tH * p.nkb;
+  const int64_t nc = p.q_num ? (int64_t)p.tB * p.tH * p.nkb : 0;
   if (wave >= nr + nc) return;
   const bool rowside = wave < nr;
   const int64_t idx = rowside ? wave : wave - nr;
@@ -449,6 +450,179 @@ __global__ __launch_bounds__(256) void scatter_kernel(BuildParams p) {
 constexpr int kSmallMaxBlocks = 16384;  // tB * NQB * NKB
 constexpr int kSmallMaxLines = 2048;    // tB * (NQB + NKB)
 constexpr int kSmallMaxTB = 64;
+
+// phases 4-6 of the one-workgroup build, shared with the row slicer: partial/full
+// counts, prefix sums and ordered compaction of an LDS class grid [tB][nqb][nkb] into
+// the table arrays, every row and column repeated for the tH heads of its tb.  The
+// query-side arrays are written only when p.q_num is set.
+__device__ void compact_small(const BuildParams& p, const uint8_t* grid_s, int32_t* cnt_s, int32_t* pre_s,
+                              int32_t* tot_s, int32_t* cum_s) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nq = p.tB * p.nqb, nl = nq + p.tB * p.nkb;
+  const bool qout = p.q_num != nullptr;
+  // phase 4: partial / full counts per row (tb, r) and per column (tb, c).  Every line
+  // of a side has the same length; a side of short lines (at most kShort entries, e.g.
+  // the query side of a decode grid) takes one thread per line, the other one wave per
+  // line (ballot counts).  Lines are [rows | columns], so each kind is one range.
+  constexpr int kShort = 8;
+  const bool rows_long = p.nkb > kShort, cols_long = p.nqb > kShort;
+  const int lw0 = rows_long ? 0 : nq, lw1 = cols_long ? nl : nq;   // long lines
+  const int ls0 = rows_long ? nq : 0, ls1 = cols_long ? nq : nl;   // short lines
+  auto line_geom = [&](int line, int& tb, int& k, int& n, bool& rowside) {
+    rowside = line < nq;
+    const int idx = rowside ? line : line - nq;
+    tb = rowside ? idx / p.nqb : idx / p.nkb;
+    k = rowside ? idx - tb * p.nqb : idx - tb * p.nkb;
+    n = rowside ? p.nkb : p.nqb;
+  };
+  auto entry = [&](const uint8_t* g, bool rowside, int k, int x) -> uint8_t {
+    return rowside ? g[k * p.nkb + x] : g[x * p.nkb + k];
+  };
+  for (int line = lw0 + wv; line < lw1; line += 16) {
+    int tb, k, n;
+    bool rowside;
+    line_geom(line, tb, k, n, rowside);
+    const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
+    int np = 0, nf = 0;
+    for (int x0 = 0; x0 < n; x0 += 64) {
+      const int x = x0 + lane;
+      const uint8_t v = x < n ? entry(g, rowside, k, x) : kEmpty;
+      np += __popcll(__ballot(v == kPartial));
+      nf += __popcll(__ballot(v == kFull));
+    }
+    if (lane == 0) {
+      cnt_s[2 * line] = np;
+      cnt_s[2 * line + 1] = nf;
+    }
+  }
+  for (int line = ls0 + tid; line < ls1; line += 1024) {
+    int tb, k, n;
+    bool rowside;
+    line_geom(line, tb, k, n, rowside);
+    const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
+    int np = 0, nf = 0;
+    for (int x = 0; x < n; ++x) {
+      const uint8_t v = entry(g, rowside, k, x);
+      np += v == kPartial;
+      nf += v == kFull;
+    }
+    cnt_s[2 * line] = np;
+    cnt_s[2 * line + 1] = nf;
+  }
+  __syncthreads();
+
+  // phase 5: exclusive prefix within each tb; one wave per (tb, side, kind) sequence
+  for (int sq = wv; sq < 4 * p.tB; sq += 16) {
+    const int tb = sq >> 2, side = (sq >> 1) & 1, kind = sq & 1;
+    const int n = side == 0 ? p.nqb : p.nkb;
+    const int first = side == 0 ? tb * p.nqb : nq + tb * p.nkb;
+    int carry = 0;
+    for (int x0 = 0; x0 < n; x0 += 64) {
+      const int x = x0 + lane;
+      const int v = x < n ? cnt_s[2 * (first + x) + kind] : 0;
+      const int excl = __ockl_wfscan_add_i32(v, false);   // DPP wave scan
+      if (x < n) pre_s[2 * (first + x) + kind] = carry + excl;
+      carry += __builtin_amdgcn_readlane(excl + v, 63);
+    }
+    if (lane == 0) tot_s[4 * tb + 2 * side + kind] = carry;
+  }
+  __syncthreads();
+  if (tid < 4) {
+    int acc = 0;
+    for (int tb = 0; tb < p.tB; ++tb) {
+      cum_s[4 * tb + tid] = acc;
+      acc += p.tH * tot_s[4 * tb + tid];
+    }
+    cum_s[4 * p.tB + tid] = acc;
+  }
+  __syncthreads();
+
+  // phase 6: counts and pointers for every replicated head, then ordered scatter
+  const int rows = p.tB * p.tH * p.nqb, cols = p.tB * p.tH * p.nkb;
+  for (int x = tid; x < rows + (qout ? cols : 0); x += 1024) {
+    const bool rowside = x < rows;
+    const int idx = rowside ? x : x - rows;
+    const int per = rowside ? p.nqb : p.nkb;
+    const int bh = idx / per, k = idx - bh * per;
+    const int tb = bh / p.tH, h = bh - tb * p.tH;
+    const int line = rowside ? tb * p.nqb + k : nq + tb * p.nkb + k;
+    const int side = rowside ? 0 : 1;
+    const int np_ = cnt_s[2 * line], nf_ = cnt_s[2 * line + 1];
+    const int pp = cum_s[4 * tb + 2 * side] + h * tot_s[4 * tb + 2 * side] + pre_s[2 * line];
+    const int pf = cum_s[4 * tb + 2 * side + 1] + h * tot_s[4 * tb + 2 * side + 1] + pre_s[2 * line + 1];
+    if (rowside) {
+      p.kv_num[idx] = np_;
+      p.kv_ptr[idx] = pp;
+      p.full_kv_num[idx] = nf_;
+      p.full_kv_ptr[idx] = pf;
+    } else {
+      p.q_num[idx] = np_;
+      p.q_ptr[idx] = pp;
+      p.full_q_num[idx] = nf_;
+      p.full_q_ptr[idx] = pf;
+    }
+  }
+  if (tid == 0) {
+    p.kv_ptr[rows] = cum_s[4 * p.tB + 0];
+    p.full_kv_ptr[rows] = cum_s[4 * p.tB + 1];
+    if (qout) {
+      p.q_ptr[cols] = cum_s[4 * p.tB + 2];
+      p.full_q_ptr[cols] = cum_s[4 * p.tB + 3];
+    }
+  }
+  // ordered scatter, per base line and then for every replicated head (head h of tb
+  // starts h * tot after head 0): long lines one wave each (ballot compaction), short
+  // lines one thread each
+  auto line_out = [&](int line, bool rowside, int tb, int& pp0, int& pf0, int& tp, int& tf) {
+    const int side = rowside ? 0 : 1;
+    tp = tot_s[4 * tb + 2 * side];
+    tf = tot_s[4 * tb + 2 * side + 1];
+    pp0 = cum_s[4 * tb + 2 * side] + pre_s[2 * line];
+    pf0 = cum_s[4 * tb + 2 * side + 1] + pre_s[2 * line + 1];
+  };
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int lw1o = qout ? lw1 : min(lw1, nq), ls1o = qout ? ls1 : min(ls1, nq);
+  for (int line = lw0 + wv; line < lw1o; line += 16) {
+    int tb, k, n, pp0, pf0, tp, tf;
+    bool rowside;
+    line_geom(line, tb, k, n, rowside);
+    line_out(line, rowside, tb, pp0, pf0, tp, tf);
+    int32_t* pidx = rowside ? p.kv_idx : p.q_idx;
+    int32_t* fidx = rowside ? p.full_kv_idx : p.full_q_idx;
+    const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
+    for (int x0 = 0; x0 < n; x0 += 64) {
+      const int y = x0 + lane;
+      const uint8_t v = y < n ? entry(g, rowside, k, y) : kEmpty;
+      const uint64_t bp = __ballot(v == kPartial);
+      const uint64_t bf = __ballot(v == kFull);
+      const int ip = pp0 + __popcll(bp & below), jf = pf0 + __popcll(bf & below);
+      for (int h = 0; h < p.tH; ++h) {
+        if (v == kPartial) pidx[ip + h * tp] = y;
+        if (v == kFull) fidx[jf + h * tf] = y;
+      }
+      pp0 += __popcll(bp);
+      pf0 += __popcll(bf);
+    }
+  }
+  for (int line = ls0 + tid; line < ls1o; line += 1024) {
+    int tb, k, n, pp0, pf0, tp, tf;
+    bool rowside;
+    line_geom(line, tb, k, n, rowside);
+    line_out(line, rowside, tb, pp0, pf0, tp, tf);
+    int32_t* pidx = rowside ? p.kv_idx : p.q_idx;
+    int32_t* fidx = rowside ? p.full_kv_idx : p.full_q_idx;
+    const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
+    for (int y = 0; y < n; ++y) {
+      const uint8_t v = entry(g, rowside, k, y);
+      for (int h = 0; h < p.tH; ++h) {
+        if (v == kPartial) pidx[pp0 + h * tp] = y;
+        if (v == kFull) fidx[pf0 + h * tf] = y;
+      }
+      pp0 += v == kPartial;
+      pf0 += v == kFull;
+    }
+  }
+}
 
 __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
   __shared__ uint8_t grid_s[kSmallMaxBlocks];
@@ -565,7 +739,7 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
   if (tid == 0) n_undecided = 0;
   __syncthreads();
   const bool docs_sorted = p.prog.has_doc && unsorted_s == 0;
-  {
+  if (total > 0) {
     // (tb, r, c) of block id, advanced by 1024 ids per step without dividing
     const int nblk = p.nqb * p.nkb;
     int tb = tid / nblk;
@@ -622,165 +796,111 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
   }
   __syncthreads();
 
-  // phase 4: partial / full counts per row (tb, r) and per column (tb, c).  Every line
-  // of a side has the same length; a side of short lines (at most kShort entries, e.g.
-  // the query side of a decode grid) takes one thread per line, the other one wave per
-  // line (ballot counts).  Lines are [rows | columns], so each kind is one range.
-  constexpr int kShort = 8;
-  const bool rows_long = p.nkb > kShort, cols_long = p.nqb > kShort;
-  const int lw0 = rows_long ? 0 : nq, lw1 = cols_long ? nl : nq;   // long lines
-  const int ls0 = rows_long ? nq : 0, ls1 = cols_long ? nq : nl;   // short lines
-  auto line_geom = [&](int line, int& tb, int& k, int& n, bool& rowside) {
-    rowside = line < nq;
-    const int idx = rowside ? line : line - nq;
-    tb = rowside ? idx / p.nqb : idx / p.nkb;
-    k = rowside ? idx - tb * p.nqb : idx - tb * p.nkb;
-    n = rowside ? p.nkb : p.nqb;
-  };
-  auto entry = [&](const uint8_t* g, bool rowside, int k, int x) -> uint8_t {
-    return rowside ? g[k * p.nkb + x] : g[x * p.nkb + k];
-  };
-  for (int line = lw0 + wv; line < lw1; line += 16) {
-    int tb, k, n;
-    bool rowside;
-    line_geom(line, tb, k, n, rowside);
-    const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
-    int np = 0, nf = 0;
-    for (int x0 = 0; x0 < n; x0 += 64) {
-      const int x = x0 + lane;
-      const uint8_t v = x < n ? entry(g, rowside, k, x) : kEmpty;
-      np += __popcll(__ballot(v == kPartial));
-      nf += __popcll(__ballot(v == kFull));
-    }
-    if (lane == 0) {
-      cnt_s[2 * line] = np;
-      cnt_s[2 * line + 1] = nf;
-    }
-  }
-  for (int line = ls0 + tid; line < ls1; line += 1024) {
-    int tb, k, n;
-    bool rowside;
-    line_geom(line, tb, k, n, rowside);
-    const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
-    int np = 0, nf = 0;
-    for (int x = 0; x < n; ++x) {
-      const uint8_t v = entry(g, rowside, k, x);
-      np += v == kPartial;
-      nf += v == kFull;
-    }
-    cnt_s[2 * line] = np;
-    cnt_s[2 * line + 1] = nf;
-  }
-  __syncthreads();
+  compact_small(p, grid_s, cnt_s, pre_s, tot_s, cum_s);
+}
 
-  // phase 5: exclusive prefix within each tb; one wave per (tb, side, kind) sequence
-  for (int sq = wv; sq < 4 * p.tB; sq += 16) {
-    const int tb = sq >> 2, side = (sq >> 1) & 1, kind = sq & 1;
-    const int n = side == 0 ? p.nqb : p.nkb;
-    const int first = side == 0 ? tb * p.nqb : nq + tb * p.nkb;
-    int carry = 0;
-    for (int x0 = 0; x0 < n; x0 += 64) {
-      const int x = x0 + lane;
-      const int v = x < n ? cnt_s[2 * (first + x) + kind] : 0;
-      const int excl = __ockl_wfscan_add_i32(v, false);   // DPP wave scan
-      if (x < n) pre_s[2 * (first + x) + kind] = carry + excl;
-      carry += __builtin_amdgcn_readlane(excl + v, 63);
-    }
-    if (lane == 0) tot_s[4 * tb + 2 * side + kind] = carry;
-  }
-  __syncthreads();
-  if (tid < 4) {
-    int acc = 0;
-    for (int tb = 0; tb < p.tB; ++tb) {
-      cum_s[4 * tb + tid] = acc;
-      acc += p.tH * tot_s[4 * tb + tid];
-    }
-    cum_s[4 * p.tB + tid] = acc;
-  }
-  __syncthreads();
+// ---------------------------------------------------------------------------------
+// Row slices of prebuilt tables: decode takes the query block of the current position
+// out of tables built once for the longest context ("FlexAttention: from rules to fused
+// kernels", section 5.2), and a shorter square crop is the top-left corner of the longer
+// one (same page, section 2.2).  New block (k, c) covers the same or fewer pairs than
+// prebuilt block (r_base + k, c), so an EMPTY block stays empty and a FULL one stays
+// full, and where the two blocks cover the same pairs a PARTIAL block stays partial.
+// Only PARTIAL blocks whose row or key range changed (the ragged last row or column,
+// or rows inside a prebuilt block) are decided again, by the builder's own bounds and
+// exact evaluation on the new geometry; the rule is evaluated nowhere else.  The result
+// equals the tables built for the new geometry.
+// ---------------------------------------------------------------------------------
+constexpr int kSliceMaxLines = 4096;   // tables B*H * (NQB + NKB)
+constexpr int kSliceMaxTB = 256;       // tables B*H
 
-  // phase 6: counts and pointers for every replicated head, then ordered scatter
-  const int rows = p.tB * p.tH * p.nqb, cols = p.tB * p.tH * p.nkb;
-  for (int x = tid; x < rows + cols; x += 1024) {
-    const bool rowside = x < rows;
-    const int idx = rowside ? x : x - rows;
-    const int per = rowside ? p.nqb : p.nkb;
-    const int bh = idx / per, k = idx - bh * per;
-    const int tb = bh / p.tH, h = bh - tb * p.tH;
-    const int line = rowside ? tb * p.nqb + k : nq + tb * p.nkb + k;
-    const int side = rowside ? 0 : 1;
-    const int np_ = cnt_s[2 * line], nf_ = cnt_s[2 * line + 1];
-    const int pp = cum_s[4 * tb + 2 * side] + h * tot_s[4 * tb + 2 * side] + pre_s[2 * line];
-    const int pf = cum_s[4 * tb + 2 * side + 1] + h * tot_s[4 * tb + 2 * side + 1] + pre_s[2 * line + 1];
-    if (rowside) {
-      p.kv_num[idx] = np_;
-      p.kv_ptr[idx] = pp;
-      p.full_kv_num[idx] = nf_;
-      p.full_kv_ptr[idx] = pf;
-    } else {
-      p.q_num[idx] = np_;
-      p.q_ptr[idx] = pp;
-      p.full_q_num[idx] = nf_;
-      p.full_q_ptr[idx] = pf;
+__device__ __forceinline__ bool cell_changes(const SliceParams& sp, int k, int c) {
+  const BuildParams& p = sp.d;
+  const int64_t r = (int64_t)sp.r_base + k;
+  const int64_t a_new = p.q_offset + (int64_t)k * p.bq;
+  const int64_t e_new = p.q_offset + min((int64_t)(k + 1) * p.bq, p.q_len);
+  const int64_t a_old = sp.src_q_offset + r * p.bq;
+  const int64_t e_old = sp.src_q_offset + min((r + 1) * p.bq, sp.src_q_len);
+  const int64_t ce = ((int64_t)c + 1) * p.bk;
+  return a_new != a_old || e_new != e_old || min(ce, p.kv_len) != min(ce, sp.src_kv_len);
+}
+
+// One wave: the classes of new row `row` into g[0, nkb) (cleared beforehand).  Source
+// lists are ascending, so each ends at its first column past the new key range.
+__device__ void mark_row(const SliceParams& sp, int row, int lane, uint8_t* g) {
+  const BuildParams& p = sp.d;
+  const int bh = row / p.nqb, k = row - bh * p.nqb;
+  const int sl = bh * sp.nqb_src + sp.r_base + k;
+  const int b_doc = bh / sp.H;
+  {
+    const int n = sp.s_num[1][sl];
+    const int32_t* a = sp.s_idx[1] + sp.s_ptr[1][sl];
+    for (int e0 = 0; e0 < n; e0 += 64) {
+      const int e = e0 + lane;
+      const int c = e < n ? a[e] : 0x7fffffff;
+      if (c < p.nkb) g[c] = kFull;
+      if (__ballot(c < p.nkb) != ~0ull) break;
     }
   }
-  if (tid == 0) {
-    p.kv_ptr[rows] = cum_s[4 * p.tB + 0];
-    p.full_kv_ptr[rows] = cum_s[4 * p.tB + 1];
-    p.q_ptr[cols] = cum_s[4 * p.tB + 2];
-    p.full_q_ptr[cols] = cum_s[4 * p.tB + 3];
-  }
-  // ordered scatter, per base line and then for every replicated head (head h of tb
-  // starts h * tot after head 0): long lines one wave each (ballot compaction), short
-  // lines one thread each
-  auto line_out = [&](int line, bool rowside, int tb, int& pp0, int& pf0, int& tp, int& tf) {
-    const int side = rowside ? 0 : 1;
-    tp = tot_s[4 * tb + 2 * side];
-    tf = tot_s[4 * tb + 2 * side + 1];
-    pp0 = cum_s[4 * tb + 2 * side] + pre_s[2 * line];
-    pf0 = cum_s[4 * tb + 2 * side + 1] + pre_s[2 * line + 1];
-  };
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int line = lw0 + wv; line < lw1; line += 16) {
-    int tb, k, n, pp0, pf0, tp, tf;
-    bool rowside;
-    line_geom(line, tb, k, n, rowside);
-    line_out(line, rowside, tb, pp0, pf0, tp, tf);
-    int32_t* pidx = rowside ? p.kv_idx : p.q_idx;
-    int32_t* fidx = rowside ? p.full_kv_idx : p.full_q_idx;
-    const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
-    for (int x0 = 0; x0 < n; x0 += 64) {
-      const int y = x0 + lane;
-      const uint8_t v = y < n ? entry(g, rowside, k, y) : kEmpty;
-      const uint64_t bp = __ballot(v == kPartial);
-      const uint64_t bf = __ballot(v == kFull);
-      const int ip = pp0 + __popcll(bp & below), jf = pf0 + __popcll(bf & below);
-      for (int h = 0; h < p.tH; ++h) {
-        if (v == kPartial) pidx[ip + h * tp] = y;
-        if (v == kFull) fidx[jf + h * tf] = y;
+  const int n = sp.s_num[0][sl];
+  const int32_t* a = sp.s_idx[0] + sp.s_ptr[0][sl];
+  for (int e0 = 0; e0 < n; e0 += 64) {
+    const int e = e0 + lane;
+    const int c = e < n ? a[e] : 0x7fffffff;
+    const bool in = c < p.nkb;
+    uint8_t cls = kPartial;
+    bool need = in && cell_changes(sp, k, c);
+    if (need && !p.prog.has_doc) {
+      const int v = classify_bounds(p, geom(p, k, c), nullptr, nullptr);
+      if (v != VU) {
+        cls = v == VT ? kFull : (v == VF ? kEmpty : kPartial);
+        need = false;
       }
-      pp0 += __popcll(bp);
-      pf0 += __popcll(bf);
     }
-  }
-  for (int line = ls0 + tid; line < ls1; line += 1024) {
-    int tb, k, n, pp0, pf0, tp, tf;
-    bool rowside;
-    line_geom(line, tb, k, n, rowside);
-    line_out(line, rowside, tb, pp0, pf0, tp, tf);
-    int32_t* pidx = rowside ? p.kv_idx : p.q_idx;
-    int32_t* fidx = rowside ? p.full_kv_idx : p.full_q_idx;
-    const uint8_t* g = grid_s + tb * p.nqb * p.nkb;
-    for (int y = 0; y < n; ++y) {
-      const uint8_t v = entry(g, rowside, k, y);
-      for (int h = 0; h < p.tH; ++h) {
-        if (v == kPartial) pidx[pp0 + h * tp] = y;
-        if (v == kFull) fidx[pf0 + h * tf] = y;
-      }
-      pp0 += v == kPartial;
-      pf0 += v == kFull;
+    // the rest (document rules, undecided or-combinations): the whole wave per block
+    uint64_t m = __ballot(need);
+    while (m) {
+      const int l = __builtin_ctzll(m);
+      m &= m - 1;
+      const int cc = __builtin_amdgcn_readlane(c, l);
+      const uint8_t x = exact_block(p, b_doc, k, cc, lane, load_block_docs(p, b_doc, k, cc, lane));
+      if (lane == l) cls = x;
     }
+    if (in && cls != kEmpty) g[c] = cls;
+    if (__ballot(in) != ~0ull) break;
   }
+}
+
+// One workgroup: the new rows are marked into an LDS class grid, then compacted by the
+// builder's own counting, prefix and scatter phases.
+__global__ __launch_bounds__(1024) void slice_small_kernel(SliceParams sp) {
+  __shared__ __attribute__((aligned(16))) uint8_t grid_s[kSmallMaxBlocks];
+  __shared__ int32_t cnt_s[2 * kSliceMaxLines];
+  __shared__ int32_t pre_s[2 * kSliceMaxLines];
+  __shared__ int32_t tot_s[4 * kSliceMaxTB];
+  __shared__ int32_t cum_s[4 * (kSliceMaxTB + 1)];
+  const BuildParams& p = sp.d;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int total = p.tB * p.nqb * p.nkb;
+  for (int x = tid; x < (total + 3) / 4; x += 1024) reinterpret_cast<uint32_t*>(grid_s)[x] = 0u;
+  __syncthreads();
+  for (int row = wv; row < p.tB * p.nqb; row += 16) mark_row(sp, row, lane, grid_s + row * p.nkb);
+  __syncthreads();
+  compact_small(p, grid_s, cnt_s, pre_s, tot_s, cum_s);
+}
+
+// larger slices: the class grid goes to the workspace (cleared here, then marked one
+// wave per new row) and the builder's count, scan and scatter launches compact it
+__global__ __launch_bounds__(256) void slice_clear_kernel(uint4* grid, int64_t n16) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t < n16) grid[t] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+__global__ __launch_bounds__(256) void slice_mark_kernel(SliceParams sp) {
+  const BuildParams& p = sp.d;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.tB * p.nqb) return;
+  mark_row(sp, row, threadIdx.x & 63, p.grid + (int64_t)row * p.nkb);
 }
 
 inline unsigned waves_to_blocks(int64_t waves) { return (unsigned)((waves + 3) / 4); }
@@ -794,21 +914,47 @@ size_t build_workspace_bytes(int64_t tB, int64_t nqb, int64_t nkb) {
 }
 
 hipError_t launch_build(const BuildParams& p, hipStream_t s) {
+  // an empty grid still gets its counts and pointers (all zero) written
   const int64_t total = (int64_t)p.tB * p.nqb * p.nkb;
-  if (total == 0) return hipSuccess;
   const int64_t lines = (int64_t)p.tB * (p.nqb + p.nkb);
   const int64_t expanded = (int64_t)p.tB * p.tH * (p.nqb + p.nkb);
   if (total <= kSmallMaxBlocks && lines <= kSmallMaxLines && p.tB <= kSmallMaxTB && expanded <= (1 << 20)) {
     hipLaunchKernelGGL(build_small_kernel, dim3(1), dim3(1024), 0, s, p);
     return hipGetLastError();
   }
-  if (p.prog.has_doc) {
-    hipLaunchKernelGGL(doc_stats_kernel, dim3(waves_to_blocks((int64_t)p.tB * (p.nqb + p.nkb))), dim3(256), 0, s, p);
-  }
-  hipLaunchKernelGGL(classify_kernel, dim3(waves_to_blocks((total + kClassifyPerWave - 1) / kClassifyPerWave)), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(count_kernel, dim3(waves_to_blocks((int64_t)p.tB * (p.nqb + p.nkb))), dim3(256), 0, s, p);
+  if (lines > 0 && p.prog.has_doc)
+    hipLaunchKernelGGL(doc_stats_kernel, dim3(waves_to_blocks(lines)), dim3(256), 0, s, p);
+  if (total > 0)
+    hipLaunchKernelGGL(classify_kernel, dim3(waves_to_blocks((total + kClassifyPerWave - 1) / kClassifyPerWave)), dim3(256), 0, s, p);
+  if (lines > 0) hipLaunchKernelGGL(count_kernel, dim3(waves_to_blocks(lines)), dim3(256), 0, s, p);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, p);
-  hipLaunchKernelGGL(scatter_kernel, dim3(waves_to_blocks((int64_t)p.tB * p.tH * (p.nqb + p.nkb))), dim3(256), 0, s, p);
+  if (expanded > 0) hipLaunchKernelGGL(scatter_kernel, dim3(waves_to_blocks(expanded)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+size_t slice_workspace_bytes(int64_t tBH, int64_t nqb, int64_t nkb) {
+  return (size_t)(tBH * nqb * nkb + 255) & ~(size_t)255;
+}
+
+hipError_t launch_slice(const SliceParams& sp, hipStream_t s) {
+  const BuildParams& p = sp.d;
+  const int64_t total = (int64_t)p.tB * p.nqb * p.nkb;
+  const int64_t lines = (int64_t)p.tB * (p.nqb + p.nkb);
+  if (total <= kSmallMaxBlocks && lines <= kSliceMaxLines && p.tB <= kSliceMaxTB) {
+    hipLaunchKernelGGL(slice_small_kernel, dim3(1), dim3(1024), 0, s, sp);
+    return hipGetLastError();
+  }
+  const int64_t n16 = (total + 15) / 16;   // the workspace is rounded up to 256 bytes
+  const int64_t rows = (int64_t)p.tB * p.nqb;
+  const int64_t out_lines = rows + (p.q_num ? (int64_t)p.tB * p.nkb : 0);
+  if (n16 > 0) {
+    hipLaunchKernelGGL(slice_clear_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+                       reinterpret_cast<uint4*>(p.grid), n16);
+    hipLaunchKernelGGL(slice_mark_kernel, dim3(waves_to_blocks(rows)), dim3(256), 0, s, sp);
+  }
+  if (out_lines > 0) hipLaunchKernelGGL(count_kernel, dim3(waves_to_blocks(out_lines)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, p);
+  if (out_lines > 0) hipLaunchKernelGGL(scatter_kernel, dim3(waves_to_blocks(out_lines)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

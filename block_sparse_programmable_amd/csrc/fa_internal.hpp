@@ -55,6 +55,22 @@ struct BuildParams {
 size_t build_workspace_bytes(int64_t tB, int64_t nqb, int64_t nkb);
 hipError_t launch_build(const BuildParams& p, hipStream_t s);
 
+// Row slice of prebuilt tables.  The destination is described as a build of its own
+// (d.tB = table B * H, d.tH = 1: every (b', h') row is sliced on its own; d.q_num ==
+// nullptr skips the query side; d.grid is the workspace); its rows are source rows
+// r_base .. r_base + nqb - 1 of the same (b', h') with columns c < d.nkb.
+struct SliceParams {
+  BuildParams d;
+  const int32_t* s_num[2];   // source kv-side lists: partial, full
+  const int32_t* s_ptr[2];
+  const int32_t* s_idx[2];
+  int32_t nqb_src, nkb_src, r_base;
+  int32_t H;                 // table head extent: (b', h') = bh gives doc batch bh / H
+  int64_t src_q_offset, src_q_len, src_kv_len;
+};
+size_t slice_workspace_bytes(int64_t tBH, int64_t nqb, int64_t nkb);
+hipError_t launch_slice(const SliceParams& p, hipStream_t s);
+
 // ---------------------------------------------------------------- forward
 struct ScoreParams {
   int32_t kind;

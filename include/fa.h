@@ -6,6 +6,7 @@
  * "FlexAttention: from rules to fused kernels", sections 1 and 2):
  *
  *   fa_create_block_mask  mask rule -> block tables (BCSR rows and their transposes)
+ *   fa_block_mask_slice   rows of prebuilt tables for a shorter or offset geometry
  *   fa_forward            O = softmax(mask(score_mod(Q K^T * scale))) V, plus LSE
  *   fa_forward_paged      the same over a paged KV cache (short-query path)
  *   fa_backward           dQ, dK, dV of fa_forward
@@ -122,7 +123,8 @@ typedef struct {
 /* Sizes for a block mask: rows = B*H*NQB (length of kv_num; kv_ptr has rows+1),
  * cols = B*H*NKB (length of q_num; q_ptr has cols+1), idx_capacity = B*H*NQB*NKB
  * (length to allocate for each of the four idx arrays), workspace_bytes = scratch
- * needed by fa_create_block_mask.  Reads only the geometry fields; pure host call. */
+ * needed by fa_create_block_mask and by fa_block_mask_slice into these tables.  Reads
+ * only the geometry fields; pure host call. */
 fa_status fa_block_mask_sizes(const fa_block_mask* bm, int64_t* rows, int64_t* cols,
                               int64_t* idx_capacity, size_t* workspace_bytes);
 
@@ -132,6 +134,36 @@ fa_status fa_block_mask_sizes(const fa_block_mask* bm, int64_t* rows, int64_t* c
  * the same tables bit for bit. */
 fa_status fa_create_block_mask(fa_block_mask* bm, void* workspace, size_t ws_bytes,
                                fa_stream_t stream);
+
+/* Row slice of prebuilt tables ("FlexAttention: from rules to fused kernels", sec. 5.2:
+ * build the tables once for the longest context, then for each decode step take the
+ * query block that holds the current position, with the rule still seeing global
+ * positions; sec. 2.2: a shorter square crop is the top-left corner of the longer one).
+ *
+ * `src` holds tables written by fa_create_block_mask (or by this call) for its
+ * geometry; only its kv side is read.  `dst` carries the new geometry -- q_len,
+ * kv_len, q_offset -- with the mask rule, table extents and block sizes of src, and
+ * caller-owned arrays sized by fa_block_mask_sizes(dst).  Requirements (else
+ * FA_ERR_SHAPE / FA_ERR_MASK_MISMATCH):
+ *   - the new rows [q_offset, q_offset + q_len) lie inside src's rows and
+ *     kv_len <= src->kv_len: positions past the prebuilt length need new tables;
+ *   - q_offset - src->q_offset is a multiple of block_q, or the new rows form one query
+ *     block that lies inside one prebuilt query block (the decode case).
+ * New block (k, c) holds a subset of the pairs of prebuilt block (k + (q_offset -
+ * src->q_offset)/block_q, c), and every rule of the menu is a predicate on global
+ * positions (none reads q_len or kv_len), so EMPTY and FULL blocks keep their class and
+ * so does a PARTIAL block that covers the same pairs; a PARTIAL block whose rows or
+ * keys were cut is classified again on the new geometry.  The written tables are
+ * therefore exactly those fa_create_block_mask would write for dst, at the cost of
+ * re-deciding only the blocks of a cut edge.
+ * The q-side arrays of dst are written when all six are set, and skipped when all six
+ * are NULL (fa_forward and fa_forward_paged read only the kv side).  `workspace` is a
+ * 16-byte aligned device buffer of at least fa_block_mask_sizes(dst)'s workspace_bytes
+ * (contents ignored on entry, unspecified on exit).  src, dst and workspace must not
+ * overlap.  Nothing is allocated; one launch for up to 16384 new blocks and 4096 new
+ * rows plus columns, five launches above. */
+fa_status fa_block_mask_slice(const fa_block_mask* src, fa_block_mask* dst, void* workspace, size_t ws_bytes,
+                              fa_stream_t stream);
 
 /* ----------------------------------------------------------------------------------
  * Score modification, applied to the scaled score s = (q . k) * scale of every pair

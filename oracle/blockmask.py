@@ -130,3 +130,53 @@ def expand(tab, B_tab, H_tab, q_len, kv_len, block_q, block_kv, spec, q_offset=0
             c0, c1 = c * block_kv, min((c + 1) * block_kv, kv_len)
             out[r0:r1, c0:c1] = M[r0:r1, c0:c1]
     return out
+
+
+def slice_rows(src, B_tab, H_tab, src_q_len, src_kv_len, block_q, block_kv, src_q_offset,
+               q_len, kv_len, q_offset):
+    """Block tables for query rows [q_offset, q_offset + q_len) (global positions) and keys
+    [0, kv_len), cut out of tables ``src`` built for a longer geometry.
+
+    Source: "FlexAttention: from rules to fused kernels", section 5.2 -- a mask prebuilt
+    for a maximum length is reused by taking the query block that holds the current
+    position (the rule keeps seeing global positions), and partial blocks keep the
+    exact rule; the query rows of one new block must lie inside one prebuilt block.
+    Section 2.2 of the same page -- a shorter square mask is the top-left crop of the
+    longer one, valid only for rules that do not read the total length.
+    A prebuilt FULL block stays FULL for a subset of its rows and in-range columns, a
+    listed PARTIAL block stays PARTIAL (it is masked exactly), an unlisted block stays
+    unlisted; columns past the new kv_len are dropped.
+
+    Raises ValueError when the new query blocks do not each sit inside one prebuilt
+    query block, or the new rows or keys are not covered by the prebuilt ones.
+    """
+    if kv_len > src_kv_len or q_offset < src_q_offset or q_offset + q_len > src_q_offset + src_q_len:
+        raise ValueError("the slice must lie inside the prebuilt rows and keys")
+    delta = q_offset - src_q_offset
+    nqb, nkb = n_blocks(q_len, block_q), n_blocks(kv_len, block_kv)
+    nqb_src = n_blocks(src_q_len, block_q)
+    aligned = delta % block_q == 0
+    single = nqb == 1 and delta // block_q == (delta + q_len - 1) // block_q
+    if nqb > 0 and not (aligned or single):
+        raise ValueError("each new query block must sit inside one prebuilt query block")
+    r_base = delta // block_q
+    rows = np.zeros((B_tab * H_tab * nqb, nkb), dtype=np.uint8)
+    for bh in range(B_tab * H_tab):
+        for k in range(nqb):
+            srow = bh * nqb_src + r_base + k
+            for key, cls in (("kv", PARTIAL), ("full_kv", FULL)):
+                lst = src[f"{key}_idx"][src[f"{key}_ptr"][srow]:src[f"{key}_ptr"][srow + 1]]
+                for c in lst:
+                    if c < nkb:
+                        rows[bh * nqb + k, c] = cls
+    cols = np.concatenate([rows[bh * nqb:(bh + 1) * nqb].T for bh in range(B_tab * H_tab)]) \
+        if B_tab * H_tab * nqb else np.zeros((B_tab * H_tab * nkb, 0), np.uint8)
+    kv = _compact(rows)
+    q = _compact(cols)
+    names = ("num", "ptr", "idx")
+    out = {}
+    for k, v in zip([f"kv_{n}" for n in names] + [f"full_kv_{n}" for n in names], kv):
+        out[k] = v
+    for k, v in zip([f"q_{n}" for n in names] + [f"full_q_{n}" for n in names], q):
+        out[k] = v
+    return out

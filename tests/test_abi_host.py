@@ -221,3 +221,52 @@ def test_compile_mask_postfix():
     from block_sparse_programmable_amd.api import compile_mask
     prog = compile_mask(("and", ("doc",), ("or", ("swa", 7), ("prefix", 3))))
     assert prog == [(L.FA_M_DOC, 0), (L.FA_M_SWA, 7), (L.FA_M_PREFIX, 3), (L.FA_M_OR, 0), (L.FA_M_AND, 0)]
+
+
+def test_slice_validation(lib):
+    from block_sparse_programmable_amd import _lib as L
+    names = ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx",
+             "q_num", "q_ptr", "q_idx", "full_q_num", "full_q_ptr", "full_q_idx")
+
+    def tabs(d, which=names, base=0x1000):
+        for i, n in enumerate(which):
+            setattr(d, n, base + 0x100 * i)       # never dereferenced: every case is rejected first
+        return d
+    src = tabs(_bm(L, q_len=4096, kv_len=4096, block_q=128, block_kv=128))
+    ok_dst = dict(q_len=1, kv_len=1000, q_offset=999, block_q=128, block_kv=128)
+    assert lib.fa_block_mask_slice(None, None, None, 0, None) == L.FA_ERR_NULL
+    # past the prebuilt length: rows and keys
+    d = tabs(_bm(L, **dict(ok_dst, q_offset=4096, kv_len=4097)), base=0x9000)
+    assert lib.fa_block_mask_slice(C.byref(src), C.byref(d), None, 0, None) == L.FA_ERR_SHAPE
+    assert b"prebuilt" in lib.fa_last_error_message()
+    d = tabs(_bm(L, **dict(ok_dst, kv_len=5000)), base=0x9000)
+    assert lib.fa_block_mask_slice(C.byref(src), C.byref(d), None, 0, None) == L.FA_ERR_SHAPE
+    # rows straddling two prebuilt query blocks, and an unaligned multi-block slice
+    d = tabs(_bm(L, **dict(ok_dst, q_len=2, q_offset=127)), base=0x9000)
+    assert lib.fa_block_mask_slice(C.byref(src), C.byref(d), None, 0, None) == L.FA_ERR_SHAPE
+    d = tabs(_bm(L, **dict(ok_dst, q_len=300, q_offset=64)), base=0x9000)
+    assert lib.fa_block_mask_slice(C.byref(src), C.byref(d), None, 0, None) == L.FA_ERR_SHAPE
+    # another rule, other block sizes, other extents
+    d = tabs(_bm(L, **dict(ok_dst, mask=("swa", 64))), base=0x9000)
+    assert lib.fa_block_mask_slice(C.byref(src), C.byref(d), None, 0, None) == L.FA_ERR_MASK_MISMATCH
+    d = tabs(_bm(L, **dict(ok_dst, block_q=64)), base=0x9000)
+    assert lib.fa_block_mask_slice(C.byref(src), C.byref(d), None, 0, None) == L.FA_ERR_MASK_MISMATCH
+    d = tabs(_bm(L, **dict(ok_dst, H=2)), base=0x9000)
+    assert lib.fa_block_mask_slice(C.byref(src), C.byref(d), None, 0, None) == L.FA_ERR_MASK_MISMATCH
+    sw = tabs(_bm(L, mask=("swa", 64), q_len=4096, kv_len=4096))
+    d = tabs(_bm(L, **dict(ok_dst, mask=("swa", 65))), base=0x9000)
+    assert lib.fa_block_mask_slice(C.byref(sw), C.byref(d), None, 0, None) == L.FA_ERR_MASK_MISMATCH
+    # missing tables: dst kv side, a partial q side, src q side for a q-side slice
+    d = _bm(L, **ok_dst)
+    assert lib.fa_block_mask_slice(C.byref(src), C.byref(d), None, 0, None) == L.FA_ERR_NULL
+    d = tabs(_bm(L, **ok_dst), which=names[:7], base=0x9000)
+    assert lib.fa_block_mask_slice(C.byref(src), C.byref(d), None, 0, None) == L.FA_ERR_NULL
+    assert b"all set or all NULL" in lib.fa_last_error_message()
+    # workspace missing, short or misaligned
+    d = tabs(_bm(L, **ok_dst), base=0x9000)
+    assert lib.fa_block_mask_slice(C.byref(src), C.byref(d), None, 0, None) == L.FA_ERR_WORKSPACE
+    assert lib.fa_block_mask_slice(C.byref(src), C.byref(d), C.c_void_p(0x20000), 1, None) == L.FA_ERR_WORKSPACE
+    assert lib.fa_block_mask_slice(C.byref(src), C.byref(d), C.c_void_p(0x20008), 1 << 20, None) == L.FA_ERR_WORKSPACE
+    # malformed geometry on either side
+    d = tabs(_bm(L, **dict(ok_dst, block_kv=96)), base=0x9000)
+    assert lib.fa_block_mask_slice(C.byref(src), C.byref(d), None, 0, None) == L.FA_ERR_UNSUPPORTED

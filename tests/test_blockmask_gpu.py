@@ -104,3 +104,24 @@ def test_large_grid_multi_launch_path(spec):
         check_tables(spec, 2, 2, n, n, 64, 64, 0, doc)
     else:
         check_tables(spec, 1, 3, n, n, 64, 64, 0, None)
+
+
+def test_empty_sides_are_written():
+    """q_len = 0 (or kv_len = 0): every count and pointer is still written (zeros), on
+    both the one-launch and the multi-launch builder paths."""
+    import block_sparse_programmable_amd as fa
+    from block_sparse_programmable_amd.api import TABLE_NAMES
+    for B, H, q_len, kv_len in ((1, 2, 0, 300), (2, 1, 300, 0), (1, 1, 0, 0), (1, 1, 0, 64 * 3000)):
+        n_rows = B * H * -(-q_len // 64)
+        n_cols = B * H * -(-kv_len // 64)
+        tables = {}
+        for side, n in (("kv", n_rows), ("full_kv", n_rows), ("q", n_cols), ("full_q", n_cols)):
+            tables[f"{side}_num"] = torch.full((max(n, 1),), -7, dtype=torch.int32, device="cuda")
+            tables[f"{side}_ptr"] = torch.full((n + 1,), -7, dtype=torch.int32, device="cuda")
+            tables[f"{side}_idx"] = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+        assert set(tables) == set(TABLE_NAMES)
+        fa.create_block_mask(("causal",), B, H, q_len, kv_len, 64, 64, 0, tables=tables)
+        torch.cuda.synchronize()
+        for side, n in (("kv", n_rows), ("full_kv", n_rows), ("q", n_cols), ("full_q", n_cols)):
+            assert (tables[f"{side}_num"][:n] == 0).all(), (B, H, q_len, kv_len, side)
+            assert (tables[f"{side}_ptr"] == 0).all(), (B, H, q_len, kv_len, side)

@@ -597,3 +597,84 @@ def test_backward_matches_sdpa_causal():
     (O * torch.tensor(do)).sum().backward()
     for a, b in ((dq, Q.grad), (dk, K.grad), (dv, V.grad)):
         assert np.abs(a - b.numpy()).max() < 1e-12
+
+
+# ---- prebuilt maximum-length tables and their slices ("FlexAttention: from rules to
+# fused kernels", section 5.2 for decode rows, section 2.2 for crops): block-aligned
+# crops of a rule on global positions equal the rebuilt tables, decode-row slices expand
+# to exactly the rule, and the crop check rejects a rule that reads the total length
+
+SLICE_SPECS = [("causal",), ("swa", 100), ("prefix", 70), ("and", ("causal",), ("swa", 150)),
+               ("or", ("swa", 60), ("prefix", 40)), ("and", ("doc",), ("causal",))]
+
+
+@pytest.mark.parametrize("spec", SLICE_SPECS, ids=[str(s) for s in SLICE_SPECS])
+def test_slice_block_aligned_crop_equals_rebuilt(spec):
+    Lmax, bq, bk = 768, 64, 128
+    doc = np.repeat(np.arange(6), [100, 200, 68, 150, 150, 100]).astype(np.int32)[None]
+    src = OB.tables(spec, 1, 2, Lmax, Lmax, bq, bk, 0, doc)
+    for L in (128, 256, 640):
+        got = OB.slice_rows(src, 1, 2, Lmax, Lmax, bq, bk, 0, L, L, 0)
+        want = OB.tables(spec, 1, 2, L, L, bq, bk, 0, doc)
+        for k in got:
+            assert np.array_equal(got[k], want[k]), (spec, L, k)
+
+
+@pytest.mark.parametrize("spec", SLICE_SPECS, ids=[str(s) for s in SLICE_SPECS])
+def test_slice_decode_rows_expand_to_the_rule(spec):
+    Lmax, bq, bk = 700, 128, 64
+    doc = np.repeat(np.arange(5), [130, 170, 100, 200, 100]).astype(np.int32)[None]
+    src = OB.tables(spec, 1, 1, Lmax, Lmax, bq, bk, 0, doc)
+    for t in (0, 63, 64, 127, 128, 300, 699):
+        for ql in (1, 3):
+            if t + ql > Lmax or t // bq != (t + ql - 1) // bq:
+                continue
+            got = OB.slice_rows(src, 1, 1, Lmax, Lmax, bq, bk, 0, ql, t + ql, t)
+            # the slice's tables, expanded with the exact rule on partial blocks, give the rule
+            M_hat = OB.expand(got, 1, 1, ql, t + ql, bq, bk, spec, t, doc)
+            M = OM.dense(spec, ql, t + ql, t, OM.doc_row_for(doc, 0))
+            assert np.array_equal(M_hat, M), (spec, t, ql)
+            # and every block the rebuilt decode tables list is listed by the slice
+            want = OB.tables(spec, 1, 1, ql, t + ql, bq, bk, t, doc)
+            listed = lambda tab: set(tab["kv_idx"].tolist()) | set(tab["full_kv_idx"].tolist())
+            assert listed(want) <= listed(got)
+            assert set(want["full_kv_idx"].tolist()) >= set(got["full_kv_idx"].tolist())
+
+
+def test_slice_rejects_straddling_rows():
+    src = OB.tables(("causal",), 1, 1, 512, 512, 128, 128)
+    with pytest.raises(ValueError):
+        OB.slice_rows(src, 1, 1, 512, 512, 128, 128, 0, 2, 200, 127)      # rows 127..128
+    with pytest.raises(ValueError):
+        OB.slice_rows(src, 1, 1, 512, 512, 128, 128, 0, 200, 200, 64)     # 64 is not aligned
+    with pytest.raises(ValueError):
+        OB.slice_rows(src, 1, 1, 512, 512, 128, 128, 0, 1, 600, 100)      # keys past the prebuilt
+
+
+def _crop_ok(spec_at, Lmax, lengths, bq, bk):
+    """Section 2.2's whitelist check: crops of tables built at Lmax against tables rebuilt
+    at each length, in block indices and in element adjacency."""
+    src = OB.tables(spec_at(Lmax), 1, 1, Lmax, Lmax, bq, bk)
+    for L in lengths:
+        crop = OB.slice_rows(src, 1, 1, Lmax, Lmax, bq, bk, 0, L, L, 0)
+        rebuilt = OB.tables(spec_at(L), 1, 1, L, L, bq, bk)
+        same_idx = all(np.array_equal(crop[k], rebuilt[k]) for k in crop)
+        M = OM.dense(spec_at(L), L, L)
+        if not (same_idx and np.array_equal(OB.expand(crop, 1, 1, L, L, bq, bk, spec_at(L)), M)):
+            return False
+    return True
+
+
+def test_crop_whitelist_rejects_a_length_dependent_rule(monkeypatch):
+    # the pages' counterexample: a token wired to the end block of the sequence.  The rule
+    # ("tail", L) lets every query see the last 64 keys of a length-L sequence, plus causal
+    base = OM.evaluate
+
+    def evaluate(spec, i, j, doc_row=None):
+        if spec[0] == "tail":
+            return (j >= spec[1] - 64) | (j <= i)
+        return base(spec, i, j, doc_row)
+    monkeypatch.setattr(OM, "evaluate", evaluate)
+    assert _crop_ok(lambda L: ("causal",), 512, (128, 256, 384), 64, 64)
+    assert _crop_ok(lambda L: ("swa", 90), 512, (128, 256, 384), 64, 64)
+    assert not _crop_ok(lambda L: ("tail", L), 512, (128, 256, 384), 64, 64)
