@@ -20,9 +20,12 @@ What it computes, in plain numpy float64:
 * ``paged``     -- the logical K/V of a paged cache (page-table gather), so that
                    paged attention is checked against dense attention on it.
 * ``backward``  -- dQ, dK, dV of the dense definition by float64 autograd.
+* ``selector``  -- block tables from selector candidate lists (range check, sort,
+                   repeat removal, rule inside the chosen blocks, exact classes) and
+                   the longest-row-first work order.
 
 Parity status of every function is stated in its docstring; each is pinned by
 the tests in ``tests/test_oracle_pins.py`` against values and identities that
 the pages and elementary mathematics fix.
 """
-from . import masks, blockmask, attention, merge, paged, backward  # noqa: F401
+from . import masks, blockmask, attention, merge, paged, backward, selector  # noqa: F401

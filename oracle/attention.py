@@ -63,7 +63,9 @@ def attention(q, k, v, mask, score="identity", cap=None, slopes=None, table=None
     """O [B, Hq, n_rows, d] and LSE [B, Hq, n_rows] in float64.
 
     q: [B, Hq, q_len, d]; k, v: [B, Hkv, kv_len, d] (any float dtype; bf16 is
-    up-cast exactly).  ``rows``/``heads``/``batches`` optionally restrict the
+    up-cast exactly).  ``mask`` is a rule of the menu, or a function
+    mask(b, h_q, i, j) -> bool array over global query positions i (column) and key
+    positions j (row).  ``rows``/``heads``/``batches`` optionally restrict the
     computed outputs to a subset (the result keeps the full B and Hq extents
     only when these are None; otherwise the leading axes follow the subsets).
     """
@@ -94,7 +96,10 @@ def attention(q, k, v, mask, score="identity", cap=None, slopes=None, table=None
                 i = (rr + int(q_offset))[:, None]
                 S = (q[b, h, rr] @ K.T) * scale
                 S = score_mod(S, score, h, i, j, cap, slopes, table, radius)
-                M = np.broadcast_to(masks.evaluate(mask, i, j, doc_row), S.shape)
+                if callable(mask):      # an arbitrary allowed-pair function of (b, h, i, j)
+                    M = np.broadcast_to(mask(b, h, i, j), S.shape)
+                else:
+                    M = np.broadcast_to(masks.evaluate(mask, i, j, doc_row), S.shape)
                 S = np.where(M, S, -np.inf)
                 empty = ~M.any(axis=1)
                 mx = np.where(empty, 0.0, S.max(axis=1))

@@ -678,3 +678,93 @@ def test_crop_whitelist_rejects_a_length_dependent_rule(monkeypatch):
     assert _crop_ok(lambda L: ("causal",), 512, (128, 256, 384), 64, 64)
     assert _crop_ok(lambda L: ("swa", 90), 512, (128, 256, 384), 64, 64)
     assert not _crop_ok(lambda L: ("tail", L), 512, (128, 256, 384), 64, 64)
+
+
+# ---- selector output into block tables ("FlexAttention: from rules to fused kernels",
+# sections 5.2 and 6.3; "Kernels: turning logical sparsity into real speed", section 3)
+
+from oracle import selector as OS  # noqa: E402
+
+
+def test_selector_canonical_sets_hand_example():
+    # range check, sort and repeat removal of one candidate row, NKB = 8
+    sets = OS.canonical_sets(np.array([[5, -1, 3, 5, 99, 0, 8, 7]]), 8)
+    assert [s.tolist() for s in sets] == [[0, 3, 5, 7]]
+    assert [s.tolist() for s in OS.canonical_sets(np.full((2, 3), -1), 8)] == [[], []]
+
+
+def test_selector_choosing_every_block_is_the_plain_rule():
+    # selecting all blocks of every row reduces to the rule's own tables
+    q_len = kv_len = 333
+    bq, bk = 64, 32
+    nqb, nkb = OB.n_blocks(q_len, bq), OB.n_blocks(kv_len, bk)
+    sel = np.tile(np.arange(nkb)[::-1], (1, 2, nqb, 1))          # reversed order on purpose
+    for spec in (("causal",), ("swa", 50), ("or", ("swa", 20), ("prefix", 40))):
+        got = OS.tables_from_selection(spec, sel, 1, 2, q_len, kv_len, bq, bk)
+        want = OB.tables(spec, 1, 2, q_len, kv_len, bq, bk)
+        for k in got:
+            assert np.array_equal(got[k], want[k]), (spec, k)
+
+
+def test_selector_under_an_all_allowing_rule_lists_exactly_the_choice():
+    # PREFIX(P >= KV_LEN) allows every pair, so each chosen block is FULL and nothing else
+    rng = np.random.default_rng(0)
+    q_len, kv_len, bq, bk = 200, 300, 64, 64
+    nqb, nkb = OB.n_blocks(q_len, bq), OB.n_blocks(kv_len, bk)
+    sel = rng.integers(-2, nkb + 2, size=(2, 1, nqb, 6))
+    tab = OS.tables_from_selection(("prefix", kv_len), sel, 2, 1, q_len, kv_len, bq, bk)
+    sets = OS.canonical_sets(sel, nkb)
+    assert tab["kv_ptr"][-1] == 0
+    for r, S in enumerate(sets):
+        got = tab["full_kv_idx"][tab["full_kv_ptr"][r]:tab["full_kv_ptr"][r + 1]]
+        assert got.tolist() == S.tolist()
+
+
+def test_selector_mask_brute_force():
+    # pair by pair: (i, j) allowed iff the rule allows it and j's block was chosen for
+    # i's query block; and the tables expand back to that matrix
+    rng = np.random.default_rng(1)
+    q_len, kv_len, bq, bk, off = 70, 90, 16, 16, 20
+    nqb, nkb = OB.n_blocks(q_len, bq), OB.n_blocks(kv_len, bk)
+    sel = rng.integers(-1, nkb + 1, size=(1, 1, nqb, 4))
+    spec = ("swa", 30)
+    sets = OS.canonical_sets(sel, nkb)
+    M = OS.selected_mask(spec, sets, 1, 0, 0, q_len, kv_len, bq, bk, off)
+    for i in range(q_len):
+        for j in range(kv_len):
+            ig = i + off
+            want = (j <= ig and ig - j < 30) and (j // bk) in set(sets[i // bq].tolist())
+            assert M[i, j] == want
+    tab = OS.tables_from_selection(spec, sel, 1, 1, q_len, kv_len, bq, bk, off)
+    hat = np.zeros_like(M)
+    for r in range(nqb):
+        for c in tab["full_kv_idx"][tab["full_kv_ptr"][r]:tab["full_kv_ptr"][r + 1]]:
+            hat[r * bq:(r + 1) * bq, c * bk:(c + 1) * bk] = True
+        for c in tab["kv_idx"][tab["kv_ptr"][r]:tab["kv_ptr"][r + 1]]:
+            sl = np.s_[r * bq:(r + 1) * bq, c * bk:(c + 1) * bk]
+            hat[sl] = M[sl]
+            assert M[sl].any() and not M[sl].all()
+    assert np.array_equal(hat, M)
+    # the q side is the transpose
+    for c in range(nkb):
+        rows = tab["q_idx"][tab["q_ptr"][c]:tab["q_ptr"][c + 1]].tolist()
+        assert rows == [r for r in range(nqb) if c in tab["kv_idx"][tab["kv_ptr"][r]:tab["kv_ptr"][r + 1]]]
+
+
+def test_work_order_is_longest_first_permutation():
+    tab = {"kv_num": np.array([1, 0, 3, 1, 2, 2, 0, 5], np.int32),
+           "full_kv_num": np.array([0, 4, 0, 0, 1, 0, 0, 0], np.int32)}
+    # two table entries of four query blocks; lengths [1, 4, 3, 1] and [3, 2, 0, 5]
+    order = OS.work_order(tab, 1, 2, 4 * 64, 64)
+    assert order.tolist() == [1, 2, 3, 0, 3, 0, 1, 2]
+
+
+def test_attention_oracle_accepts_a_pair_function():
+    # the function form of the mask gives the same result as the rule it spells out
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((1, 2, 40, 16))
+    k = rng.standard_normal((1, 1, 50, 16))
+    v = rng.standard_normal((1, 1, 50, 16))
+    O1, L1 = OA.attention(q, k, v, ("swa", 9), q_offset=10)
+    O2, L2 = OA.attention(q, k, v, lambda b, h, i, j: (j <= i) & (i - j < 9), q_offset=10)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
