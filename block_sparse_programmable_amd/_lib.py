@@ -19,7 +19,8 @@ FA_MASK_MAX_NODES = 16
 FA_S_IDENTITY, FA_S_ALIBI, FA_S_SOFTCAP, FA_S_RELPOS = 0, 1, 2, 3
 
 # names declared in include/fa.h (checked against the header by the tests)
-EXPORTS = ("fa_block_mask_sizes", "fa_create_block_mask", "fa_block_mask_slice", "fa_forward_workspace_size",
+EXPORTS = ("fa_block_mask_sizes", "fa_create_block_mask", "fa_block_mask_slice", "fa_block_mask_from_indices",
+           "fa_forward_workspace_size",
            "fa_forward", "fa_forward_paged", "fa_backward_workspace_size", "fa_backward",
            "fa_status_string", "fa_last_error_message")
 
@@ -43,7 +44,7 @@ class fa_block_mask(C.Structure):
                 ("block_q", C.c_int32), ("block_kv", C.c_int32)] + [
         (n, C.c_void_p) for n in ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr",
                                   "full_kv_idx", "q_num", "q_ptr", "q_idx", "full_q_num",
-                                  "full_q_ptr", "full_q_idx")]
+                                  "full_q_ptr", "full_q_idx", "order")]
 
 
 class fa_score_desc(C.Structure):
@@ -96,6 +97,9 @@ def load(path: str = LIB_PATH):
     lib.fa_block_mask_slice.argtypes = [C.POINTER(fa_block_mask), C.POINTER(fa_block_mask), C.c_void_p,
                                         C.c_size_t, C.c_void_p]
     lib.fa_block_mask_slice.restype = C.c_int
+    lib.fa_block_mask_from_indices.argtypes = [C.POINTER(fa_block_mask), C.c_void_p, C.c_int32, C.c_void_p,
+                                               C.c_size_t, C.c_void_p]
+    lib.fa_block_mask_from_indices.restype = C.c_int
     lib.fa_forward_workspace_size.argtypes = [C.POINTER(fa_fwd_args), C.POINTER(C.c_size_t)]
     lib.fa_forward_workspace_size.restype = C.c_int
     lib.fa_forward.argtypes = [C.POINTER(fa_fwd_args), C.c_void_p]

@@ -87,6 +87,8 @@ class BlockMask:
             num = self.tensors[f"{side}_num"][: len(ptr) - 1].cpu().numpy()   # allocated >= 1
             idx = self.tensors[f"{side}_idx"][: int(ptr[-1])].cpu().numpy()
             out[f"{side}_num"], out[f"{side}_ptr"], out[f"{side}_idx"] = num, ptr, idx
+        if "order" in self.tensors:
+            out["order"] = self.tensors["order"][: len(out["kv_ptr"]) - 1].cpu().numpy()
         return out
 
 
@@ -123,22 +125,35 @@ def block_mask_sizes(desc):
     return rows.value, cols.value, cap.value, ws.value
 
 
+def _alloc_tables(rows, cols, cap, device, q_side=True, order=False):
+    tables = {}
+    sides = (("kv", rows), ("full_kv", rows)) + ((("q", cols), ("full_q", cols)) if q_side else ())
+    for side, n in sides:
+        tables[f"{side}_num"] = torch.empty(max(n, 1), dtype=torch.int32, device=device)
+        tables[f"{side}_ptr"] = torch.empty(n + 1, dtype=torch.int32, device=device)
+        tables[f"{side}_idx"] = torch.empty(max(cap, 1), dtype=torch.int32, device=device)
+    if order:
+        tables["order"] = torch.empty(max(rows, 1), dtype=torch.int32, device=device)
+    return tables
+
+
+def _set_tables(d, tables):
+    for name in TABLE_NAMES + ("order",):
+        setattr(d, name, tables[name].data_ptr() if name in tables else None)
+
+
 def create_block_mask(mask, B, H, q_len, kv_len, block_q=128, block_kv=128, q_offset=0,
                       doc_ids: Optional[torch.Tensor] = None, device="cuda", stream=None,
-                      tables=None, workspace=None):
+                      tables=None, workspace=None, order=False):
     """Build the block tables on the GPU.  ``mask`` is a nested tuple rule
-    (see workloads); ``doc_ids`` an int32 device tensor [doc_batch, doc_len]."""
+    (see workloads); ``doc_ids`` an int32 device tensor [doc_batch, doc_len];
+    ``order`` also writes the longest-row-first work order."""
     lib = L.load()
     d, doc_ids = block_mask_desc(mask, B, H, q_len, kv_len, block_q, block_kv, q_offset, doc_ids)
     rows, cols, cap, ws = block_mask_sizes(d)
     if tables is None:
-        tables = {}
-        for side, n in (("kv", rows), ("full_kv", rows), ("q", cols), ("full_q", cols)):
-            tables[f"{side}_num"] = torch.empty(max(n, 1), dtype=torch.int32, device=device)
-            tables[f"{side}_ptr"] = torch.empty(n + 1, dtype=torch.int32, device=device)
-            tables[f"{side}_idx"] = torch.empty(max(cap, 1), dtype=torch.int32, device=device)
-    for name in TABLE_NAMES:
-        setattr(d, name, tables[name].data_ptr())
+        tables = _alloc_tables(rows, cols, cap, device, order=order)
+    _set_tables(d, tables)
     if workspace is None:
         workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
     L.check(lib.fa_create_block_mask(C.byref(d), C.c_void_p(workspace.data_ptr()),
@@ -147,7 +162,7 @@ def create_block_mask(mask, B, H, q_len, kv_len, block_q=128, block_kv=128, q_of
 
 
 def slice_block_mask(src: BlockMask, q_len, kv_len, q_offset, q_side=True, stream=None, tables=None,
-                     workspace=None):
+                     workspace=None, order=False):
     """Tables for rows [q_offset, q_offset + q_len) and keys [0, kv_len) cut out of the
     prebuilt ``src`` (fa_block_mask_slice); ``q_side=False`` writes only the kv side."""
     lib = L.load()
@@ -155,20 +170,37 @@ def slice_block_mask(src: BlockMask, q_len, kv_len, q_offset, q_side=True, strea
     d.q_len, d.kv_len, d.q_offset = int(q_len), int(kv_len), int(q_offset)
     rows, cols, cap, ws = block_mask_sizes(d)
     device = src.tensors["kv_num"].device
-    sides = (("kv", rows), ("full_kv", rows)) + ((("q", cols), ("full_q", cols)) if q_side else ())
     if tables is None:
-        tables = {}
-        for side, n in sides:
-            tables[f"{side}_num"] = torch.empty(max(n, 1), dtype=torch.int32, device=device)
-            tables[f"{side}_ptr"] = torch.empty(n + 1, dtype=torch.int32, device=device)
-            tables[f"{side}_idx"] = torch.empty(max(cap, 1), dtype=torch.int32, device=device)
-    for name in TABLE_NAMES:
-        setattr(d, name, tables[name].data_ptr() if name in tables else None)
+        tables = _alloc_tables(rows, cols, cap, device, q_side=q_side, order=order)
+    _set_tables(d, tables)
     if workspace is None:
         workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
     L.check(lib.fa_block_mask_slice(C.byref(src.desc), C.byref(d), C.c_void_p(workspace.data_ptr()),
                                     workspace.numel(), _stream(stream)))
     return BlockMask(d, tables, (src._keep[0], workspace))
+
+
+def block_mask_from_indices(sel: torch.Tensor, mask, B, H, q_len, kv_len, block_q=128, block_kv=128, q_offset=0,
+                            doc_ids: Optional[torch.Tensor] = None, stream=None, tables=None, workspace=None,
+                            order=False):
+    """Block tables from selector output (fa_block_mask_from_indices): ``sel`` is an int32
+    device tensor [B, H, NQB, k] of KV block indices per query block (values outside
+    [0, NKB) are dropped, repeats count once); ``mask`` is the rule applied inside the
+    chosen blocks."""
+    lib = L.load()
+    d, doc_ids = block_mask_desc(mask, B, H, q_len, kv_len, block_q, block_kv, q_offset, doc_ids)
+    rows, cols, cap, ws = block_mask_sizes(d)
+    if sel.dtype != torch.int32 or not sel.is_contiguous() or sel.dim() != 4 or \
+            tuple(sel.shape[:3]) != (int(B), int(H), -(-int(q_len) // int(block_q))):
+        raise ValueError("sel must be a contiguous int32 tensor [B, H, NQB, k]")
+    if tables is None:
+        tables = _alloc_tables(rows, cols, cap, sel.device, order=order)
+    _set_tables(d, tables)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=sel.device)
+    L.check(lib.fa_block_mask_from_indices(C.byref(d), C.c_void_p(sel.data_ptr()), int(sel.shape[3]),
+                                           C.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
+    return BlockMask(d, tables, (doc_ids, workspace, sel))
 
 
 def forward_args(q, k, v, block_mask: BlockMask, score="identity", softcap=0.0,

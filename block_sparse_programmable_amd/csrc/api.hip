@@ -224,10 +224,13 @@ fa_status plan_forward(const fa_fwd_args* a, FwdPlan* plan) {
   p.tab.qfnum = bm->full_q_num;
   p.tab.qfptr = bm->full_q_ptr;
   p.tab.qfidx = bm->full_q_idx;
+  p.tab.order = bm->order;
   p.tab.tB = bm->B;
   p.tab.tH = bm->H;
   p.tab.nqb = (int32_t)cdiv(a->q_len, bm->block_q);
   p.tab.nkb = (int32_t)cdiv(a->kv_len, bm->block_kv);
+  if (bm->order && p.tab.nqb > fa::kOrderMaxRows)
+    return fail(FA_ERR_UNSUPPORTED, "a work order needs at most %d query blocks", fa::kOrderMaxRows);
   p.tab.bq = bm->block_q;
   p.tab.bk = bm->block_kv;
   p.nsplit = 1;
@@ -298,6 +301,8 @@ fa_status fa_create_block_mask(fa_block_mask* bm, void* workspace, size_t ws_byt
   if (need > 0 && (!workspace || ws_bytes < need))
     return fail(FA_ERR_WORKSPACE, "builder workspace needs %zu bytes (got %zu)", need, workspace ? ws_bytes : (size_t)0);
   if (nqb > 0x7fffffff || nkb > 0x7fffffff) return fail(FA_ERR_SHAPE, "too many blocks");
+  if (bm->order && nqb > fa::kOrderMaxRows)
+    return fail(FA_ERR_UNSUPPORTED, "a work order needs at most %d query blocks", fa::kOrderMaxRows);
   fa::BuildParams p;
   p.prog = prog;
   p.doc = doc_ref(bm, prog);
@@ -327,6 +332,7 @@ fa_status fa_create_block_mask(fa_block_mask* bm, void* workspace, size_t ws_byt
   p.full_q_num = bm->full_q_num;
   p.full_q_ptr = bm->full_q_ptr;
   p.full_q_idx = bm->full_q_idx;
+  p.order = bm->order;
   hipError_t e = fa::launch_build(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, "block-mask build launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -432,6 +438,64 @@ fa_status fa_forward_paged(const fa_fwd_args* args, const fa_paged_kv* kv, fa_st
   return ok();
 }
 
+fa_status fa_block_mask_from_indices(fa_block_mask* bm, const int32_t* sel, int32_t k, void* workspace,
+                                     size_t ws_bytes, fa_stream_t stream) {
+  if (!bm) return fail(FA_ERR_NULL, "bm is NULL");
+  fa::MaskProg prog;
+  fa_status s = check_mask_geometry(bm, &prog);
+  if (s != FA_OK) return s;
+  if (!bm->kv_num || !bm->kv_ptr || !bm->kv_idx || !bm->full_kv_num || !bm->full_kv_ptr || !bm->full_kv_idx ||
+      !bm->q_num || !bm->q_ptr || !bm->q_idx || !bm->full_q_num || !bm->full_q_ptr || !bm->full_q_idx)
+    return fail(FA_ERR_NULL, "all twelve table pointers must be non-NULL");
+  const int64_t nqb = cdiv(bm->q_len, bm->block_q), nkb = cdiv(bm->kv_len, bm->block_kv);
+  const int64_t tBH = (int64_t)bm->B * bm->H;
+  if (k < 0) return fail(FA_ERR_SHAPE, "candidate count k must be >= 0 (got %d)", k);
+  if (k > 0 && tBH * nqb > 0 && !sel) return fail(FA_ERR_NULL, "sel is NULL");
+  if (tBH * nqb * nkb > 0x7fffffffLL || tBH * (nqb + nkb) > 0x7fffffffLL || tBH * nqb * (int64_t)k > (1LL << 40))
+    return fail(FA_ERR_SHAPE, "tables too large for 32-bit indices");
+  if (bm->order && nqb > fa::kOrderMaxRows)
+    return fail(FA_ERR_UNSUPPORTED, "a work order needs at most %d query blocks", fa::kOrderMaxRows);
+  const size_t need = fa::slice_workspace_bytes(tBH, nqb, nkb);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(FA_ERR_WORKSPACE, "selector tables need %zu bytes of workspace (got %zu)", need,
+                workspace ? ws_bytes : (size_t)0);
+  if (((uintptr_t)workspace & 15) != 0) return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  fa::SelectParams sp;
+  fa::BuildParams& p = sp.d;
+  p.prog = prog;
+  p.doc = doc_ref(bm, prog);
+  p.tB = (int32_t)tBH;
+  p.tH = 1;
+  p.q_len = bm->q_len;
+  p.kv_len = bm->kv_len;
+  p.q_offset = bm->q_offset;
+  p.bq = bm->block_q;
+  p.bk = bm->block_kv;
+  p.nqb = (int32_t)nqb;
+  p.nkb = (int32_t)nkb;
+  p.grid = static_cast<uint8_t*>(workspace);
+  p.qstat = p.kstat = nullptr;
+  p.kv_num = bm->kv_num;
+  p.kv_ptr = bm->kv_ptr;
+  p.kv_idx = bm->kv_idx;
+  p.full_kv_num = bm->full_kv_num;
+  p.full_kv_ptr = bm->full_kv_ptr;
+  p.full_kv_idx = bm->full_kv_idx;
+  p.q_num = bm->q_num;
+  p.q_ptr = bm->q_ptr;
+  p.q_idx = bm->q_idx;
+  p.full_q_num = bm->full_q_num;
+  p.full_q_ptr = bm->full_q_ptr;
+  p.full_q_idx = bm->full_q_idx;
+  p.order = bm->order;
+  sp.sel = sel;
+  sp.k = k;
+  sp.H = bm->H;
+  hipError_t e = fa::launch_select(sp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "selector table launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 fa_status fa_block_mask_slice(const fa_block_mask* src, fa_block_mask* dst, void* workspace, size_t ws_bytes,
                               fa_stream_t stream) {
   if (!src || !dst) return fail(FA_ERR_NULL, "src and dst must be non-NULL");
@@ -479,6 +543,8 @@ fa_status fa_block_mask_slice(const fa_block_mask* src, fa_block_mask* dst, void
   if (nq_set != 0 && nq_set != 6)
     return fail(FA_ERR_NULL, "dst q-side tables must be all set or all NULL");
   const bool qside = nq_set == 6;
+  if (dst->order && nqb > fa::kOrderMaxRows)
+    return fail(FA_ERR_UNSUPPORTED, "a work order needs at most %d query blocks", fa::kOrderMaxRows);
   const size_t need = fa::slice_workspace_bytes((int64_t)dst->B * dst->H, nqb, nkb);
   if (need > 0 && (!workspace || ws_bytes < need))
     return fail(FA_ERR_WORKSPACE, "slice workspace needs %zu bytes (got %zu)", need, workspace ? ws_bytes : (size_t)0);
@@ -510,6 +576,7 @@ fa_status fa_block_mask_slice(const fa_block_mask* src, fa_block_mask* dst, void
   p.full_q_num = qside ? dst->full_q_num : nullptr;
   p.full_q_ptr = qside ? dst->full_q_ptr : nullptr;
   p.full_q_idx = qside ? dst->full_q_idx : nullptr;
+  p.order = dst->order;
   sp.s_num[0] = src->kv_num;
   sp.s_ptr[0] = src->kv_ptr;
   sp.s_idx[0] = src->kv_idx;

@@ -267,10 +267,16 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
   __shared__ __attribute__((aligned(16))) uint8_t ks[BKM * RS];
   __shared__ __attribute__((aligned(16))) uint8_t vs[BKM * RS];
 
+  // work item: (b, h_q) and the rank-th longest query block of its table entry (the
+  // forward's order: the tables' work order when present, else descending index)
   const int nqb = p.tab.nqb;
-  const int r = blockIdx.x % nqb;
-  const int bh = blockIdx.x / nqb;   // b * Hq + h_q
+  const int nbh = p.B * p.Hq;
+  const int rank = blockIdx.x / nbh;
+  const int bh = blockIdx.x - rank * nbh;   // b * Hq + h_q
   const int b = bh / p.Hq, hq = bh - b * p.Hq, hkv = hq / p.g;
+  const int tb = p.tab.tB == 1 ? 0 : b;
+  const int th = p.tab.tH == 1 ? 0 : hq;
+  const int r = p.tab.order ? uniform(p.tab.order[(tb * p.tab.tH + th) * nqb + rank]) : nqb - 1 - rank;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, g4 = lane >> 4;
   const int q_len = (int)p.q_len, kv_len = (int)p.kv_len, bk = p.tab.bk;
   const int i = r * p.tab.bq + w * 16 + col;   // this lane's row (S^T column)
@@ -297,8 +303,6 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int tb = p.tab.tB == 1 ? 0 : b;
-  const int th = p.tab.tH == 1 ? 0 : hq;
   const int row = (tb * p.tab.tH + th) * nqb + r;
   const int nf = uniform(p.tab.fnum[row]);
   const int np = uniform(p.tab.num[row]);

@@ -871,9 +871,44 @@ __device__ void mark_row(const SliceParams& sp, int row, int lane, uint8_t* g) {
   }
 }
 
-// One workgroup: the new rows are marked into an LDS class grid, then compacted by the
+// Tables from selector output ("FlexAttention: from rules to fused kernels", sections
+// 5.2 and 6.3): the candidates of a row are range-checked, and each in-range candidate
+// block is classified under the rule (bounds, then the exact wavefront walk) and marked
+// into the class grid, which sorts the row and makes repeats collapse.
+__device__ void mark_row(const SelectParams& sp, int row, int lane, uint8_t* g) {
+  const BuildParams& p = sp.d;
+  const int bh = row / p.nqb, r = row - bh * p.nqb;
+  const int b_doc = bh / sp.H;
+  const int32_t* cand = sp.sel + (int64_t)row * sp.k;
+  for (int e0 = 0; e0 < sp.k; e0 += 64) {
+    const int e = e0 + lane;
+    const int c = e < sp.k ? cand[e] : -1;
+    const bool in = c >= 0 && c < p.nkb;
+    uint8_t cls = kEmpty;
+    bool need = in;
+    if (in && !p.prog.has_doc) {
+      const int v = classify_bounds(p, geom(p, r, c), nullptr, nullptr);
+      if (v != VU) {
+        cls = v == VT ? kFull : (v == VF ? kEmpty : kPartial);
+        need = false;
+      }
+    }
+    uint64_t m = __ballot(need);
+    while (m) {
+      const int l = __builtin_ctzll(m);
+      m &= m - 1;
+      const int cc = __builtin_amdgcn_readlane(c, l);
+      const uint8_t x = exact_block(p, b_doc, r, cc, lane, load_block_docs(p, b_doc, r, cc, lane));
+      if (lane == l) cls = x;
+    }
+    if (in && cls != kEmpty) g[c] = cls;   // repeats write the same class
+  }
+}
+
+// One workgroup: the rows are marked into an LDS class grid, then compacted by the
 // builder's own counting, prefix and scatter phases.
-__global__ __launch_bounds__(1024) void slice_small_kernel(SliceParams sp) {
+template <class MP>
+__global__ __launch_bounds__(1024) void marked_small_kernel(MP sp) {
   __shared__ __attribute__((aligned(16))) uint8_t grid_s[kSmallMaxBlocks];
   __shared__ int32_t cnt_s[2 * kSliceMaxLines];
   __shared__ int32_t pre_s[2 * kSliceMaxLines];
@@ -889,21 +924,47 @@ __global__ __launch_bounds__(1024) void slice_small_kernel(SliceParams sp) {
   compact_small(p, grid_s, cnt_s, pre_s, tot_s, cum_s);
 }
 
-// larger slices: the class grid goes to the workspace (cleared here, then marked one
-// wave per new row) and the builder's count, scan and scatter launches compact it
-__global__ __launch_bounds__(256) void slice_clear_kernel(uint4* grid, int64_t n16) {
+// larger grids: the class grid goes to the workspace (cleared here, then marked one
+// wave per row) and the builder's count, scan and scatter launches compact it
+__global__ __launch_bounds__(256) void grid_clear_kernel(uint4* grid, int64_t n16) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t < n16) grid[t] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-__global__ __launch_bounds__(256) void slice_mark_kernel(SliceParams sp) {
+template <class MP>
+__global__ __launch_bounds__(256) void marked_rows_kernel(MP sp) {
   const BuildParams& p = sp.d;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= p.tB * p.nqb) return;
   mark_row(sp, row, threadIdx.x & 63, p.grid + (int64_t)row * p.nkb);
 }
 
+// Work order: one workgroup per table group tb (rows (tb, h, r) for its tH heads, which
+// hold the same rows): query blocks ranked by descending executed-block count, ties by
+// descending index.  Every thread reads the same length at a time (LDS broadcast).
+__global__ __launch_bounds__(1024) void order_kernel(BuildParams p) {
+  __shared__ int32_t len_s[kOrderMaxRows];
+  const int64_t base = (int64_t)blockIdx.x * p.tH * p.nqb;
+  for (int r = threadIdx.x; r < p.nqb; r += 1024) len_s[r] = p.kv_num[base + r] + p.full_kv_num[base + r];
+  __syncthreads();
+  for (int r = threadIdx.x; r < p.nqb; r += 1024) {
+    const int len = len_s[r];
+    int rank = 0;
+    for (int x = 0; x < p.nqb; ++x) {
+      const int lx = len_s[x];
+      rank += (lx > len) || (lx == len && x > r);
+    }
+    for (int h = 0; h < p.tH; ++h) p.order[base + (int64_t)h * p.nqb + rank] = r;
+  }
+}
+
 inline unsigned waves_to_blocks(int64_t waves) { return (unsigned)((waves + 3) / 4); }
+
+hipError_t launch_order(const BuildParams& p, hipStream_t s) {
+  if (p.order && p.tB > 0 && p.nqb > 0) hipLaunchKernelGGL(order_kernel, dim3(p.tB), dim3(1024), 0, s, p);
+  return hipGetLastError();
+}
+
 
 }  // namespace
 
@@ -920,7 +981,7 @@ hipError_t launch_build(const BuildParams& p, hipStream_t s) {
   const int64_t expanded = (int64_t)p.tB * p.tH * (p.nqb + p.nkb);
   if (total <= kSmallMaxBlocks && lines <= kSmallMaxLines && p.tB <= kSmallMaxTB && expanded <= (1 << 20)) {
     hipLaunchKernelGGL(build_small_kernel, dim3(1), dim3(1024), 0, s, p);
-    return hipGetLastError();
+    return launch_order(p, s);
   }
   if (lines > 0 && p.prog.has_doc)
     hipLaunchKernelGGL(doc_stats_kernel, dim3(waves_to_blocks(lines)), dim3(256), 0, s, p);
@@ -929,33 +990,42 @@ hipError_t launch_build(const BuildParams& p, hipStream_t s) {
   if (lines > 0) hipLaunchKernelGGL(count_kernel, dim3(waves_to_blocks(lines)), dim3(256), 0, s, p);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, p);
   if (expanded > 0) hipLaunchKernelGGL(scatter_kernel, dim3(waves_to_blocks(expanded)), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_order(p, s);
 }
 
 size_t slice_workspace_bytes(int64_t tBH, int64_t nqb, int64_t nkb) {
   return (size_t)(tBH * nqb * nkb + 255) & ~(size_t)255;
 }
 
-hipError_t launch_slice(const SliceParams& sp, hipStream_t s) {
+namespace {
+
+template <class MP>
+hipError_t launch_marked(const MP& sp, hipStream_t s) {
   const BuildParams& p = sp.d;
   const int64_t total = (int64_t)p.tB * p.nqb * p.nkb;
   const int64_t lines = (int64_t)p.tB * (p.nqb + p.nkb);
   if (total <= kSmallMaxBlocks && lines <= kSliceMaxLines && p.tB <= kSliceMaxTB) {
-    hipLaunchKernelGGL(slice_small_kernel, dim3(1), dim3(1024), 0, s, sp);
-    return hipGetLastError();
+    hipLaunchKernelGGL(marked_small_kernel<MP>, dim3(1), dim3(1024), 0, s, sp);
+    return launch_order(p, s);
   }
   const int64_t n16 = (total + 15) / 16;   // the workspace is rounded up to 256 bytes
   const int64_t rows = (int64_t)p.tB * p.nqb;
   const int64_t out_lines = rows + (p.q_num ? (int64_t)p.tB * p.nkb : 0);
   if (n16 > 0) {
-    hipLaunchKernelGGL(slice_clear_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(grid_clear_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
                        reinterpret_cast<uint4*>(p.grid), n16);
-    hipLaunchKernelGGL(slice_mark_kernel, dim3(waves_to_blocks(rows)), dim3(256), 0, s, sp);
+    hipLaunchKernelGGL(marked_rows_kernel<MP>, dim3(waves_to_blocks(rows)), dim3(256), 0, s, sp);
   }
   if (out_lines > 0) hipLaunchKernelGGL(count_kernel, dim3(waves_to_blocks(out_lines)), dim3(256), 0, s, p);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, p);
   if (out_lines > 0) hipLaunchKernelGGL(scatter_kernel, dim3(waves_to_blocks(out_lines)), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_order(p, s);
 }
+
+}  // namespace
+
+hipError_t launch_slice(const SliceParams& sp, hipStream_t s) { return launch_marked(sp, s); }
+
+hipError_t launch_select(const SelectParams& sp, hipStream_t s) { return launch_marked(sp, s); }
 
 }  // namespace fa

@@ -50,7 +50,10 @@ struct BuildParams {
   int32_t* kstat;     // [tB][nkb][2] doc min/max over the KV block
   int32_t *kv_num, *kv_ptr, *kv_idx, *full_kv_num, *full_kv_ptr, *full_kv_idx;
   int32_t *q_num, *q_ptr, *q_idx, *full_q_num, *full_q_ptr, *full_q_idx;
+  int32_t* order;     // longest-row-first work order, or nullptr
 };
+
+constexpr int kOrderMaxRows = 4096;   // NQB limit of the work order
 
 size_t build_workspace_bytes(int64_t tB, int64_t nqb, int64_t nkb);
 hipError_t launch_build(const BuildParams& p, hipStream_t s);
@@ -71,6 +74,16 @@ struct SliceParams {
 size_t slice_workspace_bytes(int64_t tBH, int64_t nqb, int64_t nkb);
 hipError_t launch_slice(const SliceParams& p, hipStream_t s);
 
+// Tables from selector output: d as for the slice (d.grid = workspace); sel is
+// [tB = B*H][nqb][k] KV block indices; H gives the doc batch of a table entry.
+struct SelectParams {
+  BuildParams d;
+  const int32_t* sel;
+  int32_t k;
+  int32_t H;
+};
+hipError_t launch_select(const SelectParams& p, hipStream_t s);
+
 // ---------------------------------------------------------------- forward
 struct ScoreParams {
   int32_t kind;
@@ -85,6 +98,7 @@ struct TableRef {
   const int32_t *fnum, *fptr, *fidx;          // full list
   const int32_t *qnum, *qptr, *qidx;          // q side (columns): partial list
   const int32_t *qfnum, *qfptr, *qfidx;       // q side: full list
+  const int32_t* order;                       // per (b', h'): query blocks longest first, or nullptr
   int32_t tB, tH, nqb, nkb, bq, bk;
 };
 

@@ -38,8 +38,10 @@
 //   * partial blocks: the mask rule is pre-compiled on the host into a per-row key
 //     interval (intersections of causal / window / prefix) plus an optional document
 //     compare against IDs staged in LDS; other programs use the generic interpreter.
-//   * grid order: longest rows first (query block index descending), and heads
-//     grouped so that consecutive workgroups of one XCD share a KV head.
+//   * grid order: longest rows first -- by the tables' work order when they carry one
+//     ("FlexAttention: from rules to fused kernels", section 5.2: bucket query tiles by
+//     their executed blocks), else by descending query block index -- and heads grouped
+//     so that consecutive workgroups of one XCD share a KV head.
 #include "device_common.hpp"
 #include "fa_internal.hpp"
 #include "prefill_common.hpp"
@@ -80,18 +82,23 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   const int nbh = p.B * p.Hq;
   const int nqb = p.tab.nqb;
   const int Lid = blockIdx.x;
-  int bh, r;
+  int bh, rank;
   if ((nbh & 7) == 0) {
     const int per = nbh >> 3, x = Lid & 7, jj = Lid >> 3;
     bh = x * per + jj % per;
-    r = nqb - 1 - jj / per;
+    rank = jj / per;
   } else {
     bh = Lid % nbh;
-    r = nqb - 1 - Lid / nbh;
+    rank = Lid / nbh;
   }
   const int b = bh / p.Hq;
   const int hq = bh - b * p.Hq;
   const int hkv = hq / p.g;
+  const int tb = p.tab.tB == 1 ? 0 : b;
+  const int th = p.tab.tH == 1 ? 0 : hq;
+  // rank-th longest query block of this table entry: from the tables' work order when
+  // present, else by descending index (longest first for causal-like rules)
+  const int r = p.tab.order ? uniform(p.tab.order[(tb * p.tab.tH + th) * nqb + rank]) : nqb - 1 - rank;
 
   const int q_len = (int)p.q_len;
   const int kv_len = (int)p.kv_len;
@@ -116,8 +123,6 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   }
 
   // ---- block-table row
-  const int tb = p.tab.tB == 1 ? 0 : b;
-  const int th = p.tab.tH == 1 ? 0 : hq;
   const int row = (tb * p.tab.tH + th) * nqb + r;
   const int nf = uniform(p.tab.fnum[row]);
   const int np = uniform(p.tab.num[row]);

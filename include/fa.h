@@ -7,6 +7,7 @@
  *
  *   fa_create_block_mask  mask rule -> block tables (BCSR rows and their transposes)
  *   fa_block_mask_slice   rows of prebuilt tables for a shorter or offset geometry
+ *   fa_block_mask_from_indices  selector candidate lists -> block tables
  *   fa_forward            O = softmax(mask(score_mod(Q K^T * scale))) V, plus LSE
  *   fa_forward_paged      the same over a paged KV cache (short-query path)
  *   fa_backward           dQ, dK, dV of fa_forward
@@ -110,6 +111,17 @@ typedef struct {
  *   ("Kernels: turning logical sparsity into real speed", sec. 4).
  * Partial and full lists never share a block.  Entries past ptr[rows] are unspecified.
  * All twelve arrays are caller-owned device int32 buffers sized by fa_block_mask_sizes.
+ *
+ * Work order (optional; "FlexAttention: from rules to fused kernels", sec. 5.2: the
+ * row lengths of the tables are the signal for scheduling query tiles by their
+ * executed blocks; "Kernels: turning logical sparsity into real speed", sec. 1.2 and 5):
+ *   order[rows]  per table entry (b', h'), its NQB query block indices by descending
+ *                executed-block count (kv_num + full_kv_num), ties by descending index.
+ * When `order` is set, the table writers below fill it (NQB <= 4096, else
+ * FA_ERR_UNSUPPORTED) and fa_forward / fa_backward hand out query blocks longest
+ * first; when NULL, query blocks go out by descending index (the longest-first order
+ * of causal-like rules).  The order changes only which workgroup runs first, never
+ * where a result is written, so outputs are identical either way.
  * -------------------------------------------------------------------------------- */
 typedef struct {
   fa_mask_desc mask;
@@ -118,6 +130,7 @@ typedef struct {
   int32_t block_q, block_kv;        /* each 64 or 128                                   */
   int32_t *kv_num, *kv_ptr, *kv_idx, *full_kv_num, *full_kv_ptr, *full_kv_idx;
   int32_t *q_num, *q_ptr, *q_idx, *full_q_num, *full_q_ptr, *full_q_idx;
+  int32_t* order;   /* optional work order, [rows] or NULL -- see below */
 } fa_block_mask;
 
 /* Sizes for a block mask: rows = B*H*NQB (length of kv_num; kv_ptr has rows+1),
@@ -134,6 +147,26 @@ fa_status fa_block_mask_sizes(const fa_block_mask* bm, int64_t* rows, int64_t* c
  * the same tables bit for bit. */
 fa_status fa_create_block_mask(fa_block_mask* bm, void* workspace, size_t ws_bytes,
                                fa_stream_t stream);
+
+/* Block tables from selector output ("FlexAttention: from rules to fused kernels",
+ * sec. 5.2: a dynamic selector emits candidate KV blocks per query block, which are
+ * sorted and de-duplicated into each row's list; sec. 6.3: the candidates' range, order
+ * and repeats must be checked; "Kernels: turning logical sparsity into real speed",
+ * sec. 3: a repeated block would be counted twice in the softmax).
+ *
+ * `sel` is a device int32 array [B, H, NQB, k] (the table extents of *bm, k >= 0):
+ * for each table row (b', h', r) the KV block indices chosen for query block r.  A
+ * value outside [0, NKB) is dropped (padding such as -1), a repeated value counts once,
+ * and the order within a row is free.  The allowed pairs are those of bm->mask's rule
+ * inside the chosen blocks -- M(i, j) = R(i, j) and floor(j / block_kv) in S(b', h', r)
+ * -- so with whole-block selection every pair the rule allows in a chosen block takes
+ * part in the softmax (sec. 3.1 of the same page); a rule of PREFIX(P >= kv_len) allows
+ * everything.  Each chosen block is classified exactly under the rule (EMPTY blocks are
+ * left out), and all twelve arrays (and `order`, when set) are written as by
+ * fa_create_block_mask.  Selections may differ per head (H = Hq).  `workspace` as for
+ * fa_block_mask_slice.  Nothing is allocated. */
+fa_status fa_block_mask_from_indices(fa_block_mask* bm, const int32_t* sel, int32_t k, void* workspace,
+                                     size_t ws_bytes, fa_stream_t stream);
 
 /* Row slice of prebuilt tables ("FlexAttention: from rules to fused kernels", sec. 5.2:
  * build the tables once for the longest context, then for each decode step take the

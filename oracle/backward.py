@@ -50,9 +50,13 @@ def attention_grads(q, k, v, do, mask, score="identity", cap=None, slopes=None, 
     loss = torch.zeros((), dtype=torch.float64)
     for b in range(B):
         doc_row = masks.doc_row_for(doc_ids, b)
-        M = torch.as_tensor(np.broadcast_to(masks.evaluate(mask, i_np, j_np, doc_row), (q_len, kv_len)).copy())
-        empty = ~M.any(dim=1, keepdim=True)
+        if not callable(mask):
+            M = torch.as_tensor(np.broadcast_to(masks.evaluate(mask, i_np, j_np, doc_row), (q_len, kv_len)).copy())
+            empty = ~M.any(dim=1, keepdim=True)
         for h in range(Hq):
+            if callable(mask):      # an arbitrary allowed-pair function of (b, h, i, j)
+                M = torch.as_tensor(np.broadcast_to(mask(b, h, i_np, j_np), (q_len, kv_len)).copy())
+                empty = ~M.any(dim=1, keepdim=True)
             hkv = h // g
             S = (Q[b, h] @ K[b, hkv].T) * scale
             if score == "softcap":

@@ -49,7 +49,7 @@ int main(void) {
          sizeof(fa_mask_desc), sizeof(fa_block_mask), sizeof(fa_score_desc), sizeof(fa_fwd_args));
   P(fa_mask_desc, doc_ids) P(fa_mask_desc, doc_batch) P(fa_mask_desc, doc_len)
   P(fa_block_mask, B) P(fa_block_mask, q_len) P(fa_block_mask, q_offset) P(fa_block_mask, block_kv)
-  P(fa_block_mask, kv_num) P(fa_block_mask, full_q_idx)
+  P(fa_block_mask, kv_num) P(fa_block_mask, full_q_idx) P(fa_block_mask, order)
   P(fa_score_desc, softcap) P(fa_score_desc, relpos) P(fa_score_desc, relpos_radius)
   P(fa_fwd_args, lse) P(fa_fwd_args, d) P(fa_fwd_args, q_len) P(fa_fwd_args, scale)
   P(fa_fwd_args, score) P(fa_fwd_args, bm) P(fa_fwd_args, ws_bytes)
@@ -270,3 +270,36 @@ def test_slice_validation(lib):
     # malformed geometry on either side
     d = tabs(_bm(L, **dict(ok_dst, block_kv=96)), base=0x9000)
     assert lib.fa_block_mask_slice(C.byref(src), C.byref(d), None, 0, None) == L.FA_ERR_UNSUPPORTED
+
+
+def test_from_indices_and_order_validation(lib):
+    from block_sparse_programmable_amd import _lib as L
+    names = ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx",
+             "q_num", "q_ptr", "q_idx", "full_q_num", "full_q_ptr", "full_q_idx")
+
+    def tabs(d, which=names):
+        for i, n in enumerate(which):
+            setattr(d, n, 0x1000 + 0x100 * i)      # never dereferenced: every case is rejected first
+        return d
+    sel = C.c_void_p(0x80000)
+    assert lib.fa_block_mask_from_indices(None, sel, 4, None, 0, None) == L.FA_ERR_NULL
+    d = _bm(L)
+    assert lib.fa_block_mask_from_indices(C.byref(d), sel, 4, None, 0, None) == L.FA_ERR_NULL   # no tables
+    d = tabs(_bm(L))
+    assert lib.fa_block_mask_from_indices(C.byref(d), sel, -1, None, 0, None) == L.FA_ERR_SHAPE
+    assert lib.fa_block_mask_from_indices(C.byref(d), None, 4, None, 0, None) == L.FA_ERR_NULL
+    assert lib.fa_block_mask_from_indices(C.byref(d), sel, 4, None, 0, None) == L.FA_ERR_WORKSPACE
+    assert lib.fa_block_mask_from_indices(C.byref(d), sel, 4, C.c_void_p(0x20004), 1 << 20, None) == \
+        L.FA_ERR_WORKSPACE
+    d = tabs(_bm(L, mask=("swa", 0)))
+    assert lib.fa_block_mask_from_indices(C.byref(d), sel, 4, None, 0, None) == L.FA_ERR_MASK_SPEC
+    # a work order is limited to 4096 query blocks, for every writer and the forward
+    d = tabs(_bm(L, q_len=4097 * 64, kv_len=64, block_q=64, block_kv=64))
+    d.order = 0x7000
+    assert lib.fa_block_mask_from_indices(C.byref(d), sel, 4, C.c_void_p(0x20000), 1 << 30, None) == \
+        L.FA_ERR_UNSUPPORTED
+    assert lib.fa_create_block_mask(C.byref(d), C.c_void_p(0x20000), 1 << 30, None) == L.FA_ERR_UNSUPPORTED
+    a = _fwd(L, d)
+    a.q_len, a.kv_len = d.q_len, d.kv_len
+    assert lib.fa_forward(C.byref(a), None) == L.FA_ERR_UNSUPPORTED
+    assert b"work order" in lib.fa_last_error_message()

@@ -768,3 +768,16 @@ def test_attention_oracle_accepts_a_pair_function():
     O1, L1 = OA.attention(q, k, v, ("swa", 9), q_offset=10)
     O2, L2 = OA.attention(q, k, v, lambda b, h, i, j: (j <= i) & (i - j < 9), q_offset=10)
     assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_backward_oracle_accepts_a_pair_function():
+    from oracle import backward as OBW
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 2, 12, 8))
+    k = rng.standard_normal((1, 1, 15, 8))
+    v = rng.standard_normal((1, 1, 15, 8))
+    do = rng.standard_normal((1, 2, 12, 8))
+    a = OBW.attention_grads(q, k, v, do, ("swa", 5), q_offset=3)
+    b = OBW.attention_grads(q, k, v, do, lambda bb, h, i, j: (j <= i) & (i - j < 5), q_offset=3)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
