@@ -67,13 +67,21 @@ def read_traffic(kernel, workload):
         return None
 
 
-def accounting(w, tab):
-    """Executed blocks and algorithmic work of one step (tables built with B'=H'=1)."""
+def accounting(w, tab, entries=1):
+    """Executed blocks and algorithmic work of one step; ``entries`` = B' * H' of the
+    tables (1: one table row set broadcast over every (batch, head))."""
     nf = int(tab["full_kv_ptr"][-1])
     npart = int(tab["kv_ptr"][-1])
-    executed = nf + npart
     heads = w.B * w.Hq
-    acc = {"full_blocks": nf, "partial_blocks": npart, "executed_blocks_per_head": executed}
+    executed = nf + npart
+    acc = {"full_blocks": nf, "partial_blocks": npart,
+           "executed_blocks_per_head": executed if entries == 1 else None}
+    if entries > 1:
+        # per-(batch, head) tables: total executed blocks over all of them
+        lens = tab["kv_num"] + tab["full_kv_num"]
+        acc["per_entry_executed"] = lens.reshape(entries, -1).sum(axis=1).tolist()
+        acc["flop"] = int(lens.sum()) * (heads // entries) * 4 * w.block_q * w.block_kv * w.d
+        return acc
     if w.q_len == 1:
         kv_bytes = w.B * w.Hkv * executed * w.block_kv * w.d * 2 * 2
         q_bytes = w.B * w.Hq * w.q_len * w.d * 2
@@ -85,6 +93,16 @@ def accounting(w, tab):
     else:
         acc["flop"] = heads * executed * 4 * w.block_q * w.block_kv * w.d
     return acc
+
+
+def row_stats(tab):
+    """Row lengths (executed blocks per table row): mean, P50, P95, max, and the
+    full/partial split ("FlexAttention: from rules to fused kernels", section 6.3)."""
+    import numpy as np
+    lens = tab["kv_num"] + tab["full_kv_num"]
+    return {"rows": int(lens.size), "mean": float(lens.mean()), "p50": float(np.percentile(lens, 50)),
+            "p95": float(np.percentile(lens, 95)), "max": int(lens.max()),
+            "full": int(tab["full_kv_ptr"][-1]), "partial": int(tab["kv_ptr"][-1])}
 
 
 def cpu_baseline(w, aux, q, k, v, acc, budget_s):
@@ -99,7 +117,22 @@ def cpu_baseline(w, aux, q, k, v, acc, budget_s):
     except Exception:
         threads = os.cpu_count() or 1
     t0 = time.perf_counter()
-    OB.tables(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset, aux["doc_ids"])
+    mask_of = lambda h: w.mask   # noqa: E731
+    if w.selector:
+        # the selected-pair matrix is evaluated inside the attention, row chunk by chunk
+        import workloads as W
+        from oracle import selector as OS
+        sets = OS.canonical_sets(W.selector_indices(w), -(-w.kv_len // w.block_kv))
+
+        def mask_of(h):
+            def fn(b, hh, i, j):
+                rows = np.asarray(i).reshape(-1) - w.q_offset
+                M = OS.selected_mask(w.mask, sets, w.Hq, b, h, w.q_len, w.kv_len, w.block_q, w.block_kv,
+                                     w.q_offset, None, rows=rows)
+                return M[:, np.asarray(j).reshape(-1)]
+            return fn
+    else:
+        OB.tables(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset, aux["doc_ids"])
     t_tab = time.perf_counter() - t0
     kw = dict(cap=w.cap or None, slopes=aux["slopes"], table=aux["table"], radius=w.relpos_radius,
               q_offset=w.q_offset, doc_ids=aux["doc_ids"])
@@ -120,6 +153,7 @@ def cpu_baseline(w, aux, q, k, v, acc, budget_s):
     else:
         units = w.B * w.Hq
         per_unit = acc["flop"] / units
+        credited = 0.0
         kc = {}
         while done < units and t_attn < budget_s:
             b, h = divmod(done, w.Hq)
@@ -131,11 +165,15 @@ def cpu_baseline(w, aux, q, k, v, acc, budget_s):
             sl = None if aux["slopes"] is None else aux["slopes"][h:h + 1]
             tb = None if aux["table"] is None else aux["table"][h:h + 1]
             t1 = time.perf_counter()
-            OA.attention(qb, kb, vb, w.mask, w.score, cap=w.cap or None, slopes=sl, table=tb,
+            OA.attention(qb, kb, vb, mask_of(h), w.score, cap=w.cap or None, slopes=sl, table=tb,
                          radius=w.relpos_radius, q_offset=w.q_offset, doc_ids=aux["doc_ids"])
             t_attn += time.perf_counter() - t1
+            if "per_entry_executed" in acc:   # per-head tables: this head's own blocks
+                credited += acc["per_entry_executed"][done] * 4 * w.block_q * w.block_kv * w.d
+            else:
+                credited += per_unit
             done += 1
-        rate = per_unit * done / (t_attn + t_tab * done / units) / 1e12
+        rate = credited / (t_attn + t_tab * done / units) / 1e12
         unit = "TFLOP/s"
         sample = (f"{done} of {units} (batch, head) pairs, all {w.q_len} rows each, credited with "
                   f"their executed-block FLOP; block tables timed once ({t_tab:.2f} s) and prorated")
@@ -159,7 +197,19 @@ def run(args):
     sl = None if aux["slopes"] is None else torch.as_tensor(aux["slopes"]).to(dev)
     tb = None if aux["table"] is None else torch.as_tensor(aux["table"]).to(dev)
 
-    bm = fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset, docT)
+    if w.selector:
+        # selector workloads: per-head tables from the selector output, with the work order
+        selT = torch.as_tensor(W.selector_indices(w)).to(dev)
+
+        def build(tables=None, workspace=None, order=True):
+            return fa.block_mask_from_indices(selT, w.mask, w.B, w.Hq, w.q_len, w.kv_len, w.block_q,
+                                              w.block_kv, w.q_offset, docT, tables=tables,
+                                              workspace=workspace, order=order)
+    else:
+        def build(tables=None, workspace=None, order=False):
+            return fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset,
+                                        docT, tables=tables, workspace=workspace, order=order)
+    bm = build()
     tables = bm.tensors
     bws = bm._keep[1]
     out = torch.empty(w.B, w.Hq, w.q_len, w.d, dtype=torch.bfloat16, device=dev)
@@ -173,7 +223,8 @@ def run(args):
         kc, vc = W.paged_caches(w, k, v, pt_np)
         ptT = torch.as_tensor(pt_np).to(dev)
     torch.cuda.synchronize()
-    acc = accounting(w, bm.compact())
+    tab_host = bm.compact()
+    acc = accounting(w, tab_host, bm.desc.B * bm.desc.H)
 
     def fwd(b):
         if w.page_size:
@@ -184,8 +235,7 @@ def run(args):
                        relpos_radius=w.relpos_radius, out=out, lse=lse, workspace=fws)
 
     def step(ev=None, i=0):
-        b = fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset,
-                                 docT, tables=tables, workspace=bws)
+        b = build(tables=tables, workspace=bws)
         if ev is not None:
             ev[0][i].record()
         fwd(b)
@@ -222,8 +272,7 @@ def run(args):
         for i in range(args.cold_reps):
             torch.amax(flush, dim=0, out=sink[0])
             e[0][i].record()
-            b = fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset,
-                                     docT, tables=tables, workspace=bws)
+            b = build(tables=tables, workspace=bws)
             e[1][i].record()
             torch.amax(flush, dim=0, out=sink[1])
             e[2][i].record()
@@ -266,6 +315,32 @@ def run(args):
                "ms_p90": float(np.percentile(bt, 90)), "algorithmic_flop": bflop,
                "tflops": bflop / (float(np.mean(bt)) * 1e-3) / 1e12,
                "frac_bf16_peak": bflop / (float(np.mean(bt)) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+    # selector workloads: the forward over tables with and without the work order (the
+    # latter hands query blocks out by descending index), alternating, back to back, to
+    # show what the longest-first order buys
+    no_order = None
+    if w.selector:
+        bm_n = build(order=False)
+        R = max(20, K)
+        e = [[torch.cuda.Event(enable_timing=True) for _ in range(R)] for _ in range(4)]
+        for _ in range(3):
+            fwd(bm_n)
+            fwd(bm)
+        for i in range(R):
+            e[0][i].record()
+            fwd(bm_n)
+            e[1][i].record()
+            fwd(bm)
+            e[2][i].record()
+        torch.cuda.synchronize()
+        nt = [e[0][i].elapsed_time(e[1][i]) for i in range(R)]
+        ot = [e[1][i].elapsed_time(e[2][i]) for i in range(R)]
+        no_order = {"reps": R, "fwd_ms_mean": float(np.mean(nt)), "fwd_ms_p10": float(np.percentile(nt, 10)),
+                    "fwd_ms_p90": float(np.percentile(nt, 90)),
+                    "with_order_fwd_ms_mean": float(np.mean(ot)),
+                    "with_order_fwd_ms_p10": float(np.percentile(ot, 10))}
+        del bm_n
 
     # decode from tables prebuilt once for the whole context: per step, slice the query
     # block of the current position (kv side only) instead of rebuilding; the forward
@@ -330,6 +405,7 @@ def run(args):
     cfg = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "q_len": w.q_len, "kv_len": w.kv_len,
            "d": w.d, "block_q": w.block_q, "block_kv": w.block_kv, "mask": repr(w.mask),
            "score_mod": w.score, "q_offset": w.q_offset, "seed": w.seed, "page_size": w.page_size or None,
+           "selector": list(w.selector) if w.selector else None,
            "full_blocks": acc["full_blocks"], "partial_blocks": acc["partial_blocks"]}
     rec = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": K,
            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
@@ -341,6 +417,8 @@ def run(args):
            "cold_cache": cold or None,
            "backward": bwd,
            "prebuilt": pre,
+           "row_lengths": row_stats(tab_host),
+           "without_work_order": no_order,
            "kernel_source_digest": kernel_source_digest("decode" if decode else "prefill"),
            "gpu": torch.cuda.get_device_name(0),
            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}

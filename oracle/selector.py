@@ -50,10 +50,10 @@ def selected_mask(spec, sets, H_tab, b, h, q_len, kv_len, block_q, block_kv, q_o
     li = np.arange(q_len) if rows is None else np.asarray(rows, np.int64)
     M = masks.dense(spec, q_len, kv_len, q_offset, doc_row, rows=li)
     chosen = np.zeros((len(li), kv_len), dtype=bool)
+    cols = np.arange(kv_len) // block_kv
     for n, i in enumerate(li):
         S = sets[(b * H_tab + h) * nqb + int(i) // block_q]
-        for c in S:
-            chosen[n, c * block_kv:min((c + 1) * block_kv, kv_len)] = True
+        chosen[n] = np.isin(cols, S)
     return M & chosen
 
 
@@ -104,3 +104,12 @@ def work_order(tab, B_tab, H_tab, q_len, block_q):
         lens = n[g * nqb:(g + 1) * nqb]
         order[g * nqb:(g + 1) * nqb] = sorted(range(nqb), key=lambda r: (-int(lens[r]), -r))
     return order
+
+
+def row_lists(spec, sets, H_tab, b, h, r, q_len, kv_len, block_q, block_kv, q_offset=0, doc_row=None):
+    """(partial, full) KV block lists of one table row (b', h', r), from the rows of its
+    query block only (for sampled checks at sizes where whole tables are too slow)."""
+    rows = np.arange(r * block_q, min((r + 1) * block_q, q_len))
+    M = selected_mask(spec, sets, H_tab, b, h, q_len, kv_len, block_q, block_kv, q_offset, doc_row, rows=rows)
+    g = classify_dense(M, block_q, block_kv)[0]
+    return np.nonzero(g == OB.PARTIAL)[0].astype(np.int32), np.nonzero(g == OB.FULL)[0].astype(np.int32)

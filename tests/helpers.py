@@ -79,3 +79,33 @@ def oracle_forward(q, k, v, mask, score="identity", q_offset=0, doc=None, cap=No
                         table=table, radius=radius, q_offset=q_offset,
                         doc_ids=None if doc is None else np.asarray(doc), scale=scale,
                         rows=rows, heads=heads, batches=batches)
+
+
+def workload_block_mask(w, docT=None, order=False):
+    """The block tables a workload's forward runs on: built from the rule, or from the
+    workload's selector output (per-head tables) for selector workloads."""
+    import block_sparse_programmable_amd as fa
+    import workloads as W
+    if w.selector:
+        sel = torch.as_tensor(W.selector_indices(w)).cuda()
+        return fa.block_mask_from_indices(sel, w.mask, w.B, w.Hq, w.q_len, w.kv_len, w.block_q, w.block_kv,
+                                          w.q_offset, docT, order=order)
+    return fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset, docT,
+                                order=order)
+
+
+def workload_oracle_mask(w, doc_ids=None):
+    """The rule, or for selector workloads a pair function (b, h, i, j) -> bool that
+    evaluates the oracle's selected-pair matrix on the rows asked for."""
+    import workloads as W
+    from oracle import selector as OS
+    if not w.selector:
+        return w.mask
+    sets = OS.canonical_sets(W.selector_indices(w), -(-w.kv_len // w.block_kv))
+
+    def fn(b, h, i, j):
+        rows = np.asarray(i).reshape(-1) - w.q_offset
+        M = OS.selected_mask(w.mask, sets, w.Hq, b, h, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset,
+                             None if doc_ids is None else np.asarray(doc_ids)[0], rows=rows)
+        return M[:, np.asarray(j).reshape(-1)]
+    return fn

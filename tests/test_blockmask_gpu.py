@@ -78,7 +78,35 @@ def test_worked_example_n8_needs_supported_blocks():
     assert rows_part == [[0], [1], [0, 2], [1, 3]]
 
 
-@pytest.mark.parametrize("name", list(W.WORKLOADS))
+@pytest.mark.parametrize("name", [n for n in W.WORKLOADS if W.WORKLOADS[n].selector])
+def test_selector_workload_tables(name):
+    """Full-size selector workloads: every row of three heads against the oracle's
+    per-row lists, the work order of those heads, and the totals in closed form (under
+    the causal rule with equal block sizes each row keeps its diagonal block PARTIAL and
+    its other chosen blocks FULL; under a rule allowing every pair all are FULL)."""
+    from oracle import selector as OS
+    from tests.helpers import workload_block_mask
+    w = W.WORKLOADS[name]
+    bm = workload_block_mask(w, order=True)
+    torch.cuda.synchronize()
+    got = bm.compact()
+    nqb, nkb = -(-w.q_len // w.block_q), -(-w.kv_len // w.block_kv)
+    sets = OS.canonical_sets(W.selector_indices(w), nkb)
+    n_part = w.B * w.Hq * nqb if w.mask == ("causal",) else 0
+    assert w.mask == ("causal",) or w.mask == ("prefix", w.kv_len)
+    assert int(got["kv_ptr"][-1]) == n_part
+    assert int(got["full_kv_ptr"][-1]) == sum(len(x) for x in sets) - n_part
+    for h in (0, w.Hq // 2, w.Hq - 1):
+        for r in range(nqb):
+            row = h * nqb + r
+            p, f = OS.row_lists(w.mask, sets, w.Hq, 0, h, r, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset)
+            assert np.array_equal(got["kv_idx"][got["kv_ptr"][row]:got["kv_ptr"][row + 1]], p), (h, r)
+            assert np.array_equal(got["full_kv_idx"][got["full_kv_ptr"][row]:got["full_kv_ptr"][row + 1]], f), (h, r)
+        part = {k: got[k][h * nqb:(h + 1) * nqb] for k in ("kv_num", "full_kv_num")}
+        assert np.array_equal(got["order"][h * nqb:(h + 1) * nqb], OS.work_order(part, 1, 1, w.q_len, w.block_q))
+
+
+@pytest.mark.parametrize("name", [n for n in W.WORKLOADS if not W.WORKLOADS[n].selector])
 def test_workload_tables(name):
     w = W.WORKLOADS[name]
     aux = W.aux_inputs(w)

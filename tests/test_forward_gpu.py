@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import workloads as W
-from tests.helpers import compare, oracle_forward, randn_bf16, run_forward
+from tests.helpers import compare, oracle_forward, randn_bf16, run_forward, workload_block_mask, workload_oracle_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -221,7 +221,7 @@ def test_workload_full_size_sampled(name):
     aux = W.aux_inputs(w)
     q, k, v = W.qkv(w, device="cuda")
     docT = None if aux["doc_ids"] is None else torch.as_tensor(aux["doc_ids"]).cuda()
-    bm = fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset, docT)
+    bm = workload_block_mask(w, docT, order=bool(w.selector))
     sl = None if aux["slopes"] is None else torch.as_tensor(aux["slopes"]).cuda()
     tb = None if aux["table"] is None else torch.as_tensor(aux["table"]).cuda()
     if w.page_size:
@@ -253,7 +253,7 @@ def test_workload_full_size_sampled(name):
     # all indexing happens on host copies; the oracle gets the full K/V of each batch entry
     bid = bi.cuda()
     qc, kc, vc = (t.index_select(0, bid).cpu() for t in (q, k, v))
-    O, L = oracle_forward(qc, kc, vc, w.mask, w.score, w.q_offset, aux["doc_ids"],
+    O, L = oracle_forward(qc, kc, vc, workload_oracle_mask(w, aux["doc_ids"]), w.score, w.q_offset, aux["doc_ids"],
                           cap=w.cap or None, slopes=aux["slopes"], table=aux["table"],
                           radius=w.relpos_radius, rows=rows, heads=heads)
     got_o = o.index_select(0, bid).cpu()[:, hi][:, :, ri]

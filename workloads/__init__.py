@@ -4,7 +4,7 @@ This module only describes shapes and draws random inputs.  It performs none of
 the attention arithmetic: no masking, no score modification, no softmax.  Both
 the GPU path and the CPU oracle receive the exact bits drawn here.
 
-The five workloads follow the shapes the pages describe:
+The workloads follow the shapes the pages describe:
 
 * a tiny causal sliding window (the worked N=8, W=4 example of "FlexAttention:
   from rules to fused kernels", section 2.2, Fig. 1, scaled up to N=512);
@@ -17,7 +17,9 @@ The five workloads follow the shapes the pages describe:
   262,144-block grid of a 64K sequence);
 * split-KV decode with a sliding window ending at the query position
   ("FlexAttention: compiler optimization of custom attention", section 6), also
-  over a paged KV cache ("FlexAttention: from rules to fused kernels", section 5).
+  over a paged KV cache ("FlexAttention: from rules to fused kernels", section 5);
+* per-head selector output (top-k KV blocks per query block) inside a causal rule,
+  with even or long-tailed row lengths (same page, sections 5.2 and 6.3).
 
 Mask specifications are plain nested tuples, independent of any binary layout:
 ``("causal",)``, ``("swa", W)``, ``("doc",)``, ``("prefix", P)``,
@@ -59,6 +61,7 @@ class Workload:
     doc_len_range: Tuple[int, int] = (256, 2048)
     table_B: int = 1                # batch extent of the block tables (1 = broadcast)
     page_size: int = 0              # > 0: K/V live in a paged cache with this page size
+    selector: Optional[Tuple[str, float]] = None   # (row-length profile, mean kept fraction)
 
     @property
     def g(self) -> int:
@@ -92,6 +95,24 @@ WORKLOADS = {
         name="decode_paged_swa_softcap", B=64, Hq=32, Hkv=8, q_len=1, kv_len=32768, d=128,
         block_q=128, block_kv=128, mask=("swa", 4096), score="softcap", cap=30.0,
         q_offset=32767, seed=1005, aux_seed=1006, page_size=16),
+    # per-head block selection as a selector would emit it, over every pair
+    # (bidirectional: PREFIX(N) allows all keys): the same mean of 10% of the KV blocks
+    # per row, spread evenly over the rows or held by a few full rows ("FlexAttention:
+    # from rules to fused kernels", sections 5.2 and 6.3; "Kernels: turning logical
+    # sparsity into real speed", section 1.2)
+    "select_uniform": Workload(
+        name="select_uniform", B=1, Hq=32, Hkv=8, q_len=16384, kv_len=16384, d=128,
+        block_q=128, block_kv=128, mask=("prefix", 16384), score="identity",
+        seed=1007, aux_seed=1007, selector=("uniform", 0.1)),
+    "select_longtail": Workload(
+        name="select_longtail", B=1, Hq=32, Hkv=8, q_len=16384, kv_len=16384, d=128,
+        block_q=128, block_kv=128, mask=("prefix", 16384), score="identity",
+        seed=1007, aux_seed=1008, selector=("longtail", 0.1)),
+    # the same selection inside a causal rule (candidates at or before the diagonal)
+    "select_causal": Workload(
+        name="select_causal", B=1, Hq=32, Hkv=8, q_len=16384, kv_len=16384, d=128,
+        block_q=128, block_kv=128, mask=("causal",), score="identity",
+        seed=1007, aux_seed=1009, selector=("longtail", 0.1)),
 }
 
 # The N=8, W=4, 2x2-block classification case that goes with the tiny workload.
@@ -225,3 +246,40 @@ def paged_caches(w: Workload, k, v, table):
         cache.index_copy_(0, idx, src)
         out.append(cache)
     return tuple(out)
+
+
+def selector_indices(w: Workload) -> np.ndarray:
+    """Synthetic selector output int32 [B, Hq, NQB, k_max] for a selector workload:
+    for each (batch, head, query block r) the diagonal KV block (the one holding the
+    block's last row) plus distinct other candidates drawn uniformly -- earlier blocks
+    under a causal rule, any block otherwise -- padded with -1.  Row lengths: "uniform"
+    gives every row round(frac * NKB) blocks (fewer where the causal rule leaves fewer);
+    "longtail" gives a row all of its candidate blocks with probability p and 4 blocks
+    otherwise, p set so that the mean matches the uniform profile's target.  numpy seed
+    ``w.aux_seed``; this draws inputs only."""
+    kind, frac = w.selector
+    causal = w.mask == ("causal",)
+    rng = np.random.default_rng(w.aux_seed)
+    nqb = -(-w.q_len // w.block_q)
+    nkb = -(-w.kv_len // w.block_kv)
+    target = max(1, int(round(frac * nkb)))
+    small = 4
+    avg_avail = (nkb + 1) / 2.0 if causal else float(nkb)
+    p_heavy = min(1.0, max(0.0, (target - small) / (avg_avail - small)))
+    rows = []
+    for _ in range(w.B * w.Hq):
+        for r in range(nqb):
+            diag = min(nkb - 1, (min((r + 1) * w.block_q, w.q_len) - 1 + w.q_offset) // w.block_kv)
+            others = np.arange(diag) if causal else np.delete(np.arange(nkb), diag)
+            avail = len(others) + 1
+            if kind == "uniform":
+                k = min(avail, target)
+            else:
+                k = avail if rng.random() < p_heavy else min(avail, small)
+            pick = rng.choice(others, size=k - 1, replace=False) if k > 1 else np.zeros(0, np.int64)
+            rows.append(np.concatenate([[diag], pick]))
+    kmax = max(len(x) for x in rows)
+    out = np.full((len(rows), kmax), -1, dtype=np.int32)
+    for n, x in enumerate(rows):
+        out[n, :len(x)] = x
+    return out.reshape(w.B, w.Hq, nqb, kmax)
