@@ -131,14 +131,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams bp) {
   __shared__ __attribute__((aligned(16))) uint8_t gs[BQM * RS];   // dO rows
   __shared__ float lse_s[BQM], del_s[BQM];
 
+  // work item: (sub-tile, b, h_kv) fastest, then the KV block c ascending: every head's
+  // first columns go out before any head's later ones (for causal-like rules the first
+  // columns have the longest query-side lists), and consecutive (b, h_kv) spread over
+  // the XCDs
   const int nsub = p.tab.bk / 64;
   int item = blockIdx.x;
   const int sub = item % nsub;
   item /= nsub;
-  const int c = item % p.tab.nkb;
-  item /= p.tab.nkb;
-  const int hkv = item % p.Hkv;
-  const int b = item / p.Hkv;
+  const int nbh = p.B * p.Hkv;
+  const int bh = item % nbh;
+  const int c = item / nbh;
+  const int hkv = bh % p.Hkv;
+  const int b = bh / p.Hkv;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, g4 = lane >> 4;
   const int q_len = (int)p.q_len, kv_len = (int)p.kv_len, bq = p.tab.bq;
   const int key0 = c * p.tab.bk + sub * 64 + w * 16;   // first key of this wave

@@ -30,7 +30,7 @@
 //   1. doc_stats   (only with a document rule) doc-ID min/max per query/KV block
 //   2. classify    one lane per block, then the wave resolves its undecided blocks
 //   3. count       one wave per row and per column: partial/full counts (ballot+popcount)
-//   4. scan        one workgroup: exclusive prefix sums of the four count arrays
+//   4. scan        one workgroup per count array: exclusive prefix sums
 //   5. scatter     one wave per row and per column: ordered compaction (ballot+mbcnt)
 // No output position depends on an atomic or on scheduling order (the single-workgroup
 // path collects undecided blocks in an LDS list whose order does not matter), so the
@@ -376,40 +376,42 @@ __global__ __launch_bounds__(256) void count_kernel(BuildParams p) {
   }
 }
 
-// single workgroup: exclusive scans of the four count arrays
+// exclusive scans of the four count arrays, one workgroup per array (blockIdx.x), each
+// thread taking four consecutive counts per pass (DPP wave scans, wave totals in LDS)
 __global__ __launch_bounds__(1024) void scan_kernel(BuildParams p) {
-  __shared__ int32_t warp_sums[16];
-  __shared__ int32_t carry_s;
+  __shared__ int32_t wave_sums[16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int which = 0; which < 4; ++which) {
-    const int32_t* num = which == 0 ? p.kv_num : which == 1 ? p.full_kv_num : which == 2 ? p.q_num : p.full_q_num;
-    int32_t* ptr = which == 0 ? p.kv_ptr : which == 1 ? p.full_kv_ptr : which == 2 ? p.q_ptr : p.full_q_ptr;
-    const int64_t n = (which < 2) ? (int64_t)p.tB * p.tH * p.nqb : (int64_t)p.tB * p.tH * p.nkb;
-    if (num == nullptr) continue;   // query side not requested (kernel argument: uniform)
-    if (tid == 0) carry_s = 0;
+  const int which = blockIdx.x;
+  const int32_t* num = which == 0 ? p.kv_num : which == 1 ? p.full_kv_num : which == 2 ? p.q_num : p.full_q_num;
+  int32_t* ptr = which == 0 ? p.kv_ptr : which == 1 ? p.full_kv_ptr : which == 2 ? p.q_ptr : p.full_q_ptr;
+  if (num == nullptr) return;   // query side not requested (kernel argument: uniform)
+  const int64_t n = (which < 2) ? (int64_t)p.tB * p.tH * p.nqb : (int64_t)p.tB * p.tH * p.nkb;
+  int carry = 0;
+  for (int64_t base = 0; base < n; base += 4096) {
+    const int64_t x0 = base + 4 * (int64_t)tid;
+    int v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = x0 + e < n ? num[x0 + e] : 0;
+    const int t = v[0] + v[1] + v[2] + v[3];
+    const int excl = __ockl_wfscan_add_i32(t, false);
+    if (lane == 63) wave_sums[wv] = excl + t;
     __syncthreads();
-    for (int64_t base = 0; base < n; base += 1024) {
-      const int64_t x = base + tid;
-      const int v = x < n ? num[x] : 0;
-      // inclusive scan within the wave
-      int s = v;
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(s, off);
-        if (lane >= off) s += y;
-      }
-      if (lane == 63) warp_sums[wv] = s;
-      __syncthreads();
-      int wprefix = 0;
-      for (int q = 0; q < wv; ++q) wprefix += warp_sums[q];
-      const int carry = carry_s;
-      if (x < n) ptr[x] = carry + wprefix + s - v;
-      __syncthreads();
-      if (tid == 1023) carry_s = carry + wprefix + s;
-      __syncthreads();
+    int wprefix = 0, total = 0;
+    for (int q = 0; q < 16; ++q) {
+      const int ws = wave_sums[q];
+      wprefix += q < wv ? ws : 0;
+      total += ws;
     }
-    if (tid == 0) ptr[n] = carry_s;
-    __syncthreads();
+    int run = carry + wprefix + excl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (x0 + e < n) ptr[x0 + e] = run;
+      run += v[e];
+    }
+    carry += total;
+    __syncthreads();   // wave_sums is rewritten by the next pass
   }
+  if (tid == 0) ptr[n] = carry;
 }
 
 // ordered compaction, one wave per (tb, h, row) and per (tb, h, column)
@@ -988,7 +990,7 @@ hipError_t launch_build(const BuildParams& p, hipStream_t s) {
   if (total > 0)
     hipLaunchKernelGGL(classify_kernel, dim3(waves_to_blocks((total + kClassifyPerWave - 1) / kClassifyPerWave)), dim3(256), 0, s, p);
   if (lines > 0) hipLaunchKernelGGL(count_kernel, dim3(waves_to_blocks(lines)), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, p);
+  hipLaunchKernelGGL(scan_kernel, dim3(4), dim3(1024), 0, s, p);
   if (expanded > 0) hipLaunchKernelGGL(scatter_kernel, dim3(waves_to_blocks(expanded)), dim3(256), 0, s, p);
   return launch_order(p, s);
 }
@@ -1017,7 +1019,7 @@ hipError_t launch_marked(const MP& sp, hipStream_t s) {
     hipLaunchKernelGGL(marked_rows_kernel<MP>, dim3(waves_to_blocks(rows)), dim3(256), 0, s, sp);
   }
   if (out_lines > 0) hipLaunchKernelGGL(count_kernel, dim3(waves_to_blocks(out_lines)), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, p);
+  hipLaunchKernelGGL(scan_kernel, dim3(4), dim3(1024), 0, s, p);
   if (out_lines > 0) hipLaunchKernelGGL(scatter_kernel, dim3(waves_to_blocks(out_lines)), dim3(256), 0, s, p);
   return launch_order(p, s);
 }
