@@ -419,7 +419,8 @@ fa_status fa_forward_paged(const fa_fwd_args* args, const fa_paged_kv* kv, fa_st
       return fail(FA_ERR_SHAPE, "num_pages must be in [1, 2^31 - 1]");
     if (args->q_len > 0 && !plan.decode)
       return fail(FA_ERR_UNSUPPORTED, "a paged KV cache is read by the short-query path only: "
-                  "(Hq/Hkv) * q_len <= 16, one query block and block_kv == 128");
+                  "(Hq/Hkv) * q_len <= 16, one query block, block_kv == 128, and tables shared by the "
+                  "query heads of a KV head (H = 1, or Hq == Hkv)");
     plan.p.pt = kv->page_table;
     plan.p.pt_stride = kv->pt_stride;
     plan.p.page_shift = __builtin_ctz((unsigned)ps);

@@ -451,8 +451,11 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
 
 }  // namespace
 
+// The g query heads of a KV head share one walk over one table row, so their rows must
+// be one row: tables broadcast over heads (H' = 1) or one query head per KV head.
 bool decode_eligible(const FwdParams& p) {
-  return p.tab.nqb == 1 && p.tab.bk == DKT && (int64_t)p.g * p.q_len <= kDecCols && p.q_len >= 1;
+  return p.tab.nqb == 1 && p.tab.bk == DKT && (int64_t)p.g * p.q_len <= kDecCols && p.q_len >= 1 &&
+         (p.tab.tH == 1 || p.g == 1);
 }
 
 // splits per (b, h_kv): enough units for every wave slot (kDecWaves waves per CU, one

@@ -229,9 +229,10 @@ typedef struct {
  * A row with no allowed key gets O = 0 and LSE = -inf.
  * bm must have been built for the same q_len, kv_len (and B/H extents compatible
  * with B and Hq); q_offset is taken from bm.
- * Short queries (one query block, (Hq/Hkv) * q_len <= 16, block_kv == 128) take a
- * split-KV path that needs `workspace` of fa_forward_workspace_size bytes; every other
- * shape needs none (workspace may then be NULL).
+ * Short queries (one query block, (Hq/Hkv) * q_len <= 16, block_kv == 128, and tables
+ * whose rows the query heads of a KV head share: H = 1, or Hq == Hkv) take a split-KV
+ * path that needs `workspace` of fa_forward_workspace_size bytes; every other shape
+ * (per-head tables under GQA included) needs none (workspace may then be NULL).
  * -------------------------------------------------------------------------------- */
 typedef struct {
   const void* q;
@@ -272,7 +273,7 @@ fa_status fa_forward(const fa_fwd_args* args, fa_stream_t stream);
  * contiguous page_size x d slab per page and KV head), and args->kv_len is the
  * logical KV length.  Only the short-query split-KV path is paged: the shape must
  * satisfy the conditions stated for it above ((Hq/Hkv) * q_len <= 16, one query
- * block, block_kv == 128), otherwise FA_ERR_UNSUPPORTED.  The workspace is the one
+ * block, block_kv == 128, head-shared tables), otherwise FA_ERR_UNSUPPORTED.  The workspace is the one
  * fa_forward_workspace_size reports for `args`.  Results equal fa_forward on the
  * logical (gathered) K and V bit for bit.
  * -------------------------------------------------------------------------------- */

@@ -303,3 +303,18 @@ def test_from_indices_and_order_validation(lib):
     a.q_len, a.kv_len = d.q_len, d.kv_len
     assert lib.fa_forward(C.byref(a), None) == L.FA_ERR_UNSUPPORTED
     assert b"work order" in lib.fa_last_error_message()
+
+
+def test_paged_needs_head_shared_tables(lib):
+    from block_sparse_programmable_amd import _lib as L
+    # per-head tables (H = Hq = 4) under GQA (Hkv = 2): the split-KV path cannot take
+    # them, and it is the only paged path
+    bm = _bm(L, H=4, q_len=1, kv_len=1000, q_offset=999)
+    for i, n in enumerate(("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx")):
+        setattr(bm, n, 0x1000 + 0x100 * i)
+    a = _fwd(L, bm)
+    a.q_len, a.kv_len = 1, 1000
+    kv = L.fa_paged_kv()
+    kv.page_table, kv.pt_stride, kv.page_size, kv.num_pages = 0x5000, 63, 16, 1000
+    assert lib.fa_forward_paged(C.byref(a), C.byref(kv), None) == L.FA_ERR_UNSUPPORTED
+    assert b"shared by the query heads" in lib.fa_last_error_message()

@@ -161,3 +161,37 @@ def test_order_on_causal_tables_changes_nothing():
         b = fa.forward(q, k, v, fa.create_block_mask(spec, 1, 1, 1000, 1000, 128, 128))
         torch.cuda.synchronize()
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), spec
+
+
+def test_decode_over_per_head_tables():
+    """One query per request under GQA with per-head selections: the query heads of a KV
+    head walk different rows, so the forward takes the per-head path (not the split-KV
+    path that shares one row per KV head) and matches the oracle; a paged cache, which
+    only the split-KV path reads, is refused."""
+    import block_sparse_programmable_amd as fa
+    B, Hq, Hkv, d, L, bq, bk, k = 2, 8, 2, 128, 1500, 128, 128, 4
+    nkb = OB.n_blocks(L, bk)
+    rng = np.random.default_rng(9)
+    sel = rng.integers(-1, nkb, size=(B, Hq, 1, k)).astype(np.int32)
+    t = L - 1
+    q = randn_bf16((B, Hq, 1, d), 61).cuda()
+    kk = randn_bf16((B, Hkv, L, d), 62).cuda()
+    v = randn_bf16((B, Hkv, L, d), 63).cuda()
+    bm = fa.block_mask_from_indices(torch.as_tensor(sel).cuda(), ("causal",), B, Hq, 1, L, bq, bk, t)
+    o, lse = fa.forward(q, kk, v, bm, score="softcap", softcap=30.0)
+    torch.cuda.synchronize()
+    fn = selected_fn(("causal",), sel, B, Hq, 1, L, bq, bk, t)
+    O, Lo = oracle_forward(q, kk, v, fn, "softcap", q_offset=t, cap=30.0)
+    compare(o, lse, O, Lo, "decode over per-head selector tables")
+    # the same tables with MHA (one query head per KV head) stay on the split-KV path
+    kk2 = randn_bf16((B, Hq, L, d), 64).cuda()
+    v2 = randn_bf16((B, Hq, L, d), 65).cuda()
+    o2, lse2 = fa.forward(q, kk2, v2, bm, score="softcap", softcap=30.0)
+    torch.cuda.synchronize()
+    O2, L2 = oracle_forward(q, kk2, v2, fn, "softcap", q_offset=t, cap=30.0)
+    compare(o2, lse2, O2, L2, "MHA decode over per-head selector tables")
+    pages = B * nkb * 8                     # 16-key pages covering every request
+    pt = torch.arange(pages, dtype=torch.int32, device="cuda").reshape(B, -1)
+    cache = torch.zeros(pages, Hkv, 16, d, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FAError):
+        fa.forward_paged(q, cache, cache, pt, L, bm)
