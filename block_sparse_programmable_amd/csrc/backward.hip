@@ -88,11 +88,15 @@ template <int SCORE>
 __device__ __forceinline__ void grad_elem(float s, float dp, float lse2, float delta, bool ok,
                                           const ScoreCtx& sc, float scale, int ig, int j, float& pv,
                                           float& ds) {
-  const float t = score_log2<SCORE>(s, sc, ig, j);
-  float dmod = scale;
+  float t, dmod = scale;
   if constexpr (SCORE == FA_S_SOFTCAP) {
-    const float th = t / sc.cap2;   // tanh of the scaled score over the cap
-    dmod = scale * (1.f - th * th);
+    // tanh of the scaled score over the cap, 1 - 2 / (e^{2x} + 1), as in score_log2,
+    // kept for the derivative scale * (1 - tanh^2)
+    const float th = __builtin_fmaf(-2.f, fast_rcp(fast_exp2(s * sc.capk) + 1.f), 1.f);
+    t = sc.cap2 * th;
+    dmod = scale * __builtin_fmaf(-th, th, 1.f);
+  } else {
+    t = score_log2<SCORE>(s, sc, ig, j);
   }
   pv = ok ? fast_exp2(t - lse2) : 0.f;
   ds = ok ? pv * (dp - delta) * dmod : 0.f;
