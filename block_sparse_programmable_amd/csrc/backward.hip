@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams bp) {
 
 // ---- dQ: one workgroup per (b, h_q, query block), NW waves x 16 rows
 template <int D, int SCORE, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
+__global__ __launch_bounds__(NW * 64, NW / 2) void bwd_dq_kernel(BwdParams bp) {
   const FwdParams& p = bp.f;
   constexpr int NT = NW * 64;
   constexpr int RS = Pitch<D>::RS;

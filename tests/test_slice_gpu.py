@@ -181,3 +181,18 @@ def test_decode_forward_over_sliced_tables(spec):
         assert torch.equal(o, o2) and torch.equal(lse, lse2), f"{spec} t={t}: slice and rebuild differ"
         O, Lo = oracle_forward(q, k, v, spec, "softcap", t, doc if tB > 1 else None, cap=30.0)
         compare(o, lse, O, Lo, f"{spec} decode t={t} over sliced tables")
+
+
+def test_slice_writes_the_work_order():
+    """A slice asked for the work order writes the order of its own (new) rows."""
+    import block_sparse_programmable_amd as fa
+    from oracle import selector as OS
+    L, bq, bk = 1500, 64, 64
+    bm = fa.create_block_mask(("swa", 400), 1, 2, L, L, bq, bk)
+    for q_len, kv_len, q_off in ((1000, 1000, 0), (320, 1400, 640), (1, 1200, 1199)):
+        s = fa.slice_block_mask(bm, q_len, kv_len, q_off, order=True)
+        torch.cuda.synchronize()
+        got = s.compact()
+        want = OB.tables(("swa", 400), 1, 2, q_len, kv_len, bq, bk, q_off)
+        assert_tables_equal(got, want, f"slice order q={q_len}")
+        assert np.array_equal(got["order"], OS.work_order(want, 1, 2, q_len, bq)), (q_len, kv_len, q_off)
