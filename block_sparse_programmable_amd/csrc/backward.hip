@@ -14,8 +14,7 @@
 // in fp32; P and dS enter the MFMAs as bf16 (round to nearest even).
 //
 // gfx950 mapping (16x16 MFMA tiles, wave64):
-//   * bwd_dkdv_kernel: one workgroup per (b, h_kv, KV block, 64-key sub-tile), a
-//     wave per 16 keys.  K and V of the wave's keys stay in registers as the B
+//   * bwd_dkdv_kernel: one workgroup per (b, h_kv, KV block), a wave per 16 keys.  K and V of the wave's keys stay in registers as the B
 //     operands of S = Q K^T and dP = dO V^T (v_mfma_f32_16x16x32_bf16); the query
 //     rows of each listed block (for every query head of the group) are staged in
 //     LDS, and dV^T += dO^T P, dK^T += Q^T dS take their A operands from transposing
@@ -123,10 +122,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams bp) {
   if (lane == 0) bp.delta[row] = acc;
 }
 
-// ---- dK, dV: one workgroup per (b, h_kv, KV block, 64-key sub-tile), 4 waves x 16 keys
-template <int D, int SCORE>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams bp) {
+// ---- dK, dV: one workgroup per (b, h_kv, KV block), NW = block_kv / 16 waves x 16 keys
+// (the whole block shares each query block's Q and dO rows staged in LDS)
+template <int D, int SCORE, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
   const FwdParams& p = bp.f;
+  constexpr int NT = NW * 64;
   constexpr int RS = Pitch<D>::RS;
   constexpr int KS = D / 32;   // k-steps of the 16x16x32 products over the head dim
   constexpr int DT = D / 16;   // 16-row tiles of dK^T and dV^T
@@ -135,14 +136,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams bp) {
   __shared__ __attribute__((aligned(16))) uint8_t gs[BQM * RS];   // dO rows
   __shared__ float lse_s[BQM], del_s[BQM];
 
-  // work item: (sub-tile, b, h_kv) fastest, then the KV block c ascending: every head's
-  // first columns go out before any head's later ones (for causal-like rules the first
-  // columns have the longest query-side lists), and consecutive (b, h_kv) spread over
-  // the XCDs
-  const int nsub = p.tab.bk / 64;
-  int item = blockIdx.x;
-  const int sub = item % nsub;
-  item /= nsub;
+  // work item: (b, h_kv) fastest, then the KV block c ascending: every head's first
+  // columns go out before any head's later ones (for causal-like rules the first columns
+  // have the longest query-side lists), and consecutive (b, h_kv) spread over the XCDs
+  const int item = blockIdx.x;
   const int nbh = p.B * p.Hkv;
   const int bh = item % nbh;
   const int c = item / nbh;
@@ -150,7 +147,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams bp) {
   const int b = bh / p.Hkv;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, g4 = lane >> 4;
   const int q_len = (int)p.q_len, kv_len = (int)p.kv_len, bq = p.tab.bq;
-  const int key0 = c * p.tab.bk + sub * 64 + w * 16;   // first key of this wave
+  const int key0 = c * p.tab.bk + w * 16;   // first key of this wave
   const int j = key0 + col;                            // this lane's key (S column)
 
   // B operands: lane holds K[j][32 t + 8 g4 .. +8] and V[j][...] (rows past kv_len are
@@ -196,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams bp) {
       l2 = ok ? p.lse[bh * q_len + i] * kLog2e : 0.f;
       dl = ok ? bp.delta[bh * q_len + i] : 0.f;
     };
-    RowStage<D, 256> sq, sg;
+    RowStage<D, NT> sq, sg;
     float nl2 = 0.f, ndl = 0.f;
     if (n_ent > 0) {
       const int r0n = block_of(0) * bq;
@@ -372,8 +369,14 @@ __global__ __launch_bounds__(NW * 64, NW / 2) void bwd_dq_kernel(BwdParams bp) {
 template <int D, int SCORE>
 hipError_t launch_bwd_score(const BwdParams& bp, hipStream_t s) {
   const FwdParams& p = bp.f;
-  const int64_t items = (int64_t)p.B * p.Hkv * p.tab.nkb * (p.tab.bk / 64);
-  if (items > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<D, SCORE>), dim3((unsigned)items), dim3(256), 0, s, bp);
+  const int64_t items = (int64_t)p.B * p.Hkv * p.tab.nkb;
+  if (items > 0) {
+    if (p.tab.bk == 128) {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, SCORE, 8>), dim3((unsigned)items), dim3(512), 0, s, bp);
+    } else {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, SCORE, 4>), dim3((unsigned)items), dim3(256), 0, s, bp);
+    }
+  }
   const int64_t qitems = (int64_t)p.B * p.Hq * p.tab.nqb;
   if (qitems > 0) {
     if (p.tab.bq == 128) {
