@@ -79,8 +79,15 @@ def accounting(w, tab, entries=1):
     if entries > 1:
         # per-(batch, head) tables: total executed blocks over all of them
         lens = tab["kv_num"] + tab["full_kv_num"]
+        total = int(lens.sum()) * (heads // entries)
         acc["per_entry_executed"] = lens.reshape(entries, -1).sum(axis=1).tolist()
-        acc["flop"] = int(lens.sum()) * (heads // entries) * 4 * w.block_q * w.block_kv * w.d
+        if w.q_len == 1:
+            # every query head reads the K and V of its own blocks (its group's KV head)
+            acc["bytes"] = (total * w.block_kv * w.d * 2 * 2 + 2 * w.B * w.Hq * w.d * 2 + w.B * w.Hq * 4
+                            + 4 * int(lens.size + lens.sum()))
+            acc["flop"] = total * w.block_kv * 4 * w.d
+        else:
+            acc["flop"] = total * 4 * w.block_q * w.block_kv * w.d
         return acc
     if w.q_len == 1:
         kv_bytes = w.B * w.Hkv * executed * w.block_kv * w.d * 2 * 2
@@ -117,18 +124,20 @@ def cpu_baseline(w, aux, q, k, v, acc, budget_s):
     except Exception:
         threads = os.cpu_count() or 1
     t0 = time.perf_counter()
-    mask_of = lambda h: w.mask   # noqa: E731
+    mask_of = lambda b, h=None: w.mask   # noqa: E731
     if w.selector:
-        # the selected-pair matrix is evaluated inside the attention, row chunk by chunk
+        # the selected-pair matrix is evaluated inside the attention, row chunk by chunk;
+        # the oracle sees a one-request (and, for prefill, one-head) slice, so the global
+        # request and head are bound here (h None: the slice holds every head)
         import workloads as W
         from oracle import selector as OS
         sets = OS.canonical_sets(W.selector_indices(w), -(-w.kv_len // w.block_kv))
 
-        def mask_of(h):
-            def fn(b, hh, i, j):
+        def mask_of(b, h=None):
+            def fn(bb, hh, i, j):
                 rows = np.asarray(i).reshape(-1) - w.q_offset
-                M = OS.selected_mask(w.mask, sets, w.Hq, b, h, w.q_len, w.kv_len, w.block_q, w.block_kv,
-                                     w.q_offset, None, rows=rows)
+                M = OS.selected_mask(w.mask, sets, w.Hq, b, hh if h is None else h, w.q_len, w.kv_len,
+                                     w.block_q, w.block_kv, w.q_offset, None, rows=rows)
                 return M[:, np.asarray(j).reshape(-1)]
             return fn
     else:
@@ -145,7 +154,7 @@ def cpu_baseline(w, aux, q, k, v, acc, budget_s):
             b = done
             qb, kb, vb = (t[b:b + 1].cpu() for t in (q, k, v))
             t1 = time.perf_counter()
-            OA.attention(qb, kb, vb, w.mask, w.score, **kw)
+            OA.attention(qb, kb, vb, mask_of(b), w.score, **kw)
             t_attn += time.perf_counter() - t1
             done += 1
         rate = per_unit * done / (t_attn + t_tab) / 1e9
@@ -165,7 +174,7 @@ def cpu_baseline(w, aux, q, k, v, acc, budget_s):
             sl = None if aux["slopes"] is None else aux["slopes"][h:h + 1]
             tb = None if aux["table"] is None else aux["table"][h:h + 1]
             t1 = time.perf_counter()
-            OA.attention(qb, kb, vb, mask_of(h), w.score, cap=w.cap or None, slopes=sl, table=tb,
+            OA.attention(qb, kb, vb, mask_of(b, h), w.score, cap=w.cap or None, slopes=sl, table=tb,
                          radius=w.relpos_radius, q_offset=w.q_offset, doc_ids=aux["doc_ids"])
             t_attn += time.perf_counter() - t1
             if "per_entry_executed" in acc:   # per-head tables: this head's own blocks
@@ -202,9 +211,11 @@ def run(args):
         selT = torch.as_tensor(W.selector_indices(w)).to(dev)
 
         def build(tables=None, workspace=None, order=True):
+            # the forward reads only the kv side; the backward leg needs the query side too
             return fa.block_mask_from_indices(selT, w.mask, w.B, w.Hq, w.q_len, w.kv_len, w.block_q,
                                               w.block_kv, w.q_offset, docT, tables=tables,
-                                              workspace=workspace, order=order)
+                                              workspace=workspace, order=order,
+                                              q_side=bool(args.backward))
     else:
         def build(tables=None, workspace=None, order=False):
             return fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset,

@@ -182,11 +182,11 @@ def slice_block_mask(src: BlockMask, q_len, kv_len, q_offset, q_side=True, strea
 
 def block_mask_from_indices(sel: torch.Tensor, mask, B, H, q_len, kv_len, block_q=128, block_kv=128, q_offset=0,
                             doc_ids: Optional[torch.Tensor] = None, stream=None, tables=None, workspace=None,
-                            order=False):
+                            order=False, q_side=True):
     """Block tables from selector output (fa_block_mask_from_indices): ``sel`` is an int32
     device tensor [B, H, NQB, k] of KV block indices per query block (values outside
     [0, NKB) are dropped, repeats count once); ``mask`` is the rule applied inside the
-    chosen blocks."""
+    chosen blocks; ``q_side=False`` writes only the kv side (enough for the forward)."""
     lib = L.load()
     d, doc_ids = block_mask_desc(mask, B, H, q_len, kv_len, block_q, block_kv, q_offset, doc_ids)
     rows, cols, cap, ws = block_mask_sizes(d)
@@ -194,7 +194,7 @@ def block_mask_from_indices(sel: torch.Tensor, mask, B, H, q_len, kv_len, block_
             tuple(sel.shape[:3]) != (int(B), int(H), -(-int(q_len) // int(block_q))):
         raise ValueError("sel must be a contiguous int32 tensor [B, H, NQB, k]")
     if tables is None:
-        tables = _alloc_tables(rows, cols, cap, sel.device, order=order)
+        tables = _alloc_tables(rows, cols, cap, sel.device, q_side=q_side, order=order)
     _set_tables(d, tables)
     if workspace is None:
         workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=sel.device)

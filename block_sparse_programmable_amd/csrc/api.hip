@@ -142,6 +142,7 @@ int num_cus_of_current_device() {
 struct FwdPlan {
   fa::FwdParams p;
   bool decode;
+  bool per_head;   // decode path in its per-head view (fa::decode_per_head)
   size_t ws;
 };
 
@@ -239,11 +240,15 @@ fa_status plan_forward(const fa_fwd_args* a, FwdPlan* plan) {
   p.pt_stride = 0;
   p.page_shift = 0;
   p.num_pages = 0;
-  plan->decode = a->q_len > 0 && fa::decode_eligible(p);
+  p.kv_group = 1;
+  fa::FwdParams v = p;
+  plan->per_head = a->q_len > 0 && !fa::decode_eligible(p) && fa::decode_per_head(v);
+  plan->decode = a->q_len > 0 && (fa::decode_eligible(p) || plan->per_head);
   plan->ws = 0;
   if (plan->decode) {
-    p.nsplit = fa::decode_splits(p, num_cus_of_current_device());
-    plan->ws = fa::decode_workspace_bytes(p, p.nsplit);
+    const fa::FwdParams& d = plan->per_head ? v : p;
+    p.nsplit = fa::decode_splits(d, num_cus_of_current_device());
+    plan->ws = fa::decode_workspace_bytes(d, p.nsplit);
   }
   return FA_OK;
 }
@@ -419,8 +424,8 @@ fa_status fa_forward_paged(const fa_fwd_args* args, const fa_paged_kv* kv, fa_st
       return fail(FA_ERR_SHAPE, "num_pages must be in [1, 2^31 - 1]");
     if (args->q_len > 0 && !plan.decode)
       return fail(FA_ERR_UNSUPPORTED, "a paged KV cache is read by the short-query path only: "
-                  "(Hq/Hkv) * q_len <= 16, one query block, block_kv == 128, and tables shared by the "
-                  "query heads of a KV head (H = 1, or Hq == Hkv)");
+                  "(Hq/Hkv) * q_len <= 16 (q_len <= 16 with per-head tables), one query block and "
+                  "block_kv == 128");
     plan.p.pt = kv->page_table;
     plan.p.pt_stride = kv->pt_stride;
     plan.p.page_shift = __builtin_ctz((unsigned)ps);
@@ -434,7 +439,9 @@ fa_status fa_forward_paged(const fa_fwd_args* args, const fa_paged_kv* kv, fa_st
   }
   if (args->q_len == 0) return ok();
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = plan.decode ? fa::launch_decode(plan.p, st) : fa::launch_prefill(plan.p, st);
+  fa::FwdParams lp = plan.p;
+  if (plan.per_head) fa::decode_per_head(lp);
+  hipError_t e = plan.decode ? fa::launch_decode(lp, st) : fa::launch_prefill(lp, st);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -445,9 +452,12 @@ fa_status fa_block_mask_from_indices(fa_block_mask* bm, const int32_t* sel, int3
   fa::MaskProg prog;
   fa_status s = check_mask_geometry(bm, &prog);
   if (s != FA_OK) return s;
-  if (!bm->kv_num || !bm->kv_ptr || !bm->kv_idx || !bm->full_kv_num || !bm->full_kv_ptr || !bm->full_kv_idx ||
-      !bm->q_num || !bm->q_ptr || !bm->q_idx || !bm->full_q_num || !bm->full_q_ptr || !bm->full_q_idx)
-    return fail(FA_ERR_NULL, "all twelve table pointers must be non-NULL");
+  if (!bm->kv_num || !bm->kv_ptr || !bm->kv_idx || !bm->full_kv_num || !bm->full_kv_ptr || !bm->full_kv_idx)
+    return fail(FA_ERR_NULL, "kv-side table pointers must be non-NULL");
+  const int nq_set = (bm->q_num != nullptr) + (bm->q_ptr != nullptr) + (bm->q_idx != nullptr) +
+                     (bm->full_q_num != nullptr) + (bm->full_q_ptr != nullptr) + (bm->full_q_idx != nullptr);
+  if (nq_set != 0 && nq_set != 6) return fail(FA_ERR_NULL, "q-side tables must be all set or all NULL");
+  const bool qside = nq_set == 6;
   const int64_t nqb = cdiv(bm->q_len, bm->block_q), nkb = cdiv(bm->kv_len, bm->block_kv);
   const int64_t tBH = (int64_t)bm->B * bm->H;
   if (k < 0) return fail(FA_ERR_SHAPE, "candidate count k must be >= 0 (got %d)", k);
@@ -482,12 +492,12 @@ fa_status fa_block_mask_from_indices(fa_block_mask* bm, const int32_t* sel, int3
   p.full_kv_num = bm->full_kv_num;
   p.full_kv_ptr = bm->full_kv_ptr;
   p.full_kv_idx = bm->full_kv_idx;
-  p.q_num = bm->q_num;
-  p.q_ptr = bm->q_ptr;
-  p.q_idx = bm->q_idx;
-  p.full_q_num = bm->full_q_num;
-  p.full_q_ptr = bm->full_q_ptr;
-  p.full_q_idx = bm->full_q_idx;
+  p.q_num = qside ? bm->q_num : nullptr;
+  p.q_ptr = qside ? bm->q_ptr : nullptr;
+  p.q_idx = qside ? bm->q_idx : nullptr;
+  p.full_q_num = qside ? bm->full_q_num : nullptr;
+  p.full_q_ptr = qside ? bm->full_q_ptr : nullptr;
+  p.full_q_idx = qside ? bm->full_q_idx : nullptr;
   p.order = bm->order;
   sp.sel = sel;
   sp.k = k;

@@ -142,7 +142,9 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
   // first K/V row of this (b, h_kv) (contiguous layout), or the request's page-table
   // row (paged layout: logical key j lives in page pt_row[j >> page_shift], row
   // (page * Hkv + h_kv) * page_size + (j & (page_size - 1)) of the cache)
-  const int64_t krow0 = (int64_t)bk_id * p.kv_len;
+  const int hkv_m = hkv / p.kv_group;            // the KV head in memory
+  const int Hkv_m = p.Hkv / p.kv_group;
+  const int64_t krow0 = ((int64_t)b * Hkv_m + hkv_m) * p.kv_len;
   // (wave-uniform, held in scalar registers so that the per-stage table read is a
   // scalar load, tracked apart from the vector-memory copies)
   const int32_t* pt_row = PAGED ? static_cast<const int32_t*>(sreg(p.pt + (int64_t)b * p.pt_stride)) : nullptr;
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
     return min(max(pg, 0), last_page);
   };
   auto row_of = [&](int jb, int pg) -> int64_t {
-    if constexpr (PAGED) return ((int64_t)pg * p.Hkv + hkv) * (pmask + 1) + (jb & pmask);
+    if constexpr (PAGED) return ((int64_t)pg * Hkv_m + hkv_m) * (pmask + 1) + (jb & pmask);
     return krow0 + jb;
   };
   const int32_t* docr = doc_row(p.doc, b);
@@ -456,6 +458,20 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdParams p) {
 bool decode_eligible(const FwdParams& p) {
   return p.tab.nqb == 1 && p.tab.bk == DKT && (int64_t)p.g * p.q_len <= kDecCols && p.q_len >= 1 &&
          (p.tab.tH == 1 || p.g == 1);
+}
+
+// Per-head tables under GQA (selector output picks blocks per query head): every query
+// head becomes a unit of its own that walks its own row and reads its group's KV head,
+// so the K/V of a group is read once per query head, as the different lists require.
+bool decode_per_head(FwdParams& p) {
+  if (p.tab.tH == 1 || p.g == 1 || p.kv_group != 1) return false;
+  FwdParams v = p;
+  v.kv_group = p.g;
+  v.Hkv = p.Hq;
+  v.g = 1;
+  if (!decode_eligible(v)) return false;
+  p = v;
+  return true;
 }
 
 // splits per (b, h_kv): enough units for every wave slot (kDecWaves waves per CU, one

@@ -124,9 +124,15 @@ struct FwdParams {
   int64_t pt_stride;
   int32_t page_shift;   // log2(page_size)
   int64_t num_pages;
+  // decode path: query heads per memory KV head of a unit head (1 normally; g in the
+  // per-head view, where every query head is a unit of its own)
+  int32_t kv_group;
 };
 
 bool decode_eligible(const FwdParams& p);
+// Turns p into the per-head view of the decode path (Hkv := Hq, g := 1, kv_group := g)
+// when the tables hold a row per query head under GQA and the view is decode-eligible.
+bool decode_per_head(FwdParams& p);
 int32_t decode_splits(const FwdParams& p, int num_cus);
 size_t decode_workspace_bytes(const FwdParams& p, int32_t nsplit);
 hipError_t launch_prefill(const FwdParams& p, hipStream_t s);

@@ -162,9 +162,10 @@ fa_status fa_create_block_mask(fa_block_mask* bm, void* workspace, size_t ws_byt
  * -- so with whole-block selection every pair the rule allows in a chosen block takes
  * part in the softmax (sec. 3.1 of the same page); a rule of PREFIX(P >= kv_len) allows
  * everything.  Each chosen block is classified exactly under the rule (EMPTY blocks are
- * left out), and all twelve arrays (and `order`, when set) are written as by
- * fa_create_block_mask.  Selections may differ per head (H = Hq).  `workspace` as for
- * fa_block_mask_slice.  Nothing is allocated. */
+ * left out), and the tables (and `order`, when set) are written as by
+ * fa_create_block_mask; the six q-side arrays may all be NULL, and are then skipped
+ * (the forward reads only the kv side; the backward needs both).  Selections may differ
+ * per head (H = Hq).  `workspace` as for fa_block_mask_slice.  Nothing is allocated. */
 fa_status fa_block_mask_from_indices(fa_block_mask* bm, const int32_t* sel, int32_t k, void* workspace,
                                      size_t ws_bytes, fa_stream_t stream);
 
@@ -229,10 +230,11 @@ typedef struct {
  * A row with no allowed key gets O = 0 and LSE = -inf.
  * bm must have been built for the same q_len, kv_len (and B/H extents compatible
  * with B and Hq); q_offset is taken from bm.
- * Short queries (one query block, (Hq/Hkv) * q_len <= 16, block_kv == 128, and tables
- * whose rows the query heads of a KV head share: H = 1, or Hq == Hkv) take a split-KV
- * path that needs `workspace` of fa_forward_workspace_size bytes; every other shape
- * (per-head tables under GQA included) needs none (workspace may then be NULL).
+ * Short queries (one query block, block_kv == 128, and (Hq/Hkv) * q_len <= 16 -- or
+ * q_len <= 16 for tables with a row per query head under GQA, whose query heads then
+ * each walk their own row) take a split-KV path that needs `workspace` of
+ * fa_forward_workspace_size bytes; every other shape needs none (workspace may then be
+ * NULL).
  * -------------------------------------------------------------------------------- */
 typedef struct {
   const void* q;
@@ -272,8 +274,7 @@ fa_status fa_forward(const fa_fwd_args* args, fa_stream_t stream);
  * args->v are the paged caches, bf16 [num_pages, Hkv, page_size, d] each (one
  * contiguous page_size x d slab per page and KV head), and args->kv_len is the
  * logical KV length.  Only the short-query split-KV path is paged: the shape must
- * satisfy the conditions stated for it above ((Hq/Hkv) * q_len <= 16, one query
- * block, block_kv == 128, head-shared tables), otherwise FA_ERR_UNSUPPORTED.  The workspace is the one
+ * satisfy the conditions stated for it above, otherwise FA_ERR_UNSUPPORTED.  The workspace is the one
  * fa_forward_workspace_size reports for `args`.  Results equal fa_forward on the
  * logical (gathered) K and V bit for bit.
  * -------------------------------------------------------------------------------- */

@@ -94,9 +94,10 @@ def workload_block_mask(w, docT=None, order=False):
                                 order=order)
 
 
-def workload_oracle_mask(w, doc_ids=None):
+def workload_oracle_mask(w, doc_ids=None, batches=None):
     """The rule, or for selector workloads a pair function (b, h, i, j) -> bool that
-    evaluates the oracle's selected-pair matrix on the rows asked for."""
+    evaluates the oracle's selected-pair matrix on the rows asked for; ``batches`` maps
+    the oracle's batch index to the workload's when it runs on a subset of requests."""
     import workloads as W
     from oracle import selector as OS
     if not w.selector:
@@ -104,6 +105,7 @@ def workload_oracle_mask(w, doc_ids=None):
     sets = OS.canonical_sets(W.selector_indices(w), -(-w.kv_len // w.block_kv))
 
     def fn(b, h, i, j):
+        b = b if batches is None else batches[b]
         rows = np.asarray(i).reshape(-1) - w.q_offset
         M = OS.selected_mask(w.mask, sets, w.Hq, b, h, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset,
                              None if doc_ids is None else np.asarray(doc_ids)[0], rows=rows)

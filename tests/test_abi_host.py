@@ -285,6 +285,8 @@ def test_from_indices_and_order_validation(lib):
     assert lib.fa_block_mask_from_indices(None, sel, 4, None, 0, None) == L.FA_ERR_NULL
     d = _bm(L)
     assert lib.fa_block_mask_from_indices(C.byref(d), sel, 4, None, 0, None) == L.FA_ERR_NULL   # no tables
+    d = tabs(_bm(L), which=names[:8])
+    assert lib.fa_block_mask_from_indices(C.byref(d), sel, 4, None, 0, None) == L.FA_ERR_NULL   # half a q side
     d = tabs(_bm(L))
     assert lib.fa_block_mask_from_indices(C.byref(d), sel, -1, None, 0, None) == L.FA_ERR_SHAPE
     assert lib.fa_block_mask_from_indices(C.byref(d), None, 4, None, 0, None) == L.FA_ERR_NULL
@@ -305,16 +307,16 @@ def test_from_indices_and_order_validation(lib):
     assert b"work order" in lib.fa_last_error_message()
 
 
-def test_paged_needs_head_shared_tables(lib):
+def test_paged_per_head_tables_short_queries_only(lib):
     from block_sparse_programmable_amd import _lib as L
-    # per-head tables (H = Hq = 4) under GQA (Hkv = 2): the split-KV path cannot take
-    # them, and it is the only paged path
-    bm = _bm(L, H=4, q_len=1, kv_len=1000, q_offset=999)
+    # per-head tables (H = Hq = 4) under GQA (Hkv = 2): each query head walks its own row,
+    # so up to 16 query rows fit the split-KV path, the only paged one; 17 do not
+    bm = _bm(L, H=4, q_len=17, kv_len=1000, q_offset=983)
     for i, n in enumerate(("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx")):
         setattr(bm, n, 0x1000 + 0x100 * i)
     a = _fwd(L, bm)
-    a.q_len, a.kv_len = 1, 1000
+    a.q_len, a.kv_len = 17, 1000
     kv = L.fa_paged_kv()
     kv.page_table, kv.pt_stride, kv.page_size, kv.num_pages = 0x5000, 63, 16, 1000
     assert lib.fa_forward_paged(C.byref(a), C.byref(kv), None) == L.FA_ERR_UNSUPPORTED
-    assert b"shared by the query heads" in lib.fa_last_error_message()
+    assert b"short-query path" in lib.fa_last_error_message()

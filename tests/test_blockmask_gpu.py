@@ -92,8 +92,12 @@ def test_selector_workload_tables(name):
     got = bm.compact()
     nqb, nkb = -(-w.q_len // w.block_q), -(-w.kv_len // w.block_kv)
     sets = OS.canonical_sets(W.selector_indices(w), nkb)
-    n_part = w.B * w.Hq * nqb if w.mask == ("causal",) else 0
-    assert w.mask == ("causal",) or w.mask == ("prefix", w.kv_len)
+    if w.q_len == w.kv_len:
+        n_part = w.B * w.Hq * nqb if w.mask == ("causal",) else 0
+        assert w.mask == ("causal",) or w.mask == ("prefix", w.kv_len)
+    else:
+        n_part = 0   # decode: the one row sees every key up to its own, all chosen blocks FULL
+        assert w.q_len == 1 and w.q_offset == w.kv_len - 1 and w.mask == ("causal",)
     assert int(got["kv_ptr"][-1]) == n_part
     assert int(got["full_kv_ptr"][-1]) == sum(len(x) for x in sets) - n_part
     for h in (0, w.Hq // 2, w.Hq - 1):

@@ -253,7 +253,8 @@ def test_workload_full_size_sampled(name):
     # all indexing happens on host copies; the oracle gets the full K/V of each batch entry
     bid = bi.cuda()
     qc, kc, vc = (t.index_select(0, bid).cpu() for t in (q, k, v))
-    O, L = oracle_forward(qc, kc, vc, workload_oracle_mask(w, aux["doc_ids"]), w.score, w.q_offset, aux["doc_ids"],
+    O, L = oracle_forward(qc, kc, vc, workload_oracle_mask(w, aux["doc_ids"], batches), w.score, w.q_offset,
+                          aux["doc_ids"],
                           cap=w.cap or None, slopes=aux["slopes"], table=aux["table"],
                           radius=w.relpos_radius, rows=rows, heads=heads)
     got_o = o.index_select(0, bid).cpu()[:, hi][:, :, ri]

@@ -67,6 +67,12 @@ def test_selector_tables_match_oracle(spec):
         want = OS.tables_from_selection(spec, sel, B, H, q_len, kv_len, bq, bk, off, d)
         ctx = f"{spec} B={B} H={H} q={q_len} kv={kv_len} {bq}x{bk} k={k} off={off}"
         assert_tables_equal(got, want, ctx)
+        import block_sparse_programmable_amd as fa
+        docT = None if d is None else torch.as_tensor(d).cuda()
+        kv_only = fa.block_mask_from_indices(torch.as_tensor(sel).cuda(), spec, B, H, q_len, kv_len, bq, bk, off,
+                                             docT, q_side=False).compact()
+        for key in ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx"):
+            assert np.array_equal(kv_only[key], want[key]), ctx + " kv side only: " + key
         assert np.array_equal(got["order"], OS.work_order(want, B, H, q_len, bq)), ctx + ": order"
 
 
@@ -165,9 +171,9 @@ def test_order_on_causal_tables_changes_nothing():
 
 def test_decode_over_per_head_tables():
     """One query per request under GQA with per-head selections: the query heads of a KV
-    head walk different rows, so the forward takes the per-head path (not the split-KV
-    path that shares one row per KV head) and matches the oracle; a paged cache, which
-    only the split-KV path reads, is refused."""
+    head walk different rows, so each becomes a split-KV unit of its own (reading its
+    group's KV head); the result matches the oracle, MHA with the same tables too, and
+    the paged cache gives the contiguous result bit for bit."""
     import block_sparse_programmable_amd as fa
     B, Hq, Hkv, d, L, bq, bk, k = 2, 8, 2, 128, 1500, 128, 128, 4
     nkb = OB.n_blocks(L, bk)
@@ -190,8 +196,16 @@ def test_decode_over_per_head_tables():
     torch.cuda.synchronize()
     O2, L2 = oracle_forward(q, kk2, v2, fn, "softcap", q_offset=t, cap=30.0)
     compare(o2, lse2, O2, L2, "MHA decode over per-head selector tables")
-    pages = B * nkb * 8                     # 16-key pages covering every request
-    pt = torch.arange(pages, dtype=torch.int32, device="cuda").reshape(B, -1)
-    cache = torch.zeros(pages, Hkv, 16, d, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(fa.FAError):
-        fa.forward_paged(q, cache, cache, pt, L, bm)
+    # paged: one random permutation of 16-key pages holding the same logical K/V
+    npg = -(-L // 16)
+    perm = torch.as_tensor(np.random.default_rng(10).permutation(B * npg).astype(np.int32))
+    pt = perm.reshape(B, npg).cuda()
+    caches = []
+    for t in (kk, v):
+        c = torch.zeros(B * npg, Hkv, 16, d, dtype=torch.bfloat16, device="cuda")
+        src = torch.nn.functional.pad(t, (0, 0, 0, npg * 16 - L)).view(B, Hkv, npg, 16, d)
+        c.index_copy_(0, perm.long().cuda(), src.permute(0, 2, 1, 3, 4).reshape(B * npg, Hkv, 16, d))
+        caches.append(c)
+    o3, lse3 = fa.forward_paged(q, caches[0], caches[1], pt, L, bm, score="softcap", softcap=30.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o) and torch.equal(lse3, lse), "paged per-head decode differs from contiguous"

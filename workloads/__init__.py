@@ -108,6 +108,12 @@ WORKLOADS = {
         name="select_longtail", B=1, Hq=32, Hkv=8, q_len=16384, kv_len=16384, d=128,
         block_q=128, block_kv=128, mask=("prefix", 16384), score="identity",
         seed=1007, aux_seed=1008, selector=("longtail", 0.1)),
+    # decode with per-head selections (32 of the 256 KV blocks per query head, the newest
+    # block always in), each query head reading its own blocks of its group's KV head
+    "decode_select": Workload(
+        name="decode_select", B=64, Hq=32, Hkv=8, q_len=1, kv_len=32768, d=128,
+        block_q=128, block_kv=128, mask=("causal",), score="softcap", cap=30.0,
+        q_offset=32767, seed=1005, aux_seed=1010, selector=("uniform", 0.125)),
     # the same selection inside a causal rule (candidates at or before the diagonal)
     "select_causal": Workload(
         name="select_causal", B=1, Hq=32, Hkv=8, q_len=16384, kv_len=16384, d=128,
