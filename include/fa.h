@@ -174,8 +174,9 @@ fa_status fa_block_mask_from_indices(fa_block_mask* bm, const int32_t* sel, int3
  * query block that holds the current position, with the rule still seeing global
  * positions; sec. 2.2: a shorter square crop is the top-left corner of the longer one).
  *
- * `src` holds tables written by fa_create_block_mask (or by this call) for its
- * geometry; only its kv side is read.  `dst` carries the new geometry -- q_len,
+ * `src` holds tables written by fa_create_block_mask, fa_block_mask_from_indices or
+ * this call for its geometry; only its kv side is read (selector tables slice exactly
+ * too: within a chosen block the allowed pairs are the rule's).  `dst` carries the new geometry -- q_len,
  * kv_len, q_offset -- with the mask rule, table extents and block sizes of src, and
  * caller-owned arrays sized by fa_block_mask_sizes(dst).  Requirements (else
  * FA_ERR_SHAPE / FA_ERR_MASK_MISMATCH):

@@ -209,3 +209,22 @@ def test_decode_over_per_head_tables():
     o3, lse3 = fa.forward_paged(q, caches[0], caches[1], pt, L, bm, score="softcap", softcap=30.0)
     torch.cuda.synchronize()
     assert torch.equal(o3, o) and torch.equal(lse3, lse), "paged per-head decode differs from contiguous"
+
+
+def test_slices_of_selector_tables():
+    """Per-head selector tables built once for a 1500-token context, sliced for decode
+    steps and a crop: each slice equals the oracle's tables for the new geometry from the
+    same candidates (the rows the slice keeps)."""
+    import block_sparse_programmable_amd as fa
+    B, H, L, bq, bk, k = 1, 4, 1500, 128, 64, 6
+    nqb, nkb = OB.n_blocks(L, bq), OB.n_blocks(L, bk)
+    sel = random_selection(B, H, nqb, nkb, k, seed=21)
+    spec = ("causal",)
+    src = fa.block_mask_from_indices(torch.as_tensor(sel).cuda(), spec, B, H, L, L, bq, bk)
+    for q_len, kv_len, q_off in ((1, 1001, 1000), (2, 1500, 1498), (1, 1, 0), (640, 1200, 0), (256, 1500, 1024)):
+        s = fa.slice_block_mask(src, q_len, kv_len, q_off)
+        torch.cuda.synchronize()
+        r0 = q_off // bq
+        sub = sel[:, :, r0:r0 + OB.n_blocks(q_len, bq)]
+        want = OS.tables_from_selection(spec, sub, B, H, q_len, kv_len, bq, bk, q_off)
+        assert_tables_equal(s.compact(), want, f"selector slice q={q_len} kv={kv_len} off={q_off}")
