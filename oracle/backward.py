@@ -10,8 +10,9 @@ softmax, weighted sum of V) for the scalar loss sum(O * dO).  A row with no allo
 key has O = 0 and passes no gradient.
 
 Parity: pinned in tests/test_oracle_pins.py by central finite differences of the
-forward oracle (numpy, no autograd) on tiny inputs for every score_mod, and by
-torch's own scaled-dot-product-attention backward on a causal case.
+forward oracle (numpy, no autograd) on tiny inputs for every score_mod -- of Q, K, V
+and of the ALiBi slopes and the relative-position table -- and by torch's own
+scaled-dot-product-attention backward on a causal case.
 """
 from __future__ import annotations
 
@@ -30,14 +31,18 @@ def _t64(x):
 
 
 def attention_grads(q, k, v, do, mask, score="identity", cap=None, slopes=None, table=None,
-                    radius=None, q_offset=0, doc_ids=None, scale=None):
+                    radius=None, q_offset=0, doc_ids=None, scale=None, param_grads=False):
     """dQ [B, Hq, q_len, d], dK and dV [B, Hkv, kv_len, d] (float64 numpy) of
-    loss = sum(O * dO), O the dense attention output."""
+    loss = sum(O * dO), O the dense attention output.  With ``param_grads`` the
+    gradient of the score_mod parameter follows: ALiBi slopes [Hq] or the relative-
+    position table [Hq, 2R+1] (None for the other kinds)."""
     import torch
     Q = _t64(q).requires_grad_(True)
     K = _t64(k).requires_grad_(True)
     V = _t64(v).requires_grad_(True)
     dO = _t64(do)
+    SL = _t64(slopes).requires_grad_(True) if score == "alibi" else None
+    TB = _t64(table).requires_grad_(True) if score == "relpos" else None
     B, Hq, q_len, d = Q.shape
     Hkv, kv_len = K.shape[1], K.shape[2]
     g = Hq // Hkv
@@ -62,11 +67,11 @@ def attention_grads(q, k, v, do, mask, score="identity", cap=None, slopes=None, 
             if score == "softcap":
                 S = cap * torch.tanh(S / cap)
             elif score == "alibi":
-                S = S + float(slopes[h]) * (j_t - i_t)
+                S = S + SL[h] * (j_t - i_t)
             elif score == "relpos":
                 R = int(radius)
                 rel = torch.as_tensor(np.clip(i_np - j_np, -R, R) + R)
-                S = S + torch.as_tensor(np.asarray(table[h], dtype=np.float64))[rel]
+                S = S + TB[h][rel]
             elif score != "identity":
                 raise ValueError(f"unknown score_mod {score!r}")
             S = S.masked_fill(~M, -math.inf)
@@ -74,4 +79,9 @@ def attention_grads(q, k, v, do, mask, score="identity", cap=None, slopes=None, 
             P = torch.softmax(S, dim=1) * M                      # ... and zero weights
             loss = loss + ((P @ V[b, hkv]) * dO[b, h]).sum()
     loss.backward()
-    return Q.grad.numpy(), K.grad.numpy(), V.grad.numpy()
+    out = (Q.grad.numpy(), K.grad.numpy(), V.grad.numpy())
+    if param_grads:
+        P = SL if SL is not None else TB
+        grad = None if P is None else (P.grad.numpy() if P.grad is not None else np.zeros(tuple(P.shape)))
+        out = out + (grad,)
+    return out

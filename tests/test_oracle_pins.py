@@ -781,3 +781,38 @@ def test_backward_oracle_accepts_a_pair_function():
     b = OBW.attention_grads(q, k, v, do, lambda bb, h, i, j: (j <= i) & (i - j < 5), q_offset=3)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("kind", ["alibi", "relpos"])
+def test_parameter_gradients_match_finite_differences(kind):
+    # gradients of the ALiBi slopes and of every relative-position table entry, against
+    # central differences of the forward oracle
+    from oracle import backward as OBW
+    rng = np.random.default_rng(13)
+    B, Hq, Hkv, ql, kl, d = 2, 2, 1, 6, 9, 3
+    q = rng.standard_normal((B, Hq, ql, d))
+    k = rng.standard_normal((B, Hkv, kl, d))
+    v = rng.standard_normal((B, Hkv, kl, d))
+    do = rng.standard_normal((B, Hq, ql, d))
+    spec = ("or", ("swa", 3), ("prefix", 2))
+    par = np.array([0.5, -0.3]) if kind == "alibi" else rng.standard_normal((Hq, 7))
+    key = "slopes" if kind == "alibi" else "table"
+    extra = {} if kind == "alibi" else {"radius": 3}
+    out = OBW.attention_grads(q, k, v, do, spec, kind, q_offset=2, param_grads=True, **{key: par}, **extra)
+    g = out[3]
+    assert g.shape == par.shape
+
+    def loss(pv):
+        O, _ = OA.attention(q, k, v, spec, kind, q_offset=2, **{key: pv}, **extra)
+        return float((O * do).sum())
+
+    h = 1e-6
+    for idx in np.ndindex(par.shape):
+        pp, pm = par.copy(), par.copy()
+        pp[idx] += h
+        pm[idx] -= h
+        fd = (loss(pp) - loss(pm)) / (2 * h)
+        assert abs(fd - g[idx]) < 1e-6 * max(1.0, abs(fd)), (kind, idx, fd, g[idx])
+    if kind == "relpos":
+        # entries no pair reaches (here none: |i - j| spans every offset) would be zero
+        assert np.abs(g).max() > 0
