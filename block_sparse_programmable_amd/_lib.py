@@ -67,7 +67,7 @@ class fa_fwd_args(C.Structure):
 class fa_bwd_args(C.Structure):
     _fields_ = [("fwd", C.POINTER(fa_fwd_args)), ("dout", C.c_void_p), ("dq", C.c_void_p),
                 ("dk", C.c_void_p), ("dv", C.c_void_p), ("workspace", C.c_void_p),
-                ("ws_bytes", C.c_size_t)]
+                ("ws_bytes", C.c_size_t), ("dslopes", C.c_void_p), ("dtable", C.c_void_p)]
 
 
 class fa_paged_kv(C.Structure):

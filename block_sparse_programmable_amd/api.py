@@ -239,9 +239,11 @@ def forward_workspace_size(args) -> int:
 
 def backward(q, k, v, out, lse, dout, block_mask: BlockMask, score="identity", softcap=0.0,
              alibi_slopes=None, relpos=None, relpos_radius=0, scale=None, dq=None, dk=None, dv=None,
-             workspace=None, stream=None):
+             workspace=None, stream=None, param_grad=False):
     """dQ [B,Hq,q_len,d], dK and dV [B,Hkv,kv_len,d] (fp32) of the forward that produced
-    out and lse, for the output gradient dout (bf16, same shape as out)."""
+    out and lse, for the output gradient dout (bf16, same shape as out).  With
+    ``param_grad`` a fourth result is the gradient of the ALiBi slopes [Hq] or of the
+    relative-position table [Hq, 2R+1] (fp32)."""
     lib = L.load()
     if dout.dtype != torch.bfloat16 or not dout.is_contiguous() or dout.shape != out.shape:
         raise ValueError("dout must be a contiguous bfloat16 tensor shaped like out")
@@ -260,6 +262,16 @@ def backward(q, k, v, out, lse, dout, block_mask: BlockMask, score="identity", s
     ba.fwd = C.pointer(a)
     ba.dout = dout.data_ptr()
     ba.dq, ba.dk, ba.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    gpar = None
+    if param_grad:
+        if score == "alibi":
+            gpar = torch.empty(q.shape[1], dtype=torch.float32, device=q.device)
+            ba.dslopes = gpar.data_ptr()
+        elif score == "relpos":
+            gpar = torch.empty((q.shape[1], 2 * int(relpos_radius) + 1), dtype=torch.float32, device=q.device)
+            ba.dtable = gpar.data_ptr()
+        else:
+            raise ValueError("param_grad needs the alibi or relpos score")
     n = C.c_size_t()
     L.check(lib.fa_backward_workspace_size(C.byref(ba), C.byref(n)))
     if n.value > 0:
@@ -268,7 +280,7 @@ def backward(q, k, v, out, lse, dout, block_mask: BlockMask, score="identity", s
         ba.workspace = workspace.data_ptr()
         ba.ws_bytes = workspace.numel() * workspace.element_size()
     L.check(lib.fa_backward(C.byref(ba), _stream(stream)))
-    return dq, dk, dv
+    return (dq, dk, dv, gpar) if param_grad else (dq, dk, dv)
 
 
 def forward_paged(q, k_cache, v_cache, page_table, kv_len, block_mask: BlockMask, score="identity",

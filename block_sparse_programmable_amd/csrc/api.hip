@@ -373,6 +373,16 @@ fa_status plan_backward(const fa_bwd_args* a, fa::BwdParams* bp, size_t* ws) {
   bp->dk = a->dk;
   bp->dv = a->dv;
   bp->delta = nullptr;
+  const int kind = a->fwd->score.kind;
+  if (a->dslopes && kind != FA_S_ALIBI)
+    return fail(FA_ERR_UNSUPPORTED, "dslopes is the gradient of ALiBi slopes; the score kind is %d", kind);
+  if (a->dtable && kind != FA_S_RELPOS)
+    return fail(FA_ERR_UNSUPPORTED, "dtable is the gradient of a relative-position table; the score kind is %d", kind);
+  if (a->dtable && a->fwd->score.relpos_radius > fa::kRelGradMaxRadius)
+    return fail(FA_ERR_UNSUPPORTED, "the position-table gradient supports radius <= %d (got %d)",
+                fa::kRelGradMaxRadius, a->fwd->score.relpos_radius);
+  bp->dslopes = a->dslopes;
+  bp->dtable = a->dtable;
   *ws = fa::backward_workspace_bytes(plan.p);
   return FA_OK;
 }

@@ -26,6 +26,9 @@
 //     dQ^T += K^T dS^T mirror the first kernel.
 //   * bwd_delta_kernel: delta = rowsum(dO * O), one wave per row.
 // Partial blocks and ragged tails apply the mask rule per element (interpreter).
+// The dQ pass also sums the score_mod parameter gradients when asked: ALiBi slopes
+// (sum of dS (j - i)) and relative-position table entries (sum of dS per offset), with
+// floating-point atomic adds (their order, and so the last bits, may vary per run).
 #include "device_common.hpp"
 #include "fa_internal.hpp"
 #include "prefill_common.hpp"
@@ -272,6 +275,9 @@ __global__ __launch_bounds__(NW * 64, NW / 2) void bwd_dq_kernel(BwdParams bp) {
   constexpr int BKM = 128;
   __shared__ __attribute__((aligned(16))) uint8_t ks[BKM * RS];
   __shared__ __attribute__((aligned(16))) uint8_t vs[BKM * RS];
+  // gradient of the position table: one bin per offset of this query head
+  constexpr int kBins = SCORE == FA_S_RELPOS ? 2 * kRelGradMaxRadius + 1 : 1;
+  __shared__ float bins_s[kBins];
 
   // work item: (b, h_q) and the rank-th longest query block of its table entry (the
   // forward's order: the tables' work order when present, else descending index)
@@ -308,6 +314,17 @@ __global__ __launch_bounds__(NW * 64, NW / 2) void bwd_dq_kernel(BwdParams bp) {
   f32x4 dq[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // score_mod parameter gradients: dL/ds' = dS / scale per pair, with ds'/d slope =
+  // j - i (ALiBi) and ds'/d table[h][clip(i - j) + R] = 1; saturated offsets collect in
+  // registers, the others in LDS bins
+  const bool want_slope = SCORE == FA_S_ALIBI && bp.dslopes != nullptr;
+  const bool want_table = SCORE == FA_S_RELPOS && bp.dtable != nullptr;
+  const int R = p.score.radius;
+  float g_slope = 0.f, g_far = 0.f, g_ahead = 0.f;
+  if (want_table) {
+    for (int x = threadIdx.x; x < 2 * R + 1; x += NT) bins_s[x] = 0.f;
+    __syncthreads();   // (kernel argument: uniform) bins clear before any add
+  }
 
   const int row = (tb * p.tab.tH + th) * nqb + r;
   const int nf = uniform(p.tab.fnum[row]);
@@ -350,6 +367,17 @@ __global__ __launch_bounds__(NW * 64, NW / 2) void bwd_dq_kernel(BwdParams bp) {
         bool ok = row_ok && jj < kv_len;
         if (part && ok) ok = mask_allowed(p.prog, ig, jj, doc_i, p.prog.has_doc ? docr[jj] : 0);
         grad_elem<SCORE>(s[rr], dp[rr], lse2, delta, ok, sc, p.scale, ig, jj, pv[rr], ds[rr]);
+        if constexpr (SCORE == FA_S_ALIBI) {
+          if (want_slope) g_slope = __builtin_fmaf(ds[rr], (float)(jj - ig), g_slope);
+        }
+        if constexpr (SCORE == FA_S_RELPOS) {
+          if (want_table && ds[rr] != 0.f) {
+            const int rel = ig - jj;
+            if (rel >= R) g_far += ds[rr];
+            else if (rel <= -R) g_ahead += ds[rr];
+            else unsafeAtomicAdd(&bins_s[rel + R], ds[rr]);
+          }
+        }
       }
       (void)pv;
       const s16x4 db = pack4(ds[0], ds[1], ds[2], ds[3]);
@@ -359,11 +387,40 @@ __global__ __launch_bounds__(NW * 64, NW / 2) void bwd_dq_kernel(BwdParams bp) {
       for (int dt = 0; dt < DT; ++dt) dq[dt] = mma_k16(tr_read(ks + toff + 32 * dt), db, dq[dt]);
     }
   }
+  // parameter gradients: wave sums, then one global add per wave (slopes) or per bin
+  const float inv_scale = 1.f / p.scale;
+  if (want_slope) {
+    for (int off = 32; off > 0; off >>= 1) g_slope += __shfl_xor(g_slope, off);
+    if ((threadIdx.x & 63) == 0) unsafeAtomicAdd(&bp.dslopes[hq], g_slope * inv_scale);
+  }
+  if (want_table) {
+    for (int off = 32; off > 0; off >>= 1) {
+      g_far += __shfl_xor(g_far, off);
+      g_ahead += __shfl_xor(g_ahead, off);
+    }
+    if ((threadIdx.x & 63) == 0) {
+      unsafeAtomicAdd(&bins_s[2 * R], g_far);
+      unsafeAtomicAdd(&bins_s[0], g_ahead);
+    }
+    __syncthreads();
+    float* gt = bp.dtable + (int64_t)hq * (2 * R + 1);
+    for (int x = threadIdx.x; x < 2 * R + 1; x += NT) {
+      const float v = bins_s[x];
+      if (v != 0.f) unsafeAtomicAdd(&gt[x], v * inv_scale);
+    }
+  }
   if (row_ok) {
     float* out = bp.dq + ((int64_t)bh * q_len + i) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(out + 16 * dt + 4 * g4) = dq[dt];
   }
+}
+
+// clears a parameter-gradient output before the dQ pass adds into it (a kernel, not a
+// memset, so the work stays an ordinary launch on the caller's stream)
+__global__ __launch_bounds__(256) void zero_kernel(float* x, int64_t n) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t < n) x[t] = 0.f;
 }
 
 template <int D, int SCORE>
@@ -378,6 +435,11 @@ hipError_t launch_bwd_score(const BwdParams& bp, hipStream_t s) {
     }
   }
   const int64_t qitems = (int64_t)p.B * p.Hq * p.tab.nqb;
+  float* pg = SCORE == FA_S_ALIBI ? bp.dslopes : (SCORE == FA_S_RELPOS ? bp.dtable : nullptr);
+  if (pg != nullptr) {
+    const int64_t n = SCORE == FA_S_ALIBI ? (int64_t)p.Hq : (int64_t)p.Hq * (2 * p.score.radius + 1);
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, pg, n);
+  }
   if (qitems > 0) {
     if (p.tab.bq == 128) {
       hipLaunchKernelGGL((bwd_dq_kernel<D, SCORE, 8>), dim3((unsigned)qitems), dim3(512), 0, s, bp);

@@ -145,7 +145,10 @@ struct BwdParams {
   float* dk;              // fp32 [B, Hkv, kv_len, d]
   float* dv;              // fp32 [B, Hkv, kv_len, d]
   float* delta;           // fp32 [B, Hq, q_len] workspace: rowsum(dO * O)
+  float* dslopes;         // fp32 [Hq]: gradient of the ALiBi slopes, or nullptr
+  float* dtable;          // fp32 [Hq, 2R+1]: gradient of the position table, or nullptr
 };
+constexpr int kRelGradMaxRadius = 1024;   // position-table gradients: bins kept in LDS
 size_t backward_workspace_bytes(const FwdParams& p);
 hipError_t launch_backward(const BwdParams& p, hipStream_t s);
 hipError_t launch_decode(const FwdParams& p, hipStream_t s);

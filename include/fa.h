@@ -294,9 +294,15 @@ fa_status fa_forward(const fa_fwd_args* args, fa_stream_t stream);
  *              accumulated); GQA heads' contributions are summed into their KV head.
  *   workspace  device buffer of fa_backward_workspace_size bytes (fp32 row sums
  *              dO . O), 256-byte aligned, contents on entry irrelevant.
- * Gradients flow to Q, K and V only (not to ALiBi slopes or the position table).
+ *   dslopes    optional fp32 [Hq] (ALiBi only, else NULL): gradient of the slopes,
+ *              sum over allowed pairs of dL/ds' (j - i), s' the modified score.
+ *   dtable     optional fp32 [Hq, 2R+1] (relative-position bias only, R <= 1024, else
+ *              NULL): gradient of the table, sum of dL/ds' over the pairs of each
+ *              clipped offset.  Both are written (cleared first, then summed with
+ *              floating-point atomic adds, so their last bits may vary run to run).
  * Rows with no allowed key contribute nothing.  Errors as for fa_forward, plus
- * FA_ERR_NULL for missing q-side tables, dout or gradient buffers.
+ * FA_ERR_NULL for missing q-side tables, dout or gradient buffers, and
+ * FA_ERR_UNSUPPORTED for a parameter gradient of another score kind.
  * -------------------------------------------------------------------------------- */
 typedef struct {
   const fa_fwd_args* fwd;
@@ -306,6 +312,8 @@ typedef struct {
   float* dv;
   void* workspace;
   size_t ws_bytes;
+  float* dslopes;
+  float* dtable;
 } fa_bwd_args;
 
 fa_status fa_backward_workspace_size(const fa_bwd_args* args, size_t* bytes);

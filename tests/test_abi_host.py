@@ -45,14 +45,16 @@ LAYOUT_C = r"""
 #include "fa.h"
 #define P(T, F) printf(#T "." #F " %zu\n", offsetof(T, F));
 int main(void) {
-  printf("fa_mask_desc %zu\nfa_block_mask %zu\nfa_score_desc %zu\nfa_fwd_args %zu\n",
-         sizeof(fa_mask_desc), sizeof(fa_block_mask), sizeof(fa_score_desc), sizeof(fa_fwd_args));
+  printf("fa_mask_desc %zu\nfa_block_mask %zu\nfa_score_desc %zu\nfa_fwd_args %zu\nfa_bwd_args %zu\n",
+         sizeof(fa_mask_desc), sizeof(fa_block_mask), sizeof(fa_score_desc), sizeof(fa_fwd_args),
+         sizeof(fa_bwd_args));
   P(fa_mask_desc, doc_ids) P(fa_mask_desc, doc_batch) P(fa_mask_desc, doc_len)
   P(fa_block_mask, B) P(fa_block_mask, q_len) P(fa_block_mask, q_offset) P(fa_block_mask, block_kv)
   P(fa_block_mask, kv_num) P(fa_block_mask, full_q_idx) P(fa_block_mask, order)
   P(fa_score_desc, softcap) P(fa_score_desc, relpos) P(fa_score_desc, relpos_radius)
   P(fa_fwd_args, lse) P(fa_fwd_args, d) P(fa_fwd_args, q_len) P(fa_fwd_args, scale)
   P(fa_fwd_args, score) P(fa_fwd_args, bm) P(fa_fwd_args, ws_bytes)
+  P(fa_bwd_args, ws_bytes) P(fa_bwd_args, dslopes) P(fa_bwd_args, dtable)
   return 0;
 }
 """
@@ -68,7 +70,7 @@ def test_struct_layout_matches_header():
         lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
     got = dict(l.rsplit(" ", 1) for l in lines if l)
     structs = {"fa_mask_desc": L.fa_mask_desc, "fa_block_mask": L.fa_block_mask,
-               "fa_score_desc": L.fa_score_desc, "fa_fwd_args": L.fa_fwd_args}
+               "fa_score_desc": L.fa_score_desc, "fa_fwd_args": L.fa_fwd_args, "fa_bwd_args": L.fa_bwd_args}
     for k, v in got.items():
         if "." in k:
             s, f = k.split(".")
@@ -207,6 +209,13 @@ def test_forward_validation(lib):
     assert lib.fa_backward(C.byref(ok), None) == L.FA_ERR_WORKSPACE
     ok.workspace, ok.ws_bytes = 0x1010, n.value
     assert lib.fa_backward(C.byref(ok), None) == L.FA_ERR_WORKSPACE    # misaligned
+    # parameter gradients: only for their own score kind, table radius <= 1024
+    assert lib.fa_backward(C.byref(Bk(dout=0x1000, dq=0x1000, dk=0x1000, dv=0x1000, dslopes=0x2000)),
+                           None) == L.FA_ERR_UNSUPPORTED                 # identity score
+    rp = _fwd(L, bm, score_kind=L.FA_S_RELPOS, score_relpos=0x3000, score_relpos_radius=2000)
+    assert lib.fa_backward(C.byref(L.fa_bwd_args(fwd=C.pointer(rp), dout=0x1000, dq=0x1000, dk=0x1000,
+                                                 dv=0x1000, dtable=0x2000)), None) == L.FA_ERR_UNSUPPORTED
+    assert b"radius" in lib.fa_last_error_message()
     bad = _fwd(L, bm, d=96)                                           # forward checks apply
     assert lib.fa_backward(C.byref(L.fa_bwd_args(fwd=C.pointer(bad), dout=0x1000, dq=0x1000, dk=0x1000,
                                                  dv=0x1000)), None) == L.FA_ERR_UNSUPPORTED

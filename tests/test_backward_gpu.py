@@ -80,3 +80,36 @@ def test_backward_documents_gqa_and_offsets():
 def test_backward_large_scores():
     run_case(1, 2, 1, 256, 256, 128, ("causal",), 128, 128, "softcap", qscale=6.0, seed=8, ctx="bwd large softcap")
     run_case(1, 2, 1, 256, 256, 128, ("causal",), 128, 128, "identity", qscale=3.0, seed=9, ctx="bwd large identity")
+
+
+@pytest.mark.parametrize("score", ["alibi", "relpos"])
+def test_parameter_gradients(score):
+    """Gradients of the ALiBi slopes and of the relative-position table (sums over all
+    allowed pairs, accumulated with atomic adds) against the autograd oracle."""
+    import block_sparse_programmable_amd as fa
+    for (B, Hq, Hkv, n, mask, bq, bk, R) in ((2, 4, 2, 300, ("causal",), 128, 64, 40),
+                                             (1, 2, 1, 400, ("or", ("swa", 50), ("prefix", 30)), 64, 128, 1024),
+                                             (1, 4, 4, 260, ("swa", 90), 64, 64, 3)):
+        q = randn_bf16((B, Hq, n, 128), 71).cuda()
+        k = randn_bf16((B, Hkv, n, 128), 72).cuda()
+        v = randn_bf16((B, Hkv, n, 128), 73).cuda()
+        do = randn_bf16((B, Hq, n, 128), 74).cuda()
+        rng = np.random.default_rng(75)
+        slopes = np.exp2(-8.0 * (np.arange(Hq) + 1) / Hq).astype(np.float32)
+        table = (rng.standard_normal((Hq, 2 * R + 1)) * 0.5).astype(np.float32)
+        kw = dict(alibi_slopes=torch.as_tensor(slopes).cuda()) if score == "alibi" else \
+            dict(relpos=torch.as_tensor(table).cuda(), relpos_radius=R)
+        bm = fa.create_block_mask(mask, 1, 1, n, n, bq, bk)
+        o, lse = fa.forward(q, k, v, bm, score=score, **kw)
+        dq, dk, dv, gp = fa.backward(q, k, v, o, lse, do, bm, score=score, param_grad=True, **kw)
+        torch.cuda.synchronize()
+        okw = dict(slopes=slopes) if score == "alibi" else dict(table=table, radius=R)
+        DQ, DK, DV, GP = OBW.attention_grads(q.cpu(), k.cpu(), v.cpu(), do.cpu(), mask, score, param_grads=True,
+                                             **okw)
+        ctx = f"{score} B={B} {Hq}/{Hkv} n={n} {mask} R={R}"
+        for name, g, G in (("dq", dq, DQ), ("dk", dk, DK), ("dv", dv, DV), ("dparam", gp, GP)):
+            g = g.cpu().numpy()
+            assert g.shape == G.shape, (ctx, name)
+            err = float(np.abs(g - G).max())
+            bound = G_TOL * max(1.0, float(np.abs(G).max()))
+            assert err <= bound, f"{ctx}: {name} max-abs error {err:.3e} > {bound:.3e}"
