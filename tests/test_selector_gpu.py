@@ -228,3 +228,21 @@ def test_slices_of_selector_tables():
         sub = sel[:, :, r0:r0 + OB.n_blocks(q_len, bq)]
         want = OS.tables_from_selection(spec, sub, B, H, q_len, kv_len, bq, bk, q_off)
         assert_tables_equal(s.compact(), want, f"selector slice q={q_len} kv={kv_len} off={q_off}")
+
+
+def test_work_order_at_its_largest():
+    """The work order at its limit of 4096 query blocks (a 262144-token causal square in
+    64-token blocks, tables built by the multi-launch builder): a permutation of every
+    table row set, by non-increasing executed-block count, ties by descending index;
+    one more query block is refused."""
+    import block_sparse_programmable_amd as fa
+    L = 4096 * 64
+    bm = fa.create_block_mask(("swa", 20000), 1, 1, L, L, 64, 64, order=True)
+    torch.cuda.synchronize()
+    order = bm.tensors["order"][:4096].cpu().numpy()
+    lens = (bm.tensors["kv_num"][:4096] + bm.tensors["full_kv_num"][:4096]).cpu().numpy()
+    assert np.array_equal(np.sort(order), np.arange(4096))
+    key = lens[order].astype(np.int64) * 8192 + order        # (length, index), both descending
+    assert (np.diff(key) < 0).all()
+    with pytest.raises(fa.FAError):
+        fa.create_block_mask(("swa", 20000), 1, 1, L + 64, L + 64, 64, 64, order=True)
