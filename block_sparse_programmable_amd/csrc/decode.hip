@@ -145,15 +145,17 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
   const int hkv_m = hkv / p.kv_group;            // the KV head in memory
   const int Hkv_m = p.Hkv / p.kv_group;
   const int64_t krow0 = ((int64_t)b * Hkv_m + hkv_m) * p.kv_len;
-  // (wave-uniform, held in scalar registers so that the per-stage table read is a
-  // scalar load, tracked apart from the vector-memory copies)
-  const int32_t* pt_row = PAGED ? static_cast<const int32_t*>(sreg(p.pt + (int64_t)b * p.pt_stride)) : nullptr;
+  // The table is read through the constant address space at a wave-uniform index, so
+  // the per-stage read is a scalar load, counted apart from the vector-memory copies
+  // in flight (a vector read there makes the wait for it drain the copies as well).
+  using cptr = const __attribute__((address_space(4))) int32_t*;
+  const cptr pt_row = PAGED ? (cptr)sreg(p.pt + (int64_t)b * p.pt_stride) : nullptr;
   const int pshift = PAGED ? p.page_shift : 0;
   const int pmask = (1 << pshift) - 1;
   const int last_page = PAGED ? (int)(p.num_pages - 1) : 0;
   auto page_of = [&](int jb) -> int {
-    // physical page of logical key jb, clamped into the cache (scalar load)
-    const int pg = pt_row[jb >> pshift];
+    // physical page of logical key jb (wave-uniform), clamped into the cache
+    const int pg = pt_row[uniform(jb >> pshift)];
     return min(max(pg, 0), last_page);
   };
   auto row_of = [&](int jb, int pg) -> int64_t {
