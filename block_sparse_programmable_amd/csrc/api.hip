@@ -36,6 +36,45 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool block_ok(int32_t b) { return b == 64 || b == 128; }
 
+// Rewrites a valid postfix program so that every and/or node evaluates first the
+// operand whose evaluation needs the deeper stack (and/or commute, leaves have no side
+// effects, so the mask is the same).  A tree of L leaves then needs a stack of at most
+// floor(log2 L) + 1 values: 4 for the 8 leaves of a 16-node program.  Returns that
+// depth.
+int reorder_program(const fa_mask_desc& m, int32_t* op, int32_t* arg) {
+  struct Node { int op, arg, left, right, need; };
+  Node nodes[FA_MASK_MAX_NODES];
+  int st[FA_MASK_MAX_NODES], sp = 0;
+  for (int t = 0; t < m.n; ++t) {
+    Node& x = nodes[t];
+    x.op = m.node[t].op;
+    x.arg = m.node[t].arg;
+    x.left = x.right = -1;
+    x.need = 1;
+    if (x.op == FA_M_AND || x.op == FA_M_OR) {
+      x.right = st[--sp];
+      x.left = st[--sp];
+      const int a = nodes[x.left].need, b = nodes[x.right].need;
+      x.need = a == b ? a + 1 : std::max(a, b);
+    }
+    st[sp++] = t;
+  }
+  int n = 0;
+  auto emit = [&](auto&& self, int t) -> void {
+    const Node& x = nodes[t];
+    if (x.left >= 0) {
+      const bool swap = nodes[x.right].need > nodes[x.left].need;
+      self(self, swap ? x.right : x.left);
+      self(self, swap ? x.left : x.right);
+    }
+    op[n] = x.op;
+    arg[n] = x.arg;
+    ++n;
+  };
+  emit(emit, st[0]);
+  return nodes[st[0]].need;
+}
+
 // Validates the postfix program; fills the kernel-side copy.
 fa_status check_program(const fa_mask_desc& m, fa::MaskProg* out) {
   if (m.n < 1 || m.n > FA_MASK_MAX_NODES)
@@ -73,10 +112,9 @@ fa_status check_program(const fa_mask_desc& m, fa::MaskProg* out) {
   if (depth != 1) return fail(FA_ERR_MASK_SPEC, "mask program leaves %d values on the stack (expected 1)", depth);
   if (out) {
     out->n = m.n;
-    for (int t = 0; t < FA_MASK_MAX_NODES; ++t) {
-      out->op[t] = t < m.n ? m.node[t].op : 0;
-      out->arg[t] = t < m.n ? m.node[t].arg : 0;
-    }
+    for (int t = 0; t < FA_MASK_MAX_NODES; ++t) out->op[t] = out->arg[t] = 0;
+    if (reorder_program(m, out->op, out->arg) > fa::kMaskStackMax)
+      return fail(FA_ERR_MASK_SPEC, "mask program needs a deeper stack than %d", fa::kMaskStackMax);
     out->has_doc = has_doc;
     // An and-only tree of interval leaves is one key interval per row: causal and window
     // bound it above by i, the window below by i - W + 1, prefixes above by max(P-1, i).

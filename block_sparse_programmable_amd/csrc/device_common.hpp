@@ -73,6 +73,40 @@ __device__ __forceinline__ bool mask_allowed(const MaskProg& p, int i, int j, in
 }
 
 // ---------------------------------------------------------------------------------
+// The same program over a group of up to 32 keys of one query row, one bit per key.
+// For a fixed row every leaf except the document test allows one interval of keys
+// (causal [0, i], window [i - W + 1, i], prefix [0, max(i, P - 1)]), so a leaf costs
+// span(lo, hi) -- the group's bits of keys in [lo, hi], lo >= 0 -- and the document
+// leaf the caller's doc_bits.  And/or act on whole words.  The stack is kMaskStackMax
+// registers shifted on push and pop, enough for programs in the host's deeper-first
+// operand order.
+// ---------------------------------------------------------------------------------
+static_assert(kMaskStackMax == 4, "the word evaluator's stack holds four values");
+
+template <class Span>
+__device__ __forceinline__ uint32_t mask_word(const MaskProg& p, int i, const Span& span, uint32_t doc_bits) {
+  uint32_t s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+#pragma unroll
+  for (int t = 0; t < FA_MASK_MAX_NODES; ++t) {
+    if (t >= p.n) break;
+    const int op = p.op[t];
+    const int a = p.arg[t];
+    if (op == FA_M_AND || op == FA_M_OR) {
+      s0 = op == FA_M_AND ? (s0 & s1) : (s0 | s1);
+      s1 = s2; s2 = s3;
+    } else {
+      uint32_t v;
+      if (op == FA_M_CAUSAL) v = span(0, i);
+      else if (op == FA_M_SWA) v = span(max(i - a + 1, 0), i);
+      else if (op == FA_M_PREFIX) v = span(0, max(i, a - 1));
+      else v = doc_bits;
+      s3 = s2; s2 = s1; s1 = s0; s0 = v;
+    }
+  }
+  return s0;
+}
+
+// ---------------------------------------------------------------------------------
 // Score modification in the base-2 domain: returns log2(e) * score_mod(s * scale).
 // Order of operations follows the definition: scale, then modify; masking to -inf
 // happens afterwards at the call site.

@@ -16,7 +16,12 @@ enum MaskKind : int32_t {
   MK_GENERIC = 2        // anything with an or-node: postfix interpreter per element
 };
 
-// Mask program as passed to kernels (by value, in kernel arguments).
+// Stack depth that any valid program reaches once the host has ordered every and/or
+// node's operands deeper-first (8 leaves at most, so floor(log2 8) + 1).
+constexpr int kMaskStackMax = 4;
+
+// Mask program as passed to kernels (by value, in kernel arguments), operands of each
+// and/or node in deeper-first order.
 struct MaskProg {
   int32_t n;
   int32_t op[FA_MASK_MAX_NODES];

@@ -62,6 +62,9 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   constexpr int KVAR = KPK >= kSwzKeys ? 1 : kSwzKeys / KPK;  // K swizzle patterns over the copies
   constexpr int VVAR = KPK >= 8 ? 1 : 8 / KPK;                 // V pattern repeats every 8 keys
   constexpr bool kDoc = (MK == MK_INTERVAL_DOC);
+  // document IDs of each K sub-tile are staged in LDS next to it when a mask needs them
+  // (the generic interpreter only when its program has a document leaf)
+  const bool stage_doc = kDoc || (MK == MK_GENERIC && p.prog.has_doc);
   constexpr bool kRel = (SCORE == FA_S_RELPOS);
   using L = Lds<D>;
   static_assert(L::KROW * KPK == 1024, "one copy moves 1 KB");
@@ -135,7 +138,11 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   const uint16_t* kbase = p.k + (int64_t)(b * p.Hkv + hkv) * p.kv_len * D;
   const uint16_t* vbase = p.v + (int64_t)(b * p.Hkv + hkv) * p.kv_len * D;
   const int32_t* docr = doc_row(p.doc, b);
-  const int doc_i = (p.prog.has_doc && row_ok) ? docr[i_g] : 0;
+  int doc_i = (p.prog.has_doc && row_ok) ? docr[i_g] : 0;
+  // consumed here: its first use is inside the tile loop on paths that full tiles skip,
+  // and a load still counted as pending there makes every use wait for all memory,
+  // tile copies in flight included
+  asm volatile("" : "+v"(doc_i));
   const ScoreCtx sc = make_score_ctx(p.score, p.scale, hq);
 
   // per-row allowed key interval of the pre-compiled mask (partial blocks only)
@@ -211,8 +218,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
         constexpr int grp = (u / 4) * 4096;   // immediate offsets stay below 4 KB
         dma16_s<(u % 4) * 1024>(m + grp, g + grp, copy_off(isv_c, uc));
       });
-      if constexpr (kDoc && !ISV) {
-        if (wu == 0) dma4_s(md, docr + j0, (uint32_t)lane * 4);
+      if constexpr (MK != MK_INTERVAL && !ISV) {
+        if (stage_doc && wu == 0) dma4_s(md, docr + j0, (uint32_t)lane * 4);
       }
     } else {
       // ragged tail: keys past kv_len re-read the last key (they are masked)
@@ -223,8 +230,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
         const uint32_t o = copy_off(isv_c, uc);
         dma16_v(m + u * 1024, (const char*)gb + j * L::KROW + (o & (L::KROW - 1)));
       });
-      if constexpr (kDoc && !ISV) {
-        if (wu == 0) dma4_v(md, docr + min(j0 + lane, kv_len - 1));
+      if constexpr (MK != MK_INTERVAL && !ISV) {
+        if (stage_doc && wu == 0) dma4_v(md, docr + min(j0 + lane, kv_len - 1));
       }
     }
   };
@@ -280,15 +287,29 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
     const int jl = j0 + 4 * half;   // key of element (mt=0, rr=0) in this lane
     if (masked) {
       if constexpr (MK == MK_GENERIC) {
+        // the program over the lane's 32 keys at once, one bit per element
+        auto span = [&](int lo, int hi) -> uint32_t { return ge_bits(lo - jl) & ~ge_bits(hi - jl + 1); };
+        uint32_t ok = span(0, kv_len - 1);
+        if (part) {
+          uint32_t db = 0;
+          if (stage_doc) {
+            // one 4-key group at a time (unrolled, the eight reads would be issued
+            // together and hold 32 registers)
+#pragma unroll 1
+            for (int g = 0; g < 8; ++g) {   // g = 4 mt + g4
+              const u32x4 dv = *reinterpret_cast<const u32x4*>(dl + 8 * g + 4 * half);
+              uint32_t nib = 0;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) nib |= (int)dv[e] == doc_i ? 1u << e : 0u;
+              db |= nib << (4 * g);
+            }
+          }
+          ok &= mask_word(p.prog, i_g, span, db);
+        }
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int j = jl + key_of(mt, rr);
-            bool ok = (unsigned)j < (unsigned)kv_len;
-            if (part && ok) ok = mask_allowed(p.prog, i_g, j, doc_i, p.prog.has_doc ? docr[j] : 0);
-            s[mt][rr] = ok ? s[mt][rr] : kNegInf;
-          }
+          for (int rr = 0; rr < 16; ++rr) s[mt][rr] = (ok >> (16 * mt + rr)) & 1u ? s[mt][rr] : kNegInf;
       } else {
         // keys outside [lo, hi] (hi already clipped to kv_len - 1) are masked; when only
         // the ragged tail needs masking the same test applies with the tail bound alone

@@ -58,6 +58,14 @@ __device__ __forceinline__ int v_off(int key, int d) {
 // excluding the lane-half term 4*half
 __device__ __forceinline__ constexpr int key_of(int mt, int rr) { return 32 * mt + 8 * (rr >> 2) + (rr & 3); }
 
+// The lane's 32 score elements as bits of a word (bit 16 mt + rr for the key at offset
+// key_of(mt, rr) from the lane's first key): the elements whose offset is at least a.
+__device__ __forceinline__ uint32_t ge_bits(int a) {
+  const int c = min(max(a, 0), 64);
+  const int e0 = 4 * (c >> 3) + min(c & 7, 4);   // first element at or past offset c
+  return (uint32_t)(~0ull << e0);
+}
+
 template <int... U, typename F>
 __device__ __forceinline__ void static_for_impl(std::integer_sequence<int, U...>, F&& f) {
   (f(std::integral_constant<int, U>{}), ...);

@@ -69,6 +69,39 @@ def test_doc_and_compositions(score):
         check(q, k, v, mask, 128, 128, score, doc=doc, ctx=f"{mask} {score}", **score_kw(score, 8))
 
 
+def _chain(leaves, ops, right):
+    """Eight-leaf and/or chain: left-deep (((a b) c) d)... or right-deep a (b (c (d ...)))."""
+    t = leaves[-1] if right else leaves[0]
+    rest = leaves[-2::-1] if right else leaves[1:]
+    for leaf, op in zip(rest, ops):
+        t = (op, leaf, t) if right else (op, t, leaf)
+    return t
+
+
+@pytest.mark.parametrize("score", ["identity", "softcap"])
+def test_eight_leaf_programs(score):
+    """Sixteen-node-limit programs mixing every leaf with and/or: the kernels evaluate
+    them with a four-value stack after the host reorders operands, which the
+    right-deep chain needs (it would reach depth eight in the order written)."""
+    rng = np.random.default_rng(8)
+    n = 530
+    lens = []
+    while sum(lens) < n:
+        lens.append(int(rng.integers(15, 160)))
+    doc = np.repeat(np.arange(len(lens)), lens)[:n].astype(np.int32)[None]
+    q, k, v = qkv(1, 4, 2, n, n, 128, seed=18)
+    leaves = [("doc",), ("swa", 90), ("prefix", 40), ("causal",), ("swa", 300), ("doc",),
+              ("prefix", 333), ("swa", 17)]
+    ops = ["or", "and", "or", "and", "or", "and", "or"]
+    for right in (False, True):
+        mask = _chain(leaves, ops, right)
+        check(q, k, v, mask, 128, 128, score, doc=doc, ctx=f"chain right={right} {score}",
+              **score_kw(score, 4))
+    bal = ("or", ("and", ("or", ("doc",), ("swa", 50)), ("or", ("prefix", 64), ("causal",))),
+           ("and", ("or", ("swa", 200), ("doc",)), ("or", ("prefix", 7), ("swa", 400))))
+    check(q, k, v, bal, 64, 128, score, doc=doc, ctx=f"balanced {score}", **score_kw(score, 4))
+
+
 def test_nonmonotone_docs_per_batch():
     rng = np.random.default_rng(6)
     n = 400
