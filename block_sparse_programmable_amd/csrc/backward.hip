@@ -125,6 +125,31 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams bp) {
   if (lane == 0) bp.delta[row] = acc;
 }
 
+// A lane's pairs of one block as bits of a word: bit 4 m + rr for the position at offset
+// 16 m + rr from the lane's first (the rows of its key in dK/dV, the keys of its row in
+// dQ); the bits of positions at or past offset a.
+__device__ __forceinline__ uint32_t ge_bits16(int a) {
+  const int c = min(max(a, 0), 128);
+  const int e0 = 4 * (c >> 4) + min(c & 15, 4);   // first pair at or past offset c
+  return (uint32_t)(~0ull << e0);
+}
+
+// doc_bits of a lane: bit 4 m + e set when the document ID at ids[16 m + 4 g4 + e] (LDS)
+// equals own, for m < n16 (one 4-ID group at a time: unrolled, the reads would be
+// issued together and hold four times the registers)
+__device__ __forceinline__ uint32_t doc_bits16(const int32_t* ids, int g4, int n16, int own) {
+  uint32_t db = 0;
+#pragma unroll 1
+  for (int m = 0; m < n16; ++m) {
+    const u32x4 d = *reinterpret_cast<const u32x4*>(ids + 16 * m + 4 * g4);
+    uint32_t nib = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) nib |= (int)d[e] == own ? 1u << e : 0u;
+    db |= nib << (4 * m);
+  }
+  return db;
+}
+
 // ---- dK, dV: one workgroup per (b, h_kv, KV block), NW = block_kv / 16 waves x 16 keys
 // (the whole block shares each query block's Q and dO rows staged in LDS)
 template <int D, int SCORE, int NW>
@@ -138,6 +163,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
   __shared__ __attribute__((aligned(16))) uint8_t qs[BQM * RS];   // Q rows of one (head, block)
   __shared__ __attribute__((aligned(16))) uint8_t gs[BQM * RS];   // dO rows
   __shared__ float lse_s[BQM], del_s[BQM];
+  __shared__ __attribute__((aligned(16))) int32_t doc_s[BQM];   // document IDs of the rows
 
   // work item: (b, h_kv) fastest, then the KV block c ascending: every head's first
   // columns go out before any head's later ones (for causal-like rules the first columns
@@ -172,7 +198,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const int32_t* docr = doc_row(p.doc, b);
-  const int doc_j = (p.prog.has_doc && j < kv_len) ? docr[j] : 0;
+  int doc_j = (p.prog.has_doc && j < kv_len) ? docr[j] : 0;
+  // consumed here: first used inside the block loop, a load still counted as pending
+  // there would make that use wait for the next block's prefetched rows too
+  asm volatile("" : "+v"(doc_j));
   const int tb = p.tab.tB == 1 ? 0 : b;
 
   for (int hh = 0; hh < p.g; ++hh) {
@@ -190,19 +219,21 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     const int n_ent = nf + np;
     // query block of list entry e and its row statistics (one per thread, bq <= 256)
     auto block_of = [&](int e) -> int { return uniform(e >= nf ? pl[e - nf] : fl[e]); };
-    auto stats = [&](int r0, float& l2, float& dl) {
+    auto stats = [&](int r0, float& l2, float& dl, int& dc) {
       const int i = r0 + (int)threadIdx.x;
       const bool ok = (int)threadIdx.x < bq && i < q_len;
       l2 = ok ? p.lse[bh * q_len + i] * kLog2e : 0.f;
       dl = ok ? bp.delta[bh * q_len + i] : 0.f;
+      dc = (ok && p.prog.has_doc) ? docr[i + p.q_offset] : 0;
     };
     RowStage<D, NT> sq, sg;
     float nl2 = 0.f, ndl = 0.f;
+    int ndc = 0;
     if (n_ent > 0) {
       const int r0n = block_of(0) * bq;
       sq.fetch(qsrc, r0n, bq, q_len);
       sg.fetch(gsrc, r0n, bq, q_len);
-      stats(r0n, nl2, ndl);
+      stats(r0n, nl2, ndl, ndc);
     }
     for (int e = 0; e < n_ent; ++e) {
       const bool part = e >= nf;
@@ -213,13 +244,23 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
       if ((int)threadIdx.x < bq) {
         lse_s[threadIdx.x] = nl2;
         del_s[threadIdx.x] = ndl;
+        doc_s[threadIdx.x] = ndc;
       }
       __syncthreads();
       if (e + 1 < n_ent) {   // next block's rows travel while this one is computed
         const int r0n = block_of(e + 1) * bq;
         sq.fetch(qsrc, r0n, bq, q_len);
         sg.fetch(gsrc, r0n, bq, q_len);
-        stats(r0n, nl2, ndl);
+        stats(r0n, nl2, ndl, ndc);
+      }
+      // which of the lane's 32 rows (r0 + 16 m + 4 g4 + rr) may see key j: the row
+      // bounds, and on partial blocks the mask program over the whole group
+      const int rb = r0 + 4 * g4 + (int)p.q_offset;
+      auto span = [&](int lo, int hi) -> uint32_t { return ge_bits16(lo - rb) & ~ge_bits16(hi - rb + 1); };
+      uint32_t okw = j < kv_len ? span((int)p.q_offset, (int)p.q_offset + q_len - 1) : 0u;
+      if (part) {
+        const uint32_t db = p.prog.has_doc ? doc_bits16(doc_s, g4, bq >> 4, doc_j) : 0u;
+        okw &= mask_word(p.prog, [&](int op, int a) { return col_leaf(op, a, j, span, db); });
       }
       for (int q0 = 0; q0 < bq; q0 += 16) {
         // S (16 rows x 16 keys) and dP on 16x16x32 tiles
@@ -235,10 +276,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int xr = q0 + 4 * g4 + rr;
-          const int i = r0 + xr;
-          const int ig = i + (int)p.q_offset;
-          bool ok = i < q_len && j < kv_len;
-          if (part && ok) ok = mask_allowed(p.prog, ig, j, p.prog.has_doc ? docr[ig] : 0, doc_j);
+          const int ig = r0 + xr + (int)p.q_offset;
+          const bool ok = (okw >> (4 * (q0 >> 4) + rr)) & 1u;
           grad_elem<SCORE>(s[rr], dp[rr], lse_s[xr], del_s[xr], ok, sc, p.scale, ig, j, pv[rr], ds[rr]);
         }
         const s16x4 pb = pack4(pv[0], pv[1], pv[2], pv[3]);
@@ -275,6 +314,7 @@ __global__ __launch_bounds__(NW * 64, NW / 2) void bwd_dq_kernel(BwdParams bp) {
   constexpr int BKM = 128;
   __shared__ __attribute__((aligned(16))) uint8_t ks[BKM * RS];
   __shared__ __attribute__((aligned(16))) uint8_t vs[BKM * RS];
+  __shared__ __attribute__((aligned(16))) int32_t doc_s[BKM];   // document IDs of the keys
   // gradient of the position table: one bin per offset of this query head
   constexpr int kBins = SCORE == FA_S_RELPOS ? 2 * kRelGradMaxRadius + 1 : 1;
   __shared__ float bins_s[kBins];
@@ -310,7 +350,8 @@ __global__ __launch_bounds__(NW * 64, NW / 2) void bwd_dq_kernel(BwdParams bp) {
   const float delta = row_ok ? bp.delta[(int64_t)bh * q_len + i] : 0.f;
   const ScoreCtx sc = make_score_ctx(p.score, p.scale, hq);
   const int32_t* docr = doc_row(p.doc, b);
-  const int doc_i = (p.prog.has_doc && row_ok) ? docr[ig] : 0;
+  int doc_i = (p.prog.has_doc && row_ok) ? docr[ig] : 0;
+  asm volatile("" : "+v"(doc_i));   // (as doc_j in the dK/dV kernel)
   f32x4 dq[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -335,9 +376,15 @@ __global__ __launch_bounds__(NW * 64, NW / 2) void bwd_dq_kernel(BwdParams bp) {
   const int n_ent = nf + np;
   auto block_of = [&](int e) -> int { return uniform(e >= nf ? pl[e - nf] : fl[e]); };
   RowStage<D, NT> sk, sv;
+  // document ID of key j0 + threadIdx.x (threads below bk; keys past kv_len read the last)
+  auto key_doc = [&](int j0) -> int {
+    return (p.prog.has_doc && (int)threadIdx.x < bk) ? docr[min(j0 + (int)threadIdx.x, kv_len - 1)] : 0;
+  };
+  int ndc = 0;
   if (n_ent > 0) {
     sk.fetch(p.k + kvh * D, block_of(0) * bk, bk, kv_len);
     sv.fetch(p.v + kvh * D, block_of(0) * bk, bk, kv_len);
+    ndc = key_doc(block_of(0) * bk);
   }
   for (int e = 0; e < n_ent; ++e) {
     const bool part = e >= nf;
@@ -345,10 +392,21 @@ __global__ __launch_bounds__(NW * 64, NW / 2) void bwd_dq_kernel(BwdParams bp) {
     __syncthreads();
     sk.put(ks, bk);
     sv.put(vs, bk);
+    if ((int)threadIdx.x < bk) doc_s[threadIdx.x] = ndc;
     __syncthreads();
     if (e + 1 < n_ent) {   // next block's K and V travel while this one is computed
       sk.fetch(p.k + kvh * D, block_of(e + 1) * bk, bk, kv_len);
       sv.fetch(p.v + kvh * D, block_of(e + 1) * bk, bk, kv_len);
+      ndc = key_doc(block_of(e + 1) * bk);
+    }
+    // which of the lane's 32 keys (j0 + 16 m + 4 g4 + rr) row i may see: the key
+    // bounds, and on partial blocks the mask program over the whole group
+    const int kb = j0 + 4 * g4;
+    auto span = [&](int lo, int hi) -> uint32_t { return ge_bits16(lo - kb) & ~ge_bits16(hi - kb + 1); };
+    uint32_t okw = row_ok ? span(0, kv_len - 1) : 0u;
+    if (part) {
+      const uint32_t db = p.prog.has_doc ? doc_bits16(doc_s, g4, bk >> 4, doc_i) : 0u;
+      okw &= mask_word(p.prog, [&](int op, int a) { return row_leaf(op, a, ig, span, db); });
     }
     for (int k0 = 0; k0 < bk; k0 += 16) {
       // S^T (16 keys x 16 rows) = K Q^T and dP^T = V dO^T
@@ -364,8 +422,7 @@ __global__ __launch_bounds__(NW * 64, NW / 2) void bwd_dq_kernel(BwdParams bp) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int jj = j0 + k0 + 4 * g4 + rr;
-        bool ok = row_ok && jj < kv_len;
-        if (part && ok) ok = mask_allowed(p.prog, ig, jj, doc_i, p.prog.has_doc ? docr[jj] : 0);
+        const bool ok = (okw >> (4 * (k0 >> 4) + rr)) & 1u;
         grad_elem<SCORE>(s[rr], dp[rr], lse2, delta, ok, sc, p.scale, ig, jj, pv[rr], ds[rr]);
         if constexpr (SCORE == FA_S_ALIBI) {
           if (want_slope) g_slope = __builtin_fmaf(ds[rr], (float)(jj - ig), g_slope);

@@ -73,33 +73,46 @@ __device__ __forceinline__ bool mask_allowed(const MaskProg& p, int i, int j, in
 }
 
 // ---------------------------------------------------------------------------------
-// The same program over a group of up to 32 keys of one query row, one bit per key.
-// For a fixed row every leaf except the document test allows one interval of keys
-// (causal [0, i], window [i - W + 1, i], prefix [0, max(i, P - 1)]), so a leaf costs
-// span(lo, hi) -- the group's bits of keys in [lo, hi], lo >= 0 -- and the document
-// leaf the caller's doc_bits.  And/or act on whole words.  The stack is kMaskStackMax
-// registers shifted on push and pop, enough for programs in the host's deeper-first
-// operand order.
+// The same program over a group of up to 32 (query, key) pairs that share a query row
+// or a key, one bit per pair.  With one side fixed, every leaf except the document
+// test allows one interval of the other side, so a leaf costs one span(lo, hi) -- the
+// group's bits of positions in [lo, hi], 0 <= lo, hi <= kPosOpen -- and the document
+// leaf the caller's doc_bits (row_leaf: keys of row i; col_leaf: rows of key j).
+// And/or act on whole words.  The stack is kMaskStackMax registers shifted on push
+// and pop, enough for programs in the host's deeper-first operand order.
 // ---------------------------------------------------------------------------------
 static_assert(kMaskStackMax == 4, "the word evaluator's stack holds four values");
+constexpr int kPosOpen = 0x7ffffffe;   // upper bound of an interval open to the right
 
 template <class Span>
-__device__ __forceinline__ uint32_t mask_word(const MaskProg& p, int i, const Span& span, uint32_t doc_bits) {
+__device__ __forceinline__ uint32_t row_leaf(int op, int a, int i, const Span& span, uint32_t doc_bits) {
+  if (op == FA_M_CAUSAL) return span(0, i);                     // j <= i
+  if (op == FA_M_SWA) return span(max(i - a + 1, 0), i);        // i - W < j <= i
+  if (op == FA_M_PREFIX) return span(0, max(i, a - 1));         // j < P or j <= i
+  return doc_bits;
+}
+
+template <class Span>
+__device__ __forceinline__ uint32_t col_leaf(int op, int a, int j, const Span& span, uint32_t doc_bits) {
+  if (op == FA_M_CAUSAL) return span(j, kPosOpen);              // i >= j
+  if (op == FA_M_SWA) return span(j, (int)min((int64_t)j + a - 1, (int64_t)kPosOpen));
+  if (op == FA_M_PREFIX) return span(j < a ? 0 : j, kPosOpen);  // every row when j < P
+  return doc_bits;
+}
+
+// leaf(op, arg) -> word of the leaf
+template <class Leaf>
+__device__ __forceinline__ uint32_t mask_word(const MaskProg& p, const Leaf& leaf) {
   uint32_t s0 = 0, s1 = 0, s2 = 0, s3 = 0;
 #pragma unroll
   for (int t = 0; t < FA_MASK_MAX_NODES; ++t) {
     if (t >= p.n) break;
     const int op = p.op[t];
-    const int a = p.arg[t];
     if (op == FA_M_AND || op == FA_M_OR) {
       s0 = op == FA_M_AND ? (s0 & s1) : (s0 | s1);
       s1 = s2; s2 = s3;
     } else {
-      uint32_t v;
-      if (op == FA_M_CAUSAL) v = span(0, i);
-      else if (op == FA_M_SWA) v = span(max(i - a + 1, 0), i);
-      else if (op == FA_M_PREFIX) v = span(0, max(i, a - 1));
-      else v = doc_bits;
+      const uint32_t v = leaf(op, p.arg[t]);
       s3 = s2; s2 = s1; s1 = s0; s0 = v;
     }
   }

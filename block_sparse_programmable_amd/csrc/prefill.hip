@@ -304,7 +304,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
               db |= nib << (4 * g);
             }
           }
-          ok &= mask_word(p.prog, i_g, span, db);
+          ok &= mask_word(p.prog, [&](int op, int a) { return row_leaf(op, a, i_g, span, db); });
         }
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
