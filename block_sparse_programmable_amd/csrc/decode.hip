@@ -163,7 +163,14 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
     return krow0 + jb;
   };
   const int32_t* docr = doc_row(p.doc, b);
-  const int doc_i = (p.prog.has_doc && col_ok) ? docr[i_g] : 0;
+  int doc_i = (p.prog.has_doc && col_ok) ? docr[i_g] : 0;
+  // consumed here: first used inside the stage loop, a load still counted as pending
+  // there would make that use wait for all memory, copies in flight included
+  asm volatile("" : "+v"(doc_i));
+  // the keys' IDs are read as scalar loads (wave-uniform addresses in the constant
+  // address space), counted apart from the copies
+  const cptr docs = p.prog.has_doc ? (cptr)sreg(docr) : nullptr;
+  const int doc_last = p.prog.has_doc ? (int)(p.doc.len - 1) : 0;
   const ScoreCtx sc = make_score_ctx(p.score, p.scale, hq);
 
   // the unit's block list, 64 entries per register (lane e holds entry base + e)
@@ -264,13 +271,29 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
 #pragma unroll
     for (int r = 0; r < 4; ++r) sacc[r] = score_log2<SCORE>(sacc[r], sc, i_g, jl + r);
     if (part || j0 + SK > kv_len) {
+      // the mask program over the lane's four keys at once, one bit per key
+      auto span = [&](int lo, int hi) -> uint32_t {
+        auto ge = [&](int a) -> uint32_t { return (0xFu << min(max(a, 0), 4)) & 0xFu; };
+        return ge(lo - jl) & ~ge(hi - jl + 1);
+      };
+      uint32_t ok = span(0, kv_len - 1);
+      if (part) {
+        uint32_t db = 0;
+        if (p.prog.has_doc) {
+          const int js = uniform(j0);
+          int d[SK];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = jl + r;
-        bool ok = (unsigned)j < (unsigned)kv_len;
-        if (part && ok) ok = mask_allowed(p.prog, i_g, j, doc_i, p.prog.has_doc ? docr[j] : 0);
-        sacc[r] = ok ? sacc[r] : kNegInf;
+          for (int x = 0; x < SK; ++x) d[x] = docs[min(js + x, doc_last)];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int v = g4 == 0 ? d[r] : (g4 == 1 ? d[4 + r] : (g4 == 2 ? d[8 + r] : d[12 + r]));
+            db |= v == doc_i ? 1u << r : 0u;
+          }
+        }
+        ok &= mask_word(p.prog, [&](int op, int a) { return row_leaf(op, a, i_g, span, db); });
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sacc[r] = (ok >> r) & 1u ? sacc[r] : kNegInf;
     }
     float tmax = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
