@@ -161,9 +161,13 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   }
 
   // relative-position table of this query head, pre-multiplied by log2(e); the two
-  // saturated entries are kept in registers
+  // saturated entries are kept in registers.  A table too large for LDS travels as
+  // per-tile windows instead: the entries for offsets i - j of the workgroup's rows
+  // against a K sub-tile at j0, [wb, wb + BQ + KT - 2] with wb = i_wg0 - j0 - (KT - 1),
+  // clamped to [-R, R] at copy time (kRelWin per K slot, copied with the K tile)
   const int R = p.score.radius;
   const bool rel_in_lds = kRel && (2 * R + 1) <= kRelposLdsMax;
+  const int i_wg0 = r * BQ + (int)p.q_offset;   // first row of the workgroup
   float bias_far2 = 0.f, bias_ahead2 = 0.f;   // rel >= R and rel <= -R
   if constexpr (kRel) {
     if (rel_in_lds) {
@@ -203,6 +207,21 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
     }
   };
 
+  // the position-table window of the K sub-tile at j0 (wave 0, three 64-entry copies)
+  auto copy_rel_window = [&](int j0, auto isv_c, auto slot_c) {
+    if constexpr (kRel && !decltype(isv_c)::value) {
+      if (!rel_in_lds && wu == 0) {
+        const uint32_t mw = lds_addr(rel_lds + decltype(slot_c)::value * kRelWin);
+        const int wb = i_wg0 - j0 - (KT - 1);
+#pragma unroll
+        for (int u = 0; u < kRelWin / 64; ++u) {
+          const int rel = min(max(wb + 64 * u + lane, -R), R);
+          dma4_v(mw + 256 * u, sc.tab + rel + R);
+        }
+      }
+    }
+  };
+
   // copy of one operand (K with its doc IDs, or V) of the sub-tile at key j0 into a slot
   auto copy_op = [&](int j0, auto isv_c, auto slot_c) {
     constexpr bool ISV = decltype(isv_c)::value;
@@ -221,6 +240,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       if constexpr (MK != MK_INTERVAL && !ISV) {
         if (stage_doc && wu == 0) dma4_s(md, docr + j0, (uint32_t)lane * 4);
       }
+      copy_rel_window(j0, isv_c, slot_c);
     } else {
       // ragged tail: keys past kv_len re-read the last key (they are masked)
       static_for<COPIES>([&](auto uc) {
@@ -233,6 +253,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       if constexpr (MK != MK_INTERVAL && !ISV) {
         if (stage_doc && wu == 0) dma4_v(md, docr + min(j0 + lane, kv_len - 1));
       }
+      copy_rel_window(j0, isv_c, slot_c);
     }
   };
 
@@ -361,9 +382,10 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
-            int rel = i_g - (jl + key_of(mt, rr));
-            rel = rel < -R ? -R : (rel > R ? R : rel);
-            const float bb = rel_in_lds ? rel_lds[rel + R] : sc.tab[rel + R] * kLog2e;
+            const int dd = i_g - (jl + key_of(mt, rr));
+            const int rel = dd < -R ? -R : (dd > R ? R : dd);
+            const float bb = rel_in_lds ? rel_lds[rel + R]
+                                        : rel_lds[DSLOT * kRelWin + dd - (i_wg0 - j0 - (KT - 1))] * kLog2e;
             s[mt][rr] = __builtin_fmaf(s[mt][rr], sc.c2, bb);
           }
       }

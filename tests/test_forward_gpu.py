@@ -102,6 +102,23 @@ def test_eight_leaf_programs(score):
     check(q, k, v, bal, 64, 128, score, doc=doc, ctx=f"balanced {score}", **score_kw(score, 4))
 
 
+@pytest.mark.parametrize("R", [1536, 1537, 2500])
+def test_relpos_large_radius(R):
+    """Position tables around and beyond the size staged whole in LDS (2R + 1 <= 3073
+    entries): larger tables travel as per-tile windows.  Lengths past R on both sides
+    (a bidirectional prefix) reach both saturated ends; the decode path reads the same
+    table."""
+    rng = np.random.default_rng(R)
+    n = 3300
+    table = (rng.standard_normal((2, 2 * R + 1)) * 0.5).astype(np.float32)
+    q, k, v = qkv(1, 2, 1, n, n, 64, seed=19)
+    check(q, k, v, ("prefix", 2100), 128, 128, "relpos", table=table, radius=R, ctx=f"prefix R={R}")
+    check(q, k, v, ("causal",), 64, 128, "relpos", table=table, radius=R, ctx=f"causal R={R}")
+    qd = q[:, :, -3:].contiguous()
+    check(qd, k, v, ("prefix", 2100), 128, 128, "relpos", q_offset=n - 3, table=table, radius=R,
+          ctx=f"decode R={R}")
+
+
 def test_nonmonotone_docs_per_batch():
     rng = np.random.default_rng(6)
     n = 400
