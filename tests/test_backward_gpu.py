@@ -77,6 +77,29 @@ def test_backward_documents_gqa_and_offsets():
     run_case(1, 2, 2, 64, 100, 64, ("swa", 10), 64, 64, "identity", q_offset=150, seed=7, ctx="bwd empty rows")
 
 
+@pytest.mark.parametrize("bq,bk", [(128, 128), (64, 128), (128, 64)])
+def test_backward_eight_leaf_programs(bq, bk):
+    """Programs at the 16-node limit mixing every leaf with and/or, with documents: the
+    dQ kernel evaluates them per row over a block's keys, the dK/dV kernel per key over
+    a block's rows, both on words after the host's operand reordering (the right-deep
+    chain would need eight stack values in the order written)."""
+    from tests.test_forward_gpu import _chain
+    rng = np.random.default_rng(bq + bk)
+    n = 420
+    lens = []
+    while sum(lens) < n:
+        lens.append(int(rng.integers(15, 140)))
+    doc = np.repeat(np.arange(len(lens)), lens)[:n].astype(np.int32)[None]
+    leaves = [("doc",), ("swa", 90), ("prefix", 40), ("causal",), ("swa", 300), ("doc",),
+              ("prefix", 333), ("swa", 17)]
+    ops = ["or", "and", "or", "and", "or", "and", "or"]
+    for right in (False, True):
+        run_case(1, 4, 2, n, n, 64, _chain(leaves, ops, right), bq, bk, "softcap", doc=doc,
+                 seed=30 + right, ctx=f"bwd chain right={right} {bq}x{bk}")
+    run_case(1, 2, 2, 150, n, 64, _chain(leaves, ops, True), bq, bk, "identity", q_offset=n - 150,
+             doc=doc, seed=32, ctx=f"bwd chain offset rows {bq}x{bk}")
+
+
 def test_backward_large_scores():
     run_case(1, 2, 1, 256, 256, 128, ("causal",), 128, 128, "softcap", qscale=6.0, seed=8, ctx="bwd large softcap")
     run_case(1, 2, 1, 256, 256, 128, ("causal",), 128, 128, "identity", qscale=3.0, seed=9, ctx="bwd large identity")
