@@ -40,12 +40,12 @@ constexpr int kStages = 5;   // LDS ring slots per wave
 constexpr int kDecWaves = 4; // independent waves (units) per workgroup
 constexpr int kDecCols = 16; // query columns (heads sharing a KV head x positions)
 
-template <int D>
+template <int D, int NS, int XW>
 struct DLds {
   static constexpr int KROW = D * 2;            // bytes per K or V row
   static constexpr int HALF = SK * KROW;        // K (or V) part of a stage
-  static constexpr int STAGE = 2 * HALF;        // K then V
-  static constexpr int WAVE = kStages * STAGE;  // one wave's ring
+  static constexpr int STAGE = 2 * HALF + XW;   // K, V, then XW bytes of table window
+  static constexpr int WAVE = NS * STAGE;       // one wave's ring of NS slots
   static constexpr int UNITS = D / 16;          // 32-byte units per V row
 };
 
@@ -75,9 +75,17 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
   constexpr int CPS = 2 * CPO;                 // copies per stage
   constexpr int KVAR = KPK >= kSwzKeys ? 1 : kSwzKeys / KPK;   // K swizzle patterns per stage
   constexpr int VVAR = KPK >= 8 ? 1 : 8 / KPK;                  // V pattern repeats every 8 keys
-  using L = DLds<D>;
-  static_assert(CPS * (kStages - 1) <= 63, "outstanding copies must fit the vmcnt counter");
-  static_assert(kStages == 5, "the wait below spells out up to four stages in flight");
+  // The position-table score_mod reads table[clip(i - j) + R] per pair: each stage
+  // carries those entries for its 16 columns x 16 keys (clamped at copy time, four
+  // more copies) beside K and V, so no vector read waits inside the loop; its ring has
+  // one slot less to make room.
+  constexpr bool kWin = SCORE == FA_S_RELPOS;
+  constexpr int NS = kWin ? kStages - 1 : kStages;   // ring slots
+  constexpr int WCP = kWin ? kDecCols * SK / 64 : 0;  // window copies per stage
+  constexpr int CPSW = CPS + WCP;                     // copies per stage, window included
+  using L = DLds<D, NS, kWin ? kDecCols * SK * 4 : 0>;
+  static_assert(CPSW * (NS - 1) <= 63, "outstanding copies must fit the vmcnt counter");
+  static_assert(NS >= 2 && NS <= 5, "the wait below spells out up to four stages in flight");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kDecWaves * L::WAVE];
 
   const int w = threadIdx.x >> 6;
@@ -209,6 +217,29 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
   uint8_t* ring = smem + w * L::WAVE;
   const uint32_t ring_lds = lds_addr(ring);
 
+  // table window: copy u fills entries 64 u + lane = 16 c + t (column c = 4 u + g4, key
+  // j0 + t, t = col) from the centre of column c's table row (columns past the last
+  // read column 0's)
+  const int Rw = kWin ? p.score.radius : 0;
+  const float* wtab[kWin ? WCP : 1];
+  int wpos[kWin ? WCP : 1];
+  if constexpr (kWin) {
+#pragma unroll
+    for (int u = 0; u < WCP; ++u) {
+      const int c = 4 * u + g4 < ncols ? 4 * u + g4 : 0;
+      const int hh_c = c / q_len;
+      wtab[u] = p.score.table + (int64_t)(hkv * p.g + hh_c) * (2 * Rw + 1) + Rw;
+      wpos[u] = c - hh_c * q_len + (int)p.q_offset;
+    }
+  }
+  auto copy_window = [&](int j0, uint32_t mk) {
+    if constexpr (kWin) {
+      const uint32_t mw = mk + 2 * L::HALF;
+#pragma unroll
+      for (int u = 0; u < WCP; ++u) dma4_v(mw + 256 * u, wtab[u] + min(max(wpos[u] - (j0 + col), -Rw), Rw));
+    }
+  };
+
   // one stage (SK keys from j0) into ring slot `slot`; pg is the physical page of key
   // min(j0, kv_len - 1) (paged layout: a stage never crosses a page, and a ragged stage
   // only reads keys from that one up to kv_len - 1, inside the same page)
@@ -225,6 +256,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
         dma16_s<(u % 4) * 1024>(mk + grp, kg + grp, koff[u % KVAR]);
         dma16_s<(u % 4) * 1024>(mv + grp, vg + grp, voff[u % VVAR]);
       });
+      copy_window(j0, mk);
     } else {
       // ragged tail: keys past kv_len re-read the last key (they are masked); offsets
       // from jb = min(j0, kv_len - 1) stay non-negative
@@ -239,6 +271,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
         dma16_s<0>(mk + u * 1024, kg, rowoff + (koff[u % KVAR] & (L::KROW - 1)));
         dma16_s<0>(mv + u * 1024, vg, rowoff + (voff[u % VVAR] & (L::KROW - 1)));
       });
+      copy_window(j0, mk);
     }
   };
 
@@ -268,8 +301,14 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
     }
     // score_mod, then the mask (-inf) on partial and ragged stages only
     const int jl = j0 + 4 * g4;
+    if constexpr (kWin) {
+      const f32x4 tw = *reinterpret_cast<const f32x4*>(kb + 2 * L::HALF + (col * SK + 4 * g4) * 4);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sacc[r] = score_log2<SCORE>(sacc[r], sc, i_g, jl + r);
+      for (int r = 0; r < 4; ++r) sacc[r] = __builtin_fmaf(sacc[r], sc.c2, tw[r] * kLog2e);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sacc[r] = score_log2<SCORE>(sacc[r], sc, i_g, jl + r);
+    }
     if (part || j0 + SK > kv_len) {
       // the mask program over the lane's four keys at once, one bit per key
       auto span = [&](int lo, int hi) -> uint32_t {
@@ -322,11 +361,11 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
     }
   };
 
-  // ring of kStages slots: stage s in slot s % kStages, the next kStages - 1 in flight
+  // ring of NS slots: stage s in slot s % NS, the next NS - 1 in flight
   int issued = 0;
-  int j0_of[kStages];
+  int j0_of[NS];
 #pragma unroll
-  for (int k = 0; k < kStages; ++k) {
+  for (int k = 0; k < NS; ++k) {
     j0_of[k] = 0;
     if (k < nst) {
       j0_of[k] = stage_j0(rs(k));
@@ -339,30 +378,30 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
     // stage s has landed once at most (issued - s - 1) stages of copies are outstanding
     switch (issued - s - 1) {
       case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-      case 1: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(CPS) : "memory"); break;
-      case 2: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(2 * CPS) : "memory"); break;
-      case 3: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(3 * CPS) : "memory"); break;
-      default: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(4 * CPS) : "memory"); break;
+      case 1: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(CPSW) : "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(2 * CPSW) : "memory"); break;
+      case 3: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(3 * CPSW) : "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(%0)" :: "i"(4 * CPSW) : "memory"); break;
     }
     int j0 = 0;
 #pragma unroll
-    for (int k = 0; k < kStages; ++k)
+    for (int k = 0; k < NS; ++k)
       if (k == slot) j0 = j0_of[k];
     // the next stage's position (and its page, a scalar load that lands during the
     // compute below)
-    const bool more = s + kStages < nst;
-    const int jn = more ? stage_j0(rs(s + kStages)) : 0;
+    const bool more = s + NS < nst;
+    const int jn = more ? stage_j0(rs(s + NS)) : 0;
     const int pgn = (PAGED && more) ? page_of(min(jn, kv_len - 1)) : 0;
     compute(j0, stage_part(rs(s)), slot);
     if (more) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads of this slot are done
 #pragma unroll
-      for (int k = 0; k < kStages; ++k)
+      for (int k = 0; k < NS; ++k)
         if (k == slot) j0_of[k] = jn;
       copy_stage(jn, pgn, slot);
       ++issued;
     }
-    slot = slot + 1 == kStages ? 0 : slot + 1;
+    slot = slot + 1 == NS ? 0 : slot + 1;
   }
 
   // ---- results: final O and LSE (one split, or splits merged in LDS), or this
