@@ -69,11 +69,15 @@ def score_args(kind, Hq):
     if kind == "alibi":
         s = np.exp2(-8.0 * (np.arange(Hq) + 1) / Hq).astype(np.float32)
         return dict(alibi_slopes=torch.as_tensor(s).cuda()), dict(slopes=s)
+    if kind == "relpos":
+        R = 50   # rows reach past R on the far side, so both table ends are used
+        t = (np.random.default_rng(Hq).standard_normal((Hq, 2 * R + 1)) * 0.5).astype(np.float32)
+        return dict(relpos=torch.as_tensor(t).cuda(), relpos_radius=R), dict(table=t, radius=R)
     return {}, {}
 
 
 @pytest.mark.parametrize("page_size", [16, 32, 128, 256])
-@pytest.mark.parametrize("score", ["identity", "softcap", "alibi"])
+@pytest.mark.parametrize("score", ["identity", "softcap", "alibi", "relpos"])
 def test_paged_decode_matches_oracle_and_contiguous(page_size, score):
     for (B, Hq, Hkv, q_len, kv_len, mask, d, share) in (
             (3, 8, 2, 1, 2000, ("swa", 700), 128, 5),
