@@ -34,7 +34,17 @@ constexpr int64_t kMaxPos = 0x7fffffffLL;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The forward, backward and decode kernels tile 64- and 128-blocks; the table writers
+// classify any power-of-two block from 1 to 128 (the builder's wavefront walk covers
+// up to 128 rows and columns of a block).
 bool block_ok(int32_t b) { return b == 64 || b == 128; }
+bool table_block_ok(int32_t b) { return b >= 1 && b <= 128 && (b & (b - 1)) == 0; }
+
+// Largest relative-position radius: 2R + 1 table entries per head stay below 2^31.
+constexpr int32_t kMaxRelposRadius = (1 << 30) - 1;
+
+// Largest block grid B * H * NQB * NKB: list positions and pointers are int32.
+constexpr int64_t kMaxGridBlocks = 0x7fffffffLL;
 
 // Rewrites a valid postfix program so that every and/or node evaluates first the
 // operand whose evaluation needs the deeper stack (and/or commute, leaves have no side
@@ -140,13 +150,18 @@ fa_status check_program(const fa_mask_desc& m, fa::MaskProg* out) {
 
 // Geometry and mask checks shared by the builder and the forward.
 fa_status check_mask_geometry(const fa_block_mask* bm, fa::MaskProg* prog) {
-  if (!block_ok(bm->block_q) || !block_ok(bm->block_kv))
-    return fail(FA_ERR_UNSUPPORTED, "block sizes must be 64 or 128 (got %d x %d)", bm->block_q, bm->block_kv);
+  if (!table_block_ok(bm->block_q) || !table_block_ok(bm->block_kv))
+    return fail(FA_ERR_UNSUPPORTED, "block sizes must be powers of two from 1 to 128 (got %d x %d)", bm->block_q,
+                bm->block_kv);
   if (bm->B < 1 || bm->H < 1) return fail(FA_ERR_SHAPE, "table extents B, H must be >= 1 (got %d, %d)", bm->B, bm->H);
   if (bm->q_len < 0 || bm->kv_len < 0 || bm->q_offset < 0)
     return fail(FA_ERR_SHAPE, "q_len, kv_len and q_offset must be >= 0");
   if (bm->q_offset + bm->q_len > kMaxPos || bm->kv_len > kMaxPos)
     return fail(FA_ERR_SHAPE, "positions must stay below 2^31");
+  const int64_t nqb = cdiv(bm->q_len, bm->block_q), nkb = cdiv(bm->kv_len, bm->block_kv);
+  if (nqb > 0 && nkb > 0 && (int64_t)bm->B * bm->H > kMaxGridBlocks / nqb / nkb)
+    return fail(FA_ERR_SHAPE, "B*H*NQB*NKB = %d*%d*%lld*%lld blocks exceed the 32-bit list positions", bm->B, bm->H,
+                (long long)nqb, (long long)nkb);
   fa_status s = check_program(bm->mask, prog);
   if (s != FA_OK) return s;
   if (prog->has_doc) {
@@ -196,6 +211,9 @@ fa_status plan_forward(const fa_fwd_args* a, FwdPlan* plan) {
   fa::MaskProg prog;
   fa_status s = check_mask_geometry(bm, &prog);
   if (s != FA_OK) return s;
+  if (!block_ok(bm->block_q) || !block_ok(bm->block_kv))
+    return fail(FA_ERR_UNSUPPORTED, "the attention kernels run on 64- or 128-blocks (tables of %d x %d)", bm->block_q,
+                bm->block_kv);
   if (bm->q_len != a->q_len || bm->kv_len != a->kv_len)
     return fail(FA_ERR_MASK_MISMATCH, "block tables were built for q_len=%lld kv_len=%lld, forward has %lld, %lld",
                 (long long)bm->q_len, (long long)bm->kv_len, (long long)a->q_len, (long long)a->kv_len);
@@ -220,7 +238,9 @@ fa_status plan_forward(const fa_fwd_args* a, FwdPlan* plan) {
       break;
     case FA_S_RELPOS:
       if (!sd.relpos) return fail(FA_ERR_NULL, "relative-position bias needs its table");
-      if (sd.relpos_radius < 0) return fail(FA_ERR_UNSUPPORTED, "relpos_radius must be >= 0");
+      if (sd.relpos_radius < 0 || sd.relpos_radius > kMaxRelposRadius)
+        return fail(FA_ERR_UNSUPPORTED, "relpos_radius must be in [0, %d] (got %d)", kMaxRelposRadius,
+                    sd.relpos_radius);
       break;
     default:
       return fail(FA_ERR_UNSUPPORTED, "unknown score_mod kind %d", sd.kind);
@@ -314,8 +334,9 @@ const char* fa_last_error_message(void) { return g_err.c_str(); }
 fa_status fa_block_mask_sizes(const fa_block_mask* bm, int64_t* rows, int64_t* cols, int64_t* idx_capacity,
                               size_t* workspace_bytes) {
   if (!bm) return fail(FA_ERR_NULL, "bm is NULL");
-  if (!block_ok(bm->block_q) || !block_ok(bm->block_kv))
-    return fail(FA_ERR_UNSUPPORTED, "block sizes must be 64 or 128 (got %d x %d)", bm->block_q, bm->block_kv);
+  if (!table_block_ok(bm->block_q) || !table_block_ok(bm->block_kv))
+    return fail(FA_ERR_UNSUPPORTED, "block sizes must be powers of two from 1 to 128 (got %d x %d)", bm->block_q,
+                bm->block_kv);
   if (bm->B < 1 || bm->H < 1) return fail(FA_ERR_SHAPE, "table extents B, H must be >= 1");
   if (bm->q_len < 0 || bm->kv_len < 0 || bm->q_offset < 0) return fail(FA_ERR_SHAPE, "negative length or offset");
   if (bm->q_offset + bm->q_len > kMaxPos || bm->kv_len > kMaxPos) return fail(FA_ERR_SHAPE, "positions must stay below 2^31");

@@ -17,9 +17,12 @@
 //     of the row's listed blocks with equal block counts.
 //   * each wave runs one unit on its own: no barriers.  It streams 16-key stages
 //     HBM -> LDS with global_load_lds_dwordx4 (no staging registers) into a private
-//     five-slot ring and keeps four stages in flight while it computes one; a vmcnt
-//     wait per stage is the only synchronisation.  Four waves per CU fill the 160 KB
-//     of LDS.
+//     ring of NS slots and keeps NS - 1 stages in flight while it computes one; a vmcnt
+//     wait per stage is the only synchronisation.  A slot holds the stage's K rows,
+//     then its V rows, then (position-table score_mod only) the 1 KB of table entries
+//     of its 16 columns x 16 keys.  NS = 5 (8 KB slots at d = 128, 160 KB for the four
+//     waves of a workgroup) for every score_mod but the position table, whose larger
+//     slots leave room for NS = 4 (144 KB at d = 128).
 //   * K and V of a stage are row-major in LDS with the XOR swizzles of the prefill
 //     kernels (conflict-free on the 64-bank LDS): scores from ds_read_b128 fragments,
 //     the P V operand from ds_read_b64_tr_b16.

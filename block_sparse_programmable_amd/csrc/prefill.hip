@@ -460,10 +460,10 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   // latency), then multiplies P of step g-1 with V and runs QK quarter g; no MFMA of a
   // group waits on VALU of the same group.
   auto fused = [&](auto vs_c, auto ks_c, const f32x16 (&s)[2], f32x16 (&sn)[2],
-                   const TileMode& md) -> float {
+                   const TileMode& md, auto qk_c) -> float {
     constexpr int VS = decltype(vs_c)::value;
     constexpr int KS = decltype(ks_c)::value;
-    constexpr bool QK = true;
+    constexpr bool QK = decltype(qk_c)::value;   // the last step of a pass has no next tile
     constexpr int KQ = KSTEPS / 2;   // k-steps per quarter of the QK product
     const uint8_t* vb = smem + (2 + VS) * L::TILE;
     const uint8_t* kb = smem + KS * L::TILE;
@@ -559,6 +559,9 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
     f32x16 sa[2], sb[2];
     qk(std::integral_constant<int, 0>{}, sa);
     TileMode md = prep(sa, sub_part(0), sub_part(0) || j0_a + KT > kv_len, j0_a, std::integral_constant<int, 0>{});
+    // step 0 refills K slot 0 (with its document-ID and position-window slots), which
+    // every wave has just read above
+    if (nsub > 2) __syncthreads();
 
     // step s (slot parity P = s & 1): V_s in V slot P, K_{s+1} in K slot 1-P; copies of
     // K_{s+2} into K slot P and V_{s+1} into V slot 1-P
@@ -570,8 +573,10 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       if (s + 2 < nsub) copy_op(sub_j0(s + 2), std::false_type{}, SP{});
       if (more) copy_op(j0_b, std::true_type{}, SQ{});
       // the last step of a pass also multiplies the (stale) other K slot: its scores are
-      // discarded, and one code path keeps the register allocation of the loop intact
-      l_run += fused(SP{}, SQ{}, scur, snxt, md);
+      // discarded.  A second copy of the step without that product makes the register
+      // allocator spill (about 250-470 bytes per lane), which costs far more than the
+      // 16 MFMAs per pass it saves.
+      l_run += fused(SP{}, SQ{}, scur, snxt, md, std::true_type{});
       if (more) {
         const bool part = sub_part(s + 1);
         md = prep(snxt, part, part || j0_b + KT > kv_len, j0_b, SQ{});

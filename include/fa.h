@@ -127,7 +127,8 @@ typedef struct {
   fa_mask_desc mask;
   int32_t B, H;                     /* table extents                                   */
   int64_t q_len, kv_len, q_offset;  /* i_global = i + q_offset                          */
-  int32_t block_q, block_kv;        /* each 64 or 128                                   */
+  int32_t block_q, block_kv;        /* powers of two, 1 .. 128 (64 or 128 to be read by
+                                       fa_forward / fa_forward_paged / fa_backward)     */
   int32_t *kv_num, *kv_ptr, *kv_idx, *full_kv_num, *full_kv_ptr, *full_kv_idx;
   int32_t *q_num, *q_ptr, *q_idx, *full_q_num, *full_q_ptr, *full_q_idx;
   int32_t* order;   /* optional work order, [rows] or NULL -- see below */
@@ -144,7 +145,12 @@ fa_status fa_block_mask_sizes(const fa_block_mask* bm, int64_t* rows, int64_t* c
 /* Classify every block exactly and write all twelve arrays of *bm on `stream`.
  * `workspace` is a device buffer of at least workspace_bytes (its contents on entry
  * are ignored and on exit unspecified).  Deterministic: the same inputs always give
- * the same tables bit for bit. */
+ * the same tables bit for bit.  The table writers (this call, the selector and slice
+ * calls below) accept every power-of-two block size from 1 to 128 -- the pages' worked
+ * examples use 2 x 2 and 4 x 4 blocks ("FlexAttention: from rules to fused kernels",
+ * sec. 2.2; "FlexAttention: compiler optimization of custom attention", sec. 4) --
+ * while the attention kernels read tables of 64- or 128-blocks only.  B*H*NQB*NKB
+ * must stay below 2^31 (FA_ERR_SHAPE otherwise): list positions are int32. */
 fa_status fa_create_block_mask(fa_block_mask* bm, void* workspace, size_t ws_bytes,
                                fa_stream_t stream);
 
@@ -207,7 +213,8 @@ fa_status fa_block_mask_slice(const fa_block_mask* src, fa_block_mask* dst, void
  *   FA_S_IDENTITY  s
  *   FA_S_ALIBI     s + slope[h_q] * (j - i)          (slopes: device fp32 [Hq])
  *   FA_S_SOFTCAP   softcap * tanh(s / softcap)        (softcap > 0)
- *   FA_S_RELPOS    s + table[h_q][clip(i - j, -R, R) + R]   (device fp32 [Hq, 2R+1], R >= 0)
+ *   FA_S_RELPOS    s + table[h_q][clip(i - j, -R, R) + R]   (device fp32 [Hq, 2R+1],
+ *                                                           0 <= R <= 2^30 - 1)
  * ALiBi and the relative-position table are indexed by the QUERY head
  * ("FlexAttention: from rules to fused kernels", sec. 1.2); i and j are global positions.
  * -------------------------------------------------------------------------------- */
@@ -225,8 +232,8 @@ typedef struct {
  * Forward.  q: bf16 [B, Hq, q_len, d]; k, v: bf16 [B, Hkv, kv_len, d]; o: bf16
  * [B, Hq, q_len, d]; lse: fp32 [B, Hq, q_len], natural-log log-sum-exp of the modified,
  * masked row.  GQA/MQA: Hq % Hkv == 0 and query head h reads KV head h / (Hq/Hkv)
- * ("FlexAttention: from rules to fused kernels", sec. 1.2).  d in {64, 128}.
- * scale <= 0 selects 1/sqrt(d).  Only the KV blocks listed in *bm are visited; the
+ * ("FlexAttention: from rules to fused kernels", sec. 1.2).  d in {64, 128}, and the
+ * tables' blocks 64 or 128 (FA_ERR_UNSUPPORTED otherwise).  scale <= 0 selects 1/sqrt(d).  Only the KV blocks listed in *bm are visited; the
  * mask rule is evaluated only on PARTIAL blocks (and on the ragged last block).
  * A row with no allowed key gets O = 0 and LSE = -inf.
  * bm must have been built for the same q_len, kv_len (and B/H extents compatible
@@ -255,30 +262,6 @@ typedef struct {
 fa_status fa_forward_workspace_size(const fa_fwd_args* args, size_t* bytes);
 fa_status fa_forward(const fa_fwd_args* args, fa_stream_t stream);
 
-/* ----------------------------------------------------------------------------------
- * Paged KV cache ("FlexAttention: from rules to fused kernels", sec. 5: a per-request
- * page table maps logical KV block j to a physical cache block; the attention rules,
- * score_mod positions and the BlockMask stay in logical positions, and the kernel
- * follows the table while it streams K/V instead of gathering a contiguous copy).
- *
- *   page_table  device int32 [B, pt_stride]: physical page of logical page p of
- *               request b is page_table[b * pt_stride + p]; logical page p holds the
- *               logical keys [p * page_size, (p + 1) * page_size).  Entries may repeat
- *               (requests sharing a prefix share pages).
- *   page_size   keys per page: a power of two, 16 <= page_size <= 65536.
- *   pt_stride   >= ceil(kv_len / page_size) (entries past that count are never read).
- *   num_pages   pages in each cache; every entry read must lie in [0, num_pages).  An
- *               entry outside that range is clamped into it (so every access stays
- *               inside the caches) and the rows that use it get unspecified values.
- *
- * fa_forward_paged takes the same arguments as fa_forward, except that args->k and
- * args->v are the paged caches, bf16 [num_pages, Hkv, page_size, d] each (one
- * contiguous page_size x d slab per page and KV head), and args->kv_len is the
- * logical KV length.  Only the short-query split-KV path is paged: the shape must
- * satisfy the conditions stated for it above, otherwise FA_ERR_UNSUPPORTED.  The workspace is the one
- * fa_forward_workspace_size reports for `args`.  Results equal fa_forward on the
- * logical (gathered) K and V bit for bit.
- * -------------------------------------------------------------------------------- */
 /* ----------------------------------------------------------------------------------
  * Backward ("FlexAttention: from rules to fused kernels", section 4: the scores of each
  * executed block are recomputed from the saved LSE, score_mod is differentiated, and
@@ -319,6 +302,30 @@ typedef struct {
 fa_status fa_backward_workspace_size(const fa_bwd_args* args, size_t* bytes);
 fa_status fa_backward(const fa_bwd_args* args, fa_stream_t stream);
 
+/* ----------------------------------------------------------------------------------
+ * Paged KV cache ("FlexAttention: from rules to fused kernels", sec. 5: a per-request
+ * page table maps logical KV block j to a physical cache block; the attention rules,
+ * score_mod positions and the BlockMask stay in logical positions, and the kernel
+ * follows the table while it streams K/V instead of gathering a contiguous copy).
+ *
+ *   page_table  device int32 [B, pt_stride]: physical page of logical page p of
+ *               request b is page_table[b * pt_stride + p]; logical page p holds the
+ *               logical keys [p * page_size, (p + 1) * page_size).  Entries may repeat
+ *               (requests sharing a prefix share pages).
+ *   page_size   keys per page: a power of two, 16 <= page_size <= 65536.
+ *   pt_stride   >= ceil(kv_len / page_size) (entries past that count are never read).
+ *   num_pages   pages in each cache; every entry read must lie in [0, num_pages).  An
+ *               entry outside that range is clamped into it (so every access stays
+ *               inside the caches) and the rows that use it get unspecified values.
+ *
+ * fa_forward_paged takes the same arguments as fa_forward, except that args->k and
+ * args->v are the paged caches, bf16 [num_pages, Hkv, page_size, d] each (one
+ * contiguous page_size x d slab per page and KV head), and args->kv_len is the
+ * logical KV length.  Only the short-query split-KV path is paged: the shape must
+ * satisfy the conditions stated for it above, otherwise FA_ERR_UNSUPPORTED.  The workspace is the one
+ * fa_forward_workspace_size reports for `args`.  Results equal fa_forward on the
+ * logical (gathered) K and V bit for bit.
+ * -------------------------------------------------------------------------------- */
 typedef struct {
   const int32_t* page_table;
   int64_t pt_stride;

@@ -93,6 +93,10 @@ def test_block_mask_sizes(lib):
     d = _bm(L, B=2, H=3, q_len=300, kv_len=1000, block_q=64, block_kv=128)
     rows, cols, cap, ws = block_mask_sizes(d)
     assert rows == 2 * 3 * 5 and cols == 2 * 3 * 8 and cap == 2 * 3 * 5 * 8 and ws > 0
+    # table writers take any power-of-two block from 1 to 128 (the worked 2 x 2 example)
+    d = _bm(L, q_len=8, kv_len=8, block_q=2, block_kv=2)
+    rows, cols, cap, ws = block_mask_sizes(d)
+    assert (rows, cols, cap) == (4, 4, 16) and ws > 0
 
 
 def _status(fn, *a):
@@ -104,7 +108,14 @@ def test_validation_errors_before_any_launch(lib):
     # builder: bad block size, bad program, missing doc IDs, missing tables, workspace
     d = _bm(L, block_q=96)
     assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_UNSUPPORTED
-    assert b"64 or 128" in lib.fa_last_error_message()
+    assert b"powers of two from 1 to 128" in lib.fa_last_error_message()
+    for bad in (0, 256, 3):
+        d = _bm(L, block_kv=bad)
+        assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_UNSUPPORTED
+    # 32-bit list positions: B * H * NQB * NKB must stay below 2^31
+    d = _bm(L, B=4, H=2, q_len=2 ** 15, kv_len=2 ** 15, block_q=1, block_kv=1)
+    assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_SHAPE
+    assert b"32-bit" in lib.fa_last_error_message()
     d = _bm(L)
     d.mask.n = 2                                  # causal, causal: two values left
     d.mask.node[1].op = L.FA_M_CAUSAL
@@ -167,6 +178,17 @@ def test_forward_validation(lib):
     assert F(_fwd(L, bm, score_kind=L.FA_S_RELPOS)) == L.FA_ERR_NULL
     assert F(_fwd(L, bm, score_kind=L.FA_S_RELPOS, score_relpos=0x1000,
                   score_relpos_radius=-1)) == L.FA_ERR_UNSUPPORTED
+    # 2R + 1 table entries per head must stay below 2^31
+    assert F(_fwd(L, bm, score_kind=L.FA_S_RELPOS, score_relpos=0x1000,
+                  score_relpos_radius=2 ** 30)) == L.FA_ERR_UNSUPPORTED
+    assert b"relpos_radius" in lib.fa_last_error_message()
+    # tables of blocks below 64 are valid tables but not a forward geometry
+    for bq, bk in ((32, 128), (128, 16), (2, 2)):
+        bms = _bm(L, block_q=bq, block_kv=bk)
+        for name in ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx"):
+            setattr(bms, name, 0x1000)
+        assert F(_fwd(L, bms)) == L.FA_ERR_UNSUPPORTED, (bq, bk)
+        assert b"64- or 128-blocks" in lib.fa_last_error_message()
     assert F(_fwd(L, bm, scale=float("nan"))) == L.FA_ERR_SHAPE
     bm2 = _bm(L, B=3)
     for name in ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx"):

@@ -68,14 +68,65 @@ def test_deterministic_repeat():
         assert_tables_equal(b, a, "repeat")
 
 
-def test_worked_example_n8_needs_supported_blocks():
-    # the N=8, 2x2 example uses blocks below the supported 64/128; its scaled
-    # version (every length and block x 64) has the same grid
+def _grid_rows(got, nqb):
+    """Per query block: (full list, partial list) of the kv side."""
+    return [(list(got["full_kv_idx"][got["full_kv_ptr"][r]:got["full_kv_ptr"][r + 1]]),
+             list(got["kv_idx"][got["kv_ptr"][r]:got["kv_ptr"][r + 1]])) for r in range(nqb)]
+
+
+def _golden_row(line):
+    return ([c for c, ch in enumerate(line) if ch == "F"], [c for c, ch in enumerate(line) if ch == "P"])
+
+
+def test_worked_example_n8_w4_2x2(golden):
+    """The teaching example at its own size ("FlexAttention: from rules to fused
+    kernels", section 2.2, Fig. 1): length 8, window 4, 2 x 2 blocks, built by the GPU
+    builder through the C ABI; bit-exact against the oracle and the fixture's grid."""
+    kv, _ = golden("worked_n8_w4_2x2.txt")
+    got = check_tables(("swa", kv["W"]), 1, 1, kv["q_len"], kv["kv_len"], kv["block_q"], kv["block_kv"])
+    nqb = kv["q_len"] // kv["block_q"]
+    assert _grid_rows(got, nqb) == [_golden_row(line) for line in kv["grid"]]
+    executed = int(got["kv_ptr"][-1] + got["full_kv_ptr"][-1])
+    assert executed == kv["executed_blocks"]
+    assert nqb * (kv["kv_len"] // kv["block_kv"]) - executed == kv["empty_blocks"]
+    # executed elements: every pair of the executed blocks
+    assert executed * kv["block_q"] * kv["block_kv"] == kv["covered_elements"]
+
+
+def test_worked_example_n16_w8_4x4_last_row(golden):
+    """The N=16, W=8, 4 x 4 BlockMask example ("FlexAttention: compiler optimization of
+    custom attention", section 4) at its own size: the last query block's row."""
+    kv, _ = golden("worked_n16_w8_4x4_lastrow.txt")
+    got = check_tables(("swa", kv["W"]), 1, 1, kv["q_len"], kv["kv_len"], kv["block_q"], kv["block_kv"])
+    nqb = kv["q_len"] // kv["block_q"]
+    assert _grid_rows(got, nqb)[-1] == _golden_row(kv["last_row"])
+
+
+def test_worked_example_scaled_grid():
+    # the same grid with every length and block x 64: the forward's block sizes
     got = check_tables(("swa", 4 * 64), 1, 1, 8 * 64, 8 * 64, 128, 128)
-    rows_full = [list(got["full_kv_idx"][got["full_kv_ptr"][r]:got["full_kv_ptr"][r + 1]]) for r in range(4)]
-    rows_part = [list(got["kv_idx"][got["kv_ptr"][r]:got["kv_ptr"][r + 1]]) for r in range(4)]
-    assert rows_full == [[], [0], [1], [2]]
-    assert rows_part == [[0], [1], [0, 2], [1, 3]]
+    assert _grid_rows(got, 4) == [([], [0]), ([0], [1]), ([1], [0, 2]), ([2], [1, 3])]
+
+
+SMALL_BLOCKS = ((2, 2), (4, 4), (8, 8), (16, 16), (2, 8), (16, 4))
+
+
+@pytest.mark.parametrize("spec", LEAVES + PAIRS, ids=[str(s) for s in LEAVES + PAIRS])
+def test_exhaustive_sweep_small_blocks(spec):
+    """Table writers accept power-of-two blocks below 64 (the pages' worked examples use
+    2 x 2 and 4 x 4): the same sweep of rules, lengths, offsets and documents."""
+    torch.cuda.set_device(0)
+    uses_doc = W.mask_uses_doc(spec)
+    for bq, bk in SMALL_BLOCKS:
+        Bm = min(bq, bk)
+        for L in sorted({1, 3, Bm - 1 if Bm > 1 else 2, Bm, Bm + 1, 2 * Bm + 3, 97, 257}):
+            for q_len, kv_len, q_off in ((L, L, 0), (max(1, L // 2), L, L - max(1, L // 2)),
+                                         (L, L + 70, 5)):
+                for kind in (("packed", "nonmono") if uses_doc else (None,)):
+                    doc = None
+                    if kind:
+                        doc = docs_for(max(q_off + q_len, kv_len), kind, seed=L)[None]
+                    check_tables(spec, 1, 1, q_len, kv_len, bq, bk, q_off, doc)
 
 
 @pytest.mark.parametrize("name", [n for n in W.WORKLOADS if W.WORKLOADS[n].selector])
