@@ -17,11 +17,12 @@ FA_ERR_MASK_SPEC, FA_ERR_MASK_MISMATCH, FA_ERR_WORKSPACE, FA_ERR_HIP = 4, 5, 6, 
 FA_M_CAUSAL, FA_M_SWA, FA_M_DOC, FA_M_PREFIX, FA_M_AND, FA_M_OR = 1, 2, 3, 4, 5, 6
 FA_MASK_MAX_NODES = 16
 FA_S_IDENTITY, FA_S_ALIBI, FA_S_SOFTCAP, FA_S_RELPOS = 0, 1, 2, 3
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 # names declared in include/fa.h (checked against the header by the tests)
 EXPORTS = ("fa_block_mask_sizes", "fa_create_block_mask", "fa_block_mask_slice", "fa_block_mask_from_indices",
            "fa_forward_workspace_size",
-           "fa_forward", "fa_forward_paged", "fa_backward_workspace_size", "fa_backward",
+           "fa_forward", "fa_forward_noalloc", "fa_forward_paged", "fa_backward_workspace_size", "fa_backward",
            "fa_status_string", "fa_last_error_message")
 
 
@@ -106,6 +107,8 @@ def load(path: str = LIB_PATH):
     lib.fa_forward.restype = C.c_int
     lib.fa_forward_paged.argtypes = [C.POINTER(fa_fwd_args), C.POINTER(fa_paged_kv), C.c_void_p]
     lib.fa_forward_paged.restype = C.c_int
+    lib.fa_forward_noalloc.argtypes = [C.POINTER(fa_fwd_args), C.c_void_p]
+    lib.fa_forward_noalloc.restype = C.c_int
     lib.fa_backward_workspace_size.argtypes = [C.POINTER(fa_bwd_args), C.POINTER(C.c_size_t)]
     lib.fa_backward_workspace_size.restype = C.c_int
     lib.fa_backward.argtypes = [C.POINTER(fa_bwd_args), C.c_void_p]

@@ -327,3 +327,15 @@ def forward(q, k, v, block_mask: BlockMask, score="identity", softcap=0.0, alibi
         a.ws_bytes = workspace.numel() * workspace.element_size()
     L.check(lib.fa_forward(C.byref(a), _stream(stream)))
     return out, lse
+
+
+def forward_noalloc(q, k, v, block_mask: BlockMask, out, lse, score="identity", softcap=0.0,
+                    alibi_slopes=None, relpos=None, relpos_radius=0, scale=None, stream=None):
+    """fa_forward_noalloc: the forward into the caller's ``out`` [B,Hq,q_len,d] bf16 and
+    ``lse`` [B,Hq,q_len] fp32, with the split-KV partial states in the library's static
+    scratch (no workspace; the call allocates nothing)."""
+    lib = L.load()
+    a, out, lse = forward_args(q, k, v, block_mask, score, softcap, alibi_slopes, relpos,
+                               relpos_radius, scale, out, lse)
+    L.check(lib.fa_forward_noalloc(C.byref(a), _stream(stream)))
+    return out, lse

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "fa.h"
@@ -311,6 +312,48 @@ fa_status plan_forward(const fa_fwd_args* a, FwdPlan* plan) {
   return FA_OK;
 }
 
+fa_status launch_planned(const FwdPlan& plan, const fa_fwd_args* args, fa_stream_t stream) {
+  if (args->q_len == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  fa::FwdParams lp = plan.p;
+  if (plan.per_head) fa::decode_per_head(lp);
+  hipError_t e = plan.decode ? fa::launch_decode(lp, st) : fa::launch_prefill(lp, st);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------------
+// Scratch of fa_forward_noalloc: the split-KV partial states live in this file-scope
+// device array instead of a caller workspace.  Each GPU the library runs on holds its
+// own copy until the process ends.  In host code `scratch` only names the symbol: its
+// device address on the current GPU comes from hipGetSymbolAddress, looked up once per
+// device (with that device current) on the first call there, and only that address is
+// ever handed to kernels.
+// ---------------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+fa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FA_ERR_UNSUPPORTED, "device %d is beyond the %d devices with a scratch slot", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(FA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -506,13 +549,23 @@ fa_status fa_forward_paged(const fa_fwd_args* args, const fa_paged_kv* kv, fa_st
                   args->workspace ? args->ws_bytes : (size_t)0);
     plan.p.ws = static_cast<float*>(args->workspace);
   }
-  if (args->q_len == 0) return ok();
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  fa::FwdParams lp = plan.p;
-  if (plan.per_head) fa::decode_per_head(lp);
-  hipError_t e = plan.decode ? fa::launch_decode(lp, st) : fa::launch_prefill(lp, st);
-  if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return launch_planned(plan, args, stream);
+}
+
+fa_status fa_forward_noalloc(const fa_fwd_args* args, fa_stream_t stream) {
+  FwdPlan plan;
+  fa_status s = plan_forward(args, &plan);
+  if (s != FA_OK) return s;
+  if (plan.ws > (size_t)FA_NOALLOC_SCRATCH_BYTES)
+    return fail(FA_ERR_WORKSPACE, "this forward needs %zu bytes of split-KV scratch; the static scratch holds %zu",
+                plan.ws, (size_t)FA_NOALLOC_SCRATCH_BYTES);
+  if (plan.ws > 0 && args->q_len > 0) {
+    void* ptr = nullptr;
+    s = scratch_of_current_device(&ptr);
+    if (s != FA_OK) return s;
+    plan.p.ws = static_cast<float*>(ptr);
+  }
+  return launch_planned(plan, args, stream);
 }
 
 fa_status fa_block_mask_from_indices(fa_block_mask* bm, const int32_t* sel, int32_t k, void* workspace,

@@ -263,6 +263,25 @@ fa_status fa_forward_workspace_size(const fa_fwd_args* args, size_t* bytes);
 fa_status fa_forward(const fa_fwd_args* args, fa_stream_t stream);
 
 /* ----------------------------------------------------------------------------------
+ * fa_forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same forward,
+ * with the same arguments, results and errors as fa_forward, except that
+ * args->workspace and args->ws_bytes are ignored and the split-KV partial states of
+ * the short-query path live in a static device array of the library,
+ * FA_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, held from the first call on that GPU
+ * until the process ends.  A shape whose fa_forward_workspace_size exceeds it returns
+ * FA_ERR_WORKSPACE before anything is launched (the partial states take
+ * B * Hq * q_len * splits * (d + 2) * 4 bytes; no short-query shape on a 256-CU GPU
+ * needs more than about 12.2 MiB).  The call itself allocates nothing: no hipMalloc, hipFree or
+ * allocating library routine.  Every kernel reads only the scratch entries the same
+ * call wrote before, so nothing needs clearing between calls; but every call on one
+ * GPU shares that GPU's array, so calls whose device work overlaps (on different
+ * streams, or from different threads) race and must be serialised by the caller.
+ * -------------------------------------------------------------------------------- */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+fa_status fa_forward_noalloc(const fa_fwd_args* args, fa_stream_t stream);
+
+/* ----------------------------------------------------------------------------------
  * Backward ("FlexAttention: from rules to fused kernels", section 4: the scores of each
  * executed block are recomputed from the saved LSE, score_mod is differentiated, and
  * the block tables are walked per query row for dQ and per KV column -- the q-side

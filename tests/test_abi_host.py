@@ -198,6 +198,13 @@ def test_forward_validation(lib):
     for name in ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx"):
         setattr(bm3, name, 0x1000)
     assert F(_fwd(L, bm3)) == L.FA_ERR_MASK_MISMATCH
+    # the no-allocation forward validates exactly like fa_forward, before any GPU work
+    N = lambda a: lib.fa_forward_noalloc(C.byref(a), None)
+    assert lib.fa_forward_noalloc(None, None) == L.FA_ERR_NULL
+    assert N(_fwd(L, bm, q=None)) == L.FA_ERR_NULL
+    assert N(_fwd(L, bm, d=96)) == L.FA_ERR_UNSUPPORTED
+    assert N(_fwd(L, bm, q_len=128)) == L.FA_ERR_MASK_MISMATCH
+    assert N(_fwd(L, bm2)) == L.FA_ERR_MASK_MISMATCH
     # paged caches: argument checks, and the paged cache is only read by the short-query path
     P = lambda a, kv: lib.fa_forward_paged(C.byref(a), C.byref(kv), None)
     kv = L.fa_paged_kv(page_table=0x1000, pt_stride=16, page_size=16, num_pages=4)
