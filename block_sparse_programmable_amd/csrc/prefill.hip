@@ -110,7 +110,19 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   const int i_g = i_loc + (int)p.q_offset;
   const int i_wave0 = r * BQ + w * 32 + (int)p.q_offset;   // first row of the wave
 
-  // ---- Q fragments (B operand of S^T = K Q^T): lane holds Q[row][16t + 8 half .. +8]
+  // ---- block-table row, read through the constant address space at wave-uniform
+  // indexes (scalar loads): it starts the item's longest chain of dependent loads (row
+  // -> list entries -> tile copies), so it goes out first
+  using cptr = const __attribute__((address_space(4))) int32_t*;
+  const int row = (tb * p.tab.tH + th) * nqb + r;
+  const int nf = ((cptr)sreg(p.tab.fnum))[row];
+  const int np = ((cptr)sreg(p.tab.num))[row];
+  const int32_t* flist = p.tab.fidx + ((cptr)sreg(p.tab.fptr))[row];
+  const int32_t* plist = p.tab.idx + ((cptr)sreg(p.tab.ptr))[row];
+  const int bk = p.tab.bk;
+
+  // ---- Q fragments (B operand of S^T = K Q^T): lane holds Q[row][16t + 8 half .. +8].
+  // The loads stay in flight until the first tiles have arrived (see the prologue).
   bf16x8 qf[KSTEPS];
   {
     const uint16_t* qrow = p.q + ((int64_t)bh * p.q_len + (row_ok ? i_loc : 0)) * D;
@@ -119,19 +131,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       u32x4 v = row_ok ? load16(qrow + 16 * t + 8 * half) : u32x4{0, 0, 0, 0};
       qf[t] = __builtin_bit_cast(bf16x8, v);
     }
-    // consume the loads here: the block loop's HBM -> LDS copies are invisible to the
-    // compiler's wait counting, which would otherwise wait for all memory at every tile
-#pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) asm volatile("" : "+v"(qf[t]));
   }
-
-  // ---- block-table row
-  const int row = (tb * p.tab.tH + th) * nqb + r;
-  const int nf = uniform(p.tab.fnum[row]);
-  const int np = uniform(p.tab.num[row]);
-  const int32_t* flist = p.tab.fidx + uniform(p.tab.fptr[row]);
-  const int32_t* plist = p.tab.idx + uniform(p.tab.ptr[row]);
-  const int bk = p.tab.bk;
   const int spb_sh = bk == 2 * KT ? 1 : 0;   // sub-tiles per block = 1 << spb_sh
   const int n_ent = nf + np;
 
@@ -139,10 +139,6 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   const uint16_t* vbase = p.v + (int64_t)(b * p.Hkv + hkv) * p.kv_len * D;
   const int32_t* docr = doc_row(p.doc, b);
   int doc_i = (p.prog.has_doc && row_ok) ? docr[i_g] : 0;
-  // consumed here: its first use is inside the tile loop on paths that full tiles skip,
-  // and a load still counted as pending there makes every use wait for all memory,
-  // tile copies in flight included
-  asm volatile("" : "+v"(doc_i));
   const ScoreCtx sc = make_score_ctx(p.score, p.scale, hq);
 
   // per-row allowed key interval of the pre-compiled mask (partial blocks only)
@@ -537,24 +533,35 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   // Software pipeline over sub-tiles: while the weights of sub-tile s are formed and
   // multiplied with V_s, the scores of s+1 are computed from K_{s+1}; K runs one sub-tile
   // ahead of V in the copies (K_{s+2} and V_{s+1} are in flight during step s).
+  const cptr flist_c = (cptr)sreg(flist), plist_c = (cptr)sreg(plist);
   for (int c0 = 0; c0 < n_ent; c0 += kListCap) {
     const int cnt = min(kListCap, n_ent - c0);
+    const int nsub = cnt << spb_sh;
+    // prologue: K_0, V_0 (and K_1) resident, scores of sub-tile 0 prepared.  The first
+    // tiles' positions come from scalar loads of the list, so their copies go out
+    // before the list is staged in LDS and the two round trips overlap.
+    auto ent = [&](int e) -> int { return c0 + e < nf ? flist_c[c0 + e] : plist_c[c0 + e - nf]; };
+    int j0_a = ent(0) * bk;                                                  // sub-tile s
+    int j0_b = nsub > 1 ? ent(1 >> spb_sh) * bk + (1 & spb_sh) * KT : 0;     // sub-tile s + 1
+    copy_op(j0_a, std::false_type{}, std::integral_constant<int, 0>{});
+    copy_op(j0_a, std::true_type{}, std::integral_constant<int, 0>{});
+    if (nsub > 1) copy_op(j0_b, std::false_type{}, std::integral_constant<int, 1>{});
     for (int e = tid; e < cnt; e += NT) {
       const int ge = c0 + e;
       list_s[e] = ge < nf ? flist[ge] : plist[ge - nf];
     }
-    __syncthreads();
-    const int nsub = cnt << spb_sh;
     auto sub_j0 = [&](int s) -> int { return uniform(list_s[s >> spb_sh]) * bk + (s & spb_sh) * KT; };
     auto sub_part = [&](int s) -> bool { return c0 + (s >> spb_sh) >= nf; };
-
-    // prologue: K_0, V_0 (and K_1) resident, scores of sub-tile 0 prepared
-    int j0_a = sub_j0(0);                       // sub-tile s
-    int j0_b = nsub > 1 ? sub_j0(1) : 0;        // sub-tile s + 1
-    copy_op(j0_a, std::false_type{}, std::integral_constant<int, 0>{});
-    copy_op(j0_a, std::true_type{}, std::integral_constant<int, 0>{});
-    if (nsub > 1) copy_op(j0_b, std::false_type{}, std::integral_constant<int, 1>{});
     wait_dma();
+    if (c0 == 0) {
+      // consume Q and the row's document ID now that every load of the prologue has
+      // landed: the tile copies are invisible to the compiler's wait counting, so a
+      // load still counted as pending inside the tile loop would make its uses wait
+      // for all memory, copies in flight included
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t) asm volatile("" : "+v"(qf[t]));
+      asm volatile("" : "+v"(doc_i));
+    }
     __syncthreads();
     f32x16 sa[2], sb[2];
     qk(std::integral_constant<int, 0>{}, sa);
