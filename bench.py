@@ -2,13 +2,17 @@
 """Benchmark of the block-sparse attention hot path on one MI355X.
 
 One step = fa_create_block_mask + fa_forward over one synthetic batch of the chosen
-workload (default: causal attention with tanh soft-cap, B=2, H=16, N=4096, d=128,
-128x128 blocks).  Inputs are resident in HBM before the timed region starts.
+workload (default: the 64K prefix-LM with a relative-position table, B=1, Hq=16,
+Hkv=2, N=65536, d=128, 128x128 blocks -- the largest single-GPU configuration).
+Inputs are resident in HBM before the timed region starts.
 
 Printed: ONE JSON line with the throughput over executed blocks (TFLOP/s for prefill
-workloads, GB/s for the decode workload), the roofline position of the dominant
-kernel (timed with HIP events on its own stream inside the timed region) and the
-CPU oracle timed on a bounded sample of the same workload.
+workloads, GB/s for decode workloads), the roofline position of the dominant kernel
+(timed with HIP events on its launch stream inside the timed region) and the CPU oracle
+timed on a bounded sample of the same workload.  The same line carries a "decode"
+object (split-KV decode, B=64, KV 32768, GB/s against HBM) and an "extra" object with
+the causal soft-cap and GQA document-window workloads, each with its own steps,
+roofline and oracle baseline.
 """
 from __future__ import annotations
 
@@ -112,19 +116,46 @@ def row_stats(tab):
             "full": int(tab["full_kv_ptr"][-1]), "partial": int(tab["kv_ptr"][-1])}
 
 
-def cpu_baseline(w, aux, q, k, v, acc, budget_s):
-    """The oracle, as is, on a bounded sample: whole heads (prefill) or whole
-    batch entries (decode) until the time budget is used."""
+def _blas_threads():
+    """BLAS threads numpy uses: os.cpu_count(), capped by OMP_NUM_THREADS when the
+    environment sets it (a machine's CPU share can be smaller than its core count)."""
+    n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return n
+
+
+def _spread(n):
+    """0 .. n-1 in an order that samples the whole range early (stride coprime to n)."""
+    if n <= 2:
+        return list(range(n))
+    step = max(1, int(n * 0.618))
+    while math.gcd(step, n) != 1:
+        step += 1
+    return [(x * step) % n for x in range(n)]
+
+
+def cpu_baseline(w, aux, q, k, v, acc, tab_host, budget_s):
+    """The oracle, as is, on a bounded sample of the same workload, with numpy's BLAS
+    on ``_blas_threads()`` threads.  Block tables: the whole grid, or for grids of more
+    than 64 query blocks 16 query blocks (four runs of four, spread over the grid, each
+    classified as the rows [r0 B_q, (r0 + 4) B_q) of the same rule) prorated to the grid.
+    Attention: whole query blocks (prefill; spread over the rows, heads in turn) or whole
+    requests (decode), until the time budget is used, each credited with its own
+    executed-block FLOP (bytes for decode)."""
     import numpy as np
     from oracle import attention as OA
     from oracle import blockmask as OB
+    threads = _blas_threads()
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    t0 = time.perf_counter()
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(threads)
+    except Exception:   # pragma: no cover - threadpoolctl is part of the image
+        limiter = None
+    nqb = -(-w.q_len // w.block_q)
     mask_of = lambda b, h=None: w.mask   # noqa: E731
+    t0 = time.perf_counter()
     if w.selector:
         # the selected-pair matrix is evaluated inside the attention, row chunk by chunk;
         # the oracle sees a one-request (and, for prefill, one-head) slice, so the global
@@ -132,6 +163,8 @@ def cpu_baseline(w, aux, q, k, v, acc, budget_s):
         import workloads as W
         from oracle import selector as OS
         sets = OS.canonical_sets(W.selector_indices(w), -(-w.kv_len // w.block_kv))
+        t_tab = time.perf_counter() - t0
+        tab_sample = "selector candidate sets (canonicalised)"
 
         def mask_of(b, h=None):
             def fn(bb, hh, i, j):
@@ -140,64 +173,89 @@ def cpu_baseline(w, aux, q, k, v, acc, budget_s):
                                      w.block_q, w.block_kv, w.q_offset, None, rows=rows)
                 return M[:, np.asarray(j).reshape(-1)]
             return fn
-    else:
+    elif nqb <= 64:
         OB.tables(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset, aux["doc_ids"])
-    t_tab = time.perf_counter() - t0
-    kw = dict(cap=w.cap or None, slopes=aux["slopes"], table=aux["table"], radius=w.relpos_radius,
-              q_offset=w.q_offset, doc_ids=aux["doc_ids"])
+        t_tab = time.perf_counter() - t0
+        tab_sample = f"whole grid ({nqb} query blocks)"
+    else:
+        starts = [(nqb * x) // 4 for x in range(4)]
+        for r0 in starts:
+            n = min(4, nqb - r0)
+            OB.tables(w.mask, 1, 1, min(n * w.block_q, w.q_len - r0 * w.block_q), w.kv_len, w.block_q,
+                      w.block_kv, w.q_offset + r0 * w.block_q, aux["doc_ids"])
+        t_tab = (time.perf_counter() - t0) * nqb / 16
+        tab_sample = f"16 of {nqb} query blocks (rows from blocks {starts}, four each), prorated"
+    kw = dict(cap=w.cap or None, radius=w.relpos_radius, doc_ids=aux["doc_ids"])
     done = 0
     t_attn = 0.0
+    credited = 0.0
     if w.q_len == 1:
         units = w.B
         per_unit = acc["bytes"] / w.B
         while done < units and t_attn < budget_s:
             b = done
-            qb, kb, vb = (t[b:b + 1].cpu() for t in (q, k, v))
+            qb, kb, vb = (OA._as_f64(t[b:b + 1]) for t in (q, k, v))
             t1 = time.perf_counter()
-            OA.attention(qb, kb, vb, mask_of(b), w.score, **kw)
+            OA.attention(qb, kb, vb, mask_of(b), w.score, slopes=aux["slopes"], table=aux["table"],
+                         q_offset=w.q_offset, **kw)
             t_attn += time.perf_counter() - t1
             done += 1
-        rate = per_unit * done / (t_attn + t_tab) / 1e9
-        unit, sample = "GB/s", f"{done} of {units} requests (all {w.Hq} heads), plus the block tables"
+            credited += per_unit
+        value = credited / (t_attn + t_tab) / 1e9
+        unit = "GB/s"
+        sample = f"{done} of {units} requests (all {w.Hq} heads), credited with their bytes"
     else:
-        units = w.B * w.Hq
-        per_unit = acc["flop"] / units
-        credited = 0.0
-        kc = {}
+        lens = np.asarray(tab_host["kv_num"]) + np.asarray(tab_host["full_kv_num"])
+        per_entry = "per_entry_executed" in acc
+        blk_flop = 4 * w.block_q * w.block_kv * w.d
+        units = w.B * w.Hq * nqb
+        order = _spread(nqb)
+        kvc, qc = {}, {}
         while done < units and t_attn < budget_s:
-            b, h = divmod(done, w.Hq)
+            r = order[done % nqb]
+            b, h = divmod((done // nqb + done) % (w.B * w.Hq), w.Hq)
             hkv = h // w.g
-            if (b, hkv) not in kc:
-                kc = {(b, hkv): (k[b:b + 1, hkv:hkv + 1].cpu(), v[b:b + 1, hkv:hkv + 1].cpu())}
-            kb, vb = kc[(b, hkv)]
-            qb = q[b:b + 1, h:h + 1].cpu()
+            if (b, hkv) not in kvc:
+                kvc = {(b, hkv): (OA._as_f64(k[b:b + 1, hkv:hkv + 1]), OA._as_f64(v[b:b + 1, hkv:hkv + 1]))}
+            if (b, h) not in qc:
+                qc = {(b, h): OA._as_f64(q[b:b + 1, h:h + 1])}
+            kb, vb = kvc[(b, hkv)]
+            r0, r1 = r * w.block_q, min((r + 1) * w.block_q, w.q_len)
+            qb = qc[(b, h)][:, :, r0:r1]
             sl = None if aux["slopes"] is None else aux["slopes"][h:h + 1]
             tb = None if aux["table"] is None else aux["table"][h:h + 1]
+            fn = mask_of(b, h)   # rules and pair functions both see global positions
             t1 = time.perf_counter()
-            OA.attention(qb, kb, vb, mask_of(b, h), w.score, cap=w.cap or None, slopes=sl, table=tb,
-                         radius=w.relpos_radius, q_offset=w.q_offset, doc_ids=aux["doc_ids"])
+            OA.attention(qb, kb, vb, fn, w.score, slopes=sl, table=tb, q_offset=w.q_offset + r0, **kw)
             t_attn += time.perf_counter() - t1
-            if "per_entry_executed" in acc:   # per-head tables: this head's own blocks
-                credited += acc["per_entry_executed"][done] * 4 * w.block_q * w.block_kv * w.d
-            else:
-                credited += per_unit
+            row = (b * w.Hq + h) * nqb + r if per_entry else r
+            credited += int(lens[row]) * blk_flop
             done += 1
-        rate = credited / (t_attn + t_tab * done / units) / 1e12
+        value = credited / (t_attn + t_tab * min(1.0, done / units)) / 1e12
         unit = "TFLOP/s"
-        sample = (f"{done} of {units} (batch, head) pairs, all {w.q_len} rows each, credited with "
-                  f"their executed-block FLOP; block tables timed once ({t_tab:.2f} s) and prorated")
-    return {"value": rate, "unit": unit, "cores": int(threads), "kind": "oracle", "sample": sample,
-            "seconds": round(t_attn + t_tab, 3)}
+        sample = (f"{done} of {units} (batch, head, query block) items, whole query blocks spread over "
+                  f"the rows, each credited with its executed-block FLOP; block tables prorated to the "
+                  f"sampled share")
+    if limiter is not None:
+        limiter.restore_original_limits()
+    return {"value": value, "unit": unit, "cores": int(threads), "cpu_count": os.cpu_count(),
+            "blas_threads": int(threads), "kind": "oracle", "sample": sample,
+            "blockmask_oracle_s": round(t_tab, 3), "blockmask_sample": tab_sample,
+            "attention_oracle_s": round(t_attn, 3), "seconds": round(t_attn + t_tab, 3)}
 
 
-def run(args):
+def run_workload(args, name, headline=True):
+    """One workload: K timed steps (build + forward) after W warm-up steps, the forward
+    timed with HIP events on its launch stream, the cold-cache legs, and the oracle on a
+    bounded sample.  The optional legs (backward, prebuilt slices, the work-order
+    comparison of selector tables) run for the headline workload only."""
     import numpy as np
     import torch
 
     import block_sparse_programmable_amd as fa
     import workloads as W
 
-    w = W.WORKLOADS[args.workload]
+    w = W.WORKLOADS[name]
     torch.cuda.set_device(0)
     dev = "cuda"
     aux = W.aux_inputs(w)
@@ -302,7 +360,7 @@ def run(args):
     # backward of the same step's forward (prefill workloads): dQ, dK, dV over the
     # block tables, credited with 5 products of 2 Bq Bk d FLOP per executed block
     bwd = None
-    if args.backward and w.q_len > 1:
+    if headline and args.backward and w.q_len > 1:
         dout = W.randn_bf16(tuple(out.shape), w.seed + 7, device=dev)
         fwd(bm)
         gq = torch.empty(q.shape, dtype=torch.float32, device=dev)
@@ -331,7 +389,7 @@ def run(args):
     # latter hands query blocks out by descending index), alternating, back to back, to
     # show what the longest-first order buys
     no_order = None
-    if w.selector:
+    if headline and w.selector:
         bm_n = build(order=False)
         R = max(20, K)
         e = [[torch.cuda.Event(enable_timing=True) for _ in range(R)] for _ in range(4)]
@@ -358,7 +416,7 @@ def run(args):
     # over the slice is timed beside the forward over rebuilt tables
     pre = None
     decode = w.q_len == 1
-    if args.prebuilt and decode:
+    if headline and args.prebuilt and decode:
         Lmax = w.kv_len
         eb = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         eb[0].record()
@@ -411,16 +469,14 @@ def run(args):
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, aux, q, k, v, acc, args.cpu_seconds)
+        cpu = cpu_baseline(w, aux, q, k, v, acc, tab_host, args.cpu_seconds)
 
     cfg = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "q_len": w.q_len, "kv_len": w.kv_len,
            "d": w.d, "block_q": w.block_q, "block_kv": w.block_kv, "mask": repr(w.mask),
            "score_mod": w.score, "q_offset": w.q_offset, "seed": w.seed, "page_size": w.page_size or None,
            "selector": list(w.selector) if w.selector else None,
            "full_blocks": acc["full_blocks"], "partial_blocks": acc["partial_blocks"]}
-    rec = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": K,
-           "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+    rec = {"value": value, "unit": unit, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
            "config": cfg, "roofline": roof, "cpu_baseline": cpu,
            "fwd_ms": fwd_avg, "fwd_ms_p10": float(np.percentile(fwd_ms, 10)),
            "fwd_ms_p90": float(np.percentile(fwd_ms, 90)),
@@ -435,6 +491,34 @@ def run(args):
            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
     if decode:
         rec["forward_workspace_bytes"] = fws_bytes
+    return rec
+
+
+# Workloads timed beside the headline in the same line: the split-KV decode (GB/s
+# against HBM) and the two shorter prefill workloads.
+DECODE_WORKLOAD = "decode_swa_softcap"
+EXTRA_WORKLOADS = ("causal_softcap", "gqa_doc_swa_alibi")
+
+
+def run(args):
+    import torch
+    head = run_workload(args, args.workload, headline=True)
+    torch.cuda.empty_cache()
+    rec = {"metric": METRIC, "value": head.pop("value"), "unit": head.pop("unit"), "n_gpus": 1,
+           "steps": head.pop("steps"), "warmup": head.pop("warmup"), "ms_per_step": head.pop("ms_per_step"),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic"}
+    rec.update(head)
+    rec["decode"] = None
+    rec["extra"] = {}
+    if not args.no_extras:
+        if args.workload != DECODE_WORKLOAD:
+            rec["decode"] = run_workload(args, DECODE_WORKLOAD, headline=False)
+            torch.cuda.empty_cache()
+        for name in EXTRA_WORKLOADS:
+            if name != args.workload:
+                rec["extra"][name] = run_workload(args, name, headline=False)
+                torch.cuda.empty_cache()
     return rec
 
 
@@ -456,9 +540,12 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="causal_softcap")
+    ap.add_argument("--workload", default="prefix_relpos_64k")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the chosen workload only (no decode / extra prefill objects)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the oracle's attention sample per workload")
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward of the forward (prefill workloads)")
     ap.add_argument("--prebuilt", action="store_true",

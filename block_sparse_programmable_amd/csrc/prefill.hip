@@ -551,6 +551,10 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       list_s[e] = ge < nf ? flist[ge] : plist[ge - nf];
     }
     auto sub_j0 = [&](int s) -> int { return uniform(list_s[s >> spb_sh]) * bk + (s & spb_sh) * KT; };
+    // the list entry of the K copy of the next step, read one step ahead and kept as the
+    // raw LDS value, so that no step starts with an LDS round trip
+    auto raw_ent = [&](int s) -> int { return list_s[s >> spb_sh]; };
+    int kpos_raw = 0;
     auto sub_part = [&](int s) -> bool { return c0 + (s >> spb_sh) >= nf; };
     wait_dma();
     if (c0 == 0) {
@@ -569,6 +573,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
     // step 0 refills K slot 0 (with its document-ID and position-window slots), which
     // every wave has just read above
     if (nsub > 2) __syncthreads();
+    kpos_raw = nsub > 2 ? raw_ent(2) : 0;
 
     // step s (slot parity P = s & 1): V_s in V slot P, K_{s+1} in K slot 1-P; copies of
     // K_{s+2} into K slot P and V_{s+1} into V slot 1-P
@@ -577,7 +582,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       using SP = std::integral_constant<int, P>;
       using SQ = std::integral_constant<int, 1 - P>;
       const bool more = s + 1 < nsub;
-      if (s + 2 < nsub) copy_op(sub_j0(s + 2), std::false_type{}, SP{});
+      if (s + 2 < nsub) copy_op(uniform(kpos_raw) * bk + ((s + 2) & spb_sh) * KT, std::false_type{}, SP{});
       if (more) copy_op(j0_b, std::true_type{}, SQ{});
       // the last step of a pass also multiplies the (stale) other K slot: its scores are
       // discarded.  A second copy of the step without that product makes the register
@@ -590,6 +595,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
         j0_a = j0_b;
         j0_b = s + 2 < nsub ? sub_j0(s + 2) : 0;
       }
+      kpos_raw = s + 3 < nsub ? raw_ent(s + 3) : 0;
       wait_dma();
       __syncthreads();
     };
