@@ -394,25 +394,31 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
         for (int rr = 0; rr < 16; ++rr)
           s[mt][rr] = __builtin_fmaf(s[mt][rr], sc.c2, __builtin_fmaf(sc.slope2, (float)key_of(mt, rr), base));
     }
+    // the maximum of this lane's half of the row's tile (16 of the 32 keys per 32-key
+    // tile; the other half lives in lane ^ 32)
     float tmax = kNegInf;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, s[mt][rr]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     // map a raw-score maximum into the base-2 domain
-    float m_cand = tmax;
-    if (raw && tmax != kNegInf) {
-      if constexpr (SCORE == FA_S_SOFTCAP) {
-        m_cand = sc.cap2 - 2.f * sc.cap2 * fast_rcp(fast_exp2(tmax * sc.capk) + 1.f);
-      } else {
-        m_cand = __builtin_fmaf(tmax, sc.c2, bias2);
+    auto to_base2 = [&](float t) -> float {
+      if (raw && t != kNegInf) {
+        if constexpr (SCORE == FA_S_SOFTCAP) {
+          return sc.cap2 - 2.f * sc.cap2 * fast_rcp(fast_exp2(t * sc.capk) + 1.f);
+        } else {
+          return __builtin_fmaf(t, sc.c2, bias2);
+        }
       }
-    }
+      return t;
+    };
     // lazy rescale (wave-uniform branch): the reference moves only when a row's tile
-    // maximum exceeds it by more than kRescaleThresh
-    const bool grow = m_cand > m_run + kRescaleThresh;
-    if (__ballot(grow) != 0) {
+    // maximum exceeds it by more than kRescaleThresh.  A row's maximum exceeds it iff one
+    // of its halves does, so the exchange between the halves (an LDS round trip) is
+    // needed only inside the rare rescale branch.
+    if (__ballot(to_base2(tmax) > m_run + kRescaleThresh) != 0) {
+      const float m_cand = to_base2(fmaxf(tmax, __shfl_xor(tmax, 32)));
+      const bool grow = m_cand > m_run + kRescaleThresh;
       const float m_new = grow ? m_cand : m_run;
       const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;   // 0 when m_run = -inf
       m_run = m_new;
@@ -507,10 +513,14 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
         psum += pv2[0] + pv2[1];
       }
     };
+    // The fragments of each group are read one group ahead, right after the MFMAs that
+    // consumed the previous ones were issued, so their LDS latency runs under those
+    // MFMAs; only group 0's K quarter is read at entry, where the weights of 16-key
+    // step 0 (VALU) cover it.
+    if constexpr (QK) read_k(std::integral_constant<int, 0>{}, kf);
+    __builtin_amdgcn_sched_barrier(0);
     static_for<5>([&](auto g_c) {
       constexpr int g = decltype(g_c)::value;
-      if constexpr (g >= 1) read_v(std::integral_constant<int, g - 1>{}, vf);
-      if constexpr (QK && g < 4) read_k(g_c, kf);
       if constexpr (g < 4) p_step(g_c, pk[g & 1]);
       if constexpr (g >= 1) {
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[(g - 1) & 1]);
@@ -524,6 +534,8 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
         for (int i = 0; i < KQ; ++i)
           sn[mt] = mfma32(__builtin_bit_cast(bf16x8, kf[i]), qf[(g & 1) * KQ + i], sn[mt]);
       }
+      if constexpr (g < 4) read_v(g_c, vf);
+      if constexpr (QK && g + 1 < 4) read_k(std::integral_constant<int, g + 1>{}, kf);
       __builtin_amdgcn_sched_barrier(0);
     });
     return psum;
