@@ -562,9 +562,9 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       const int ge = c0 + e;
       list_s[e] = ge < nf ? flist[ge] : plist[ge - nf];
     }
-    auto sub_j0 = [&](int s) -> int { return uniform(list_s[s >> spb_sh]) * bk + (s & spb_sh) * KT; };
     // the list entry of the K copy of the next step, read one step ahead and kept as the
-    // raw LDS value, so that no step starts with an LDS round trip
+    // raw LDS value, so that no step starts with an LDS round trip (it also gives the
+    // next step's tile start without another read)
     auto raw_ent = [&](int s) -> int { return list_s[s >> spb_sh]; };
     int kpos_raw = 0;
     auto sub_part = [&](int s) -> bool { return c0 + (s >> spb_sh) >= nf; };
@@ -605,7 +605,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
         const bool part = sub_part(s + 1);
         md = prep(snxt, part, part || j0_b + KT > kv_len, j0_b, SQ{});
         j0_a = j0_b;
-        j0_b = s + 2 < nsub ? sub_j0(s + 2) : 0;
+        j0_b = s + 2 < nsub ? uniform(kpos_raw) * bk + ((s + 2) & spb_sh) * KT : 0;
       }
       kpos_raw = s + 3 < nsub ? raw_ent(s + 3) : 0;
       wait_dma();

@@ -136,3 +136,30 @@ def test_parameter_gradients(score):
             err = float(np.abs(g - G).max())
             bound = G_TOL * max(1.0, float(np.abs(G).max()))
             assert err <= bound, f"{ctx}: {name} max-abs error {err:.3e} > {bound:.3e}"
+
+
+def test_backward_full_size_causal_softcap():
+    """The causal soft-cap workload at full size (B=2, H=16, N=4096, d=128, cap 20,
+    128-blocks): the whole backward on the GPU, dQ, dK and dV compared element by
+    element with the float64 autograd oracle on three sampled (batch, head) pairs (with
+    Hkv = Hq every KV head's gradient comes from its own query head only)."""
+    import block_sparse_programmable_amd as fa
+    import workloads as W
+    w = W.WORKLOADS["causal_softcap"]
+    assert w.Hq == w.Hkv
+    q, k, v = W.qkv(w, device="cuda")
+    do = W.randn_bf16((w.B, w.Hq, w.q_len, w.d), w.seed + 7, device="cuda")
+    bm = fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset)
+    o, lse = fa.forward(q, k, v, bm, score=w.score, softcap=w.cap)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, bm, score=w.score, softcap=w.cap)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, 7), (1, w.Hq - 1)):
+        print(f"full-size backward: oracle for batch {b}, head {h}", flush=True)
+        sl = lambda t: t[b:b + 1, h:h + 1].cpu()   # noqa: E731
+        DQ, DK, DV = OBW.attention_grads(sl(q), sl(k), sl(v), sl(do), w.mask, w.score, cap=w.cap)
+        for name, g, G in (("dq", dq, DQ), ("dk", dk, DK), ("dv", dv, DV)):
+            g = g[b:b + 1, h:h + 1].cpu().numpy()
+            assert np.isfinite(g).all(), f"({b},{h}): non-finite {name}"
+            err = float(np.abs(g - G).max())
+            bound = G_TOL * max(1.0, float(np.abs(G).max()))
+            assert err <= bound, f"({b},{h}): {name} max-abs error {err:.3e} > {bound:.3e}"
