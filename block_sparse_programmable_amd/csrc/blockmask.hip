@@ -115,6 +115,22 @@ __device__ int classify_interval(const BuildParams& p, const BlockGeom& g, const
   return v;
 }
 
+// classify_interval for positions that fit in 32 bits, with the row block's quantities
+// (first row a, last row bb, lo(bb), hi(a)) computed once per row by the caller
+__device__ __forceinline__ int classify_interval32(const MaskProg& m, int a, int bb, int lo_bb, int hi_a, int c0,
+                                                   int c1, const int32_t* qs, const int32_t* ks, bool docs_sorted) {
+  int v;
+  if (lo_bb <= c0 && hi_a >= c1) {
+    v = VT;
+  } else {
+    const int i1 = m.hi_self ? max(a, c0) : (m.pmin >= 0 ? (m.pmin - 1 >= c0 ? a : max(a, c0)) : a);
+    const int lo_i1 = m.wmin > 0 ? max(0, i1 - m.wmin + 1) : 0;
+    v = (i1 > bb || lo_i1 > c1) ? VF : VM;
+  }
+  if (m.has_doc) v = v_and(v, classify_doc(qs, ks, docs_sorted));
+  return v;
+}
+
 __device__ int classify_bounds(const BuildParams& p, const BlockGeom& g, const int32_t* qs, const int32_t* ks,
                                bool docs_sorted = false) {
   if (p.prog.mk != MK_GENERIC) return classify_interval(p, g, qs, ks, docs_sorted);
@@ -380,7 +396,7 @@ __global__ __launch_bounds__(256) void count_kernel(BuildParams p) {
 // thread taking four consecutive counts per pass (DPP wave scans, wave totals in LDS)
 __global__ __launch_bounds__(1024) void scan_kernel(BuildParams p) {
   __shared__ int32_t wave_sums[16];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
   const int which = blockIdx.x;
   const int32_t* num = which == 0 ? p.kv_num : which == 1 ? p.full_kv_num : which == 2 ? p.q_num : p.full_q_num;
   int32_t* ptr = which == 0 ? p.kv_ptr : which == 1 ? p.full_kv_ptr : which == 2 ? p.q_ptr : p.full_q_ptr;
@@ -454,12 +470,13 @@ constexpr int kSmallMaxLines = 2048;    // tB * (NQB + NKB)
 constexpr int kSmallMaxTB = 64;
 
 // phases 4-6 of the one-workgroup build, shared with the row slicer: partial/full
-// counts, prefix sums and ordered compaction of an LDS class grid [tB][nqb][nkb] into
-// the table arrays, every row and column repeated for the tH heads of its tb.  The
-// query-side arrays are written only when p.q_num is set.
+// counts (skipped when `counted`: cnt_s already holds them), prefix sums and ordered
+// compaction of an LDS class grid [tB][nqb][nkb] into the table arrays, every row and
+// column repeated for the tH heads of its tb.  The query-side arrays are written only
+// when p.q_num is set.
 __device__ void compact_small(const BuildParams& p, const uint8_t* grid_s, int32_t* cnt_s, int32_t* pre_s,
-                              int32_t* tot_s, int32_t* cum_s) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+                              int32_t* tot_s, int32_t* cum_s, bool counted) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
   const int nq = p.tB * p.nqb, nl = nq + p.tB * p.nkb;
   const bool qout = p.q_num != nullptr;
   // phase 4: partial / full counts per row (tb, r) and per column (tb, c).  Every line
@@ -473,14 +490,14 @@ __device__ void compact_small(const BuildParams& p, const uint8_t* grid_s, int32
   auto line_geom = [&](int line, int& tb, int& k, int& n, bool& rowside) {
     rowside = line < nq;
     const int idx = rowside ? line : line - nq;
-    tb = rowside ? idx / p.nqb : idx / p.nkb;
+    tb = p.tB == 1 ? 0 : (rowside ? idx / p.nqb : idx / p.nkb);   // (no divide for one group)
     k = rowside ? idx - tb * p.nqb : idx - tb * p.nkb;
     n = rowside ? p.nkb : p.nqb;
   };
   auto entry = [&](const uint8_t* g, bool rowside, int k, int x) -> uint8_t {
     return rowside ? g[k * p.nkb + x] : g[x * p.nkb + k];
   };
-  for (int line = lw0 + wv; line < lw1; line += 16) {
+  for (int line = lw0 + wv; line < (counted ? lw0 : lw1); line += 16) {
     int tb, k, n;
     bool rowside;
     line_geom(line, tb, k, n, rowside);
@@ -497,7 +514,7 @@ __device__ void compact_small(const BuildParams& p, const uint8_t* grid_s, int32
       cnt_s[2 * line + 1] = nf;
     }
   }
-  for (int line = ls0 + tid; line < ls1; line += 1024) {
+  for (int line = ls0 + tid; line < (counted ? ls0 : ls1); line += 1024) {
     int tb, k, n;
     bool rowside;
     line_geom(line, tb, k, n, rowside);
@@ -545,8 +562,8 @@ __device__ void compact_small(const BuildParams& p, const uint8_t* grid_s, int32
     const bool rowside = x < rows;
     const int idx = rowside ? x : x - rows;
     const int per = rowside ? p.nqb : p.nkb;
-    const int bh = idx / per, k = idx - bh * per;
-    const int tb = bh / p.tH, h = bh - tb * p.tH;
+    const int bh = p.tB * p.tH == 1 ? 0 : idx / per, k = idx - bh * per;
+    const int tb = p.tH == 1 ? bh : bh / p.tH, h = bh - tb * p.tH;
     const int line = rowside ? tb * p.nqb + k : nq + tb * p.nkb + k;
     const int side = rowside ? 0 : 1;
     const int np_ = cnt_s[2 * line], nf_ = cnt_s[2 * line + 1];
@@ -626,28 +643,15 @@ __device__ void compact_small(const BuildParams& p, const uint8_t* grid_s, int32
   }
 }
 
-__global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
-  __shared__ uint8_t grid_s[kSmallMaxBlocks];
-  __shared__ int32_t stat_s[2 * kSmallMaxLines];   // doc min/max: query blocks, then KV blocks
-  __shared__ int32_t cnt_s[2 * kSmallMaxLines];    // partial/full counts: rows, then columns
-  __shared__ int32_t pre_s[2 * kSmallMaxLines];    // exclusive prefix of cnt_s within each tb
-  __shared__ int32_t tot_s[4 * kSmallMaxTB];       // per tb: rows partial/full, cols partial/full
-  __shared__ int32_t cum_s[4 * (kSmallMaxTB + 1)]; // prefix over tb of tH * tot_s
-  __shared__ int32_t list_s[kSmallMaxBlocks];      // undecided block ids
-  __shared__ int32_t n_undecided;
-  __shared__ int32_t unsorted_s;   // some document ID decreases along the positions read
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int nq = p.tB * p.nqb, nk = p.tB * p.nkb, nl = nq + nk;
-  const int total = p.tB * p.nqb * p.nkb;
-  if (tid == 0) unsorted_s = 0;
-  __syncthreads();
-
-  // phase 1: document-ID ranges per query block and per KV block, and whether the IDs
-  // are non-decreasing inside each block.  A wave takes eight lines at a time (at most
-  // 128 IDs each: two per lane, plus the ID after each for the order test) and issues
-  // all their loads before reducing, so the HBM latency is paid once per eight lines;
-  // the reductions are wave-wide DPP reductions.
-  if (p.prog.has_doc) {
+// Document-ID ranges per query block and per KV block by reduction, for IDs that are not
+// sorted (the general case of phase 1), and the same order test as doc_ends.  A wave
+// takes eight lines at a time (at most 128 IDs each: two per lane, plus the ID after each
+// for the order test) and issues all their loads before reducing, so the memory latency
+// is paid once per eight lines; the reductions are wave-wide DPP reductions.
+__device__ void doc_ranges(const BuildParams& p, int32_t* stat_s, int32_t* unsorted_s) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
+  const int nq = p.tB * p.nqb, nl = nq + p.tB * p.nkb;
+  {
     constexpr int G = 8;
     for (int l0 = wv * G; l0 < nl; l0 += 16 * G) {
       int v[G][2];
@@ -713,7 +717,7 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
           stat_s[2 * (l0 + u) + 1] = mx;
         }
       }
-      if (any_desc && lane == 0) unsorted_s = 1;
+      if (any_desc && lane == 0) *unsorted_s = 1;
     }
   }
   __syncthreads();
@@ -722,7 +726,7 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
   // side, and when the query positions start at or after the last key the query side
   // must not be below the key side (otherwise the two ranges overlap and each being
   // ordered orders their union)
-  if (p.prog.has_doc) {
+  {
     for (int line = tid; line < nl; line += 1024) {
       const bool qside = line < nq;
       const int idx = qside ? line : line - nq;
@@ -733,72 +737,205 @@ __global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
         const int tb = idx / per;
         bad = bad || stat_s[2 * line] < stat_s[2 * (nq + tb * p.nkb + p.nkb - 1) + 1];
       }
-      if (bad) unsorted_s = 1;
+      if (bad) *unsorted_s = 1;
     }
   }
-  // phase 2: bounds classification, one thread per block; undecided blocks go to a
-  // list (its order is irrelevant: each entry's class is decided on its own)
-  if (tid == 0) n_undecided = 0;
+}
+
+// Phase 1, sorted IDs: whether the document IDs are non-decreasing over every position
+// either side reads (*unsorted_s = 1 when not: a descent inside the query positions or
+// inside the key positions of a table group, or, when the query positions start at or
+// after the last key, a query ID below the last key's), and each block line's first and
+// last ID, which are its minimum and maximum when they are.  Every thread tests eight
+// neighbour pairs per side and pass, all loads of a pass issued before any test.
+__device__ void doc_ends(const BuildParams& p, int32_t* stat_s, int32_t* unsorted_s) {
+  const int tid = threadIdx.x;
+  const int nq = p.tB * p.nqb, nl = nq + p.tB * p.nkb;
+  constexpr int U = 8;
+  bool bad = false;
+  for (int tb = 0; tb < p.tB; ++tb) {
+    const int32_t* d = doc_row(p.doc, tb);
+    const int64_t nqp = p.q_len - 1, nkp = p.kv_len - 1;   // neighbour pairs per side
+    for (int64_t base = 0; base < max(nqp, nkp); base += 1024 * U) {
+      // loads at clamped positions (a side without pairs reads nothing), so that all of
+      // them are in flight at once
+      int a[2][U] = {}, b[2][U] = {};
+      bool in[2][U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t x = base + tid + 1024 * u;
+        in[0][u] = x < nqp;
+        in[1][u] = x < nkp;
+      }
+      if (nqp > 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t xq = p.q_offset + min(base + tid + 1024 * u, nqp - 1);
+          a[0][u] = d[xq];
+          b[0][u] = d[xq + 1];
+        }
+      }
+      if (nkp > 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t xk = min(base + tid + 1024 * u, nkp - 1);
+          a[1][u] = d[xk];
+          b[1][u] = d[xk + 1];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) bad = bad || (in[0][u] && b[0][u] < a[0][u]) || (in[1][u] && b[1][u] < a[1][u]);
+    }
+    if (tid == 0 && p.q_offset >= p.kv_len && p.q_len > 0 && p.kv_len > 0 && d[p.q_offset] < d[p.kv_len - 1])
+      bad = true;
+  }
+  if (bad) *unsorted_s = 1;
+  // first and last ID of every line
+  for (int line = tid; line < nl; line += 1024) {
+    const bool qside = line < nq;
+    const int idx = qside ? line : line - nq;
+    const int per = qside ? p.nqb : p.nkb;
+    const int tb = p.tB == 1 ? 0 : idx / per, blk = idx - tb * per;
+    const int32_t* d = doc_row(p.doc, tb);
+    int64_t lo, hi;
+    if (qside) {
+      lo = (int64_t)blk * p.bq + p.q_offset;
+      hi = min((int64_t)(blk + 1) * p.bq, p.q_len) + p.q_offset;
+    } else {
+      lo = (int64_t)blk * p.bk;
+      hi = min((int64_t)(blk + 1) * p.bk, p.kv_len);
+    }
+    stat_s[2 * line] = d[lo];
+    stat_s[2 * line + 1] = d[hi - 1];
+  }
+}
+
+__global__ __launch_bounds__(1024) void build_small_kernel(BuildParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t grid_s[kSmallMaxBlocks];
+  __shared__ int32_t stat_s[2 * kSmallMaxLines];   // doc min/max: query blocks, then KV blocks
+  __shared__ int32_t cnt_s[2 * kSmallMaxLines];    // partial/full counts: rows, then columns
+  __shared__ int32_t pre_s[2 * kSmallMaxLines];    // exclusive prefix of cnt_s within each tb
+  __shared__ int32_t tot_s[4 * kSmallMaxTB];       // per tb: rows partial/full, cols partial/full
+  __shared__ int32_t cum_s[4 * (kSmallMaxTB + 1)]; // prefix over tb of tH * tot_s
+  __shared__ int32_t list_s[kSmallMaxBlocks];      // undecided block ids
+  __shared__ int32_t n_undecided;
+  __shared__ int32_t unsorted_s;   // some document ID decreases along the positions read
+  const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
+  const int nq = p.tB * p.nqb, nl = nq + p.tB * p.nkb;
+  const int total = p.tB * p.nqb * p.nkb;
+  // every block starts EMPTY and every count at zero
+  for (int x = tid; x < (total + 3) / 4; x += 1024) reinterpret_cast<uint32_t*>(grid_s)[x] = 0u;
+  for (int x = tid; x < 2 * nl; x += 1024) cnt_s[x] = 0;
+  if (tid == 0) {
+    unsorted_s = 0;
+    n_undecided = 0;
+  }
   __syncthreads();
-  const bool docs_sorted = p.prog.has_doc && unsorted_s == 0;
-  if (total > 0) {
-    // (tb, r, c) of block id, advanced by 1024 ids per step without dividing
-    const int nblk = p.nqb * p.nkb;
-    int tb = tid / nblk;
-    int r = (tid - tb * nblk) / p.nkb;
-    int c = tid - tb * nblk - r * p.nkb;
-    const int st_tb = 1024 / nblk, st_rem = 1024 - st_tb * nblk;
-    const int st_r = st_rem / p.nkb, st_c = st_rem - st_r * p.nkb;
-    for (int id = tid; id < total; id += 1024) {
-      const int v = classify_bounds(p, geom(p, r, c), stat_s + 2 * (tb * p.nqb + r),
-                                    stat_s + 2 * (nq + tb * p.nkb + c), docs_sorted);
-      grid_s[id] = v == VU ? kEmpty : (v == VT ? kFull : (v == VF ? kEmpty : kPartial));
-      if (v == VU) list_s[atomicAdd(&n_undecided, 1)] = id;
-      c += st_c;
-      r += st_r;
-      tb += st_tb;
-      if (c >= p.nkb) {
-        c -= p.nkb;
-        ++r;
+
+  // phase 1: document-ID ranges per block line, from the lines' end IDs when the IDs are
+  // sorted, else by reduction over every ID
+  if (p.prog.has_doc) {
+    doc_ends(p, stat_s, &unsorted_s);
+    __syncthreads();
+    if (uniform(unsorted_s) != 0) doc_ranges(p, stat_s, &unsorted_s);
+    __syncthreads();
+  }
+  const bool docs_sorted = p.prog.has_doc && uniform(unsorted_s) == 0;
+
+  // phase 2: one wave per row (tb, r).  For and-only programs the row's possible columns
+  // form one band: the allowed keys of a row i are [lo(i), hi(i)], both ends
+  // non-decreasing and consecutive rows' intervals touching, so the union over the
+  // block's rows a..bb is [lo(a), hi(bb)] and every block outside it is EMPTY.  Blocks
+  // in the band (all blocks for programs with an or-node) are classified from their
+  // bounds, one per lane; the row's counts come from ballots, the columns' from LDS
+  // atomics, and undecided blocks go to a list (its order is irrelevant: each entry's
+  // class is decided on its own).
+  // positions below 2^30 take 32-bit arithmetic with the row's quantities hoisted
+  const bool pos32 = p.prog.mk != MK_GENERIC && p.q_offset + p.q_len < (1ll << 30) && p.kv_len < (1ll << 30);
+  const int bk_sh = __builtin_ctz(p.bk);   // block sizes are powers of two
+  for (int row = wv; row < nq; row += 16) {
+    const int tb = p.tB == 1 ? 0 : row / p.nqb, r = row - tb * p.nqb;
+    int c_lo = 0, c_hi = p.nkb - 1;
+    const BlockGeom g = geom(p, r, 0);
+    if (p.prog.mk != MK_GENERIC) {
+      const int64_t lo = p.prog.wmin > 0 ? max((int64_t)0, g.a - p.prog.wmin + 1) : (int64_t)0;
+      c_lo = (int)min(lo >> bk_sh, (int64_t)p.nkb);
+      if (p.prog.hi_self || p.prog.pmin >= 0) {
+        const int64_t hi = p.prog.hi_self ? g.bb : max((int64_t)p.prog.pmin - 1, g.bb);
+        c_hi = (int)min(hi >> bk_sh, (int64_t)p.nkb - 1);
       }
-      if (r >= p.nqb) {
-        r -= p.nqb;
-        ++tb;
+    }
+    // row quantities of the 32-bit form: lo(bb) and hi(a) (hi unbounded: INT_MAX)
+    const int a32 = (int)g.a, bb32 = (int)g.bb;
+    const int lo_bb = p.prog.wmin > 0 ? max(0, bb32 - p.prog.wmin + 1) : 0;
+    const int hi_a = p.prog.hi_self ? a32 : (p.prog.pmin >= 0 ? max(p.prog.pmin - 1, a32) : 0x7fffffff);
+    int np = 0, nf = 0;
+    for (int c0 = c_lo; c0 <= c_hi; c0 += 64) {
+      const int c = c0 + lane;
+      const bool in = c <= c_hi;
+      int v = VF;
+      if (in) {
+        const int32_t* qs = stat_s + 2 * row;
+        const int32_t* ks = stat_s + 2 * (nq + tb * p.nkb + c);
+        if (pos32) {
+          const int k0 = c * p.bk, k1 = min(k0 + p.bk, (int)p.kv_len) - 1;
+          v = classify_interval32(p.prog, a32, bb32, lo_bb, hi_a, k0, k1, qs, ks, docs_sorted);
+        } else {
+          v = classify_bounds(p, geom(p, r, c), qs, ks, docs_sorted);
+        }
+        if (v == VT || v == VM) {
+          grid_s[row * p.nkb + c] = v == VT ? kFull : kPartial;
+          atomicAdd(&cnt_s[2 * (nq + tb * p.nkb + c) + (v == VT ? 1 : 0)], 1);
+        } else if (v == VU) {
+          list_s[atomicAdd(&n_undecided, 1)] = (row << 16) | c;
+        }
       }
+      np += __popcll(__ballot(v == VM));
+      nf += __popcll(__ballot(v == VT));
+    }
+    if (lane == 0) {
+      cnt_s[2 * row] = np;
+      cnt_s[2 * row + 1] = nf;
     }
   }
   __syncthreads();
 
   // phase 3: exact evaluation of the undecided blocks, spread over the 16 waves; the
   // document IDs of a wave's next block are loaded while the current one is decided
-  const int nu = n_undecided;
+  const int nu = uniform(n_undecided);
+  // entries are (row << 16) | column (rows below kSmallMaxLines, columns below 2^16)
   auto decode_id = [&](int uid, int& tb, int& r, int& c) {
-    tb = uid / (p.nqb * p.nkb);
-    const int rem = uid - tb * p.nqb * p.nkb;
-    r = rem / p.nkb;
-    c = rem - r * p.nkb;
+    const int row = uid >> 16;
+    tb = p.tB == 1 ? 0 : row / p.nqb;
+    r = row - tb * p.nqb;
+    c = uid & 0xffff;
   };
   if (wv < nu) {
     int tb, r, c;
-    decode_id(list_s[wv], tb, r, c);
+    decode_id(uniform(list_s[wv]), tb, r, c);
     BlockDocs cur = load_block_docs(p, tb, r, c, lane);
     for (int k = wv; k < nu; k += 16) {
-      const int uid = list_s[k];
+      const int uid = uniform(list_s[k]);
       decode_id(uid, tb, r, c);
       BlockDocs nxt = {0, 0, 0, 0};
       if (k + 16 < nu) {
         int tb2, r2, c2;
-        decode_id(list_s[k + 16], tb2, r2, c2);
+        decode_id(uniform(list_s[k + 16]), tb2, r2, c2);
         nxt = load_block_docs(p, tb2, r2, c2, lane);
       }
       const uint8_t cls = exact_block(p, tb, r, c, lane, cur);
-      if (lane == 0) grid_s[uid] = cls;
+      if (lane == 0 && cls != kEmpty) {
+        grid_s[(tb * p.nqb + r) * p.nkb + c] = cls;
+        const int kind = cls == kFull ? 1 : 0;
+        atomicAdd(&cnt_s[2 * (tb * p.nqb + r) + kind], 1);
+        atomicAdd(&cnt_s[2 * (nq + tb * p.nkb + c) + kind], 1);
+      }
       cur = nxt;
     }
   }
   __syncthreads();
 
-  compact_small(p, grid_s, cnt_s, pre_s, tot_s, cum_s);
+  compact_small(p, grid_s, cnt_s, pre_s, tot_s, cum_s, true);
 }
 
 // ---------------------------------------------------------------------------------
@@ -917,13 +1054,13 @@ __global__ __launch_bounds__(1024) void marked_small_kernel(MP sp) {
   __shared__ int32_t tot_s[4 * kSliceMaxTB];
   __shared__ int32_t cum_s[4 * (kSliceMaxTB + 1)];
   const BuildParams& p = sp.d;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = uniform(tid >> 6);
   const int total = p.tB * p.nqb * p.nkb;
   for (int x = tid; x < (total + 3) / 4; x += 1024) reinterpret_cast<uint32_t*>(grid_s)[x] = 0u;
   __syncthreads();
   for (int row = wv; row < p.tB * p.nqb; row += 16) mark_row(sp, row, lane, grid_s + row * p.nkb);
   __syncthreads();
-  compact_small(p, grid_s, cnt_s, pre_s, tot_s, cum_s);
+  compact_small(p, grid_s, cnt_s, pre_s, tot_s, cum_s, false);
 }
 
 // larger grids: the class grid goes to the workspace (cleared here, then marked one
