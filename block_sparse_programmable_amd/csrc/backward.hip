@@ -13,18 +13,20 @@
 // scale * (1 - tanh^2) (soft-cap).  Gradients are accumulated in fp32 and written
 // in fp32; P and dS enter the MFMAs as bf16 (round to nearest even).
 //
-// gfx950 mapping (16x16 MFMA tiles, wave64):
-//   * bwd_dkdv_kernel: one workgroup per (b, h_kv, KV block), a wave per 16 keys.  K and V of the wave's keys stay in registers as the B
-//     operands of S = Q K^T and dP = dO V^T (v_mfma_f32_16x16x32_bf16); the query
-//     rows of each listed block (for every query head of the group) are staged in
-//     LDS, and dV^T += dO^T P, dK^T += Q^T dS take their A operands from transposing
-//     LDS reads (ds_read_b64_tr_b16) and P, dS straight from the accumulator layout
-//     (v_mfma_f32_16x16x16_bf16).
+// gfx950 mapping (16x16 MFMA tiles, wave64; every product on v_mfma_f32_16x16x32_bf16,
+// which does twice the work of the 16x16x16 form in the same 16 cycles):
+//   * bwd_dkdv_kernel: one workgroup per (b, h_kv, KV block), a wave per 16 keys.  K
+//     and V of the wave's keys stay in registers as the B operands of S = Q K^T and
+//     dP = dO V^T; the query rows of each listed block (for every query head of the
+//     group) are staged in LDS.  dV^T += dO^T P and dK^T += Q^T dS contract over 32
+//     query rows at a time: P and dS of two 16-row tiles go straight from the
+//     accumulator layout into the B operand, and the A operands are two transposing LDS
+//     reads (ds_read_b64_tr_b16) each, in the same row order.
 //   * bwd_dq_kernel: one workgroup per (b, h_q, query block), a wave per 16 rows;
 //     Q and dO of the wave's rows stay in registers, the K and V tiles of each
 //     listed block are staged in LDS, and S^T = K Q^T, dP^T = V dO^T,
-//     dQ^T += K^T dS^T mirror the first kernel.
-//   * bwd_delta_kernel: delta = rowsum(dO * O), one wave per row.
+//     dQ^T += K^T dS^T (over 32 keys at a time) mirror the first kernel.
+//   * bwd_delta_kernel: delta = rowsum(dO * O), D / 8 lanes per row.
 // Partial blocks and ragged tails apply the mask rule per element (interpreter).
 // The dQ pass also sums the score_mod parameter gradients when asked: ALiBi slopes
 // (sum of dS (j - i)) and relative-position table entries (sum of dS per offset), with
@@ -40,22 +42,36 @@ namespace {
 __device__ __forceinline__ f32x4 mma_k32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mma_k16(const s16x4& a, const s16x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ s16x4 tr_read(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
-__device__ __forceinline__ s16x4 pack4(float a, float b, float c, float d) {
-  const u32x2 v = {cvt_pk_bf16(a, b), cvt_pk_bf16(c, d)};
-  return __builtin_bit_cast(s16x4, v);
+__device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
+  const u32x4 v = {cvt_pk_bf16(x[0], x[1]), cvt_pk_bf16(x[2], x[3]), cvt_pk_bf16(x[4], x[5]),
+                   cvt_pk_bf16(x[6], x[7])};
+  return __builtin_bit_cast(bf16x8, v);
+}
+// two transposing reads side by side: the A operand of a 16x16x32 product whose
+// contraction index k = 8 g + e takes rows base + 4 g + e (e < 4) from the first read and
+// rows base + 16 + 4 g + e - 4 from the second
+__device__ __forceinline__ bf16x8 cat_tr(const uint8_t* p0, const uint8_t* p1) {
+  const u32x2 a = __builtin_bit_cast(u32x2, tr_read(p0));
+  const u32x2 b = __builtin_bit_cast(u32x2, tr_read(p1));
+  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
 }
 
-// LDS row pitch: D bf16 plus 16 bytes, so the 16 rows a ds_read_b128 pass touches at one
-// column fall on distinct bank groups
+// LDS layout of staged rows.  D = 128: 256-byte rows, 16-byte chunk c of row r stored at
+// chunk c ^ (2 (r & 7) + ((r >> 3) & 1)), so the 16 rows that a ds_read_b128 pass reads
+// at one chunk land on 16 different chunk positions, and the 8 rows x 32 bytes that a
+// pass of transposing reads covers land on all 64 banks once.  D = 64: 144-byte rows
+// (128 plus 16 of padding), so a ds_read_b128 pass's 16 rows fall on distinct banks.
 template <int D>
-struct Pitch {
-  static constexpr int RS = D * 2 + 16;
+struct Lay {
+  static constexpr int RS = D == 128 ? 256 : D * 2 + 16;
+  // byte offset of bf16 element e (a multiple of 4, below D) of row r
+  static __device__ __forceinline__ int off(int r, int e) {
+    if constexpr (D == 128) return r * RS + ((((e >> 3) ^ (2 * (r & 7) + ((r >> 3) & 1))) << 4) | ((e & 7) << 1));
+    else return r * RS + 2 * e;
+  }
 };
 
 // Rows [r0, r0 + n) (n <= 128) of a [rows_total, D] bf16 matrix, staged through
@@ -80,7 +96,7 @@ struct RowStage {
     for (int u = 0; u < PER; ++u) {
       const int x = threadIdx.x + u * NT;
       const int row = x / CH, ch = x - row * CH;
-      if (row < n) *reinterpret_cast<u32x4*>(dst + row * Pitch<D>::RS + ch * 16) = r[u];
+      if (row < n) *reinterpret_cast<u32x4*>(dst + Lay<D>::off(row, 8 * ch)) = r[u];
     }
   }
 };
@@ -104,25 +120,38 @@ __device__ __forceinline__ void grad_elem(float s, float dp, float lse2, float d
   ds = ok ? pv * (dp - delta) * dmod : 0.f;
 }
 
-// ---- delta = rowsum(dO * O), one wave per row
+// ---- delta = rowsum(dO * O): D / 8 lanes per row, each with 16 bytes (8 values) of O
+// and of dO per pass, the row's lanes reduced by xor shuffles inside their group; a
+// workgroup takes kDeltaPasses groups of 256 / (D / 8) rows, all loads issued first
+constexpr int kDeltaPasses = 4;
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams bp) {
   const FwdParams& p = bp.f;
+  constexpr int LPR = D / 8;          // lanes per row
+  constexpr int RPP = 256 / LPR;      // rows per pass
   const int64_t rows = (int64_t)p.B * p.Hq * p.q_len;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  float acc = 0.f;
-  constexpr int PER = D / 64;
+  const int sub = threadIdx.x & (LPR - 1);
+  const int64_t row0 = (int64_t)blockIdx.x * (RPP * kDeltaPasses) + threadIdx.x / LPR;
+  u32x4 o[kDeltaPasses], g[kDeltaPasses];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int64_t x = row * D + lane * PER + k;
-    const float o = __builtin_bit_cast(float, (uint32_t)p.o[x] << 16);
-    const float g = __builtin_bit_cast(float, (uint32_t)bp.dout[x] << 16);
-    acc += o * g;
+  for (int k = 0; k < kDeltaPasses; ++k) {
+    const int64_t row = min(row0 + (int64_t)k * RPP, rows - 1);   // clamped: out-of-range rows write nothing
+    o[k] = load16(p.o + row * D + 8 * sub);
+    g[k] = load16(bp.dout + row * D + 8 * sub);
   }
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) bp.delta[row] = acc;
+#pragma unroll
+  for (int k = 0; k < kDeltaPasses; ++k) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc += __builtin_bit_cast(float, o[k][e] << 16) * __builtin_bit_cast(float, g[k][e] << 16);
+      acc += __builtin_bit_cast(float, o[k][e] & 0xffff0000u) * __builtin_bit_cast(float, g[k][e] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    const int64_t row = row0 + (int64_t)k * RPP;
+    if (sub == 0 && row < rows) bp.delta[row] = acc;
+  }
 }
 
 // A lane's pairs of one block as bits of a word: bit 4 m + rr for the position at offset
@@ -156,7 +185,8 @@ template <int D, int SCORE, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
   const FwdParams& p = bp.f;
   constexpr int NT = NW * 64;
-  constexpr int RS = Pitch<D>::RS;
+  using L = Lay<D>;
+  constexpr int RS = L::RS;
   constexpr int KS = D / 32;   // k-steps of the 16x16x32 products over the head dim
   constexpr int DT = D / 16;   // 16-row tiles of dK^T and dV^T
   constexpr int BQM = 128;     // largest query block
@@ -262,32 +292,43 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
         const uint32_t db = p.prog.has_doc ? doc_bits16(doc_s, g4, bq >> 4, doc_j) : 0u;
         okw &= mask_word(p.prog, [&](int op, int a) { return col_leaf(op, a, j, span, db); });
       }
-      for (int q0 = 0; q0 < bq; q0 += 16) {
-        // S (16 rows x 16 keys) and dP on 16x16x32 tiles
-        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int q0 = 0; q0 < bq; q0 += 32) {
+        // S and dP (16 rows x 16 keys each) of rows q0 + 16 h + (0..15), h = 0, 1, on
+        // 16x16x32 tiles over the head dim
+        f32x4 s[2], dp[2];
 #pragma unroll
-        for (int t = 0; t < KS; ++t) {
-          const int off = (q0 + col) * RS + (32 * t + 8 * g4) * 2;
-          s = mma_k32(*reinterpret_cast<const bf16x8*>(qs + off), kf[t], s);
-          dp = mma_k32(*reinterpret_cast<const bf16x8*>(gs + off), vf[t], dp);
-        }
-        // lane: rows q0 + 4 g4 + rr, key j
-        float pv[4], ds[4];
+        for (int h = 0; h < 2; ++h) {
+          s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int xr = q0 + 4 * g4 + rr;
-          const int ig = r0 + xr + (int)p.q_offset;
-          const bool ok = (okw >> (4 * (q0 >> 4) + rr)) & 1u;
-          grad_elem<SCORE>(s[rr], dp[rr], lse_s[xr], del_s[xr], ok, sc, p.scale, ig, j, pv[rr], ds[rr]);
+          for (int t = 0; t < KS; ++t) {
+            const int off = L::off(q0 + 16 * h + col, 32 * t + 8 * g4);
+            s[h] = mma_k32(*reinterpret_cast<const bf16x8*>(qs + off), kf[t], s[h]);
+            dp[h] = mma_k32(*reinterpret_cast<const bf16x8*>(gs + off), vf[t], dp[h]);
+          }
         }
-        const s16x4 pb = pack4(pv[0], pv[1], pv[2], pv[3]);
-        const s16x4 db = pack4(ds[0], ds[1], ds[2], ds[3]);
-        // dV^T += dO^T P and dK^T += Q^T dS (A: head-dim x 16 rows, transposing reads)
-        const int toff = (q0 + 4 * g4 + (col >> 2)) * RS + 4 * (col & 3) * 2;
+        // lane: rows q0 + 16 h + 4 g4 + rr, key j
+        float pv[8], ds[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int xr = q0 + 16 * h + 4 * g4 + rr;
+            const int ig = r0 + xr + (int)p.q_offset;
+            const bool ok = (okw >> (4 * ((q0 >> 4) + h) + rr)) & 1u;
+            grad_elem<SCORE>(s[h][rr], dp[h][rr], lse_s[xr], del_s[xr], ok, sc, p.scale, ig, j, pv[4 * h + rr],
+                             ds[4 * h + rr]);
+          }
+        const bf16x8 pb = pack8(pv), db = pack8(ds);
+        // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (16x16x32): the lane holds P
+        // and dS in the contraction order of cat_tr (rows q0 + 4 g4 + e, then q0 + 16 +
+        // 4 g4 + e), and the A operands (head dim x rows) come from transposing reads
+        const int tr0 = q0 + 4 * g4 + (col >> 2);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          dv[dt] = mma_k16(tr_read(gs + toff + 32 * dt), pb, dv[dt]);
-          dk[dt] = mma_k16(tr_read(qs + toff + 32 * dt), db, dk[dt]);
+          const int e = 16 * dt + 4 * (col & 3);
+          dv[dt] = mma_k32(cat_tr(gs + L::off(tr0, e), gs + L::off(tr0 + 16, e)), pb, dv[dt]);
+          dk[dt] = mma_k32(cat_tr(qs + L::off(tr0, e), qs + L::off(tr0 + 16, e)), db, dk[dt]);
         }
       }
     }
@@ -305,10 +346,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
 
 // ---- dQ: one workgroup per (b, h_q, query block), NW waves x 16 rows
 template <int D, int SCORE, int NW>
-__global__ __launch_bounds__(NW * 64, NW / 2) void bwd_dq_kernel(BwdParams bp) {
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
   const FwdParams& p = bp.f;
   constexpr int NT = NW * 64;
-  constexpr int RS = Pitch<D>::RS;
+  using L = Lay<D>;
+  constexpr int RS = L::RS;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   constexpr int BKM = 128;
@@ -408,40 +450,51 @@ __global__ __launch_bounds__(NW * 64, NW / 2) void bwd_dq_kernel(BwdParams bp) {
       const uint32_t db = p.prog.has_doc ? doc_bits16(doc_s, g4, bk >> 4, doc_i) : 0u;
       okw &= mask_word(p.prog, [&](int op, int a) { return row_leaf(op, a, ig, span, db); });
     }
-    for (int k0 = 0; k0 < bk; k0 += 16) {
-      // S^T (16 keys x 16 rows) = K Q^T and dP^T = V dO^T
-      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < bk; k0 += 32) {
+      // S^T (16 keys x 16 rows) = K Q^T and dP^T = V dO^T for keys k0 + 16 h + (0..15)
+      f32x4 s[2], dp[2];
 #pragma unroll
-      for (int t = 0; t < KS; ++t) {
-        const int off = (k0 + col) * RS + (32 * t + 8 * g4) * 2;
-        s = mma_k32(*reinterpret_cast<const bf16x8*>(ks + off), qf[t], s);
-        dp = mma_k32(*reinterpret_cast<const bf16x8*>(vs + off), gf[t], dp);
-      }
-      // lane: keys j0 + k0 + 4 g4 + rr, row i
-      float pv[4], ds[4];
+      for (int h = 0; h < 2; ++h) {
+        s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int jj = j0 + k0 + 4 * g4 + rr;
-        const bool ok = (okw >> (4 * (k0 >> 4) + rr)) & 1u;
-        grad_elem<SCORE>(s[rr], dp[rr], lse2, delta, ok, sc, p.scale, ig, jj, pv[rr], ds[rr]);
-        if constexpr (SCORE == FA_S_ALIBI) {
-          if (want_slope) g_slope = __builtin_fmaf(ds[rr], (float)(jj - ig), g_slope);
+        for (int t = 0; t < KS; ++t) {
+          const int off = L::off(k0 + 16 * h + col, 32 * t + 8 * g4);
+          s[h] = mma_k32(*reinterpret_cast<const bf16x8*>(ks + off), qf[t], s[h]);
+          dp[h] = mma_k32(*reinterpret_cast<const bf16x8*>(vs + off), gf[t], dp[h]);
         }
-        if constexpr (SCORE == FA_S_RELPOS) {
-          if (want_table && ds[rr] != 0.f) {
-            const int rel = ig - jj;
-            if (rel >= R) g_far += ds[rr];
-            else if (rel <= -R) g_ahead += ds[rr];
-            else unsafeAtomicAdd(&bins_s[rel + R], ds[rr]);
+      }
+      // lane: keys j0 + k0 + 16 h + 4 g4 + rr, row i
+      float pv[8], ds[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int jj = j0 + k0 + 16 * h + 4 * g4 + rr;
+          const bool ok = (okw >> (4 * ((k0 >> 4) + h) + rr)) & 1u;
+          float& d = ds[4 * h + rr];
+          grad_elem<SCORE>(s[h][rr], dp[h][rr], lse2, delta, ok, sc, p.scale, ig, jj, pv[4 * h + rr], d);
+          if constexpr (SCORE == FA_S_ALIBI) {
+            if (want_slope) g_slope = __builtin_fmaf(d, (float)(jj - ig), g_slope);
+          }
+          if constexpr (SCORE == FA_S_RELPOS) {
+            if (want_table && d != 0.f) {
+              const int rel = ig - jj;
+              if (rel >= R) g_far += d;
+              else if (rel <= -R) g_ahead += d;
+              else unsafeAtomicAdd(&bins_s[rel + R], d);
+            }
           }
         }
-      }
       (void)pv;
-      const s16x4 db = pack4(ds[0], ds[1], ds[2], ds[3]);
-      // dQ^T += K^T dS^T (A: head-dim x 16 keys, transposing reads)
-      const int toff = (k0 + 4 * g4 + (col >> 2)) * RS + 4 * (col & 3) * 2;
+      const bf16x8 db = pack8(ds);
+      // dQ^T += K^T dS^T over the 32 keys (16x16x32; contraction order as in cat_tr)
+      const int tr0 = k0 + 4 * g4 + (col >> 2);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) dq[dt] = mma_k16(tr_read(ks + toff + 32 * dt), db, dq[dt]);
+      for (int dt = 0; dt < DT; ++dt) {
+        const int e = 16 * dt + 4 * (col & 3);
+        dq[dt] = mma_k32(cat_tr(ks + L::off(tr0, e), ks + L::off(tr0 + 16, e)), db, dq[dt]);
+      }
     }
   }
   // parameter gradients: wave sums, then one global add per wave (slopes) or per bin
@@ -511,7 +564,8 @@ template <int D>
 hipError_t launch_bwd_d(const BwdParams& bp, hipStream_t s) {
   const FwdParams& p = bp.f;
   const int64_t rows = (int64_t)p.B * p.Hq * p.q_len;
-  if (rows > 0) hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, bp);
+  constexpr int64_t kDeltaRows = 256 / (D / 8) * kDeltaPasses;   // rows per workgroup
+  if (rows > 0) hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + kDeltaRows - 1) / kDeltaRows)), dim3(256), 0, s, bp);
   switch (p.score.kind) {
     case FA_S_IDENTITY: return launch_bwd_score<D, FA_S_IDENTITY>(bp, s);
     case FA_S_ALIBI: return launch_bwd_score<D, FA_S_ALIBI>(bp, s);
