@@ -203,6 +203,10 @@ struct FwdPlan {
 fa_status plan_forward(const fa_fwd_args* a, FwdPlan* plan) {
   if (!a) return fail(FA_ERR_NULL, "args is NULL");
   if (!a->q || !a->k || !a->v || !a->o || !a->lse) return fail(FA_ERR_NULL, "q, k, v, o and lse must be non-NULL");
+  // rows move in 16-byte chunks (global_load_lds_dwordx4 and 16-byte loads and stores)
+  if (((uintptr_t)a->q | (uintptr_t)a->k | (uintptr_t)a->v | (uintptr_t)a->o) & 15)
+    return fail(FA_ERR_SHAPE, "q, k, v and o must be 16-byte aligned");
+  if ((uintptr_t)a->lse & 3) return fail(FA_ERR_SHAPE, "lse must be 4-byte aligned");
   if (!a->bm) return fail(FA_ERR_NULL, "bm (block tables) is NULL");
   const fa_block_mask* bm = a->bm;
   if (a->d != 64 && a->d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim must be 64 or 128 (got %d)", a->d);
@@ -469,6 +473,8 @@ fa_status plan_backward(const fa_bwd_args* a, fa::BwdParams* bp, size_t* ws) {
   if (!bm->q_num || !bm->q_ptr || !bm->q_idx || !bm->full_q_num || !bm->full_q_ptr || !bm->full_q_idx)
     return fail(FA_ERR_NULL, "the backward needs the q-side block tables");
   if (!a->dout || !a->dq || !a->dk || !a->dv) return fail(FA_ERR_NULL, "dout, dq, dk and dv must be non-NULL");
+  if (((uintptr_t)a->dout | (uintptr_t)a->dq | (uintptr_t)a->dk | (uintptr_t)a->dv) & 15)
+    return fail(FA_ERR_SHAPE, "dout, dq, dk and dv must be 16-byte aligned");
   bp->f = plan.p;
   bp->dout = static_cast<const uint16_t*>(a->dout);
   bp->dq = a->dq;
@@ -547,6 +553,7 @@ fa_status fa_forward_paged(const fa_fwd_args* args, const fa_paged_kv* kv, fa_st
     if (!args->workspace || args->ws_bytes < plan.ws)
       return fail(FA_ERR_WORKSPACE, "forward workspace needs %zu bytes (got %zu)", plan.ws,
                   args->workspace ? args->ws_bytes : (size_t)0);
+    if ((uintptr_t)args->workspace & 15) return fail(FA_ERR_WORKSPACE, "forward workspace must be 16-byte aligned");
     plan.p.ws = static_cast<float*>(args->workspace);
   }
   return launch_planned(plan, args, stream);

@@ -237,12 +237,13 @@ typedef struct {
  * mask rule is evaluated only on PARTIAL blocks (and on the ragged last block).
  * A row with no allowed key gets O = 0 and LSE = -inf.
  * bm must have been built for the same q_len, kv_len (and B/H extents compatible
- * with B and Hq); q_offset is taken from bm.
+ * with B and Hq); q_offset is taken from bm.  q, k, v and o must be 16-byte aligned and
+ * lse 4-byte aligned (FA_ERR_SHAPE otherwise): rows move in 16-byte chunks.
  * Short queries (one query block, block_kv == 128, and (Hq/Hkv) * q_len <= 16 -- or
  * q_len <= 16 for tables with a row per query head under GQA, whose query heads then
  * each walk their own row) take a split-KV path that needs `workspace` of
- * fa_forward_workspace_size bytes; every other shape needs none (workspace may then be
- * NULL).
+ * fa_forward_workspace_size bytes, 16-byte aligned (FA_ERR_WORKSPACE otherwise); every
+ * other shape needs none (workspace may then be NULL).
  * -------------------------------------------------------------------------------- */
 typedef struct {
   const void* q;
@@ -303,8 +304,9 @@ fa_status fa_forward_noalloc(const fa_fwd_args* args, fa_stream_t stream);
  *              clipped offset.  Both are written (cleared first, then summed with
  *              floating-point atomic adds, so their last bits may vary run to run).
  * Rows with no allowed key contribute nothing.  Errors as for fa_forward, plus
- * FA_ERR_NULL for missing q-side tables, dout or gradient buffers, and
- * FA_ERR_UNSUPPORTED for a parameter gradient of another score kind.
+ * FA_ERR_NULL for missing q-side tables, dout or gradient buffers, FA_ERR_SHAPE when
+ * dout, dq, dk or dv is not 16-byte aligned, and FA_ERR_UNSUPPORTED for a parameter
+ * gradient of another score kind.
  * -------------------------------------------------------------------------------- */
 typedef struct {
   const fa_fwd_args* fwd;

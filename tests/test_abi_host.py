@@ -190,6 +190,21 @@ def test_forward_validation(lib):
         assert F(_fwd(L, bms)) == L.FA_ERR_UNSUPPORTED, (bq, bk)
         assert b"64- or 128-blocks" in lib.fa_last_error_message()
     assert F(_fwd(L, bm, scale=float("nan"))) == L.FA_ERR_SHAPE
+    # rows move in 16-byte chunks: q, k, v, o 16-byte aligned, lse 4-byte aligned
+    for name in ("q", "k", "v", "o"):
+        assert F(_fwd(L, bm, **{name: 0x1008})) == L.FA_ERR_SHAPE, name
+        assert b"16-byte aligned" in lib.fa_last_error_message()
+    assert F(_fwd(L, bm, lse=0x1002)) == L.FA_ERR_SHAPE
+    # a decode step's split-KV workspace must be 16-byte aligned
+    bmd = _bm(L, q_len=1, kv_len=4096, q_offset=4095)
+    for name in ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx"):
+        setattr(bmd, name, 0x1000)
+    dec = _fwd(L, bmd, q_len=1, kv_len=4096)
+    n = C.c_size_t(0)
+    assert lib.fa_forward_workspace_size(C.byref(dec), C.byref(n)) == L.FA_OK and n.value > 0
+    dec.workspace, dec.ws_bytes = 0x1008, n.value
+    assert F(dec) == L.FA_ERR_WORKSPACE
+    assert b"16-byte aligned" in lib.fa_last_error_message()
     bm2 = _bm(L, B=3)
     for name in ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx"):
         setattr(bm2, name, 0x1000)
@@ -238,6 +253,10 @@ def test_forward_validation(lib):
     assert lib.fa_backward(C.byref(ok), None) == L.FA_ERR_WORKSPACE
     ok.workspace, ok.ws_bytes = 0x1010, n.value
     assert lib.fa_backward(C.byref(ok), None) == L.FA_ERR_WORKSPACE    # misaligned
+    for name in ("dout", "dq", "dk", "dv"):
+        kw = dict(dout=0x1000, dq=0x1000, dk=0x1000, dv=0x1000)
+        kw[name] = 0x1004
+        assert lib.fa_backward(C.byref(Bk(**kw)), None) == L.FA_ERR_SHAPE, name
     # parameter gradients: only for their own score kind, table radius <= 1024
     assert lib.fa_backward(C.byref(Bk(dout=0x1000, dq=0x1000, dk=0x1000, dv=0x1000, dslopes=0x2000)),
                            None) == L.FA_ERR_UNSUPPORTED                 # identity score
