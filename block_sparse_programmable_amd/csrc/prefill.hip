@@ -50,6 +50,10 @@ namespace fa {
 
 namespace {
 
+// soft-cap kernels keep a fixed softmax reference at cap2 = softcap * log2(e) when
+// cap2 <= this (softcap <= 34.6): weights then stay within [2^-100, 1]
+constexpr float kFixedRefMax = 50.0f;
+
 template <int D, int NW, int SCORE, int MK>
 __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   constexpr int NT = NW * 64;
@@ -274,8 +278,12 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   for (int dm = 0; dm < DM; ++dm)
     vaddr[dm] = (uint32_t)v_off<D>(4 * half + (li >> 2), 32 * dm + 16 * (g16 & 1) + 4 * (li & 3));
 
-  // ---- online softmax state (per lane: one query row; halves share m)
-  float m_run = kNegInf;
+  // ---- online softmax state (per lane: one query row; halves share m).  Soft-cap scores
+  // never exceed the cap, so with the reference fixed at cap2 every weight lies in
+  // [2^(-2 cap2), 1]; for caps with 2 cap2 <= 2 kFixedRefMax that range stays far inside
+  // the normal floats and bf16, and the running maximum and its rescales are skipped.
+  const bool fixed_ref = SCORE == FA_S_SOFTCAP && sc.cap2 <= kFixedRefMax;
+  float m_run = fixed_ref ? sc.cap2 : kNegInf;
   float l_run = 0.f;
   f32x16 oacc[DM];
 #pragma unroll
@@ -395,12 +403,14 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
           s[mt][rr] = __builtin_fmaf(s[mt][rr], sc.c2, __builtin_fmaf(sc.slope2, (float)key_of(mt, rr), base));
     }
     // the maximum of this lane's half of the row's tile (16 of the 32 keys per 32-key
-    // tile; the other half lives in lane ^ 32)
+    // tile; the other half lives in lane ^ 32); not needed with a fixed reference
     float tmax = kNegInf;
+    if (!fixed_ref) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, s[mt][rr]);
+        for (int rr = 0; rr < 16; ++rr) tmax = fmaxf(tmax, s[mt][rr]);
+    }
     // map a raw-score maximum into the base-2 domain
     auto to_base2 = [&](float t) -> float {
       if (raw && t != kNegInf) {
@@ -416,7 +426,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
     // maximum exceeds it by more than kRescaleThresh.  A row's maximum exceeds it iff one
     // of its halves does, so the exchange between the halves (an LDS round trip) is
     // needed only inside the rare rescale branch.
-    if (__ballot(to_base2(tmax) > m_run + kRescaleThresh) != 0) {
+    if (!fixed_ref && __ballot(to_base2(tmax) > m_run + kRescaleThresh) != 0) {
       const float m_cand = to_base2(fmaxf(tmax, __shfl_xor(tmax, 32)));
       const bool grow = m_cand > m_run + kRescaleThresh;
       const float m_new = grow ? m_cand : m_run;
