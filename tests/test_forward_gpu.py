@@ -147,6 +147,18 @@ def test_large_scores_and_single_key_rows():
     check(q, k, v, ("swa", 1), 64, 64, ctx="single-key rows")
 
 
+@pytest.mark.parametrize("cap", [0.5, 5.0, 34.0, 35.0, 200.0])
+def test_softcap_reference_both_sides_of_the_fixed_bound(cap):
+    """Soft-cap kernels fix the softmax reference at cap * log2(e) for caps up to 34.6
+    (every weight then lies in [2^(-2 cap log2 e), 1]) and keep a running maximum above;
+    both sides, a tiny cap and a cap far above the scores, on causal and window masks
+    with large scores, all blocks partial and full."""
+    q, k, v = qkv(1, 4, 2, 384, 384, 128, seed=31, qscale=4.0)
+    for mask in (("causal",), ("swa", 100)):
+        for bq, bk in ((128, 128), (64, 64)):
+            check(q, k, v, mask, bq, bk, "softcap", cap=cap, ctx=f"softcap {cap} {mask} {bq}x{bk}")
+
+
 def test_explicit_scale():
     q, k, v = qkv(1, 2, 2, 200, 200, 64, seed=17)
     check(q, k, v, ("causal",), 64, 64, scale=0.3, ctx="scale 0.3")
