@@ -502,6 +502,17 @@ EXTRA_WORKLOADS = ("causal_softcap", "gqa_doc_swa_alibi")
 
 def run(args):
     import torch
+    # the short workloads go first: right after seconds of the 64K prefill at full power
+    # the memory-bound decode measured 7% slower than on its own
+    decode, extra = None, {}
+    if not args.no_extras:
+        if args.workload != DECODE_WORKLOAD:
+            decode = run_workload(args, DECODE_WORKLOAD, headline=False)
+            torch.cuda.empty_cache()
+        for name in EXTRA_WORKLOADS:
+            if name != args.workload:
+                extra[name] = run_workload(args, name, headline=False)
+                torch.cuda.empty_cache()
     head = run_workload(args, args.workload, headline=True)
     torch.cuda.empty_cache()
     rec = {"metric": METRIC, "value": head.pop("value"), "unit": head.pop("unit"), "n_gpus": 1,
@@ -509,16 +520,8 @@ def run(args):
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic"}
     rec.update(head)
-    rec["decode"] = None
-    rec["extra"] = {}
-    if not args.no_extras:
-        if args.workload != DECODE_WORKLOAD:
-            rec["decode"] = run_workload(args, DECODE_WORKLOAD, headline=False)
-            torch.cuda.empty_cache()
-        for name in EXTRA_WORKLOADS:
-            if name != args.workload:
-                rec["extra"][name] = run_workload(args, name, headline=False)
-                torch.cuda.empty_cache()
+    rec["decode"] = decode
+    rec["extra"] = extra
     return rec
 
 
