@@ -289,13 +289,27 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
 #pragma unroll
   for (int dm = 0; dm < DM; ++dm) oacc[dm] = f32x16{};
 
-  // ---- S^T = K Q^T for the sub-tile in K slot SLOT
-  auto qk = [&](auto slot_c, f32x16 (&s)[2]) {
+  // ---- accumulator start of the S^T tile at key j0n, M-tile mt: zero, or for ALiBi the
+  // bias over the scale, slope (j - i) / scale, so that the product itself carries the
+  // bias and the score stays monotone in the accumulator (t = c2 * acc)
+  const float alibi_bs = SCORE == FA_S_ALIBI ? sc.slope2 / sc.c2 : 0.f;
+  auto acc_start = [&](int j0n, int mt) -> f32x16 {
+    f32x16 a = f32x16{};
+    if constexpr (SCORE == FA_S_ALIBI) {
+      const float base = alibi_bs * (float)(j0n + 4 * half - i_g);
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) a[rr] = __builtin_fmaf(alibi_bs, (float)key_of(mt, rr), base);
+    }
+    return a;
+  };
+
+  // ---- S^T = K Q^T (plus the accumulator start) for the sub-tile at key j0n in K slot SLOT
+  auto qk = [&](auto slot_c, f32x16 (&s)[2], int j0n) {
     constexpr int SLOT = decltype(slot_c)::value;
     const uint8_t* kb = smem + SLOT * L::TILE;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      s[mt] = f32x16{};
+      s[mt] = acc_start(j0n, mt);
 #pragma unroll
       for (int t = 0; t < KSTEPS; ++t) {
         const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + kfrag(t) + mt * 32 * L::KROW);
@@ -394,13 +408,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
           }
       }
     } else {
-      raw = false;
-      const float base = sc.slope2 * (float)(jl - i_g);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-          s[mt][rr] = __builtin_fmaf(s[mt][rr], sc.c2, __builtin_fmaf(sc.slope2, (float)key_of(mt, rr), base));
+      raw = true;   // ALiBi: the bias is already in the accumulator (acc_start)
     }
     // the maximum of this lane's half of the row's tile (16 of the 32 keys per 32-key
     // tile; the other half lives in lane ^ 32); not needed with a fixed reference
@@ -472,7 +480,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   // latency), then multiplies P of step g-1 with V and runs QK quarter g; no MFMA of a
   // group waits on VALU of the same group.
   auto fused = [&](auto vs_c, auto ks_c, const f32x16 (&s)[2], f32x16 (&sn)[2],
-                   const TileMode& md, auto qk_c) -> float {
+                   const TileMode& md, auto qk_c, int jn) -> float {
     constexpr int VS = decltype(vs_c)::value;
     constexpr int KS = decltype(ks_c)::value;
     constexpr bool QK = decltype(qk_c)::value;   // the last step of a pass has no next tile
@@ -539,7 +547,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       }
       if constexpr (QK && g < 4) {
         constexpr int mt = g >> 1;
-        if constexpr ((g & 1) == 0) sn[mt] = f32x16{};
+        if constexpr ((g & 1) == 0) sn[mt] = acc_start(jn, mt);
 #pragma unroll
         for (int i = 0; i < KQ; ++i)
           sn[mt] = mfma32(__builtin_bit_cast(bf16x8, kf[i]), qf[(g & 1) * KQ + i], sn[mt]);
@@ -590,7 +598,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
     }
     __syncthreads();
     f32x16 sa[2], sb[2];
-    qk(std::integral_constant<int, 0>{}, sa);
+    qk(std::integral_constant<int, 0>{}, sa, j0_a);
     TileMode md = prep(sa, sub_part(0), sub_part(0) || j0_a + KT > kv_len, j0_a, std::integral_constant<int, 0>{});
     // step 0 refills K slot 0 (with its document-ID and position-window slots), which
     // every wave has just read above
@@ -610,7 +618,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       // discarded.  A second copy of the step without that product makes the register
       // allocator spill (about 250-470 bytes per lane), which costs far more than the
       // 16 MFMAs per pass it saves.
-      l_run += fused(SP{}, SQ{}, scur, snxt, md, std::true_type{});
+      l_run += fused(SP{}, SQ{}, scur, snxt, md, std::true_type{}, j0_b);
       if (more) {
         const bool part = sub_part(s + 1);
         md = prep(snxt, part, part || j0_b + KT > kv_len, j0_b, SQ{});
