@@ -116,8 +116,15 @@ __device__ __forceinline__ void grad_elem(float s, float dp, float lse2, float d
   } else {
     t = score_log2<SCORE>(s, sc, ig, j);
   }
-  pv = ok ? fast_exp2(t - lse2) : 0.f;
-  ds = ok ? pv * (dp - delta) * dmod : 0.f;
+  // computed for every pair and selected at the end: under a branch per pair each
+  // pair's work (and the LDS reads feeding it) would be serialized behind its own exec
+  // mask (the empty asm keeps the compiler from sinking the work into such a branch;
+  // the values of a masked pair may be inf or NaN and are discarded by the select)
+  float e = fast_exp2(t - lse2);
+  float gr = e * (dp - delta) * dmod;
+  asm volatile("" : "+v"(e), "+v"(gr));
+  pv = ok ? e : 0.f;
+  ds = ok ? gr : 0.f;
 }
 
 // ---- delta = rowsum(dO * O): D / 8 lanes per row, each with 16 bytes (8 values) of O
@@ -192,7 +199,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
   constexpr int BQM = 128;     // largest query block
   __shared__ __attribute__((aligned(16))) uint8_t qs[BQM * RS];   // Q rows of one (head, block)
   __shared__ __attribute__((aligned(16))) uint8_t gs[BQM * RS];   // dO rows
-  __shared__ float lse_s[BQM], del_s[BQM];
+  __shared__ __attribute__((aligned(16))) float lse_s[BQM];
+  __shared__ __attribute__((aligned(16))) float del_s[BQM];
   __shared__ __attribute__((aligned(16))) int32_t doc_s[BQM];   // document IDs of the rows
 
   // work item: (b, h_kv) fastest, then the KV block c ascending: every head's first
@@ -307,18 +315,22 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
             dp[h] = mma_k32(*reinterpret_cast<const bf16x8*>(gs + off), vf[t], dp[h]);
           }
         }
-        // lane: rows q0 + 16 h + 4 g4 + rr, key j
+        // lane: rows q0 + 16 h + 4 g4 + rr, key j; the rows' LSE and delta as one 16-byte
+        // LDS word each per h
         float pv[8], ds[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + q0 + 16 * h + 4 * g4);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(del_s + q0 + 16 * h + 4 * g4);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int xr = q0 + 16 * h + 4 * g4 + rr;
             const int ig = r0 + xr + (int)p.q_offset;
             const bool ok = (okw >> (4 * ((q0 >> 4) + h) + rr)) & 1u;
-            grad_elem<SCORE>(s[h][rr], dp[h][rr], lse_s[xr], del_s[xr], ok, sc, p.scale, ig, j, pv[4 * h + rr],
+            grad_elem<SCORE>(s[h][rr], dp[h][rr], l4[rr], d4[rr], ok, sc, p.scale, ig, j, pv[4 * h + rr],
                              ds[4 * h + rr]);
           }
+        }
         const bf16x8 pb = pack8(pv), db = pack8(ds);
         // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (16x16x32): the lane holds P
         // and dS in the contraction order of cat_tr (rows q0 + 4 g4 + e, then q0 + 16 +
