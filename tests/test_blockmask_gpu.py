@@ -59,6 +59,16 @@ def test_broadcast_extents_and_per_batch_docs():
     del rng
 
 
+def test_positions_beyond_the_32_bit_fast_path():
+    """Query positions at and above 2^30 take the one-workgroup builder's 64-bit
+    classification (the 32-bit form covers positions below 2^30); the tables stay exact
+    on both sides of that bound and near 2^31."""
+    for q_off in ((1 << 30) - 400, (1 << 30) - 100, 1 << 30, (1 << 31) - 600):
+        for spec in (("causal",), ("swa", 300), ("prefix", 700), ("swa", 1 << 30),
+                     ("and", ("swa", (1 << 30) + 200), ("prefix", 500))):
+            check_tables(spec, 1, 1, 300, 1000, 128, 128, q_off)
+
+
 def test_deterministic_repeat():
     doc = docs_for(3000, "nonmono", 9)[None]
     spec = ("or", ("and", ("doc",), ("swa", 300)), ("prefix", 64))
