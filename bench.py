@@ -275,7 +275,9 @@ def run_workload(args, name, headline=True):
                                               workspace=workspace, order=order,
                                               q_side=bool(args.backward))
     else:
-        def build(tables=None, workspace=None, order=False):
+        # rule workloads: tables with the work order (longest rows first), which the
+        # one-workgroup builder ranks in place for up to 256 query blocks
+        def build(tables=None, workspace=None, order=True):
             return fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset,
                                         docT, tables=tables, workspace=workspace, order=order)
     bm = build()

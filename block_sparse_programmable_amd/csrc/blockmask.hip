@@ -468,6 +468,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(BuildParams p) {
 constexpr int kSmallMaxBlocks = 16384;  // tB * NQB * NKB
 constexpr int kSmallMaxLines = 2048;    // tB * (NQB + NKB)
 constexpr int kSmallMaxTB = 64;
+constexpr int kOrderInlineRows = 256;   // groups of at most this many rows are ranked in place
 
 // phases 4-6 of the one-workgroup build, shared with the row slicer: partial/full
 // counts (skipped when `counted`: cnt_s already holds them), prefix sums and ordered
@@ -555,6 +556,23 @@ __device__ void compact_small(const BuildParams& p, const uint8_t* grid_s, int32
     cum_s[4 * p.tB + tid] = acc;
   }
   __syncthreads();
+
+  // work order (when asked for and the groups are short): each row's rank by descending
+  // executed-block count, ties by descending index, as order_kernel computes it; every
+  // thread of a wave reads the same count at a time (LDS broadcast)
+  if (p.order && p.nqb <= kOrderInlineRows) {
+    for (int x = tid; x < nq; x += 1024) {
+      const int tb = p.tB == 1 ? 0 : x / p.nqb, r = x - tb * p.nqb;
+      const int32_t* c = cnt_s + 2 * tb * p.nqb;
+      const int len = c[2 * r] + c[2 * r + 1];
+      int rank = 0;
+      for (int y = 0; y < p.nqb; ++y) {
+        const int ly = c[2 * y] + c[2 * y + 1];
+        rank += (ly > len) || (ly == len && y > r);
+      }
+      for (int h = 0; h < p.tH; ++h) p.order[((int64_t)tb * p.tH + h) * p.nqb + rank] = r;
+    }
+  }
 
   // phase 6: counts and pointers for every replicated head, then ordered scatter
   const int rows = p.tB * p.tH * p.nqb, cols = p.tB * p.tH * p.nkb;
@@ -1104,6 +1122,11 @@ hipError_t launch_order(const BuildParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// the one-workgroup writers rank short groups themselves (compact_small)
+hipError_t launch_order_after_small(const BuildParams& p, hipStream_t s) {
+  return p.nqb <= kOrderInlineRows ? hipGetLastError() : launch_order(p, s);
+}
+
 
 }  // namespace
 
@@ -1120,7 +1143,7 @@ hipError_t launch_build(const BuildParams& p, hipStream_t s) {
   const int64_t expanded = (int64_t)p.tB * p.tH * (p.nqb + p.nkb);
   if (total <= kSmallMaxBlocks && lines <= kSmallMaxLines && p.tB <= kSmallMaxTB && expanded <= (1 << 20)) {
     hipLaunchKernelGGL(build_small_kernel, dim3(1), dim3(1024), 0, s, p);
-    return launch_order(p, s);
+    return launch_order_after_small(p, s);
   }
   if (lines > 0 && p.prog.has_doc)
     hipLaunchKernelGGL(doc_stats_kernel, dim3(waves_to_blocks(lines)), dim3(256), 0, s, p);
@@ -1145,7 +1168,7 @@ hipError_t launch_marked(const MP& sp, hipStream_t s) {
   const int64_t lines = (int64_t)p.tB * (p.nqb + p.nkb);
   if (total <= kSmallMaxBlocks && lines <= kSliceMaxLines && p.tB <= kSliceMaxTB) {
     hipLaunchKernelGGL(marked_small_kernel<MP>, dim3(1), dim3(1024), 0, s, sp);
-    return launch_order(p, s);
+    return launch_order_after_small(p, s);
   }
   const int64_t n16 = (total + 15) / 16;   // the workspace is rounded up to 256 bytes
   const int64_t rows = (int64_t)p.tB * p.nqb;

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
   // with K).  Every LDS read is a per-lane base plus an immediate offset.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * L::TILE + 2 * KT * 4];
   __shared__ int32_t list_s[kListCap];
-  __shared__ float rel_lds[kRel ? kRelposLdsMax : 1];
+  __shared__ float rel_lds[kRel ? kRelposLdsMax + 2 * kRelPad : 1];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -160,18 +160,22 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
     }
   }
 
-  // relative-position table of this query head, pre-multiplied by log2(e); the two
-  // saturated entries are kept in registers.  A table too large for LDS travels as
-  // per-tile windows instead: the entries for offsets i - j of the workgroup's rows
-  // against a K sub-tile at j0, [wb, wb + BQ + KT - 2] with wb = i_wg0 - j0 - (KT - 1),
-  // clamped to [-R, R] at copy time (kRelWin per K slot, copied with the K tile)
+  // relative-position table of this query head, entry of offset i - j at index
+  // i - j + R + kRelPad, with kRelPad copies of each saturated entry on either side: a
+  // tile that is not saturated for the wave spans offsets within 94 of [-R, R], so its
+  // reads need no clamping.  The two saturated entries (times log2 e) are also kept in
+  // registers.  A table too large for LDS travels as per-tile windows instead: the
+  // entries for offsets i - j of the workgroup's rows against a K sub-tile at j0,
+  // [wb, wb + BQ + KT - 2] with wb = i_wg0 - j0 - (KT - 1), clamped to [-R, R] at copy
+  // time (kRelWin per K slot, copied with the K tile)
   const int R = p.score.radius;
   const bool rel_in_lds = kRel && (2 * R + 1) <= kRelposLdsMax;
   const int i_wg0 = r * BQ + (int)p.q_offset;   // first row of the workgroup
   float bias_far2 = 0.f, bias_ahead2 = 0.f;   // rel >= R and rel <= -R
   if constexpr (kRel) {
     if (rel_in_lds) {
-      for (int x = tid; x < 2 * R + 1; x += NT) rel_lds[x] = sc.tab[x] * kLog2e;
+      for (int x = tid; x < 2 * R + 1 + 2 * kRelPad; x += NT)
+        rel_lds[x] = sc.tab[min(max(x - kRelPad, 0), 2 * R)];
     }
     bias_far2 = sc.tab[2 * R] * kLog2e;
     bias_ahead2 = sc.tab[0] * kLog2e;
@@ -324,6 +328,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
     constexpr int DSLOT = decltype(dslot_c)::value;
     const int32_t* dl = reinterpret_cast<const int32_t*>(smem + 4 * L::TILE + DSLOT * KT * 4);
     const int jl = j0 + 4 * half;   // key of element (mt=0, rr=0) in this lane
+    bool empty_tile = false;        // no row of the wave allows a key of the sub-tile
     if (masked) {
       if constexpr (MK == MK_GENERIC) {
         // the program over the lane's 32 keys at once, one bit per element
@@ -350,35 +355,67 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) s[mt][rr] = (ok >> (16 * mt + rr)) & 1u ? s[mt][rr] : kNegInf;
       } else {
-        // keys outside [lo, hi] (hi already clipped to kv_len - 1) are masked; when only
-        // the ragged tail needs masking the same test applies with the tail bound alone
+        // Keys outside the row's [lo, hi] (hi already clipped to kv_len - 1) are masked;
+        // when only the ragged tail needs masking the same test applies with the tail
+        // bound alone.  The sub-tile is first decided for the whole wave: every row
+        // allowing every key (nothing to mask), no row allowing any key (no weights), or
+        // a test per element, which compares documents only when the sub-tile's keys
+        // belong to more than one document.
+        static_assert(KT == 64, "one key of the sub-tile per lane");
         uint32_t lo_t = lo_u, span_t = span;
         if (!part) {
           lo_t = 0;
           span_t = (uint32_t)(kv_len - 1);
         }
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            int dq[4] = {doc_i, doc_i, doc_i, doc_i};
-            if constexpr (kDoc) {
-              if (part) {
-                const u32x4 dv = *reinterpret_cast<const u32x4*>(dl + 32 * mt + 8 * g4 + 4 * half);
-                dq[0] = (int)dv[0];
-                dq[1] = (int)dv[1];
-                dq[2] = (int)dv[2];
-                dq[3] = (int)dv[3];
-              }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int rr = 4 * g4 + e;
-              const uint32_t j = (uint32_t)(jl + key_of(mt, rr));
-              const bool ok = (j - lo_t) <= span_t && dq[e] == doc_i;
-              s[mt][rr] = ok ? s[mt][rr] : kNegInf;
+        const uint32_t ju = (uint32_t)j0;
+        const uint32_t hi_t = lo_t + span_t;
+        bool all_in = lo_t <= ju && ju + (KT - 1) <= hi_t;
+        bool none_in = hi_t < ju || lo_t > ju + (KT - 1);
+        bool key_docs = false;
+        if constexpr (kDoc) {
+          if (part) {
+            const int dk = dl[lane];   // document of key j0 + lane
+            const int dt = __builtin_amdgcn_readfirstlane(dk);
+            if (__ballot(dk != dt) != 0) {
+              key_docs = true;
+              all_in = false;
+            } else if (dt != doc_i) {   // one document, not the row's: nothing allowed
+              all_in = false;
+              none_in = true;
+              lo_t = 0x80000000u;
+              span_t = 0;
             }
           }
+        }
+        if (__ballot(!all_in) == 0) {
+          masked = false;
+        } else if (__ballot(!none_in) == 0) {
+          masked = false;
+          empty_tile = true;
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              int dq[4] = {doc_i, doc_i, doc_i, doc_i};
+              if constexpr (kDoc) {
+                if (key_docs) {
+                  const u32x4 dv = *reinterpret_cast<const u32x4*>(dl + 32 * mt + 8 * g4 + 4 * half);
+                  dq[0] = (int)dv[0];
+                  dq[1] = (int)dv[1];
+                  dq[2] = (int)dv[2];
+                  dq[3] = (int)dv[3];
+                }
+              }
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int rr = 4 * g4 + e;
+                const uint32_t j = (uint32_t)(jl + key_of(mt, rr));
+                const bool ok = (j - lo_t) <= span_t && dq[e] == doc_i;
+                s[mt][rr] = ok ? s[mt][rr] : kNegInf;
+              }
+            }
+        }
       }
     }
 
@@ -396,16 +433,18 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       raw = dmin >= R || dmax <= -R;
       bias2 = dmin >= R ? bias_far2 : bias_ahead2;
       if (!raw) {
+        // stored in natural units, s * scale + table[i - j] (mapped to base 2 with the
+        // tile maximum and in the weights).  The lane's entries sit at fixed offsets
+        // below the entry of its last key, in the padded table or in the K slot's window.
+        constexpr int kLast = key_of(1, 15);
+        const int dd_last = i_g - (jl + kLast);
+        const float* tb = rel_in_lds ? rel_lds + (dd_last + R + kRelPad)
+                                     : rel_lds + (DSLOT * kRelWin + dd_last - (i_wg0 - j0 - (KT - 1)));
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int dd = i_g - (jl + key_of(mt, rr));
-            const int rel = dd < -R ? -R : (dd > R ? R : dd);
-            const float bb = rel_in_lds ? rel_lds[rel + R]
-                                        : rel_lds[DSLOT * kRelWin + dd - (i_wg0 - j0 - (KT - 1))] * kLog2e;
-            s[mt][rr] = __builtin_fmaf(s[mt][rr], sc.c2, bb);
-          }
+          for (int rr = 0; rr < 16; ++rr)
+            s[mt][rr] = __builtin_fmaf(s[mt][rr], p.scale, tb[kLast - key_of(mt, rr)]);
       }
     } else {
       raw = true;   // ALiBi: the bias is already in the accumulator (acc_start)
@@ -413,7 +452,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
     // the maximum of this lane's half of the row's tile (16 of the 32 keys per 32-key
     // tile; the other half lives in lane ^ 32); not needed with a fixed reference
     float tmax = kNegInf;
-    if (!fixed_ref) {
+    if (!fixed_ref && !empty_tile) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -428,6 +467,7 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
           return __builtin_fmaf(t, sc.c2, bias2);
         }
       }
+      if constexpr (SCORE == FA_S_RELPOS) return t * kLog2e;   // natural units (-inf stays)
       return t;
     };
     // lazy rescale (wave-uniform branch): the reference moves only when a row's tile
@@ -467,9 +507,10 @@ __global__ __launch_bounds__(NW * 64, 2) void prefill_kernel(FwdParams p) {
       md.mul = sc.c2;
       md.add = bias2 - m_use;
     } else {
-      md.mul = 1.f;
+      md.mul = SCORE == FA_S_RELPOS ? kLog2e : 1.f;
       md.add = -m_use;
     }
+    if (empty_tile) md.add = kNegInf;   // every weight of the sub-tile is exactly zero
     return md;
   };
 

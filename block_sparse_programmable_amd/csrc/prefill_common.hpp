@@ -12,6 +12,7 @@ namespace {
 
 constexpr int KT = 64;                 // keys per sub-tile
 constexpr int kRelposLdsMax = 3073;    // table entries staged in LDS (2R+1 <= this)
+constexpr int kRelPad = 96;            // saturated copies staged on each side of that table
 constexpr int kRelWin = 192;           // per-K-slot window of a larger table (>= 128 + 64 - 1)
 constexpr float kRescaleThresh = 8.0f; // base-2 growth allowed before rescaling O
 
