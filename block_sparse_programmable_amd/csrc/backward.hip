@@ -101,30 +101,36 @@ struct RowStage {
   }
 };
 
-// weight and score gradient of one element: P = exp2(t - lse2); dS = P (dP - delta) dmod
+// weight and gradient of one element with respect to the scaled score x = scale * q.k:
+// P = exp2(t - lse2), dS = P (dP - delta) dmod with dmod = d score_mod / dx (the factor
+// scale of dL/d(q.k) is applied once to dQ and dK).  Computed for every pair; on blocks
+// where some pair is outside the mask, mask_pair then zeroes both values of such pairs
+// (a masked pair's values may be inf or NaN for an empty row and are discarded there).
 template <int SCORE>
-__device__ __forceinline__ void grad_elem(float s, float dp, float lse2, float delta, bool ok,
-                                          const ScoreCtx& sc, float scale, int ig, int j, float& pv,
-                                          float& ds) {
-  float t, dmod = scale;
+__device__ __forceinline__ void grad_elem(float s, float dp, float lse2, float delta,
+                                          const ScoreCtx& sc, int ig, int j, float& pv, float& ds) {
+  float t, dmod = 1.f;
   if constexpr (SCORE == FA_S_SOFTCAP) {
     // tanh of the scaled score over the cap, 1 - 2 / (e^{2x} + 1), as in score_log2,
-    // kept for the derivative scale * (1 - tanh^2)
+    // kept for the derivative 1 - tanh^2
     const float th = __builtin_fmaf(-2.f, fast_rcp(fast_exp2(s * sc.capk) + 1.f), 1.f);
     t = sc.cap2 * th;
-    dmod = scale * __builtin_fmaf(-th, th, 1.f);
+    dmod = __builtin_fmaf(-th, th, 1.f);
   } else {
     t = score_log2<SCORE>(s, sc, ig, j);
   }
-  // computed for every pair and selected at the end: under a branch per pair each
-  // pair's work (and the LDS reads feeding it) would be serialized behind its own exec
-  // mask (the empty asm keeps the compiler from sinking the work into such a branch;
-  // the values of a masked pair may be inf or NaN and are discarded by the select)
-  float e = fast_exp2(t - lse2);
-  float gr = e * (dp - delta) * dmod;
-  asm volatile("" : "+v"(e), "+v"(gr));
-  pv = ok ? e : 0.f;
-  ds = ok ? gr : 0.f;
+  const float e = fast_exp2(t - lse2);
+  pv = e;
+  ds = SCORE == FA_S_SOFTCAP ? e * (dp - delta) * dmod : e * (dp - delta);
+}
+
+// zero the weight and gradient of a pair outside the mask.  The empty asm keeps the
+// compiler from sinking the pair's work into a branch on `ok`, which would serialize
+// each pair behind its own exec mask.
+__device__ __forceinline__ void mask_pair(bool ok, float& pv, float& ds) {
+  asm volatile("" : "+v"(pv), "+v"(ds));
+  pv = ok ? pv : 0.f;
+  ds = ok ? ds : 0.f;
 }
 
 // ---- delta = rowsum(dO * O): D / 8 lanes per row, each with 16 bytes (8 values) of O
@@ -300,6 +306,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
         const uint32_t db = p.prog.has_doc ? doc_bits16(doc_s, g4, bq >> 4, doc_j) : 0u;
         okw &= mask_word(p.prog, [&](int op, int a) { return col_leaf(op, a, j, span, db); });
       }
+      // pairs outside the mask are zeroed only on blocks where the wave has some
+      const bool sel = __ballot(okw != 0xffffffffu) != 0;
       for (int q0 = 0; q0 < bq; q0 += 32) {
         // S and dP (16 rows x 16 keys each) of rows q0 + 16 h + (0..15), h = 0, 1, on
         // 16x16x32 tiles over the head dim
@@ -326,10 +334,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
           for (int rr = 0; rr < 4; ++rr) {
             const int xr = q0 + 16 * h + 4 * g4 + rr;
             const int ig = r0 + xr + (int)p.q_offset;
-            const bool ok = (okw >> (4 * ((q0 >> 4) + h) + rr)) & 1u;
-            grad_elem<SCORE>(s[h][rr], dp[h][rr], l4[rr], d4[rr], ok, sc, p.scale, ig, j, pv[4 * h + rr],
-                             ds[4 * h + rr]);
+            grad_elem<SCORE>(s[h][rr], dp[h][rr], l4[rr], d4[rr], sc, ig, j, pv[4 * h + rr], ds[4 * h + rr]);
           }
+        }
+        if (sel) {
+#pragma unroll
+          for (int x = 0; x < 8; ++x) mask_pair((okw >> (4 * (q0 >> 4) + x)) & 1u, pv[x], ds[x]);
         }
         const bf16x8 pb = pack8(pv), db = pack8(ds);
         // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (16x16x32): the lane holds P
@@ -345,6 +355,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
       }
     }
   }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dk[dt] *= p.scale;   // dL/d(q.k) = scale dL/dx
   // lane holds key j, head dims 16 dt + 4 g4 .. +4
   if (j < kv_len) {
     const int64_t base = ((int64_t)(b * p.Hkv + hkv) * kv_len + j) * D;
@@ -409,9 +421,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
   f32x4 dq[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // score_mod parameter gradients: dL/ds' = dS / scale per pair, with ds'/d slope =
-  // j - i (ALiBi) and ds'/d table[h][clip(i - j) + R] = 1; saturated offsets collect in
-  // registers, the others in LDS bins
+  // score_mod parameter gradients: dL/ds' = dS per pair (ALiBi and the position table
+  // add to the scaled score, dmod = 1), with ds'/d slope = j - i (ALiBi) and
+  // ds'/d table[h][clip(i - j) + R] = 1; saturated offsets collect in registers, the
+  // others in LDS bins
   const bool want_slope = SCORE == FA_S_ALIBI && bp.dslopes != nullptr;
   const bool want_table = SCORE == FA_S_RELPOS && bp.dtable != nullptr;
   const int R = p.score.radius;
@@ -462,6 +475,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
       const uint32_t db = p.prog.has_doc ? doc_bits16(doc_s, g4, bk >> 4, doc_i) : 0u;
       okw &= mask_word(p.prog, [&](int op, int a) { return row_leaf(op, a, ig, span, db); });
     }
+    // pairs outside the mask are zeroed only on blocks where the wave has some
+    const bool sel = __ballot(okw != 0xffffffffu) != 0;
     for (int k0 = 0; k0 < bk; k0 += 32) {
       // S^T (16 keys x 16 rows) = K Q^T and dP^T = V dO^T for keys k0 + 16 h + (0..15)
       f32x4 s[2], dp[2];
@@ -481,11 +496,19 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          grad_elem<SCORE>(s[h][rr], dp[h][rr], lse2, delta, sc, ig, j0 + k0 + 16 * h + 4 * g4 + rr,
+                           pv[4 * h + rr], ds[4 * h + rr]);
+      if (sel) {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) mask_pair((okw >> (4 * (k0 >> 4) + x)) & 1u, pv[x], ds[x]);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int jj = j0 + k0 + 16 * h + 4 * g4 + rr;
-          const bool ok = (okw >> (4 * ((k0 >> 4) + h) + rr)) & 1u;
-          float& d = ds[4 * h + rr];
-          grad_elem<SCORE>(s[h][rr], dp[h][rr], lse2, delta, ok, sc, p.scale, ig, jj, pv[4 * h + rr], d);
+          const float d = ds[4 * h + rr];
           if constexpr (SCORE == FA_S_ALIBI) {
             if (want_slope) g_slope = __builtin_fmaf(d, (float)(jj - ig), g_slope);
           }
@@ -510,10 +533,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
     }
   }
   // parameter gradients: wave sums, then one global add per wave (slopes) or per bin
-  const float inv_scale = 1.f / p.scale;
   if (want_slope) {
     for (int off = 32; off > 0; off >>= 1) g_slope += __shfl_xor(g_slope, off);
-    if ((threadIdx.x & 63) == 0) unsafeAtomicAdd(&bp.dslopes[hq], g_slope * inv_scale);
+    if ((threadIdx.x & 63) == 0) unsafeAtomicAdd(&bp.dslopes[hq], g_slope);
   }
   if (want_table) {
     for (int off = 32; off > 0; off >>= 1) {
@@ -528,13 +550,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
     float* gt = bp.dtable + (int64_t)hq * (2 * R + 1);
     for (int x = threadIdx.x; x < 2 * R + 1; x += NT) {
       const float v = bins_s[x];
-      if (v != 0.f) unsafeAtomicAdd(&gt[x], v * inv_scale);
+      if (v != 0.f) unsafeAtomicAdd(&gt[x], v);
     }
   }
   if (row_ok) {
     float* out = bp.dq + ((int64_t)bh * q_len + i) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(out + 16 * dt + 4 * g4) = dq[dt];
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(out + 16 * dt + 4 * g4) = dq[dt] * p.scale;
   }
 }
 

@@ -171,6 +171,30 @@ def test_selector_workload_tables(name):
         assert np.array_equal(got["order"][h * nqb:(h + 1) * nqb], OS.work_order(part, 1, 1, w.q_len, w.block_q))
 
 
+@pytest.mark.parametrize("case", ["causal_softcap", "gqa_doc_swa_alibi", "prefix_relpos_64k", "groups"])
+def test_rule_tables_work_order(case):
+    """The longest-first work order of rule tables: ranked in place by the one-workgroup
+    builder for groups of up to 256 rows (several batch and head groups included), by
+    its own kernel for longer groups (512 rows), against the oracle's ranking of the
+    tables' own row lengths (ties by descending index)."""
+    import block_sparse_programmable_amd as fa
+    from oracle import selector as OS
+    if case == "groups":
+        rng = np.random.default_rng(41)
+        doc = np.stack([np.repeat(np.arange(40), rng.integers(20, 200, 40))[:1500] for _ in range(2)]).astype(np.int32)
+        spec, B, H, q_len, kv_len, bq, bk, off = ("or", ("and", ("doc",), ("swa", 300)), ("prefix", 64)), 2, 3, 1500, 1500, 64, 64, 0
+    else:
+        w = W.WORKLOADS[case]
+        doc = W.aux_inputs(w)["doc_ids"]
+        spec, B, H, q_len, kv_len, bq, bk, off = w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset
+    docT = None if doc is None else torch.as_tensor(np.asarray(doc, np.int32)).cuda()
+    bm = fa.create_block_mask(spec, B, H, q_len, kv_len, bq, bk, off, docT, order=True)
+    torch.cuda.synchronize()
+    got = bm.compact()
+    want = OS.work_order({k: np.asarray(got[k]) for k in ("kv_num", "full_kv_num")}, B, H, q_len, bq)
+    assert np.array_equal(np.asarray(got["order"]), want)
+
+
 @pytest.mark.parametrize("name", [n for n in W.WORKLOADS if not W.WORKLOADS[n].selector])
 def test_workload_tables(name):
     w = W.WORKLOADS[name]
