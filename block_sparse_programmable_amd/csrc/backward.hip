@@ -101,27 +101,42 @@ struct RowStage {
   }
 };
 
-// weight and gradient of one element with respect to the scaled score x = scale * q.k:
-// P = exp2(t - lse2), dS = P (dP - delta) dmod with dmod = d score_mod / dx (the factor
-// scale of dL/d(q.k) is applied once to dQ and dK).  Computed for every pair; on blocks
-// where some pair is outside the mask, mask_pair then zeroes both values of such pairs
-// (a masked pair's values may be inf or NaN for an empty row and are discarded there).
+// weight and gradient of one element with respect to the scaled score x = scale * q.k,
+// from its raw score s, dpw = dP - delta (the dP product starts from -delta) and the
+// row term lrow: P = exp2(t - lse2) and dS = P dpw dmod with dmod = d score_mod / dx.
+//   soft-cap: t = cap2 tanh, tanh = 1 - 2 r with r = 1 / (e^{2x/cap} + 1), so
+//             t - lse2 = lrow - 2 cap2 r with lrow = cap2 - lse2, and 1 - tanh^2 =
+//             4 (r - r^2): dS is formed with r - r^2 and the factor 4 joins the scale
+//   others:   t = score_log2(s), lrow = -lse2, dmod = 1
+// The factor scale (times 4 for soft-cap) of dL/d(q.k) is applied once to dQ and dK.
+// Computed for every pair; on blocks where some pair is outside the mask, mask_pair
+// then zeroes both values of such pairs (a masked pair's values may be inf or NaN for
+// an empty row and are discarded there).
 template <int SCORE>
-__device__ __forceinline__ void grad_elem(float s, float dp, float lse2, float delta,
-                                          const ScoreCtx& sc, int ig, int j, float& pv, float& ds) {
-  float t, dmod = 1.f;
+__device__ __forceinline__ void grad_elem(float s, float dpw, float lrow, const ScoreCtx& sc, int ig,
+                                          int j, float& pv, float& ds) {
   if constexpr (SCORE == FA_S_SOFTCAP) {
-    // tanh of the scaled score over the cap, 1 - 2 / (e^{2x} + 1), as in score_log2,
-    // kept for the derivative 1 - tanh^2
-    const float th = __builtin_fmaf(-2.f, fast_rcp(fast_exp2(s * sc.capk) + 1.f), 1.f);
-    t = sc.cap2 * th;
-    dmod = __builtin_fmaf(-th, th, 1.f);
+    const float r = fast_rcp(fast_exp2(s * sc.capk) + 1.f);
+    const float e = fast_exp2(__builtin_fmaf(-2.f * sc.cap2, r, lrow));
+    pv = e;
+    ds = e * dpw * __builtin_fmaf(-r, r, r);
   } else {
-    t = score_log2<SCORE>(s, sc, ig, j);
+    const float e = fast_exp2(score_log2<SCORE>(s, sc, ig, j) + lrow);
+    pv = e;
+    ds = e * dpw;
   }
-  const float e = fast_exp2(t - lse2);
-  pv = e;
-  ds = SCORE == FA_S_SOFTCAP ? e * (dp - delta) * dmod : e * (dp - delta);
+}
+
+// the row term of grad_elem from a row's natural-log LSE
+template <int SCORE>
+__device__ __forceinline__ float grad_row_term(float lse, const ScoreCtx& sc) {
+  return (SCORE == FA_S_SOFTCAP ? sc.cap2 : 0.f) - lse * kLog2e;
+}
+
+// the factor of dL/d(q.k) over the gradient grad_elem forms
+template <int SCORE>
+__device__ __forceinline__ float grad_scale(float scale) {
+  return SCORE == FA_S_SOFTCAP ? 4.f * scale : scale;
 }
 
 // zero the weight and gradient of a pair outside the mask.  The empty asm keeps the
@@ -266,8 +281,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     auto stats = [&](int r0, float& l2, float& dl, int& dc) {
       const int i = r0 + (int)threadIdx.x;
       const bool ok = (int)threadIdx.x < bq && i < q_len;
-      l2 = ok ? p.lse[bh * q_len + i] * kLog2e : 0.f;
-      dl = ok ? bp.delta[bh * q_len + i] : 0.f;
+      l2 = ok ? grad_row_term<SCORE>(p.lse[bh * q_len + i], sc) : 0.f;
+      dl = ok ? -bp.delta[bh * q_len + i] : 0.f;
       dc = (ok && p.prog.has_doc) ? docr[i + p.q_offset] : 0;
     };
     RowStage<D, NT> sq, sg;
@@ -311,11 +326,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
       for (int q0 = 0; q0 < bq; q0 += 32) {
         // S and dP (16 rows x 16 keys each) of rows q0 + 16 h + (0..15), h = 0, 1, on
         // 16x16x32 tiles over the head dim
+        // (lane: rows q0 + 16 h + 4 g4 + rr, key j; the rows' terms and -delta as one
+        // 16-byte LDS word each per h; dP starts from -delta)
         f32x4 s[2], dp[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[h] = *reinterpret_cast<const f32x4*>(del_s + q0 + 16 * h + 4 * g4);
 #pragma unroll
           for (int t = 0; t < KS; ++t) {
             const int off = L::off(q0 + 16 * h + col, 32 * t + 8 * g4);
@@ -323,18 +340,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
             dp[h] = mma_k32(*reinterpret_cast<const bf16x8*>(gs + off), vf[t], dp[h]);
           }
         }
-        // lane: rows q0 + 16 h + 4 g4 + rr, key j; the rows' LSE and delta as one 16-byte
-        // LDS word each per h
         float pv[8], ds[8];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + q0 + 16 * h + 4 * g4);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(del_s + q0 + 16 * h + 4 * g4);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int xr = q0 + 16 * h + 4 * g4 + rr;
             const int ig = r0 + xr + (int)p.q_offset;
-            grad_elem<SCORE>(s[h][rr], dp[h][rr], l4[rr], d4[rr], sc, ig, j, pv[4 * h + rr], ds[4 * h + rr]);
+            grad_elem<SCORE>(s[h][rr], dp[h][rr], l4[rr], sc, ig, j, pv[4 * h + rr], ds[4 * h + rr]);
           }
         }
         if (sel) {
@@ -356,7 +370,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     }
   }
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) dk[dt] *= p.scale;   // dL/d(q.k) = scale dL/dx
+  for (int dt = 0; dt < DT; ++dt) dk[dt] *= grad_scale<SCORE>(p.scale);
   // lane holds key j, head dims 16 dt + 4 g4 .. +4
   if (j < kv_len) {
     const int64_t base = ((int64_t)(b * p.Hkv + hkv) * kv_len + j) * D;
@@ -412,9 +426,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
       gf[t] = __builtin_bit_cast(bf16x8, load16(bp.dout + base + 32 * t + 8 * g4));
     }
   }
-  const float lse2 = row_ok ? p.lse[(int64_t)bh * q_len + i] * kLog2e : 0.f;
-  const float delta = row_ok ? bp.delta[(int64_t)bh * q_len + i] : 0.f;
   const ScoreCtx sc = make_score_ctx(p.score, p.scale, hq);
+  const float lrow = row_ok ? grad_row_term<SCORE>(p.lse[(int64_t)bh * q_len + i], sc) : 0.f;
+  const float ndelta = row_ok ? -bp.delta[(int64_t)bh * q_len + i] : 0.f;
+  const f32x4 dp0 = f32x4{ndelta, ndelta, ndelta, ndelta};   // dP^T starts from -delta
   const int32_t* docr = doc_row(p.doc, b);
   int doc_i = (p.prog.has_doc && row_ok) ? docr[ig] : 0;
   asm volatile("" : "+v"(doc_i));   // (as doc_j in the dK/dV kernel)
@@ -483,7 +498,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[h] = dp0;
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
           const int off = L::off(k0 + 16 * h + col, 32 * t + 8 * g4);
@@ -497,8 +512,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
-          grad_elem<SCORE>(s[h][rr], dp[h][rr], lse2, delta, sc, ig, j0 + k0 + 16 * h + 4 * g4 + rr,
-                           pv[4 * h + rr], ds[4 * h + rr]);
+          grad_elem<SCORE>(s[h][rr], dp[h][rr], lrow, sc, ig, j0 + k0 + 16 * h + 4 * g4 + rr, pv[4 * h + rr],
+                           ds[4 * h + rr]);
       if (sel) {
 #pragma unroll
         for (int x = 0; x < 8; ++x) mask_pair((okw >> (4 * (k0 >> 4) + x)) & 1u, pv[x], ds[x]);
@@ -556,7 +571,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
   if (row_ok) {
     float* out = bp.dq + ((int64_t)bh * q_len + i) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(out + 16 * dt + 4 * g4) = dq[dt] * p.scale;
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4*>(out + 16 * dt + 4 * g4) = dq[dt] * grad_scale<SCORE>(p.scale);
   }
 }
 
