@@ -470,6 +470,21 @@ constexpr int kSmallMaxLines = 2048;    // tB * (NQB + NKB)
 constexpr int kSmallMaxTB = 64;
 constexpr int kOrderInlineRows = 256;   // groups of at most this many rows are ranked in place
 
+// the work-order entry of row r of table group tb, by one wave: its rank among the
+// group's rows by descending length, ties by descending index (the lanes count 64 rows
+// at a time with a ballot), written for every head of the group
+template <class LenF>
+__device__ __forceinline__ void rank_row(const BuildParams& p, int tb, int r, int lane, LenF len_of) {
+  const int len = len_of(r);
+  int rank = 0;
+  for (int y0 = 0; y0 < p.nqb; y0 += 64) {
+    const int y = y0 + lane;
+    const int ly = y < p.nqb ? len_of(y) : -1;
+    rank += __popcll(__ballot(ly > len || (ly == len && y > r)));
+  }
+  for (int h = lane; h < p.tH; h += 64) p.order[((int64_t)tb * p.tH + h) * p.nqb + rank] = r;
+}
+
 // phases 4-6 of the one-workgroup build, shared with the row slicer: partial/full
 // counts (skipped when `counted`: cnt_s already holds them), prefix sums and ordered
 // compaction of an LDS class grid [tB][nqb][nkb] into the table arrays, every row and
@@ -557,20 +572,12 @@ __device__ void compact_small(const BuildParams& p, const uint8_t* grid_s, int32
   }
   __syncthreads();
 
-  // work order (when asked for and the groups are short): each row's rank by descending
-  // executed-block count, ties by descending index, as order_kernel computes it; every
-  // thread of a wave reads the same count at a time (LDS broadcast)
+  // work order (when asked for and the groups are short), as order_kernel writes it
   if (p.order && p.nqb <= kOrderInlineRows) {
-    for (int x = tid; x < nq; x += 1024) {
-      const int tb = p.tB == 1 ? 0 : x / p.nqb, r = x - tb * p.nqb;
+    for (int x = wv; x < nq; x += 16) {
+      const int tb = p.tB == 1 ? 0 : x / p.nqb;
       const int32_t* c = cnt_s + 2 * tb * p.nqb;
-      const int len = c[2 * r] + c[2 * r + 1];
-      int rank = 0;
-      for (int y = 0; y < p.nqb; ++y) {
-        const int ly = c[2 * y] + c[2 * y + 1];
-        rank += (ly > len) || (ly == len && y > r);
-      }
-      for (int h = 0; h < p.tH; ++h) p.order[((int64_t)tb * p.tH + h) * p.nqb + rank] = r;
+      rank_row(p, tb, x - tb * p.nqb, lane, [&](int y) { return c[2 * y] + c[2 * y + 1]; });
     }
   }
 
@@ -1098,21 +1105,15 @@ __global__ __launch_bounds__(256) void marked_rows_kernel(MP sp) {
 
 // Work order: one workgroup per table group tb (rows (tb, h, r) for its tH heads, which
 // hold the same rows): query blocks ranked by descending executed-block count, ties by
-// descending index.  Every thread reads the same length at a time (LDS broadcast).
+// descending index.
 __global__ __launch_bounds__(1024) void order_kernel(BuildParams p) {
   __shared__ int32_t len_s[kOrderMaxRows];
-  const int64_t base = (int64_t)blockIdx.x * p.tH * p.nqb;
+  const int tb = blockIdx.x;
+  const int64_t base = (int64_t)tb * p.tH * p.nqb;
   for (int r = threadIdx.x; r < p.nqb; r += 1024) len_s[r] = p.kv_num[base + r] + p.full_kv_num[base + r];
   __syncthreads();
-  for (int r = threadIdx.x; r < p.nqb; r += 1024) {
-    const int len = len_s[r];
-    int rank = 0;
-    for (int x = 0; x < p.nqb; ++x) {
-      const int lx = len_s[x];
-      rank += (lx > len) || (lx == len && x > r);
-    }
-    for (int h = 0; h < p.tH; ++h) p.order[base + (int64_t)h * p.nqb + rank] = r;
-  }
+  for (int r = uniform(threadIdx.x >> 6); r < p.nqb; r += 16)
+    rank_row(p, tb, r, threadIdx.x & 63, [&](int y) { return len_s[y]; });
 }
 
 inline unsigned waves_to_blocks(int64_t waves) { return (unsigned)((waves + 3) / 4); }
