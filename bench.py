@@ -276,10 +276,12 @@ def run_workload(args, name, headline=True):
                                               q_side=bool(args.backward))
     else:
         # rule workloads: tables with the work order (longest rows first), which the
-        # one-workgroup builder ranks in place for up to 256 query blocks
+        # one-workgroup builder ranks in place for up to 256 query blocks; the forward
+        # reads only the kv side, the backward leg needs the query side too
         def build(tables=None, workspace=None, order=True):
             return fa.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset,
-                                        docT, tables=tables, workspace=workspace, order=order)
+                                        docT, tables=tables, workspace=workspace, order=order,
+                                        q_side=bool(args.backward))
     bm = build()
     tables = bm.tensors
     bws = bm._keep[1]

@@ -144,15 +144,16 @@ def _set_tables(d, tables):
 
 def create_block_mask(mask, B, H, q_len, kv_len, block_q=128, block_kv=128, q_offset=0,
                       doc_ids: Optional[torch.Tensor] = None, device="cuda", stream=None,
-                      tables=None, workspace=None, order=False):
+                      tables=None, workspace=None, order=False, q_side=True):
     """Build the block tables on the GPU.  ``mask`` is a nested tuple rule
     (see workloads); ``doc_ids`` an int32 device tensor [doc_batch, doc_len];
-    ``order`` also writes the longest-row-first work order."""
+    ``order`` also writes the longest-row-first work order; ``q_side=False`` writes only
+    the kv side (all a forward reads; the backward needs both)."""
     lib = L.load()
     d, doc_ids = block_mask_desc(mask, B, H, q_len, kv_len, block_q, block_kv, q_offset, doc_ids)
     rows, cols, cap, ws = block_mask_sizes(d)
     if tables is None:
-        tables = _alloc_tables(rows, cols, cap, device, order=order)
+        tables = _alloc_tables(rows, cols, cap, device, q_side=q_side, order=order)
     _set_tables(d, tables)
     if workspace is None:
         workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)

@@ -403,9 +403,12 @@ fa_status fa_create_block_mask(fa_block_mask* bm, void* workspace, size_t ws_byt
   fa::MaskProg prog;
   fa_status s = check_mask_geometry(bm, &prog);
   if (s != FA_OK) return s;
-  if (!bm->kv_num || !bm->kv_ptr || !bm->kv_idx || !bm->full_kv_num || !bm->full_kv_ptr || !bm->full_kv_idx ||
-      !bm->q_num || !bm->q_ptr || !bm->q_idx || !bm->full_q_num || !bm->full_q_ptr || !bm->full_q_idx)
-    return fail(FA_ERR_NULL, "all twelve table pointers must be non-NULL");
+  if (!bm->kv_num || !bm->kv_ptr || !bm->kv_idx || !bm->full_kv_num || !bm->full_kv_ptr || !bm->full_kv_idx)
+    return fail(FA_ERR_NULL, "the six kv-side table pointers must be non-NULL");
+  const int nq_set = (bm->q_num != nullptr) + (bm->q_ptr != nullptr) + (bm->q_idx != nullptr) +
+                     (bm->full_q_num != nullptr) + (bm->full_q_ptr != nullptr) + (bm->full_q_idx != nullptr);
+  if (nq_set != 0 && nq_set != 6)
+    return fail(FA_ERR_NULL, "the six q-side table pointers must be all set or all NULL");
   const int64_t nqb = cdiv(bm->q_len, bm->block_q);
   const int64_t nkb = cdiv(bm->kv_len, bm->block_kv);
   const size_t need = fa::build_workspace_bytes(bm->B, nqb, nkb);

@@ -477,10 +477,18 @@ template <class LenF>
 __device__ __forceinline__ void rank_row(const BuildParams& p, int tb, int r, int lane, LenF len_of) {
   const int len = len_of(r);
   int rank = 0;
-  for (int y0 = 0; y0 < p.nqb; y0 += 64) {
-    const int y = y0 + lane;
-    const int ly = y < p.nqb ? len_of(y) : -1;
-    rank += __popcll(__ballot(ly > len || (ly == len && y > r)));
+  for (int y0 = 0; y0 < p.nqb; y0 += 512) {   // eight reads in flight, then their ballots
+    int ly[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int y = y0 + 64 * u + lane;
+      ly[u] = y < p.nqb ? len_of(y) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int y = y0 + 64 * u + lane;
+      rank += __popcll(__ballot(ly[u] > len || (ly[u] == len && y > r)));
+    }
   }
   for (int h = lane; h < p.tH; h += 64) p.order[((int64_t)tb * p.tH + h) * p.nqb + rank] = r;
 }

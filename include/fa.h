@@ -142,7 +142,9 @@ typedef struct {
 fa_status fa_block_mask_sizes(const fa_block_mask* bm, int64_t* rows, int64_t* cols,
                               int64_t* idx_capacity, size_t* workspace_bytes);
 
-/* Classify every block exactly and write all twelve arrays of *bm on `stream`.
+/* Classify every block exactly and write the arrays of *bm on `stream`: all twelve,
+ * or the six kv-side ones when the six q-side pointers are all NULL (a forward reads
+ * only the kv side; FA_ERR_NULL when some q-side pointers are set and others not).
  * `workspace` is a device buffer of at least workspace_bytes (its contents on entry
  * are ignored and on exit unspecified).  Deterministic: the same inputs always give
  * the same tables bit for bit.  The table writers (this call, the selector and slice

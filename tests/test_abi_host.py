@@ -135,9 +135,16 @@ def test_validation_errors_before_any_launch(lib):
     assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_NULL
     d = _bm(L)
     assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_NULL   # no tables
-    for name in ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx",
-                 "q_num", "q_ptr", "q_idx", "full_q_num", "full_q_ptr", "full_q_idx"):
+    for name in ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx"):
         setattr(d, name, 0x1000)                  # never dereferenced: rejected first
+    # the q side: all six pointers or none
+    d.q_num = 0x1000
+    assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_NULL
+    assert b"q-side" in lib.fa_last_error_message()
+    d.q_num = None
+    assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_WORKSPACE   # kv side only
+    for name in ("q_num", "q_ptr", "q_idx", "full_q_num", "full_q_ptr", "full_q_idx"):
+        setattr(d, name, 0x1000)
     assert lib.fa_create_block_mask(C.byref(d), None, 0, None) == L.FA_ERR_WORKSPACE
     assert lib.fa_create_block_mask(C.byref(d), C.c_void_p(0x2000), 1, None) == L.FA_ERR_WORKSPACE
     d = _bm(L, q_len=-1)

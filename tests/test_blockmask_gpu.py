@@ -195,6 +195,25 @@ def test_rule_tables_work_order(case):
     assert np.array_equal(np.asarray(got["order"]), want)
 
 
+@pytest.mark.parametrize("name", ["gqa_doc_swa_alibi", "prefix_relpos_64k"])
+def test_kv_side_only_tables(name):
+    """Tables built without the query side (the one-workgroup builder, and the
+    multi-launch builder for the 512 x 512 grid) equal the kv side and the work order of
+    tables built with it."""
+    import block_sparse_programmable_amd as fa
+    w = W.WORKLOADS[name]
+    doc = W.aux_inputs(w)["doc_ids"]
+    docT = None if doc is None else torch.as_tensor(np.asarray(doc, np.int32)).cuda()
+    args = (w.mask, 1, 1, w.q_len, w.kv_len, w.block_q, w.block_kv, w.q_offset, docT)
+    both = fa.create_block_mask(*args, order=True).compact()
+    kv = fa.create_block_mask(*args, order=True, q_side=False)
+    torch.cuda.synchronize()
+    assert "q_num" not in kv.tensors
+    got = kv.compact()
+    for k in ("kv_num", "kv_ptr", "kv_idx", "full_kv_num", "full_kv_ptr", "full_kv_idx", "order"):
+        assert np.array_equal(np.asarray(got[k]), np.asarray(both[k])), k
+
+
 @pytest.mark.parametrize("name", [n for n in W.WORKLOADS if not W.WORKLOADS[n].selector])
 def test_workload_tables(name):
     w = W.WORKLOADS[name]
