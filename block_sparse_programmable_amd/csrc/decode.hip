@@ -256,8 +256,8 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
       static_for<CPO>([&](auto uc) {
         constexpr int u = decltype(uc)::value;
         constexpr int grp = (u / 4) * 4096;   // immediate offsets stay below 4 KB
-        dma16_s<(u % 4) * 1024>(mk + grp, kg + grp, koff[u % KVAR]);
-        dma16_s<(u % 4) * 1024>(mv + grp, vg + grp, voff[u % VVAR]);
+        dma16_s_nt<(u % 4) * 1024>(mk + grp, kg + grp, koff[u % KVAR]);
+        dma16_s_nt<(u % 4) * 1024>(mv + grp, vg + grp, voff[u % VVAR]);
       });
       copy_window(j0, mk);
     } else {
@@ -271,8 +271,8 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_kernel(FwdParams p) 
         constexpr int u = decltype(uc)::value;
         const int key = u * KPK + lane / DCH;
         const uint32_t rowoff = (uint32_t)(min(j0 + key, kv_len - 1) - jb) * L::KROW;
-        dma16_s<0>(mk + u * 1024, kg, rowoff + (koff[u % KVAR] & (L::KROW - 1)));
-        dma16_s<0>(mv + u * 1024, vg, rowoff + (voff[u % VVAR] & (L::KROW - 1)));
+        dma16_s_nt<0>(mk + u * 1024, kg, rowoff + (koff[u % KVAR] & (L::KROW - 1)));
+        dma16_s_nt<0>(mv + u * 1024, vg, rowoff + (voff[u % VVAR] & (L::KROW - 1)));
       });
       copy_window(j0, mk);
     }
