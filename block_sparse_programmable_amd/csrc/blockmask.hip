@@ -1111,23 +1111,24 @@ __global__ __launch_bounds__(256) void marked_rows_kernel(MP sp) {
   mark_row(sp, row, threadIdx.x & 63, p.grid + (int64_t)row * p.nkb);
 }
 
-// Work order: one workgroup per table group tb (rows (tb, h, r) for its tH heads, which
-// hold the same rows): query blocks ranked by descending executed-block count, ties by
-// descending index.
+// Work order: workgroup (tb, x) ranks rows 16 x .. 16 x + 15 of table group tb (rows
+// (tb, h, r) for its tH heads, which hold the same rows), one per wave, by descending
+// executed-block count, ties by descending index.
 __global__ __launch_bounds__(1024) void order_kernel(BuildParams p) {
   __shared__ int32_t len_s[kOrderMaxRows];
   const int tb = blockIdx.x;
   const int64_t base = (int64_t)tb * p.tH * p.nqb;
   for (int r = threadIdx.x; r < p.nqb; r += 1024) len_s[r] = p.kv_num[base + r] + p.full_kv_num[base + r];
   __syncthreads();
-  for (int r = uniform(threadIdx.x >> 6); r < p.nqb; r += 16)
-    rank_row(p, tb, r, threadIdx.x & 63, [&](int y) { return len_s[y]; });
+  const int r = (int)blockIdx.y * 16 + uniform(threadIdx.x >> 6);
+  if (r < p.nqb) rank_row(p, tb, r, threadIdx.x & 63, [&](int y) { return len_s[y]; });
 }
 
 inline unsigned waves_to_blocks(int64_t waves) { return (unsigned)((waves + 3) / 4); }
 
 hipError_t launch_order(const BuildParams& p, hipStream_t s) {
-  if (p.order && p.tB > 0 && p.nqb > 0) hipLaunchKernelGGL(order_kernel, dim3(p.tB), dim3(1024), 0, s, p);
+  if (p.order && p.tB > 0 && p.nqb > 0)
+    hipLaunchKernelGGL(order_kernel, dim3(p.tB, (p.nqb + 15) / 16), dim3(1024), 0, s, p);
   return hipGetLastError();
 }
 
