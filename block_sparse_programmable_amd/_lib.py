@@ -22,7 +22,8 @@ FA_NOALLOC_SCRATCH_BYTES = 16 << 20
 # names declared in include/fa.h (checked against the header by the tests)
 EXPORTS = ("fa_block_mask_sizes", "fa_create_block_mask", "fa_block_mask_slice", "fa_block_mask_from_indices",
            "fa_forward_workspace_size",
-           "fa_forward", "fa_forward_noalloc", "fa_forward_paged", "fa_backward_workspace_size", "fa_backward",
+           "fa_forward", "fa_forward_noalloc", "fa_forward_paged", "fa_backward_workspace_size",
+           "fa_backward_workspace_min_size", "fa_backward",
            "fa_status_string", "fa_last_error_message")
 
 
@@ -111,6 +112,8 @@ def load(path: str = LIB_PATH):
     lib.fa_forward_noalloc.restype = C.c_int
     lib.fa_backward_workspace_size.argtypes = [C.POINTER(fa_bwd_args), C.POINTER(C.c_size_t)]
     lib.fa_backward_workspace_size.restype = C.c_int
+    lib.fa_backward_workspace_min_size.argtypes = [C.POINTER(fa_bwd_args), C.POINTER(C.c_size_t)]
+    lib.fa_backward_workspace_min_size.restype = C.c_int
     lib.fa_backward.argtypes = [C.POINTER(fa_bwd_args), C.c_void_p]
     lib.fa_backward.restype = C.c_int
     lib.fa_status_string.argtypes = [C.c_int]

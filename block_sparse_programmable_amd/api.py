@@ -240,11 +240,13 @@ def forward_workspace_size(args) -> int:
 
 def backward(q, k, v, out, lse, dout, block_mask: BlockMask, score="identity", softcap=0.0,
              alibi_slopes=None, relpos=None, relpos_radius=0, scale=None, dq=None, dk=None, dv=None,
-             workspace=None, stream=None, param_grad=False):
+             workspace=None, stream=None, param_grad=False, store_grads=True):
     """dQ [B,Hq,q_len,d], dK and dV [B,Hkv,kv_len,d] (fp32) of the forward that produced
     out and lse, for the output gradient dout (bf16, same shape as out).  With
     ``param_grad`` a fourth result is the gradient of the ALiBi slopes [Hq] or of the
-    relative-position table [Hq, 2R+1] (fp32)."""
+    relative-position table [Hq, 2R+1] (fp32).  ``store_grads`` gives the call the
+    workspace in which the dK/dV pass stores the per-pair gradients for the dQ pass
+    (where the library offers it); without it the dQ pass recomputes them."""
     lib = L.load()
     if dout.dtype != torch.bfloat16 or not dout.is_contiguous() or dout.shape != out.shape:
         raise ValueError("dout must be a contiguous bfloat16 tensor shaped like out")
@@ -274,12 +276,13 @@ def backward(q, k, v, out, lse, dout, block_mask: BlockMask, score="identity", s
         else:
             raise ValueError("param_grad needs the alibi or relpos score")
     n = C.c_size_t()
-    L.check(lib.fa_backward_workspace_size(C.byref(ba), C.byref(n)))
+    size_fn = lib.fa_backward_workspace_size if store_grads else lib.fa_backward_workspace_min_size
+    L.check(size_fn(C.byref(ba), C.byref(n)))
     if n.value > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < n.value:
             workspace = torch.empty(n.value, dtype=torch.uint8, device=q.device)
         ba.workspace = workspace.data_ptr()
-        ba.ws_bytes = workspace.numel() * workspace.element_size()
+        ba.ws_bytes = n.value   # exactly the size asked for: a larger buffer may not pick the path
     L.check(lib.fa_backward(C.byref(ba), _stream(stream)))
     return (dq, dk, dv, gpar) if param_grad else (dq, dk, dv)
 

@@ -467,7 +467,9 @@ fa_status fa_forward(const fa_fwd_args* args, fa_stream_t stream) {
 
 namespace {
 
-fa_status plan_backward(const fa_bwd_args* a, fa::BwdParams* bp, size_t* ws) {
+// ws: the minimum workspace (row sums dO . O); ds_ws: the stored-gradient part that may
+// follow it (0 when this shape always recomputes the gradients in the dQ pass)
+fa_status plan_backward(const fa_bwd_args* a, fa::BwdParams* bp, size_t* ws, size_t* ds_ws) {
   if (!a) return fail(FA_ERR_NULL, "args is NULL");
   FwdPlan plan;
   fa_status s = plan_forward(a->fwd, &plan);
@@ -484,6 +486,7 @@ fa_status plan_backward(const fa_bwd_args* a, fa::BwdParams* bp, size_t* ws) {
   bp->dk = a->dk;
   bp->dv = a->dv;
   bp->delta = nullptr;
+  bp->ds = nullptr;
   const int kind = a->fwd->score.kind;
   if (a->dslopes && kind != FA_S_ALIBI)
     return fail(FA_ERR_UNSUPPORTED, "dslopes is the gradient of ALiBi slopes; the score kind is %d", kind);
@@ -494,7 +497,8 @@ fa_status plan_backward(const fa_bwd_args* a, fa::BwdParams* bp, size_t* ws) {
                 fa::kRelGradMaxRadius, a->fwd->score.relpos_radius);
   bp->dslopes = a->dslopes;
   bp->dtable = a->dtable;
-  *ws = fa::backward_workspace_bytes(plan.p);
+  *ws = fa::backward_workspace_min_bytes(plan.p);
+  *ds_ws = fa::backward_ds_bytes(plan.p, a->dslopes != nullptr || a->dtable != nullptr);
   return FA_OK;
 }
 
@@ -502,8 +506,18 @@ fa_status plan_backward(const fa_bwd_args* a, fa::BwdParams* bp, size_t* ws) {
 
 fa_status fa_backward_workspace_size(const fa_bwd_args* args, size_t* bytes) {
   fa::BwdParams bp;
-  size_t ws = 0;
-  fa_status s = plan_backward(args, &bp, &ws);
+  size_t ws = 0, ds_ws = 0;
+  fa_status s = plan_backward(args, &bp, &ws, &ds_ws);
+  if (s != FA_OK) return s;
+  if (!bytes) return fail(FA_ERR_NULL, "bytes is NULL");
+  *bytes = ws + ds_ws;
+  return ok();
+}
+
+fa_status fa_backward_workspace_min_size(const fa_bwd_args* args, size_t* bytes) {
+  fa::BwdParams bp;
+  size_t ws = 0, ds_ws = 0;
+  fa_status s = plan_backward(args, &bp, &ws, &ds_ws);
   if (s != FA_OK) return s;
   if (!bytes) return fail(FA_ERR_NULL, "bytes is NULL");
   *bytes = ws;
@@ -512,8 +526,8 @@ fa_status fa_backward_workspace_size(const fa_bwd_args* args, size_t* bytes) {
 
 fa_status fa_backward(const fa_bwd_args* args, fa_stream_t stream) {
   fa::BwdParams bp;
-  size_t ws = 0;
-  fa_status s = plan_backward(args, &bp, &ws);
+  size_t ws = 0, ds_ws = 0;
+  fa_status s = plan_backward(args, &bp, &ws, &ds_ws);
   if (s != FA_OK) return s;
   if (ws > 0) {
     if (!args->workspace || args->ws_bytes < ws)
@@ -522,6 +536,8 @@ fa_status fa_backward(const fa_bwd_args* args, fa_stream_t stream) {
     if (((uintptr_t)args->workspace & 255) != 0)
       return fail(FA_ERR_WORKSPACE, "backward workspace must be 256-byte aligned");
     bp.delta = static_cast<float*>(args->workspace);
+    if (ds_ws > 0 && args->ws_bytes >= ws + ds_ws)   // ws is a multiple of 256 bytes
+      bp.ds = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(args->workspace) + ws);
   }
   hipError_t e = fa::launch_backward(bp, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));

@@ -223,6 +223,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
   __shared__ __attribute__((aligned(16))) float lse_s[BQM];
   __shared__ __attribute__((aligned(16))) float del_s[BQM];
   __shared__ __attribute__((aligned(16))) int32_t doc_s[BQM];   // document IDs of the rows
+  __shared__ int32_t slot_s[kDsMaxRows];   // stored-gradient tiles of the column's blocks
 
   // work item: (b, h_kv) fastest, then the KV block c ascending: every head's first
   // columns go out before any head's later ones (for causal-like rules the first columns
@@ -278,6 +279,31 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     const int n_ent = nf + np;
     // query block of list entry e and its row statistics (one per thread, bq <= 256)
     auto block_of = [&](int e) -> int { return uniform(e >= nf ? pl[e - nf] : fl[e]); };
+    if (bp.ds) {
+      // Each block (r, c) of the column's list gets the tile of the stored gradients at
+      // its kv-side position within the table entry (the row's full list, then its
+      // partial list): found by one wave per entry in row r's list of the same kind.
+      // A position outside the grid (tables that are not exact transposes) is -1: the
+      // block's tile is not written.
+      const int nqb = p.tab.nqb;
+      const int g0 = (tb * p.tab.tH + th) * nqb;
+      const int nfg = uniform(p.tab.fptr[g0 + nqb]) - uniform(p.tab.fptr[g0]);
+      for (int e = uniform(w); e < n_ent; e += NW) {
+        const bool full = e < nf;
+        const int row = g0 + block_of(e);
+        const int* lst = full ? p.tab.fidx + uniform(p.tab.fptr[row]) : p.tab.idx + uniform(p.tab.ptr[row]);
+        const int n = uniform(full ? p.tab.fnum[row] : p.tab.num[row]);
+        int pos = -1;
+        for (int x0 = 0; x0 < n && pos < 0; x0 += 64) {
+          const uint64_t m = __ballot(x0 + lane < n && lst[x0 + lane] == c);
+          if (m != 0) pos = x0 + (int)__builtin_ctzll(m);
+        }
+        const int base = full ? uniform(p.tab.fptr[row]) - uniform(p.tab.fptr[g0])
+                              : nfg + uniform(p.tab.ptr[row]) - uniform(p.tab.ptr[g0]);
+        const int local = pos < 0 ? -1 : base + pos;
+        if (lane == 0) slot_s[e] = (local >= 0 && local < nqb * p.tab.nkb) ? local : -1;
+      }
+    }
     auto stats = [&](int r0, float& l2, float& dl, int& dc) {
       const int i = r0 + (int)threadIdx.x;
       const bool ok = (int)threadIdx.x < bq && i < q_len;
@@ -297,7 +323,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     for (int e = 0; e < n_ent; ++e) {
       const bool part = e >= nf;
       const int r0 = block_of(e) * bq;
-      __syncthreads();   // the previous block's rows are consumed
+      __syncthreads();   // the previous block's rows are consumed (and the tiles are found)
+      // this block's stored-gradient tile: rows are the block's keys, bq values each
+      uint16_t* dst_tile = nullptr;
+      if (bp.ds) {
+        const int slot = uniform(slot_s[e]);
+        if (slot >= 0) dst_tile = bp.ds + ((bh * p.tab.nqb * p.tab.nkb + slot) * p.tab.bk + w * 16 + col) * bq;
+      }
       sq.put(qs, bq);
       sg.put(gs, bq);
       if ((int)threadIdx.x < bq) {
@@ -356,6 +388,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
           for (int x = 0; x < 8; ++x) mask_pair((okw >> (4 * (q0 >> 4) + x)) & 1u, pv[x], ds[x]);
         }
         const bf16x8 pb = pack8(pv), db = pack8(ds);
+        if (dst_tile) {
+          // the lane's key row: rows q0 + 4 g4 .. +3 and q0 + 16 + 4 g4 .. +3
+          const u32x4 dw = __builtin_bit_cast(u32x4, db);
+          *reinterpret_cast<u32x2*>(dst_tile + q0 + 4 * g4) = u32x2{dw[0], dw[1]};
+          *reinterpret_cast<u32x2*>(dst_tile + q0 + 16 + 4 * g4) = u32x2{dw[2], dw[3]};
+        }
         // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (16x16x32): the lane holds P
         // and dS in the contraction order of cat_tr (rows q0 + 4 g4 + e, then q0 + 16 +
         // 4 g4 + e), and the A operands (head dim x rows) come from transposing reads
@@ -576,6 +614,93 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
   }
 }
 
+// ---- dQ from the gradients stored by the dK/dV pass (128 x 128 blocks, D = 128): one
+// workgroup per (b, h_q, query block), one wave per 16 rows.  For each listed KV block
+// its K rows and its stored tile (rows are the block's keys, 128 values each: the same
+// 256-byte rows as K) go to LDS, and dQ^T += K^T dS^T over 32 keys at a time takes both
+// operands from transposing reads.  No score is recomputed.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_ds_kernel(BwdParams bp) {
+  static_assert(D == 128 && NW == 8, "stored gradient tiles are read for 128 x 128 blocks at d = 128");
+  const FwdParams& p = bp.f;
+  constexpr int NT = NW * 64;
+  using L = Lay<D>;
+  constexpr int RS = L::RS;
+  constexpr int DT = D / 16;
+  constexpr int BKM = 128;
+  __shared__ __attribute__((aligned(16))) uint8_t ks[BKM * RS];
+  __shared__ __attribute__((aligned(16))) uint8_t ts[BKM * RS];   // the stored tile
+
+  // work item as in bwd_dq_kernel
+  const int nqb = p.tab.nqb;
+  const int nbh = p.B * p.Hq;
+  const int rank = blockIdx.x / nbh;
+  const int bh = blockIdx.x - rank * nbh;
+  const int b = bh / p.Hq, hq = bh - b * p.Hq, hkv = hq / p.g;
+  const int tb = p.tab.tB == 1 ? 0 : b;
+  const int th = p.tab.tH == 1 ? 0 : hq;
+  const int r = p.tab.order ? uniform(p.tab.order[(tb * p.tab.tH + th) * nqb + rank]) : nqb - 1 - rank;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, g4 = lane >> 4;
+  const int q_len = (int)p.q_len, kv_len = (int)p.kv_len, bk = p.tab.bk;
+  const int i = r * p.tab.bq + w * 16 + col;
+  f32x4 dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int g0 = (tb * p.tab.tH + th) * nqb;
+  const int row = g0 + r;
+  const int nf = uniform(p.tab.fnum[row]);
+  const int np = uniform(p.tab.num[row]);
+  const int32_t* fl = p.tab.fidx + uniform(p.tab.fptr[row]);
+  const int32_t* pl = p.tab.idx + uniform(p.tab.ptr[row]);
+  // tile positions: the row's full entries, then its partial ones, within the table entry
+  const int fbase = uniform(p.tab.fptr[row]) - uniform(p.tab.fptr[g0]);
+  const int pbase = uniform(p.tab.fptr[g0 + nqb]) - uniform(p.tab.fptr[g0]) + uniform(p.tab.ptr[row]) -
+                    uniform(p.tab.ptr[g0]);
+  const int ntiles = nqb * p.tab.nkb;
+  const int64_t kvh = (int64_t)(b * p.Hkv + hkv) * kv_len;
+  const uint16_t* tiles = bp.ds + (int64_t)bh * ntiles * (BKM * BKM);
+  const int n_ent = nf + np;
+  auto block_of = [&](int e) -> int { return uniform(e >= nf ? pl[e - nf] : fl[e]); };
+  auto tile_of = [&](int e) -> const uint16_t* {
+    const int slot = e < nf ? fbase + e : pbase + (e - nf);
+    return (slot >= 0 && slot < ntiles) ? tiles + (int64_t)slot * (BKM * BKM) : nullptr;
+  };
+  RowStage<D, NT> sk, st;
+  auto fetch = [&](int e) {
+    sk.fetch(p.k + kvh * D, block_of(e) * bk, bk, kv_len);
+    const uint16_t* t = tile_of(e);
+    st.fetch(t ? t : tiles, 0, t ? bk : 0, bk);   // an unusable position stages zeros
+  };
+  if (n_ent > 0) fetch(0);
+  for (int e = 0; e < n_ent; ++e) {
+    __syncthreads();
+    sk.put(ks, bk);
+    st.put(ts, bk);
+    __syncthreads();
+    if (e + 1 < n_ent) fetch(e + 1);   // the next block travels while this one is used
+#pragma unroll
+    for (int k0 = 0; k0 < BKM; k0 += 32) {
+      // B: the stored gradients of rows 16 w + col for keys k0 + 4 g4 + (0..3) and
+      // k0 + 16 + 4 g4 + (0..3), the contraction order of cat_tr
+      const int kr = k0 + 4 * g4 + (col >> 2);
+      const int ro = 16 * w + 4 * (col & 3);
+      const bf16x8 db = cat_tr(ts + L::off(kr, ro), ts + L::off(kr + 16, ro));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int ee = 16 * dt + 4 * (col & 3);
+        dq[dt] = mma_k32(cat_tr(ks + L::off(kr, ee), ks + L::off(kr + 16, ee)), db, dq[dt]);
+      }
+    }
+  }
+  if (i < q_len) {
+    const float gs = p.score.kind == FA_S_SOFTCAP ? 4.f * p.scale : p.scale;   // as grad_scale
+    float* out = bp.dq + ((int64_t)bh * q_len + i) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(out + 16 * dt + 4 * g4) = dq[dt] * gs;
+  }
+}
+
 // clears a parameter-gradient output before the dQ pass adds into it (a kernel, not a
 // memset, so the work stays an ordinary launch on the caller's stream)
 __global__ __launch_bounds__(256) void zero_kernel(float* x, int64_t n) {
@@ -601,6 +726,12 @@ hipError_t launch_bwd_score(const BwdParams& bp, hipStream_t s) {
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, pg, n);
   }
   if (qitems > 0) {
+    if constexpr (D == 128) {
+      if (bp.ds) {   // the host enables stored gradients for 128 x 128 blocks only
+        hipLaunchKernelGGL((bwd_dq_ds_kernel<128, 8>), dim3((unsigned)qitems), dim3(512), 0, s, bp);
+        return hipGetLastError();
+      }
+    }
     if (p.tab.bq == 128) {
       hipLaunchKernelGGL((bwd_dq_kernel<D, SCORE, 8>), dim3((unsigned)qitems), dim3(512), 0, s, bp);
     } else {
@@ -626,8 +757,14 @@ hipError_t launch_bwd_d(const BwdParams& bp, hipStream_t s) {
 
 }  // namespace
 
-size_t backward_workspace_bytes(const FwdParams& p) {
+size_t backward_workspace_min_bytes(const FwdParams& p) {
   return ((size_t)p.B * p.Hq * p.q_len * sizeof(float) + 255) & ~(size_t)255;
+}
+
+size_t backward_ds_bytes(const FwdParams& p, bool param_grads) {
+  if (param_grads || p.d != 128 || p.tab.bq != 128 || p.tab.bk != 128 || p.tab.nqb > kDsMaxRows) return 0;
+  const size_t bytes = (size_t)p.B * p.Hq * p.tab.nqb * p.tab.nkb * 128 * 128 * sizeof(uint16_t);
+  return bytes <= kDsMaxBytes ? bytes : 0;
 }
 
 hipError_t launch_backward(const BwdParams& bp, hipStream_t s) {

@@ -297,8 +297,14 @@ fa_status fa_forward_noalloc(const fa_fwd_args* args, fa_stream_t stream);
  *   dout       bf16 [B, Hq, q_len, d]: gradient of the loss with respect to O.
  *   dq         fp32 [B, Hq, q_len, d]; dk, dv fp32 [B, Hkv, kv_len, d]: written (not
  *              accumulated); GQA heads' contributions are summed into their KV head.
- *   workspace  device buffer of fa_backward_workspace_size bytes (fp32 row sums
- *              dO . O), 256-byte aligned, contents on entry irrelevant.
+ *   workspace  device buffer, 256-byte aligned, contents on entry irrelevant: at least
+ *              fa_backward_workspace_min_size bytes (fp32 row sums dO . O).  With the
+ *              fa_backward_workspace_size bytes, which can be larger, the dK/dV pass also
+ *              stores every executed block's per-pair gradients (bf16) and the dQ pass
+ *              reads them instead of recomputing the scores: B * Hq * NQB * NKB
+ *              tiles of 32 KiB, offered for d = 128, 128 x 128 blocks, NQB <= 1024, no
+ *              parameter gradient and at most 8 GiB (else both sizes are equal).  The
+ *              gradients are the same bf16 values either way.
  *   dslopes    optional fp32 [Hq] (ALiBi only, else NULL): gradient of the slopes,
  *              sum over allowed pairs of dL/ds' (j - i), s' the modified score.
  *   dtable     optional fp32 [Hq, 2R+1] (relative-position bias only, R <= 1024, else
@@ -323,6 +329,7 @@ typedef struct {
 } fa_bwd_args;
 
 fa_status fa_backward_workspace_size(const fa_bwd_args* args, size_t* bytes);
+fa_status fa_backward_workspace_min_size(const fa_bwd_args* args, size_t* bytes);
 fa_status fa_backward(const fa_bwd_args* args, fa_stream_t stream);
 
 /* ----------------------------------------------------------------------------------

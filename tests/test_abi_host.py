@@ -255,8 +255,12 @@ def test_forward_validation(lib):
         setattr(bm, name, 0x1000)
     ok = Bk(dout=0x1000, dq=0x1000, dk=0x1000, dv=0x1000)
     n = C.c_size_t(0)
-    assert lib.fa_backward_workspace_size(C.byref(ok), C.byref(n)) == L.FA_OK
+    assert lib.fa_backward_workspace_min_size(C.byref(ok), C.byref(n)) == L.FA_OK
     assert n.value == 1 * 4 * 256 * 4                                 # fp32 row sums
+    full = C.c_size_t(0)
+    assert lib.fa_backward_workspace_size(C.byref(ok), C.byref(full)) == L.FA_OK
+    # plus the stored per-pair gradients: B * Hq * NQB * NKB tiles of 128 x 128 bf16
+    assert full.value == n.value + 1 * 4 * 2 * 2 * 128 * 128 * 2
     assert lib.fa_backward(C.byref(ok), None) == L.FA_ERR_WORKSPACE
     ok.workspace, ok.ws_bytes = 0x1010, n.value
     assert lib.fa_backward(C.byref(ok), None) == L.FA_ERR_WORKSPACE    # misaligned

@@ -163,3 +163,40 @@ def test_backward_full_size_causal_softcap():
             err = float(np.abs(g - G).max())
             bound = G_TOL * max(1.0, float(np.abs(G).max()))
             assert err <= bound, f"({b},{h}): {name} max-abs error {err:.3e} > {bound:.3e}"
+
+
+def test_stored_and_recomputed_gradients_agree():
+    """The dQ pass over the per-pair gradients stored by the dK/dV pass (the full
+    workspace, 128 x 128 blocks at d = 128) against the dQ pass that recomputes them
+    (the minimum workspace): dK and dV are the same computation, so they match exactly;
+    dQ sums the same bf16 gradients (up to the rounding of a recomputed score), and both
+    match the oracle within the bar of the other tests."""
+    import block_sparse_programmable_amd as fa
+    n = 640
+    doc = np.repeat(np.arange(6), [100, 200, 90, 150, 100, 60]).astype(np.int32)[None]
+    for (B, Hq, Hkv, ql, kl, mask, score, q_offset) in (
+            (2, 4, 2, n, n, ("causal",), "softcap", 0),
+            (1, 4, 1, 300, 700, ("and", ("doc",), ("swa", 200)), "identity", 400),
+            (1, 2, 2, n, n, ("or", ("swa", 100), ("prefix", 64)), "alibi", 0)):
+        q = randn_bf16((B, Hq, ql, 128), 81).cuda()
+        k = randn_bf16((B, Hkv, kl, 128), 82).cuda()
+        v = randn_bf16((B, Hkv, kl, 128), 83).cuda()
+        do = randn_bf16((B, Hq, ql, 128), 84).cuda()
+        kw = score_kw(score, Hq, 85)
+        fkw = dict(score=score, softcap=kw.get("cap", 0.0),
+                   alibi_slopes=None if "slopes" not in kw else torch.as_tensor(kw["slopes"]).cuda())
+        docT = torch.as_tensor(doc[:, :kl]).cuda() if "doc" in str(mask) else None
+        bm = fa.create_block_mask(mask, 1, 1, ql, kl, 128, 128, q_offset, docT)
+        o, lse = fa.forward(q, k, v, bm, **fkw)
+        a = fa.backward(q, k, v, o, lse, do, bm, store_grads=True, **fkw)
+        r = fa.backward(q, k, v, o, lse, do, bm, store_grads=False, **fkw)
+        torch.cuda.synchronize()
+        ctx = f"{B}x{Hq}/{Hkv} q{ql} kv{kl} {mask} {score} off{q_offset}"
+        assert torch.equal(a[1], r[1]) and torch.equal(a[2], r[2]), ctx
+        scale = max(1.0, float(r[0].abs().max()))
+        assert float((a[0] - r[0]).abs().max()) <= 2.0 ** -7 * scale, ctx
+        DQ, _, _ = OBW.attention_grads(q.cpu(), k.cpu(), v.cpu(), do.cpu(), mask, score, q_offset=q_offset,
+                                       doc_ids=None if docT is None else doc[:, :kl], **kw)
+        for g in (a[0], r[0]):
+            err = float(np.abs(g.cpu().numpy() - DQ).max())
+            assert err <= G_TOL * max(1.0, float(np.abs(DQ).max())), f"{ctx}: dq {err:.3e}"
