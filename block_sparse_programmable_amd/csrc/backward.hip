@@ -223,7 +223,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
   __shared__ __attribute__((aligned(16))) float lse_s[BQM];
   __shared__ __attribute__((aligned(16))) float del_s[BQM];
   __shared__ __attribute__((aligned(16))) int32_t doc_s[BQM];   // document IDs of the rows
-  __shared__ int32_t slot_s[kDsMaxRows];   // stored-gradient tiles of the column's blocks
+  // stored gradients (128 x 128 blocks at d = 128 only): the tiles of the column's
+  // blocks, and each wave's 16 key rows of the current tile (padded rows: the lanes'
+  // 8-byte writes of one key column fall on distinct bank pairs), written out whole
+  // after the block
+  constexpr bool kDs = NW == 8 && D == 128;
+  constexpr int kDsRow = 272;
+  __shared__ int32_t slot_s[kDs ? kDsMaxRows : 1];
+  __shared__ __attribute__((aligned(16))) uint8_t dss[kDs ? NW * 16 * kDsRow : 16];
 
   // work item: (b, h_kv) fastest, then the KV block c ascending: every head's first
   // columns go out before any head's later ones (for causal-like rules the first columns
@@ -279,7 +286,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     const int n_ent = nf + np;
     // query block of list entry e and its row statistics (one per thread, bq <= 256)
     auto block_of = [&](int e) -> int { return uniform(e >= nf ? pl[e - nf] : fl[e]); };
-    if (bp.ds) {
+    if (kDs && bp.ds) {
       // Each block (r, c) of the column's list gets the tile of the stored gradients at
       // its kv-side position within the table entry (the row's full list, then its
       // partial list): found by one wave per entry in row r's list of the same kind.
@@ -325,11 +332,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
       const int r0 = block_of(e) * bq;
       __syncthreads();   // the previous block's rows are consumed (and the tiles are found)
       // this block's stored-gradient tile: rows are the block's keys, bq values each
-      uint16_t* dst_tile = nullptr;
-      if (bp.ds) {
+      uint16_t* dst_tile = nullptr;   // the wave's 16 key rows of the tile
+      if (kDs && bp.ds) {
         const int slot = uniform(slot_s[e]);
-        if (slot >= 0) dst_tile = bp.ds + ((bh * p.tab.nqb * p.tab.nkb + slot) * p.tab.bk + w * 16 + col) * bq;
+        if (slot >= 0) dst_tile = bp.ds + ((bh * p.tab.nqb * p.tab.nkb + slot) * p.tab.bk + w * 16) * bq;
       }
+      uint8_t* mys = dss + w * 16 * kDsRow;
       sq.put(qs, bq);
       sg.put(gs, bq);
       if ((int)threadIdx.x < bq) {
@@ -388,11 +396,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
           for (int x = 0; x < 8; ++x) mask_pair((okw >> (4 * (q0 >> 4) + x)) & 1u, pv[x], ds[x]);
         }
         const bf16x8 pb = pack8(pv), db = pack8(ds);
-        if (dst_tile) {
+        if (kDs && dst_tile) {
           // the lane's key row: rows q0 + 4 g4 .. +3 and q0 + 16 + 4 g4 .. +3
           const u32x4 dw = __builtin_bit_cast(u32x4, db);
-          *reinterpret_cast<u32x2*>(dst_tile + q0 + 4 * g4) = u32x2{dw[0], dw[1]};
-          *reinterpret_cast<u32x2*>(dst_tile + q0 + 16 + 4 * g4) = u32x2{dw[2], dw[3]};
+          *reinterpret_cast<u32x2*>(mys + col * kDsRow + 2 * (q0 + 4 * g4)) = u32x2{dw[0], dw[1]};
+          *reinterpret_cast<u32x2*>(mys + col * kDsRow + 2 * (q0 + 16 + 4 * g4)) = u32x2{dw[2], dw[3]};
         }
         // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (16x16x32): the lane holds P
         // and dS in the contraction order of cat_tr (rows q0 + 4 g4 + e, then q0 + 16 +
@@ -403,6 +411,17 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
           const int e = 16 * dt + 4 * (col & 3);
           dv[dt] = mma_k32(cat_tr(gs + L::off(tr0, e), gs + L::off(tr0 + 16, e)), pb, dv[dt]);
           dk[dt] = mma_k32(cat_tr(qs + L::off(tr0, e), qs + L::off(tr0 + 16, e)), db, dk[dt]);
+        }
+      }
+      if (kDs && dst_tile) {
+        // the wave's 16 key rows (bq = 128 values, 256 bytes each), four rows per store
+        // instruction: every instruction writes 1 KB of consecutive bytes, with the
+        // non-temporal policy (the tiles are read once, by the dQ pass)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int kr = 4 * u + (lane >> 4);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(mys + kr * kDsRow + 16 * (lane & 15));
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst_tile + kr * 128 + 8 * (lane & 15)));
         }
       }
     }
