@@ -223,13 +223,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
   __shared__ __attribute__((aligned(16))) float lse_s[BQM];
   __shared__ __attribute__((aligned(16))) float del_s[BQM];
   __shared__ __attribute__((aligned(16))) int32_t doc_s[BQM];   // document IDs of the rows
-  // stored gradients (128 x 128 blocks at d = 128 only): the tiles of the column's
-  // blocks, and each wave's 16 key rows of the current tile (padded rows: the lanes'
-  // 8-byte writes of one key column fall on distinct bank pairs), written out whole
-  // after the block
+  // stored gradients (128 x 128 blocks at d = 128 only): each wave's 16 key rows of
+  // the current block's tile (padded rows: the lanes' 8-byte writes of one key column
+  // fall on distinct bank pairs), written out whole later
   constexpr bool kDs = NW == 8 && D == 128;
   constexpr int kDsRow = 272;
-  __shared__ int32_t slot_s[kDs ? kDsMaxRows : 1];
   __shared__ __attribute__((aligned(16))) uint8_t dss[kDs ? NW * 16 * kDsRow : 16];
 
   // work item: (b, h_kv) fastest, then the KV block c ascending: every head's first
@@ -285,32 +283,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     const uint16_t* gsrc = bp.dout + bh * q_len * D;
     const int n_ent = nf + np;
     // query block of list entry e and its row statistics (one per thread, bq <= 256)
-    auto block_of = [&](int e) -> int { return uniform(e >= nf ? pl[e - nf] : fl[e]); };
-    if (kDs && bp.ds) {
-      // Each block (r, c) of the column's list gets the tile of the stored gradients at
-      // its kv-side position within the table entry (the row's full list, then its
-      // partial list): found by one wave per entry in row r's list of the same kind.
-      // A position outside the grid (tables that are not exact transposes) is -1: the
-      // block's tile is not written.
-      const int nqb = p.tab.nqb;
-      const int g0 = (tb * p.tab.tH + th) * nqb;
-      const int nfg = uniform(p.tab.fptr[g0 + nqb]) - uniform(p.tab.fptr[g0]);
-      for (int e = uniform(w); e < n_ent; e += NW) {
-        const bool full = e < nf;
-        const int row = g0 + block_of(e);
-        const int* lst = full ? p.tab.fidx + uniform(p.tab.fptr[row]) : p.tab.idx + uniform(p.tab.ptr[row]);
-        const int n = uniform(full ? p.tab.fnum[row] : p.tab.num[row]);
-        int pos = -1;
-        for (int x0 = 0; x0 < n && pos < 0; x0 += 64) {
-          const uint64_t m = __ballot(x0 + lane < n && lst[x0 + lane] == c);
-          if (m != 0) pos = x0 + (int)__builtin_ctzll(m);
-        }
-        const int base = full ? uniform(p.tab.fptr[row]) - uniform(p.tab.fptr[g0])
-                              : nfg + uniform(p.tab.ptr[row]) - uniform(p.tab.ptr[g0]);
-        const int local = pos < 0 ? -1 : base + pos;
-        if (lane == 0) slot_s[e] = (local >= 0 && local < nqb * p.tab.nkb) ? local : -1;
-      }
-    }
+    auto block_of = [&](int e) -> int { return load_uniform(e >= nf ? pl + (e - nf) : fl + e); };
     auto stats = [&](int r0, float& l2, float& dl, int& dc) {
       const int i = r0 + (int)threadIdx.x;
       const bool ok = (int)threadIdx.x < bq && i < q_len;
@@ -321,6 +294,24 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     RowStage<D, NT> sq, sg;
     float nl2 = 0.f, ndl = 0.f;
     int ndc = 0;
+    // The wave's 16 key rows of a block's stored gradients wait in its LDS rows until
+    // the next block has issued its row copies: stores issued at the end of a block
+    // would make the wait for those copies (a wait on the count of all the wave's
+    // vector memory operations) a wait for the stores' completion too. Four rows per
+    // store instruction (1 KB of consecutive bytes), with the non-temporal policy: the
+    // tiles are read once, by the dQ pass.
+    uint16_t* pend = nullptr;
+    uint8_t* mys = dss + w * 16 * kDsRow;
+    auto flush = [&]() {
+      if (kDs && pend) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int kr = 4 * u + (lane >> 4);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(mys + kr * kDsRow + 16 * (lane & 15));
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(pend + kr * 128 + 8 * (lane & 15)));
+        }
+      }
+    };
     if (n_ent > 0) {
       const int r0n = block_of(0) * bq;
       sq.fetch(qsrc, r0n, bq, q_len);
@@ -329,15 +320,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     }
     for (int e = 0; e < n_ent; ++e) {
       const bool part = e >= nf;
-      const int r0 = block_of(e) * bq;
-      __syncthreads();   // the previous block's rows are consumed (and the tiles are found)
-      // this block's stored-gradient tile: rows are the block's keys, bq values each
+      const int rblk = block_of(e), r0 = rblk * bq;
+      __syncthreads();   // the previous block's rows are consumed
+      // this block's stored-gradient tile, (r, c) of the head's NQB x NKB grid of tiles:
+      // rows are the block's keys, bq values each
       uint16_t* dst_tile = nullptr;   // the wave's 16 key rows of the tile
-      if (kDs && bp.ds) {
-        const int slot = uniform(slot_s[e]);
-        if (slot >= 0) dst_tile = bp.ds + ((bh * p.tab.nqb * p.tab.nkb + slot) * p.tab.bk + w * 16) * bq;
+      if (kDs && bp.ds && rblk < p.tab.nqb) {
+        const int64_t slot = (bh * p.tab.nqb + rblk) * p.tab.nkb + c;
+        dst_tile = bp.ds + (slot * p.tab.bk + w * 16) * bq;
       }
-      uint8_t* mys = dss + w * 16 * kDsRow;
       sq.put(qs, bq);
       sg.put(gs, bq);
       if ((int)threadIdx.x < bq) {
@@ -352,6 +343,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
         sg.fetch(gsrc, r0n, bq, q_len);
         stats(r0n, nl2, ndl, ndc);
       }
+      flush();   // the previous block's rows (read before this block writes its own)
+      pend = dst_tile;
       // which of the lane's 32 rows (r0 + 16 m + 4 g4 + rr) may see key j: the row
       // bounds, and on partial blocks the mask program over the whole group
       const int rb = r0 + 4 * g4 + (int)p.q_offset;
@@ -413,18 +406,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
           dk[dt] = mma_k32(cat_tr(qs + L::off(tr0, e), qs + L::off(tr0 + 16, e)), db, dk[dt]);
         }
       }
-      if (kDs && dst_tile) {
-        // the wave's 16 key rows (bq = 128 values, 256 bytes each), four rows per store
-        // instruction: every instruction writes 1 KB of consecutive bytes, with the
-        // non-temporal policy (the tiles are read once, by the dQ pass)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int kr = 4 * u + (lane >> 4);
-          const u32x4 v = *reinterpret_cast<const u32x4*>(mys + kr * kDsRow + 16 * (lane & 15));
-          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst_tile + kr * 128 + 8 * (lane & 15)));
-        }
-      }
     }
+    flush();
   }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dk[dt] *= grad_scale<SCORE>(p.scale);
@@ -513,7 +496,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
   const int32_t* pl = p.tab.idx + uniform(p.tab.ptr[row]);
   const int64_t kvh = (int64_t)(b * p.Hkv + hkv) * kv_len;
   const int n_ent = nf + np;
-  auto block_of = [&](int e) -> int { return uniform(e >= nf ? pl[e - nf] : fl[e]); };
+  auto block_of = [&](int e) -> int { return load_uniform(e >= nf ? pl + (e - nf) : fl + e); };
   RowStage<D, NT> sk, sv;
   // document ID of key j0 + threadIdx.x (threads below bk; keys past kv_len read the last)
   auto key_doc = [&](int j0) -> int {
@@ -672,24 +655,16 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_ds_kernel(BwdParams bp) {
   const int np = uniform(p.tab.num[row]);
   const int32_t* fl = p.tab.fidx + uniform(p.tab.fptr[row]);
   const int32_t* pl = p.tab.idx + uniform(p.tab.ptr[row]);
-  // tile positions: the row's full entries, then its partial ones, within the table entry
-  const int fbase = uniform(p.tab.fptr[row]) - uniform(p.tab.fptr[g0]);
-  const int pbase = uniform(p.tab.fptr[g0 + nqb]) - uniform(p.tab.fptr[g0]) + uniform(p.tab.ptr[row]) -
-                    uniform(p.tab.ptr[g0]);
-  const int ntiles = nqb * p.tab.nkb;
   const int64_t kvh = (int64_t)(b * p.Hkv + hkv) * kv_len;
-  const uint16_t* tiles = bp.ds + (int64_t)bh * ntiles * (BKM * BKM);
+  // the row's tiles: (r, c) of the head's NQB x NKB grid
+  const uint16_t* tiles = bp.ds + ((int64_t)bh * nqb + r) * p.tab.nkb * (BKM * BKM);
   const int n_ent = nf + np;
-  auto block_of = [&](int e) -> int { return uniform(e >= nf ? pl[e - nf] : fl[e]); };
-  auto tile_of = [&](int e) -> const uint16_t* {
-    const int slot = e < nf ? fbase + e : pbase + (e - nf);
-    return (slot >= 0 && slot < ntiles) ? tiles + (int64_t)slot * (BKM * BKM) : nullptr;
-  };
+  auto block_of = [&](int e) -> int { return load_uniform(e >= nf ? pl + (e - nf) : fl + e); };
   RowStage<D, NT> sk, st;
   auto fetch = [&](int e) {
-    sk.fetch(p.k + kvh * D, block_of(e) * bk, bk, kv_len);
-    const uint16_t* t = tile_of(e);
-    st.fetch(t ? t : tiles, 0, t ? bk : 0, bk);   // an unusable position stages zeros
+    const int c = block_of(e);
+    sk.fetch(p.k + kvh * D, c * bk, bk, kv_len);
+    st.fetch(tiles + (int64_t)c * (BKM * BKM), 0, bk, bk);
   };
   if (n_ent > 0) fetch(0);
   for (int e = 0; e < n_ent; ++e) {
@@ -781,7 +756,7 @@ size_t backward_workspace_min_bytes(const FwdParams& p) {
 }
 
 size_t backward_ds_bytes(const FwdParams& p, bool param_grads) {
-  if (param_grads || p.d != 128 || p.tab.bq != 128 || p.tab.bk != 128 || p.tab.nqb > kDsMaxRows) return 0;
+  if (param_grads || p.d != 128 || p.tab.bq != 128 || p.tab.bk != 128) return 0;
   const size_t bytes = (size_t)p.B * p.Hq * p.tab.nqb * p.tab.nkb * 128 * 128 * sizeof(uint16_t);
   return bytes <= kDsMaxBytes ? bytes : 0;
 }

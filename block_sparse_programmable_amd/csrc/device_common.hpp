@@ -40,6 +40,13 @@ __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cas
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Wave-uniform read of memory no kernel in flight writes (block tables): through the
+// constant address space it becomes a scalar load, whose wait does not include the
+// wave's pending vector loads and stores.
+__device__ __forceinline__ int load_uniform(const int32_t* p) {
+  return uniform(*(const __attribute__((address_space(4))) int32_t*)p);
+}
+
 // ---------------------------------------------------------------------------------
 // Element predicate of the mask menu: postfix program over a one-bit-per-slot stack.
 // i is the global query position, j the key position, di/dj their document IDs

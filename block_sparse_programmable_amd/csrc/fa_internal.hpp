@@ -151,14 +151,13 @@ struct BwdParams {
   float* dv;              // fp32 [B, Hkv, kv_len, d]
   float* delta;           // fp32 [B, Hq, q_len] workspace: rowsum(dO * O)
   uint16_t* ds;           // bf16 per-pair gradients of every executed block, stored by the
-                          // dK/dV pass for the dQ pass: tile [b][h_q][kv-side position in
-                          // the table entry] of block_kv key rows x block_q values; or
-                          // nullptr (the dQ pass recomputes them)
+                          // dK/dV pass for the dQ pass: tile [b][h_q][query block][KV
+                          // block] of block_kv key rows x block_q values; or nullptr (the
+                          // dQ pass recomputes them)
   float* dslopes;         // fp32 [Hq]: gradient of the ALiBi slopes, or nullptr
   float* dtable;          // fp32 [Hq, 2R+1]: gradient of the position table, or nullptr
 };
 constexpr int kRelGradMaxRadius = 1024;   // position-table gradients: bins kept in LDS
-constexpr int kDsMaxRows = 1024;          // stored gradients: query blocks per table entry
 constexpr size_t kDsMaxBytes = (size_t)8 << 30;   // stored gradients: largest workspace part
 size_t backward_workspace_min_bytes(const FwdParams& p);
 // bytes of the stored-gradient part of the backward workspace (0: not used for this shape)

@@ -302,8 +302,8 @@ fa_status fa_forward_noalloc(const fa_fwd_args* args, fa_stream_t stream);
  *              fa_backward_workspace_size bytes, which can be larger, the dK/dV pass also
  *              stores every executed block's per-pair gradients (bf16) and the dQ pass
  *              reads them instead of recomputing the scores: B * Hq * NQB * NKB
- *              tiles of 32 KiB, offered for d = 128, 128 x 128 blocks, NQB <= 1024, no
- *              parameter gradient and at most 8 GiB (else both sizes are equal).  The
+ *              tiles of 32 KiB, offered for d = 128, 128 x 128 blocks, no parameter
+ *              gradient and at most 8 GiB (else both sizes are equal).  The
  *              gradients are the same bf16 values either way.
  *   dslopes    optional fp32 [Hq] (ALiBi only, else NULL): gradient of the slopes,
  *              sum over allowed pairs of dL/ds' (j - i), s' the modified score.
