@@ -223,12 +223,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
   __shared__ __attribute__((aligned(16))) float lse_s[BQM];
   __shared__ __attribute__((aligned(16))) float del_s[BQM];
   __shared__ __attribute__((aligned(16))) int32_t doc_s[BQM];   // document IDs of the rows
-  // stored gradients (128 x 128 blocks at d = 128 only): each wave's 16 key rows of
-  // the current block's tile (padded rows: the lanes' 8-byte writes of one key column
-  // fall on distinct bank pairs), written out whole later
+  // stored gradients: 128 x 128 blocks at d = 128 only
   constexpr bool kDs = NW == 8 && D == 128;
-  constexpr int kDsRow = 272;
-  __shared__ __attribute__((aligned(16))) uint8_t dss[kDs ? NW * 16 * kDsRow : 16];
 
   // work item: (b, h_kv) fastest, then the KV block c ascending: every head's first
   // columns go out before any head's later ones (for causal-like rules the first columns
@@ -294,24 +290,6 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     RowStage<D, NT> sq, sg;
     float nl2 = 0.f, ndl = 0.f;
     int ndc = 0;
-    // The wave's 16 key rows of a block's stored gradients wait in its LDS rows until
-    // the next block has issued its row copies: stores issued at the end of a block
-    // would make the wait for those copies (a wait on the count of all the wave's
-    // vector memory operations) a wait for the stores' completion too. Four rows per
-    // store instruction (1 KB of consecutive bytes), with the non-temporal policy: the
-    // tiles are read once, by the dQ pass.
-    uint16_t* pend = nullptr;
-    uint8_t* mys = dss + w * 16 * kDsRow;
-    auto flush = [&]() {
-      if (kDs && pend) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int kr = 4 * u + (lane >> 4);
-          const u32x4 v = *reinterpret_cast<const u32x4*>(mys + kr * kDsRow + 16 * (lane & 15));
-          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(pend + kr * 128 + 8 * (lane & 15)));
-        }
-      }
-    };
     if (n_ent > 0) {
       const int r0n = block_of(0) * bq;
       sq.fetch(qsrc, r0n, bq, q_len);
@@ -322,12 +300,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
       const bool part = e >= nf;
       const int rblk = block_of(e), r0 = rblk * bq;
       __syncthreads();   // the previous block's rows are consumed
-      // this block's stored-gradient tile, (r, c) of the head's NQB x NKB grid of tiles:
-      // rows are the block's keys, bq values each
-      uint16_t* dst_tile = nullptr;   // the wave's 16 key rows of the tile
+      // this block's stored-gradient tile, (r, c) of the head's NQB x NKB grid of tiles,
+      // in the order of the lanes that form it (BwdParams::ds)
+      uint16_t* dst_tile = nullptr;
       if (kDs && bp.ds && rblk < p.tab.nqb) {
         const int64_t slot = (bh * p.tab.nqb + rblk) * p.tab.nkb + c;
-        dst_tile = bp.ds + (slot * p.tab.bk + w * 16) * bq;
+        dst_tile = bp.ds + slot * (128 * 128) + w * (4 * 64 * 8) + lane * 8;
       }
       sq.put(qs, bq);
       sg.put(gs, bq);
@@ -343,8 +321,6 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
         sg.fetch(gsrc, r0n, bq, q_len);
         stats(r0n, nl2, ndl, ndc);
       }
-      flush();   // the previous block's rows (read before this block writes its own)
-      pend = dst_tile;
       // which of the lane's 32 rows (r0 + 16 m + 4 g4 + rr) may see key j: the row
       // bounds, and on partial blocks the mask program over the whole group
       const int rb = r0 + 4 * g4 + (int)p.q_offset;
@@ -390,10 +366,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
         }
         const bf16x8 pb = pack8(pv), db = pack8(ds);
         if (kDs && dst_tile) {
-          // the lane's key row: rows q0 + 4 g4 .. +3 and q0 + 16 + 4 g4 .. +3
-          const u32x4 dw = __builtin_bit_cast(u32x4, db);
-          *reinterpret_cast<u32x2*>(mys + col * kDsRow + 2 * (q0 + 4 * g4)) = u32x2{dw[0], dw[1]};
-          *reinterpret_cast<u32x2*>(mys + col * kDsRow + 2 * (q0 + 16 + 4 * g4)) = u32x2{dw[2], dw[3]};
+          // 16 bytes per lane, 1 KB per wave, with the non-temporal policy (the tiles are
+          // read once, by the dQ pass)
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, db),
+                                      reinterpret_cast<u32x4*>(dst_tile + (q0 >> 5) * (64 * 8)));
         }
         // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows (16x16x32): the lane holds P
         // and dS in the contraction order of cat_tr (rows q0 + 4 g4 + e, then q0 + 16 +
@@ -407,7 +383,6 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
         }
       }
     }
-    flush();
   }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dk[dt] *= grad_scale<SCORE>(p.scale);
@@ -670,7 +645,16 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_ds_kernel(BwdParams bp) {
   for (int e = 0; e < n_ent; ++e) {
     __syncthreads();
     sk.put(ks, bk);
-    st.put(ts, bk);
+    // the tile's 16-byte chunk x (BwdParams::ds) holds key 16 (x >> 8) + (x & 15) for
+    // rows 32 ((x >> 6) & 3) + 4 ((x >> 4) & 3) + (0..3), then for those rows + 16
+#pragma unroll
+    for (int u = 0; u < RowStage<D, NT>::PER; ++u) {
+      const int x = threadIdx.x + u * NT;
+      const int key = 16 * (x >> 8) + (x & 15);
+      const int rw = 32 * ((x >> 6) & 3) + 4 * ((x >> 4) & 3);
+      *reinterpret_cast<u32x2*>(ts + L::off(key, rw)) = u32x2{st.r[u][0], st.r[u][1]};
+      *reinterpret_cast<u32x2*>(ts + L::off(key, rw + 16)) = u32x2{st.r[u][2], st.r[u][3]};
+    }
     __syncthreads();
     if (e + 1 < n_ent) fetch(e + 1);   // the next block travels while this one is used
 #pragma unroll

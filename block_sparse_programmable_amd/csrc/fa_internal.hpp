@@ -151,9 +151,11 @@ struct BwdParams {
   float* dv;              // fp32 [B, Hkv, kv_len, d]
   float* delta;           // fp32 [B, Hq, q_len] workspace: rowsum(dO * O)
   uint16_t* ds;           // bf16 per-pair gradients of every executed block, stored by the
-                          // dK/dV pass for the dQ pass: tile [b][h_q][query block][KV
-                          // block] of block_kv key rows x block_q values; or nullptr (the
-                          // dQ pass recomputes them)
+                          // dK/dV pass for the dQ pass, or nullptr (the dQ pass recomputes
+                          // them).  Tile [b][h_q][query block][KV block] of 128 x 128
+                          // values in the order of the lanes that form them: 16-byte
+                          // chunk ((w * 4 + s) * 64 + l) holds key 16 w + (l & 15) for
+                          // query rows 32 s + 4 (l >> 4) + (0..3), then those rows + 16
   float* dslopes;         // fp32 [Hq]: gradient of the ALiBi slopes, or nullptr
   float* dtable;          // fp32 [Hq, 2R+1]: gradient of the position table, or nullptr
 };
