@@ -218,13 +218,16 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
   constexpr int KS = D / 32;   // k-steps of the 16x16x32 products over the head dim
   constexpr int DT = D / 16;   // 16-row tiles of dK^T and dV^T
   constexpr int BQM = 128;     // largest query block
-  __shared__ __attribute__((aligned(16))) uint8_t qs[BQM * RS];   // Q rows of one (head, block)
-  __shared__ __attribute__((aligned(16))) uint8_t gs[BQM * RS];   // dO rows
-  __shared__ __attribute__((aligned(16))) float lse_s[BQM];
-  __shared__ __attribute__((aligned(16))) float del_s[BQM];
-  __shared__ __attribute__((aligned(16))) int32_t doc_s[BQM];   // document IDs of the rows
-  // stored gradients: 128 x 128 blocks at d = 128 only
+  // stored gradients, and rows copied HBM -> LDS into two buffers (128 KB): 128-key
+  // blocks at d = 128 only
   constexpr bool kDs = NW == 8 && D == 128;
+  constexpr bool kDma = kDs;
+  constexpr int NB = kDma ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t qs2[NB][BQM * RS];   // Q rows of one (head, block)
+  __shared__ __attribute__((aligned(16))) uint8_t gs2[NB][BQM * RS];   // dO rows
+  __shared__ __attribute__((aligned(16))) float lse2[NB][BQM];         // row terms
+  __shared__ __attribute__((aligned(16))) float del2[NB][BQM];         // -delta
+  __shared__ __attribute__((aligned(16))) int32_t doc2[NB][BQM];       // document IDs of the rows
 
   // work item: (b, h_kv) fastest, then the KV block c ascending: every head's first
   // columns go out before any head's later ones (for causal-like rules the first columns
@@ -280,47 +283,134 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     const int n_ent = nf + np;
     // query block of list entry e and its row statistics (one per thread, bq <= 256)
     auto block_of = [&](int e) -> int { return load_uniform(e >= nf ? pl + (e - nf) : fl + e); };
-    auto stats = [&](int r0, float& l2, float& dl, int& dc) {
+    // (with the LDS-DMA copies, loaded raw and converted when written to LDS, so that
+    // no wait for them, which would also wait for the copies, falls before the next
+    // block)
+    float nl2 = 0.f, ndl = 0.f;
+    int ndc = 0, nr0 = 0;
+    auto stats = [&](int r0) {
       const int i = r0 + (int)threadIdx.x;
       const bool ok = (int)threadIdx.x < bq && i < q_len;
-      l2 = ok ? grad_row_term<SCORE>(p.lse[bh * q_len + i], sc) : 0.f;
-      dl = ok ? -bp.delta[bh * q_len + i] : 0.f;
-      dc = (ok && p.prog.has_doc) ? docr[i + p.q_offset] : 0;
+      if constexpr (kDma) {
+        nr0 = r0;
+        nl2 = ok ? p.lse[bh * q_len + i] : 0.f;
+        ndl = ok ? bp.delta[bh * q_len + i] : 0.f;
+      } else {
+        nl2 = ok ? grad_row_term<SCORE>(p.lse[bh * q_len + i], sc) : 0.f;
+        ndl = ok ? -bp.delta[bh * q_len + i] : 0.f;
+      }
+      ndc = (ok && p.prog.has_doc) ? docr[i + p.q_offset] : 0;
     };
-    RowStage<D, NT> sq, sg;
-    float nl2 = 0.f, ndl = 0.f;
-    int ndc = 0;
-    if (n_ent > 0) {
-      const int r0n = block_of(0) * bq;
-      sq.fetch(qsrc, r0n, bq, q_len);
-      sg.fetch(gsrc, r0n, bq, q_len);
-      stats(r0n, nl2, ndl, ndc);
-    }
-    for (int e = 0; e < n_ent; ++e) {
+    // The steps of 32 query rows of one block (128-key blocks at d = 128), software
+    // pipelined over nine scheduler-fenced stages: every stage issues the products whose
+    // LDS operands the previous stage read, then reads the next stage's operands, so the
+    // LDS latency runs under the products. Stages 1-4: S and dP over k-steps t = 0..3
+    // (four independent accumulators per stage); 5: weights and gradients (VALU); 6-9:
+    // dV and dK over head-dim tiles 2k, 2k + 1 (four accumulators per stage). Stages 8
+    // and 9 read k-steps 0 and 1 of the next step.
+    auto pipelined = [&](int r0, const uint8_t* qs, const uint8_t* gs, const float* lse_s,
+                         const float* del_s, uint32_t okw, bool sel, uint16_t* dst_tile) {
+      // operands of k-step t for rows qn + 16 h + col: Q h0, dO h0, Q h1, dO h1
+      auto rd1 = [&](int qn, int t, bf16x8 (&f)[4]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int off = L::off(qn + 16 * h + col, 32 * t + 8 * g4);
+          f[2 * h] = *reinterpret_cast<const bf16x8*>(qs + off);
+          f[2 * h + 1] = *reinterpret_cast<const bf16x8*>(gs + off);
+        }
+      };
+      // transposed dO and Q operands of head-dim tiles 2k and 2k + 1
+      auto rd3 = [&](int q0, int k, bf16x8 (&f)[4]) {
+        const int tr0 = q0 + 4 * g4 + (col >> 2);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int e = 16 * (2 * k + x) + 4 * (col & 3);
+          f[2 * x] = cat_tr(gs + L::off(tr0, e), gs + L::off(tr0 + 16, e));
+          f[2 * x + 1] = cat_tr(qs + L::off(tr0, e), qs + L::off(tr0 + 16, e));
+        }
+      };
+      bf16x8 n0[4], n1[4];
+      rd1(0, 0, n0);
+      rd1(0, 1, n1);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int q0 = 0; q0 < bq; q0 += 32) {
+        f32x4 s[2], dp[2], l4[2];
+        bf16x8 f2[4], f3[4], p0[4], p1[4], p2[4], p3[4];
+        auto mm1 = [&](const bf16x8 (&f)[4], int t) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            s[h] = mma_k32(f[2 * h], kf[t], s[h]);
+            dp[h] = mma_k32(f[2 * h + 1], vf[t], dp[h]);
+          }
+        };
+        float pv[8], ds[8];
+        bf16x8 pb, db;
+        auto mm3 = [&](const bf16x8 (&f)[4], int k) {
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            dv[2 * k + x] = mma_k32(f[2 * x], pb, dv[2 * k + x]);
+            dk[2 * k + x] = mma_k32(f[2 * x + 1], db, dk[2 * k + x]);
+          }
+        };
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[h] = *reinterpret_cast<const f32x4*>(del_s + q0 + 16 * h + 4 * g4);
+          l4[h] = *reinterpret_cast<const f32x4*>(lse_s + q0 + 16 * h + 4 * g4);
+        }
+        mm1(n0, 0);
+        rd1(q0, 2, f2);
+        __builtin_amdgcn_sched_barrier(0);
+        mm1(n1, 1);
+        rd1(q0, 3, f3);
+        __builtin_amdgcn_sched_barrier(0);
+        mm1(f2, 2);
+        rd3(q0, 0, p0);
+        __builtin_amdgcn_sched_barrier(0);
+        mm1(f3, 3);
+        rd3(q0, 1, p1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int ig = r0 + q0 + 16 * h + 4 * g4 + rr + (int)p.q_offset;
+            grad_elem<SCORE>(s[h][rr], dp[h][rr], l4[h][rr], sc, ig, j, pv[4 * h + rr], ds[4 * h + rr]);
+          }
+        }
+        if (sel) {
+#pragma unroll
+          for (int x = 0; x < 8; ++x) mask_pair((okw >> (4 * (q0 >> 4) + x)) & 1u, pv[x], ds[x]);
+        }
+        pb = pack8(pv);
+        db = pack8(ds);
+        if (dst_tile) {
+          // 16 bytes per lane, 1 KB per wave, with the non-temporal policy (the tiles are
+          // read once, by the dQ pass)
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, db),
+                                      reinterpret_cast<u32x4*>(dst_tile + (q0 >> 5) * (64 * 8)));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mm3(p0, 0);
+        rd3(q0, 2, p2);
+        __builtin_amdgcn_sched_barrier(0);
+        mm3(p1, 1);
+        rd3(q0, 3, p3);
+        __builtin_amdgcn_sched_barrier(0);
+        const int qn = min(q0 + 32, bq - 32);   // the last step reads its own rows again
+        mm3(p2, 2);
+        rd1(qn, 0, n0);
+        __builtin_amdgcn_sched_barrier(0);
+        mm3(p3, 3);
+        rd1(qn, 1, n1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // the block of list entry e, rows r0.., from the staged rows, row terms, -delta and
+    // document IDs
+    auto compute = [&](int e, int r0, const uint8_t* qs, const uint8_t* gs, const float* lse_s,
+                       const float* del_s, const int32_t* doc_s, uint16_t* dst_tile) {
       const bool part = e >= nf;
-      const int rblk = block_of(e), r0 = rblk * bq;
-      __syncthreads();   // the previous block's rows are consumed
-      // this block's stored-gradient tile, (r, c) of the head's NQB x NKB grid of tiles,
-      // in the order of the lanes that form it (BwdParams::ds)
-      uint16_t* dst_tile = nullptr;
-      if (kDs && bp.ds && rblk < p.tab.nqb) {
-        const int64_t slot = (bh * p.tab.nqb + rblk) * p.tab.nkb + c;
-        dst_tile = bp.ds + slot * (128 * 128) + w * (4 * 64 * 8) + lane * 8;
-      }
-      sq.put(qs, bq);
-      sg.put(gs, bq);
-      if ((int)threadIdx.x < bq) {
-        lse_s[threadIdx.x] = nl2;
-        del_s[threadIdx.x] = ndl;
-        doc_s[threadIdx.x] = ndc;
-      }
-      __syncthreads();
-      if (e + 1 < n_ent) {   // next block's rows travel while this one is computed
-        const int r0n = block_of(e + 1) * bq;
-        sq.fetch(qsrc, r0n, bq, q_len);
-        sg.fetch(gsrc, r0n, bq, q_len);
-        stats(r0n, nl2, ndl, ndc);
-      }
       // which of the lane's 32 rows (r0 + 16 m + 4 g4 + rr) may see key j: the row
       // bounds, and on partial blocks the mask program over the whole group
       const int rb = r0 + 4 * g4 + (int)p.q_offset;
@@ -332,6 +422,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
       }
       // pairs outside the mask are zeroed only on blocks where the wave has some
       const bool sel = __ballot(okw != 0xffffffffu) != 0;
+      if constexpr (kDma) {
+        pipelined(r0, qs, gs, lse_s, del_s, okw, sel, dst_tile);
+        return;
+      }
       for (int q0 = 0; q0 < bq; q0 += 32) {
         // S and dP (16 rows x 16 keys each) of rows q0 + 16 h + (0..15), h = 0, 1, on
         // 16x16x32 tiles over the head dim
@@ -381,6 +475,92 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
           dv[dt] = mma_k32(cat_tr(gs + L::off(tr0, e), gs + L::off(tr0 + 16, e)), pb, dv[dt]);
           dk[dt] = mma_k32(cat_tr(qs + L::off(tr0, e), qs + L::off(tr0 + 16, e)), db, dk[dt]);
         }
+      }
+    };
+    // the block's stored-gradient tile, (r, c) of the head's NQB x NKB grid of tiles, in
+    // the order of the lanes that form it (BwdParams::ds); the wave's part
+    auto tile_of = [&](int rblk) -> uint16_t* {
+      if (!(kDs && bp.ds && rblk < p.tab.nqb)) return nullptr;
+      const int64_t slot = (bh * p.tab.nqb + rblk) * p.tab.nkb + c;
+      return bp.ds + slot * (128 * 128) + w * (4 * 64 * 8) + lane * 8;
+    };
+    auto put_stats = [&](int buf) {
+      if ((int)threadIdx.x < bq) {
+        if constexpr (kDma) {
+          const bool ok = nr0 + (int)threadIdx.x < q_len;
+          lse2[buf][threadIdx.x] = ok ? grad_row_term<SCORE>(nl2, sc) : 0.f;
+          del2[buf][threadIdx.x] = -ndl;
+        } else {
+          lse2[buf][threadIdx.x] = nl2;
+          del2[buf][threadIdx.x] = ndl;
+        }
+        doc2[buf][threadIdx.x] = ndc;
+      }
+    };
+    if constexpr (kDma) {
+      // Q and dO rows of entry e's block land in buffer e & 1 by LDS-DMA issued one
+      // block ahead (no staging registers). The row terms, -delta and document IDs are
+      // loaded two blocks ahead into three registers and written to their buffer one
+      // block ahead, so one wait and one barrier per block publish both.
+      auto copy_rows = [&](int r0, int buf) {
+        const uint16_t* qb = qsrc + (int64_t)r0 * D;
+        const uint16_t* gb = gsrc + (int64_t)r0 * D;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int row = 16 * w + 4 * u;   // the instruction's first row (wave-uniform)
+          if (row < bq) {
+            // lane l fills 16-byte slot l & 15 of row row + (l >> 4): the chunk that
+            // Lay's swizzle puts there; rows past the end repeat the last row (masked)
+            const int rl = row + (lane >> 4);
+            const int rg = min(r0 + rl, q_len - 1) - r0;
+            const int lc = (lane & 15) ^ (2 * (rl & 7) + ((rl >> 3) & 1));
+            const uint32_t voff = (uint32_t)(rg * (D * 2) + lc * 16);
+            dma16_s<0>(lds_addr(qs2[buf]) + row * RS, qb, voff);
+            dma16_s<0>(lds_addr(gs2[buf]) + row * RS, gb, voff);
+          }
+        }
+      };
+      __syncthreads();   // the previous head's last block is consumed in every wave
+      if (n_ent > 0) {
+        const int r00 = block_of(0) * bq;
+        copy_rows(r00, 0);
+        stats(r00);
+        put_stats(0);
+        if (n_ent > 1) stats(block_of(1) * bq);
+      }
+      for (int e = 0; e < n_ent; ++e) {
+        const int rblk = block_of(e), cur = e & 1;
+        wait_dma();        // this block's rows (and every earlier load of the wave) landed
+        __syncthreads();   // in every wave; the other buffers' block is consumed
+        if (e + 1 < n_ent) {
+          put_stats(cur ^ 1);   // loaded during the previous block
+          copy_rows(block_of(e + 1) * bq, cur ^ 1);
+          if (e + 2 < n_ent) stats(block_of(e + 2) * bq);
+        }
+        compute(e, rblk * bq, qs2[cur], gs2[cur], lse2[cur], del2[cur], doc2[cur], tile_of(rblk));
+      }
+    } else {
+      RowStage<D, NT> sq, sg;
+      if (n_ent > 0) {
+        const int r0n = block_of(0) * bq;
+        sq.fetch(qsrc, r0n, bq, q_len);
+        sg.fetch(gsrc, r0n, bq, q_len);
+        stats(r0n);
+      }
+      for (int e = 0; e < n_ent; ++e) {
+        const int rblk = block_of(e);
+        __syncthreads();   // the previous block's rows are consumed
+        sq.put(qs2[0], bq);
+        sg.put(gs2[0], bq);
+        put_stats(0);
+        __syncthreads();
+        if (e + 1 < n_ent) {   // next block's rows travel while this one is computed
+          const int r0n = block_of(e + 1) * bq;
+          sq.fetch(qsrc, r0n, bq, q_len);
+          sg.fetch(gsrc, r0n, bq, q_len);
+          stats(r0n);
+        }
+        compute(e, rblk * bq, qs2[0], gs2[0], lse2[0], del2[0], doc2[0], tile_of(rblk));
       }
     }
   }

@@ -60,6 +60,7 @@ def run_case(B, Hq, Hkv, q_len, kv_len, d, mask, bq, bk, score, q_offset=0, doc=
 def test_backward_scores_and_masks(score):
     for (B, Hq, Hkv, ql, kl, d, mask, bq, bk) in (
             (1, 4, 2, 256, 256, 128, ("causal",), 128, 128),
+            (1, 4, 2, 300, 300, 128, ("causal",), 128, 128),   # ragged last block, two heads per KV head
             (2, 2, 1, 300, 300, 64, ("swa", 90), 64, 64),
             (1, 4, 4, 200, 333, 128, ("prefix", 70), 128, 64),
             (1, 2, 2, 190, 190, 128, ("or", ("swa", 40), ("prefix", 20)), 64, 128)):
