@@ -485,7 +485,8 @@ fa_status plan_backward(const fa_bwd_args* a, fa::BwdParams* bp, size_t* ws, siz
   bp->dq = a->dq;
   bp->dk = a->dk;
   bp->dv = a->dv;
-  bp->delta = nullptr;
+  bp->ndelta = nullptr;
+  bp->lrow = nullptr;
   bp->ds = nullptr;
   const int kind = a->fwd->score.kind;
   if (a->dslopes && kind != FA_S_ALIBI)
@@ -535,7 +536,8 @@ fa_status fa_backward(const fa_bwd_args* args, fa_stream_t stream) {
                   args->workspace ? args->ws_bytes : (size_t)0);
     if (((uintptr_t)args->workspace & 255) != 0)
       return fail(FA_ERR_WORKSPACE, "backward workspace must be 256-byte aligned");
-    bp.delta = static_cast<float*>(args->workspace);
+    bp.ndelta = static_cast<float*>(args->workspace);
+    bp.lrow = bp.ndelta + ws / (2 * sizeof(float));   // the second 256-byte-aligned half
     if (ds_ws > 0 && args->ws_bytes >= ws + ds_ws)   // ws is a multiple of 256 bytes
       bp.ds = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(args->workspace) + ws);
   }

@@ -178,7 +178,11 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams bp) {
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     const int64_t row = row0 + (int64_t)k * RPP;
-    if (sub == 0 && row < rows) bp.delta[row] = acc;
+    if (sub == 0 && row < rows) {
+      bp.ndelta[row] = -acc;
+      const float cap2 = p.score.kind == FA_S_SOFTCAP ? p.score.softcap * kLog2e : 0.f;   // as grad_row_term
+      bp.lrow[row] = cap2 - p.lse[row] * kLog2e;
+    }
   }
 }
 
@@ -223,8 +227,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
   constexpr bool kDs = NW == 8 && D == 128;
   constexpr bool kDma = kDs;
   constexpr int NB = kDma ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t qs2[NB][BQM * RS];   // Q rows of one (head, block)
-  __shared__ __attribute__((aligned(16))) uint8_t gs2[NB][BQM * RS];   // dO rows
+  // Q rows of one (head, block), then its dO rows
+  __shared__ __attribute__((aligned(16))) uint8_t qg2[NB][2 * BQM * RS];
   __shared__ __attribute__((aligned(16))) float lse2[NB][BQM];         // row terms
   __shared__ __attribute__((aligned(16))) float del2[NB][BQM];         // -delta
   __shared__ __attribute__((aligned(16))) int32_t doc2[NB][BQM];       // document IDs of the rows
@@ -283,22 +287,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     const int n_ent = nf + np;
     // query block of list entry e and its row statistics (one per thread, bq <= 256)
     auto block_of = [&](int e) -> int { return load_uniform(e >= nf ? pl + (e - nf) : fl + e); };
-    // (with the LDS-DMA copies, loaded raw and converted when written to LDS, so that
-    // no wait for them, which would also wait for the copies, falls before the next
-    // block)
     float nl2 = 0.f, ndl = 0.f;
-    int ndc = 0, nr0 = 0;
+    int ndc = 0;
     auto stats = [&](int r0) {
       const int i = r0 + (int)threadIdx.x;
       const bool ok = (int)threadIdx.x < bq && i < q_len;
-      if constexpr (kDma) {
-        nr0 = r0;
-        nl2 = ok ? p.lse[bh * q_len + i] : 0.f;
-        ndl = ok ? bp.delta[bh * q_len + i] : 0.f;
-      } else {
-        nl2 = ok ? grad_row_term<SCORE>(p.lse[bh * q_len + i], sc) : 0.f;
-        ndl = ok ? -bp.delta[bh * q_len + i] : 0.f;
-      }
+      nl2 = ok ? bp.lrow[bh * q_len + i] : 0.f;
+      ndl = ok ? bp.ndelta[bh * q_len + i] : 0.f;
       ndc = (ok && p.prog.has_doc) ? docr[i + p.q_offset] : 0;
     };
     // The steps of 32 query rows of one block (128-key blocks at d = 128), software
@@ -308,8 +303,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     // (four independent accumulators per stage); 5: weights and gradients (VALU); 6-9:
     // dV and dK over head-dim tiles 2k, 2k + 1 (four accumulators per stage). Stages 8
     // and 9 read k-steps 0 and 1 of the next step.
-    auto pipelined = [&](int r0, const uint8_t* qs, const uint8_t* gs, const float* lse_s,
-                         const float* del_s, uint32_t okw, bool sel, uint16_t* dst_tile) {
+    auto pipelined = [&](int r0, const uint8_t* qs, const float* lse_s, const float* del_s,
+                         uint32_t okw, bool sel, uint16_t* dst_tile) {
+      const uint8_t* gs = qs + BQM * RS;   // one base: dO offsets become immediates
       // operands of k-step t for rows qn + 16 h + col: Q h0, dO h0, Q h1, dO h1
       auto rd1 = [&](int qn, int t, bf16x8 (&f)[4]) {
 #pragma unroll
@@ -423,7 +419,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
       // pairs outside the mask are zeroed only on blocks where the wave has some
       const bool sel = __ballot(okw != 0xffffffffu) != 0;
       if constexpr (kDma) {
-        pipelined(r0, qs, gs, lse_s, del_s, okw, sel, dst_tile);
+        pipelined(r0, qs, lse_s, del_s, okw, sel, dst_tile);
         return;
       }
       for (int q0 = 0; q0 < bq; q0 += 32) {
@@ -486,22 +482,16 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     };
     auto put_stats = [&](int buf) {
       if ((int)threadIdx.x < bq) {
-        if constexpr (kDma) {
-          const bool ok = nr0 + (int)threadIdx.x < q_len;
-          lse2[buf][threadIdx.x] = ok ? grad_row_term<SCORE>(nl2, sc) : 0.f;
-          del2[buf][threadIdx.x] = -ndl;
-        } else {
-          lse2[buf][threadIdx.x] = nl2;
-          del2[buf][threadIdx.x] = ndl;
-        }
+        lse2[buf][threadIdx.x] = nl2;
+        del2[buf][threadIdx.x] = ndl;
         doc2[buf][threadIdx.x] = ndc;
       }
     };
     if constexpr (kDma) {
-      // Q and dO rows of entry e's block land in buffer e & 1 by LDS-DMA issued one
-      // block ahead (no staging registers). The row terms, -delta and document IDs are
-      // loaded two blocks ahead into three registers and written to their buffer one
-      // block ahead, so one wait and one barrier per block publish both.
+      // Entry e's block lands in buffer e & 1 by LDS-DMA issued one block ahead: its Q
+      // and dO rows, row terms, -delta and document IDs (rows past the end repeat the
+      // last row; their pairs are masked). No staging registers and no load the compiler
+      // sees, so one explicit wait and one barrier per block publish it.
       auto copy_rows = [&](int r0, int buf) {
         const uint16_t* qb = qsrc + (int64_t)r0 * D;
         const uint16_t* gb = gsrc + (int64_t)r0 * D;
@@ -515,29 +505,44 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
             const int rg = min(r0 + rl, q_len - 1) - r0;
             const int lc = (lane & 15) ^ (2 * (rl & 7) + ((rl >> 3) & 1));
             const uint32_t voff = (uint32_t)(rg * (D * 2) + lc * 16);
-            dma16_s<0>(lds_addr(qs2[buf]) + row * RS, qb, voff);
-            dma16_s<0>(lds_addr(gs2[buf]) + row * RS, gb, voff);
+            dma16_s<0>(lds_addr(qg2[buf]) + row * RS, qb, voff);
+            dma16_s<0>(lds_addr(qg2[buf]) + (BQM + row) * RS, gb, voff);
+          }
+        }
+        // waves 0, 1, 2: row terms, -delta, document IDs, 64 rows of 4 bytes per copy
+        if (w < (p.prog.has_doc ? 3 : 2)) {
+          const int32_t* src = w == 0 ? reinterpret_cast<const int32_t*>(bp.lrow + bh * q_len)
+                             : w == 1 ? reinterpret_cast<const int32_t*>(bp.ndelta + bh * q_len)
+                                      : docr + p.q_offset;
+          const uint32_t dst = w == 0 ? lds_addr(lse2[buf]) : w == 1 ? lds_addr(del2[buf]) : lds_addr(doc2[buf]);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            if (64 * u < bq) {
+              const int rg = min(r0 + 64 * u + lane, q_len - 1);
+              dma4_s(dst + 256 * u, src, (uint32_t)(rg * 4));
+            }
           }
         }
       };
       __syncthreads();   // the previous head's last block is consumed in every wave
-      if (n_ent > 0) {
-        const int r00 = block_of(0) * bq;
-        copy_rows(r00, 0);
-        stats(r00);
-        put_stats(0);
-        if (n_ent > 1) stats(block_of(1) * bq);
-      }
+      if (n_ent > 0) copy_rows(block_of(0) * bq, 0);
+      bool stored = false;   // the previous block stored gradient tiles
       for (int e = 0; e < n_ent; ++e) {
         const int rblk = block_of(e), cur = e & 1;
-        wait_dma();        // this block's rows (and every earlier load of the wave) landed
-        __syncthreads();   // in every wave; the other buffers' block is consumed
-        if (e + 1 < n_ent) {
-          put_stats(cur ^ 1);   // loaded during the previous block
-          copy_rows(block_of(e + 1) * bq, cur ^ 1);
-          if (e + 2 < n_ent) stats(block_of(e + 2) * bq);
+        // This block's copies have landed. Vector memory operations complete in issue
+        // order for this count, and a block that stores tiles issues its last store
+        // after the next block's copies, so that store, issued a few hundred cycles
+        // ago, may stay in flight.
+        if (stored) {
+          asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+        } else {
+          wait_dma();
         }
-        compute(e, rblk * bq, qs2[cur], gs2[cur], lse2[cur], del2[cur], doc2[cur], tile_of(rblk));
+        __syncthreads();   // in every wave; the other buffers' block is consumed
+        if (e + 1 < n_ent) copy_rows(block_of(e + 1) * bq, cur ^ 1);
+        uint16_t* tile = tile_of(rblk);
+        stored = tile != nullptr;
+        compute(e, rblk * bq, qg2[cur], qg2[cur] + BQM * RS, lse2[cur], del2[cur], doc2[cur], tile);
       }
     } else {
       RowStage<D, NT> sq, sg;
@@ -550,8 +555,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
       for (int e = 0; e < n_ent; ++e) {
         const int rblk = block_of(e);
         __syncthreads();   // the previous block's rows are consumed
-        sq.put(qs2[0], bq);
-        sg.put(gs2[0], bq);
+        sq.put(qg2[0], bq);
+        sg.put(qg2[0] + BQM * RS, bq);
         put_stats(0);
         __syncthreads();
         if (e + 1 < n_ent) {   // next block's rows travel while this one is computed
@@ -560,7 +565,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
           sg.fetch(gsrc, r0n, bq, q_len);
           stats(r0n);
         }
-        compute(e, rblk * bq, qs2[0], gs2[0], lse2[0], del2[0], doc2[0], tile_of(rblk));
+        compute(e, rblk * bq, qg2[0], qg2[0] + BQM * RS, lse2[0], del2[0], doc2[0], tile_of(rblk));
       }
     }
   }
@@ -622,8 +627,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
     }
   }
   const ScoreCtx sc = make_score_ctx(p.score, p.scale, hq);
-  const float lrow = row_ok ? grad_row_term<SCORE>(p.lse[(int64_t)bh * q_len + i], sc) : 0.f;
-  const float ndelta = row_ok ? -bp.delta[(int64_t)bh * q_len + i] : 0.f;
+  const float lrow = row_ok ? bp.lrow[(int64_t)bh * q_len + i] : 0.f;
+  const float ndelta = row_ok ? bp.ndelta[(int64_t)bh * q_len + i] : 0.f;
   const f32x4 dp0 = f32x4{ndelta, ndelta, ndelta, ndelta};   // dP^T starts from -delta
   const int32_t* docr = doc_row(p.doc, b);
   int doc_i = (p.prog.has_doc && row_ok) ? docr[ig] : 0;
@@ -916,7 +921,8 @@ hipError_t launch_bwd_d(const BwdParams& bp, hipStream_t s) {
 }  // namespace
 
 size_t backward_workspace_min_bytes(const FwdParams& p) {
-  return ((size_t)p.B * p.Hq * p.q_len * sizeof(float) + 255) & ~(size_t)255;
+  // -delta, then the row terms, each from a 256-byte boundary
+  return 2 * (((size_t)p.B * p.Hq * p.q_len * sizeof(float) + 255) & ~(size_t)255);
 }
 
 size_t backward_ds_bytes(const FwdParams& p, bool param_grads) {

@@ -149,7 +149,9 @@ struct BwdParams {
   float* dq;              // fp32 [B, Hq, q_len, d]
   float* dk;              // fp32 [B, Hkv, kv_len, d]
   float* dv;              // fp32 [B, Hkv, kv_len, d]
-  float* delta;           // fp32 [B, Hq, q_len] workspace: rowsum(dO * O)
+  float* ndelta;          // fp32 [B, Hq, q_len] workspace: -rowsum(dO * O)
+  float* lrow;            // fp32 [B, Hq, q_len] workspace: the row term of the weights,
+                          // (cap log2 e for soft-cap, else 0) - LSE log2 e
   uint16_t* ds;           // bf16 per-pair gradients of every executed block, stored by the
                           // dK/dV pass for the dQ pass, or nullptr (the dQ pass recomputes
                           // them).  Tile [b][h_q][query block][KV block] of 128 x 128

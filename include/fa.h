@@ -298,7 +298,8 @@ fa_status fa_forward_noalloc(const fa_fwd_args* args, fa_stream_t stream);
  *   dq         fp32 [B, Hq, q_len, d]; dk, dv fp32 [B, Hkv, kv_len, d]: written (not
  *              accumulated); GQA heads' contributions are summed into their KV head.
  *   workspace  device buffer, 256-byte aligned, contents on entry irrelevant: at least
- *              fa_backward_workspace_min_size bytes (fp32 row sums dO . O).  With the
+ *              fa_backward_workspace_min_size bytes (two fp32 values per query row:
+ *              -dO . O and the row's log-sum-exp term of the weights).  With the
  *              fa_backward_workspace_size bytes, which can be larger, the dK/dV pass also
  *              stores every executed block's per-pair gradients (bf16) and the dQ pass
  *              reads them instead of recomputing the scores: B * Hq * NQB * NKB

@@ -256,7 +256,7 @@ def test_forward_validation(lib):
     ok = Bk(dout=0x1000, dq=0x1000, dk=0x1000, dv=0x1000)
     n = C.c_size_t(0)
     assert lib.fa_backward_workspace_min_size(C.byref(ok), C.byref(n)) == L.FA_OK
-    assert n.value == 1 * 4 * 256 * 4                                 # fp32 row sums
+    assert n.value == 2 * 1 * 4 * 256 * 4                             # two fp32 values per row
     full = C.c_size_t(0)
     assert lib.fa_backward_workspace_size(C.byref(ok), C.byref(full)) == L.FA_OK
     # plus the stored per-pair gradients: B * Hq * NQB * NKB tiles of 128 x 128 bf16
