@@ -824,7 +824,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_ds_kernel(BwdParams bp) {
   auto fetch = [&](int e) {
     const int c = block_of(e);
     sk.fetch(p.k + kvh * D, c * bk, bk, kv_len);
-    st.fetch(tiles + (int64_t)c * (BKM * BKM), 0, bk, bk);
+    // the tile: 32 KB read once, with the non-temporal policy (streaming reads run at
+    // about 7 TB/s with it, 5.2 TB/s without)
+    const u32x4* t = reinterpret_cast<const u32x4*>(tiles + (int64_t)c * (BKM * BKM));
+#pragma unroll
+    for (int u = 0; u < RowStage<D, NT>::PER; ++u) st.r[u] = __builtin_nontemporal_load(t + threadIdx.x + u * NT);
   };
   if (n_ent > 0) fetch(0);
   for (int e = 0; e < n_ent; ++e) {
