@@ -372,10 +372,14 @@ def run_workload(args, name, headline=True):
         gv = torch.empty(v.shape, dtype=torch.float32, device=dev)
         bkw = dict(score=w.score, softcap=w.cap, alibi_slopes=sl, relpos=tb, relpos_radius=w.relpos_radius,
                    dq=gq, dk=gk, dv=gv)
-        for _ in range(3):
-            fa.backward(q, k, v, out, lse, dout, bm, **bkw)
-        torch.cuda.synchronize()
-        nb = max(3, K // 2)
+        # warm-up to the steady state: the first few tens of milliseconds of back-to-back
+        # backward calls run up to 15% slower on MI355X (clocks ramping under the load)
+        t_end = time.perf_counter() + 0.2
+        while time.perf_counter() < t_end:
+            for _ in range(10):
+                fa.backward(q, k, v, out, lse, dout, bm, **bkw)
+            torch.cuda.synchronize()
+        nb = max(10, K)
         e = [[torch.cuda.Event(enable_timing=True) for _ in range(nb)] for _ in range(2)]
         for i in range(nb):
             e[0][i].record()
