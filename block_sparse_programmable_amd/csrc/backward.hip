@@ -297,12 +297,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
       ndc = (ok && p.prog.has_doc) ? docr[i + p.q_offset] : 0;
     };
     // The steps of 32 query rows of one block (128-key blocks at d = 128), software
-    // pipelined over nine scheduler-fenced stages: every stage issues the products whose
-    // LDS operands the previous stage read, then reads the next stage's operands, so the
-    // LDS latency runs under the products. Stages 1-4: S and dP over k-steps t = 0..3
-    // (four independent accumulators per stage); 5: weights and gradients (VALU); 6-9:
-    // dV and dK over head-dim tiles 2k, 2k + 1 (four accumulators per stage). Stages 8
-    // and 9 read k-steps 0 and 1 of the next step.
+    // pipelined over scheduler-fenced stages. Stages 1-4 issue S and dP of step n over
+    // k-steps t = 0..3 (four independent accumulators each), each from operands the
+    // previous stage read, and read the transposed operands of step n - 1. Stage 5 forms
+    // the weights and gradients of step n (VALU) with the dV and dK products of step n - 1
+    // (MFMA, independent of that VALU) issued among them, so one wave's VALU and MFMA
+    // overlap; it ends by reading step n + 1's first operands. The first step has no
+    // previous products, and the block ends with those of its last step.
     auto pipelined = [&](int r0, const uint8_t* qs, const float* lse_s, const float* del_s,
                          uint32_t okw, bool sel, uint16_t* dst_tile) {
       const uint8_t* gs = qs + BQM * RS;   // one base: dO offsets become immediates
@@ -325,29 +326,26 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
           f[2 * x + 1] = cat_tr(qs + L::off(tr0, e), qs + L::off(tr0 + 16, e));
         }
       };
-      bf16x8 n0[4], n1[4];
-      rd1(0, 0, n0);
-      rd1(0, 1, n1);
-      __builtin_amdgcn_sched_barrier(0);
-      for (int q0 = 0; q0 < bq; q0 += 32) {
-        f32x4 s[2], dp[2], l4[2];
-        bf16x8 f2[4], f3[4], p0[4], p1[4], p2[4], p3[4];
-        auto mm1 = [&](const bf16x8 (&f)[4], int t) {
+      f32x4 s[2], dp[2], l4[2];
+      bf16x8 pb, db;   // P and dS of the previous step: the B operands of its dV and dK
+      bf16x8 n0[4], n1[4], f2[4], f3[4], p0[4], p1[4], p2[4], p3[4];
+      auto mm1 = [&](const bf16x8 (&f)[4], int t) {
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            s[h] = mma_k32(f[2 * h], kf[t], s[h]);
-            dp[h] = mma_k32(f[2 * h + 1], vf[t], dp[h]);
-          }
-        };
-        float pv[8], ds[8];
-        bf16x8 pb, db;
-        auto mm3 = [&](const bf16x8 (&f)[4], int k) {
+        for (int h = 0; h < 2; ++h) {
+          s[h] = mma_k32(f[2 * h], kf[t], s[h]);
+          dp[h] = mma_k32(f[2 * h + 1], vf[t], dp[h]);
+        }
+      };
+      auto mm3 = [&](const bf16x8 (&f)[4], int k) {
 #pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            dv[2 * k + x] = mma_k32(f[2 * x], pb, dv[2 * k + x]);
-            dk[2 * k + x] = mma_k32(f[2 * x + 1], db, dk[2 * k + x]);
-          }
-        };
+        for (int x = 0; x < 2; ++x) {
+          dv[2 * k + x] = mma_k32(f[2 * x], pb, dv[2 * k + x]);
+          dk[2 * k + x] = mma_k32(f[2 * x + 1], db, dk[2 * k + x]);
+        }
+      };
+      auto sdp = [&](int q0, auto prev_c) {
+        constexpr bool PREV = decltype(prev_c)::value;
+        const int qp = q0 - 32;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -361,11 +359,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
         rd1(q0, 3, f3);
         __builtin_amdgcn_sched_barrier(0);
         mm1(f2, 2);
-        rd3(q0, 0, p0);
+        if constexpr (PREV) rd3(qp, 0, p0);
         __builtin_amdgcn_sched_barrier(0);
         mm1(f3, 3);
-        rd3(q0, 1, p1);
+        if constexpr (PREV) rd3(qp, 1, p1);
         __builtin_amdgcn_sched_barrier(0);
+      };
+      auto grads = [&](int q0, auto prev_c) {
+        constexpr bool PREV = decltype(prev_c)::value;
+        float pv[8], ds[8];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -373,6 +375,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
             const int ig = r0 + q0 + 16 * h + 4 * g4 + rr + (int)p.q_offset;
             grad_elem<SCORE>(s[h][rr], dp[h][rr], l4[h][rr], sc, ig, j, pv[4 * h + rr], ds[4 * h + rr]);
           }
+        }
+        if constexpr (PREV) {
+          mm3(p0, 0);
+          mm3(p1, 1);
+          rd3(q0 - 32, 2, p2);
+          rd3(q0 - 32, 3, p3);
+          mm3(p2, 2);
+          mm3(p3, 3);
         }
         if (sel) {
 #pragma unroll
@@ -386,21 +396,34 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
           __builtin_nontemporal_store(__builtin_bit_cast(u32x4, db),
                                       reinterpret_cast<u32x4*>(dst_tile + (q0 >> 5) * (64 * 8)));
         }
-        __builtin_amdgcn_sched_barrier(0);
-        mm3(p0, 0);
-        rd3(q0, 2, p2);
-        __builtin_amdgcn_sched_barrier(0);
-        mm3(p1, 1);
-        rd3(q0, 3, p3);
-        __builtin_amdgcn_sched_barrier(0);
         const int qn = min(q0 + 32, bq - 32);   // the last step reads its own rows again
-        mm3(p2, 2);
         rd1(qn, 0, n0);
-        __builtin_amdgcn_sched_barrier(0);
-        mm3(p3, 3);
         rd1(qn, 1, n1);
         __builtin_amdgcn_sched_barrier(0);
+      };
+      rd1(0, 0, n0);
+      rd1(0, 1, n1);
+      __builtin_amdgcn_sched_barrier(0);
+      sdp(0, std::false_type{});
+      grads(0, std::false_type{});
+      for (int q0 = 32; q0 < bq; q0 += 32) {
+        sdp(q0, std::true_type{});
+        grads(q0, std::true_type{});
       }
+      // the last step's dV and dK
+      const int ql = bq - 32;
+      rd3(ql, 0, p0);
+      rd3(ql, 1, p1);
+      __builtin_amdgcn_sched_barrier(0);
+      mm3(p0, 0);
+      rd3(ql, 2, p2);
+      __builtin_amdgcn_sched_barrier(0);
+      mm3(p1, 1);
+      rd3(ql, 3, p3);
+      __builtin_amdgcn_sched_barrier(0);
+      mm3(p2, 2);
+      mm3(p3, 3);
+      __builtin_amdgcn_sched_barrier(0);
     };
     // the block of list entry e, rows r0.., from the staged rows, row terms, -delta and
     // document IDs
