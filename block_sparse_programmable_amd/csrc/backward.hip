@@ -289,6 +289,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     auto block_of = [&](int e) -> int { return load_uniform(e >= nf ? pl + (e - nf) : fl + e); };
     float nl2 = 0.f, ndl = 0.f;
     int ndc = 0;
+    u32x4 pend_v = {0u, 0u, 0u, 0u};   // a gradient store held back (flush_pend)
+    uint16_t* pend_p = nullptr;
     auto stats = [&](int r0) {
       const int i = r0 + (int)threadIdx.x;
       const bool ok = (int)threadIdx.x < bq && i < q_len;
@@ -390,9 +392,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
         }
         pb = pack8(pv);
         db = pack8(ds);
-        if (dst_tile) {
+        if (dst_tile && q0 + 32 < bq) {
           // 16 bytes per lane, 1 KB per wave, with the non-temporal policy (the tiles are
-          // read once, by the dQ pass)
+          // read once, by the dQ pass); the last step's part waits (pend)
           __builtin_nontemporal_store(__builtin_bit_cast(u32x4, db),
                                       reinterpret_cast<u32x4*>(dst_tile + (q0 >> 5) * (64 * 8)));
         }
@@ -424,6 +426,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
       mm3(p2, 2);
       mm3(p3, 3);
       __builtin_amdgcn_sched_barrier(0);
+      if (dst_tile) {
+        pend_v = __builtin_bit_cast(u32x4, db);
+        pend_p = dst_tile + ((bq - 32) >> 5) * (64 * 8);
+      }
     };
     // the block of list entry e, rows r0.., from the staged rows, row terms, -delta and
     // document IDs
@@ -503,6 +509,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
       const int64_t slot = (bh * p.tab.nqb + rblk) * p.tab.nkb + c;
       return bp.ds + slot * (128 * 128) + w * (4 * 64 * 8) + lane * 8;
     };
+    // the previous block's last gradient store, held until the next block's wait so that
+    // the wait does not wait for it
+    auto flush_pend = [&]() {
+      if (pend_p) {
+        __builtin_nontemporal_store(pend_v, reinterpret_cast<u32x4*>(pend_p));
+        pend_p = nullptr;
+      }
+    };
     auto put_stats = [&](int buf) {
       if ((int)threadIdx.x < bq) {
         lse2[buf][threadIdx.x] = nl2;
@@ -549,24 +563,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
       };
       __syncthreads();   // the previous head's last block is consumed in every wave
       if (n_ent > 0) copy_rows(block_of(0) * bq, 0);
-      bool stored = false;   // the previous block stored gradient tiles
       for (int e = 0; e < n_ent; ++e) {
         const int rblk = block_of(e), cur = e & 1;
-        // This block's copies have landed. Vector memory operations complete in issue
-        // order for this count, and a block that stores tiles issues its last store
-        // after the next block's copies, so that store, issued a few hundred cycles
-        // ago, may stay in flight.
-        if (stored) {
-          asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-        } else {
-          wait_dma();
-        }
+        wait_dma();        // this block's copies (and every earlier store) have landed
         __syncthreads();   // in every wave; the other buffers' block is consumed
         if (e + 1 < n_ent) copy_rows(block_of(e + 1) * bq, cur ^ 1);
-        uint16_t* tile = tile_of(rblk);
-        stored = tile != nullptr;
-        compute(e, rblk * bq, qg2[cur], qg2[cur] + BQM * RS, lse2[cur], del2[cur], doc2[cur], tile);
+        flush_pend();      // after the wait: it completes during this block
+        compute(e, rblk * bq, qg2[cur], qg2[cur] + BQM * RS, lse2[cur], del2[cur], doc2[cur], tile_of(rblk));
       }
+      flush_pend();
     } else {
       RowStage<D, NT> sq, sg;
       if (n_ent > 0) {
