@@ -874,19 +874,35 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_ds_kernel(BwdParams bp) {
     }
     __syncthreads();
     if (e + 1 < n_ent) fetch(e + 1);   // the next block travels while this one is used
-#pragma unroll
-    for (int k0 = 0; k0 < BKM; k0 += 32) {
-      // B: the stored gradients of rows 16 w + col for keys k0 + 4 g4 + (0..3) and
-      // k0 + 16 + 4 g4 + (0..3), the contraction order of cat_tr
-      const int kr = k0 + 4 * g4 + (col >> 2);
+    // 32 products per block: key step k = i / 8 (32 keys), head-dim tile i % 8. Each
+    // product's A operand is read two products ahead and the next key step's B operand
+    // three ahead, one scheduler-fenced product at a time, so the LDS latency runs under
+    // the MFMAs.
+    // B of key step k: the stored gradients of rows 16 w + col for keys 32 k + 4 g4 +
+    // (0..3) and 32 k + 16 + 4 g4 + (0..3), the contraction order of cat_tr
+    auto rd_b = [&](int k) {
+      const int kr = 32 * k + 4 * g4 + (col >> 2);
       const int ro = 16 * w + 4 * (col & 3);
-      const bf16x8 db = cat_tr(ts + L::off(kr, ro), ts + L::off(kr + 16, ro));
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int ee = 16 * dt + 4 * (col & 3);
-        dq[dt] = mma_k32(cat_tr(ks + L::off(kr, ee), ks + L::off(kr + 16, ee)), db, dq[dt]);
-      }
-    }
+      return cat_tr(ts + L::off(kr, ro), ts + L::off(kr + 16, ro));
+    };
+    auto rd_a = [&](int i) {
+      const int kr = 32 * (i >> 3) + 4 * g4 + (col >> 2);
+      const int ee = 16 * (i & 7) + 4 * (col & 3);
+      return cat_tr(ks + L::off(kr, ee), ks + L::off(kr + 16, ee));
+    };
+    bf16x8 a0 = rd_a(0), a1 = rd_a(1), b0 = rd_b(0), b1 = b0;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<4 * DT>([&](auto i_c) {
+      constexpr int i = decltype(i_c)::value;
+      bf16x8 a2 = a1;
+      if constexpr (i + 2 < 4 * DT) a2 = rd_a(i + 2);
+      if constexpr ((i & 7) == 5 && i + 3 < 4 * DT) b1 = rd_b((i >> 3) + 1);
+      dq[i & 7] = mma_k32(a0, b0, dq[i & 7]);
+      a0 = a1;
+      a1 = a2;
+      if constexpr ((i & 7) == 7) b0 = b1;
+      __builtin_amdgcn_sched_barrier(0);
+    });
   }
   if (i < q_len) {
     const float gs = p.score.kind == FA_S_SOFTCAP ? 4.f * p.scale : p.scale;   // as grad_scale
