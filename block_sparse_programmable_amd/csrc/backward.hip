@@ -720,20 +720,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
     }
     // pairs outside the mask are zeroed only on blocks where the wave has some
     const bool sel = __ballot(okw != 0xffffffffu) != 0;
-    for (int k0 = 0; k0 < bk; k0 += 32) {
-      // S^T (16 keys x 16 rows) = K Q^T and dP^T = V dO^T for keys k0 + 16 h + (0..15)
-      f32x4 s[2], dp[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[h] = dp0;
-#pragma unroll
-        for (int t = 0; t < KS; ++t) {
-          const int off = L::off(k0 + 16 * h + col, 32 * t + 8 * g4);
-          s[h] = mma_k32(*reinterpret_cast<const bf16x8*>(ks + off), qf[t], s[h]);
-          dp[h] = mma_k32(*reinterpret_cast<const bf16x8*>(vs + off), gf[t], dp[h]);
-        }
-      }
+    // lane: keys j0 + k0 + 16 h + 4 g4 + rr, row i: weights and gradients of the 32
+    // keys from S^T and dP^T, the parameter gradients, and dS^T as the B operand db
+    auto grads = [&](int k0, const f32x4 (&s)[2], const f32x4 (&dp)[2]) -> bf16x8 {
       // lane: keys j0 + k0 + 16 h + 4 g4 + rr, row i
       float pv[8], ds[8];
 #pragma unroll
@@ -765,13 +754,89 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
           }
         }
       (void)pv;
-      const bf16x8 db = pack8(ds);
-      // dQ^T += K^T dS^T over the 32 keys (16x16x32; contraction order as in cat_tr)
-      const int tr0 = k0 + 4 * g4 + (col >> 2);
+      return pack8(ds);
+    };
+    if constexpr (D == 128 && NW == 8) {
+      // 128-dim heads, 128-row query blocks: each 32-key step is software-pipelined over
+      // scheduler-fenced stages whose products use LDS operands the previous stage read
+      // (S^T and dP^T over k-steps 0..3, then the gradients, then dQ^T over head-dim
+      // tiles 0..3 and 4..7, which read the next step's first operands)
+      auto rd_s = [&](int kn, int t, bf16x8 (&f)[4]) {   // K h0, V h0, K h1, V h1
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int e = 16 * dt + 4 * (col & 3);
-        dq[dt] = mma_k32(cat_tr(ks + L::off(tr0, e), ks + L::off(tr0 + 16, e)), db, dq[dt]);
+        for (int h = 0; h < 2; ++h) {
+          const int off = L::off(kn + 16 * h + col, 32 * t + 8 * g4);
+          f[2 * h] = *reinterpret_cast<const bf16x8*>(ks + off);
+          f[2 * h + 1] = *reinterpret_cast<const bf16x8*>(vs + off);
+        }
+      };
+      auto rd_q = [&](int k0, int grp, bf16x8 (&f)[4]) {   // K^T tiles 4 grp .. + 3
+        const int tr0 = k0 + 4 * g4 + (col >> 2);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int e = 16 * (4 * grp + x) + 4 * (col & 3);
+          f[x] = cat_tr(ks + L::off(tr0, e), ks + L::off(tr0 + 16, e));
+        }
+      };
+      bf16x8 n0[4], n1[4];
+      rd_s(0, 0, n0);
+      rd_s(0, 1, n1);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int k0 = 0; k0 < bk; k0 += 32) {
+        f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}, dp[2] = {dp0, dp0};
+        bf16x8 f2[4], f3[4], a0[4], a1[4];
+        auto mm_s = [&](const bf16x8 (&f)[4], int t) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            s[h] = mma_k32(f[2 * h], qf[t], s[h]);
+            dp[h] = mma_k32(f[2 * h + 1], gf[t], dp[h]);
+          }
+        };
+        mm_s(n0, 0);
+        rd_s(k0, 2, f2);
+        __builtin_amdgcn_sched_barrier(0);
+        mm_s(n1, 1);
+        rd_s(k0, 3, f3);
+        __builtin_amdgcn_sched_barrier(0);
+        mm_s(f2, 2);
+        rd_q(k0, 0, a0);
+        __builtin_amdgcn_sched_barrier(0);
+        mm_s(f3, 3);
+        rd_q(k0, 1, a1);
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 db = grads(k0, s, dp);
+        __builtin_amdgcn_sched_barrier(0);
+        const int kn = min(k0 + 32, bk - 32);   // the last step reads its own keys again
+#pragma unroll
+        for (int x = 0; x < 4; ++x) dq[x] = mma_k32(a0[x], db, dq[x]);
+        rd_s(kn, 0, n0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) dq[4 + x] = mma_k32(a1[x], db, dq[4 + x]);
+        rd_s(kn, 1, n1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      for (int k0 = 0; k0 < bk; k0 += 32) {
+        f32x4 s[2], dp[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[h] = dp0;
+#pragma unroll
+          for (int t = 0; t < KS; ++t) {
+            const int off = L::off(k0 + 16 * h + col, 32 * t + 8 * g4);
+            s[h] = mma_k32(*reinterpret_cast<const bf16x8*>(ks + off), qf[t], s[h]);
+            dp[h] = mma_k32(*reinterpret_cast<const bf16x8*>(vs + off), gf[t], dp[h]);
+          }
+        }
+        const bf16x8 db = grads(k0, s, dp);
+        // dQ^T += K^T dS^T over the 32 keys (16x16x32; contraction order as in cat_tr)
+        const int tr0 = k0 + 4 * g4 + (col >> 2);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int e = 16 * dt + 4 * (col & 3);
+          dq[dt] = mma_k32(cat_tr(ks + L::off(tr0, e), ks + L::off(tr0 + 16, e)), db, dq[dt]);
+        }
       }
     }
   }
