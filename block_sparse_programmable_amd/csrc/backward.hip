@@ -243,6 +243,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
   const int hkv = bh % p.Hkv;
   const int b = bh / p.Hkv;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, g4 = lane >> 4;
+  // the 8-element k-slice of lane group g4 in the S and dP products (the same for the
+  // LDS-read and the register operand): groups 1 and 2 swapped. A probe of these 16-byte
+  // row reads on the swizzled rows counted bank conflicts in half of their LDS cycles with
+  // slice g4 and none with this order
+  const int g4k = ((g4 & 1) << 1) | (g4 >> 1);
   const int q_len = (int)p.q_len, kv_len = (int)p.kv_len, bq = p.tab.bq;
   const int key0 = c * p.tab.bk + w * 16;   // first key of this wave
   const int j = key0 + col;                            // this lane's key (S column)
@@ -255,8 +260,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
     const int64_t base = ((int64_t)(b * p.Hkv + hkv) * kv_len + jr) * D;
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
-      kf[t] = __builtin_bit_cast(bf16x8, kv_len > 0 ? load16(p.k + base + 32 * t + 8 * g4) : u32x4{0, 0, 0, 0});
-      vf[t] = __builtin_bit_cast(bf16x8, kv_len > 0 ? load16(p.v + base + 32 * t + 8 * g4) : u32x4{0, 0, 0, 0});
+      kf[t] = __builtin_bit_cast(bf16x8, kv_len > 0 ? load16(p.k + base + 32 * t + 8 * g4k) : u32x4{0, 0, 0, 0});
+      vf[t] = __builtin_bit_cast(bf16x8, kv_len > 0 ? load16(p.v + base + 32 * t + 8 * g4k) : u32x4{0, 0, 0, 0});
     }
   }
   f32x4 dk[DT], dv[DT];
@@ -313,7 +318,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
       auto rd1 = [&](int qn, int t, bf16x8 (&f)[4]) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int off = L::off(qn + 16 * h + col, 32 * t + 8 * g4);
+          const int off = L::off(qn + 16 * h + col, 32 * t + 8 * g4k);
           f[2 * h] = *reinterpret_cast<const bf16x8*>(qs + off);
           f[2 * h + 1] = *reinterpret_cast<const bf16x8*>(gs + off);
         }
@@ -463,7 +468,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams bp) {
           dp[h] = *reinterpret_cast<const f32x4*>(del_s + q0 + 16 * h + 4 * g4);
 #pragma unroll
           for (int t = 0; t < KS; ++t) {
-            const int off = L::off(q0 + 16 * h + col, 32 * t + 8 * g4);
+            const int off = L::off(q0 + 16 * h + col, 32 * t + 8 * g4k);
             s[h] = mma_k32(*reinterpret_cast<const bf16x8*>(qs + off), kf[t], s[h]);
             dp[h] = mma_k32(*reinterpret_cast<const bf16x8*>(gs + off), vf[t], dp[h]);
           }
@@ -638,6 +643,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
   const int th = p.tab.tH == 1 ? 0 : hq;
   const int r = p.tab.order ? uniform(p.tab.order[(tb * p.tab.tH + th) * nqb + rank]) : nqb - 1 - rank;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, g4 = lane >> 4;
+  // the 8-element k-slice of lane group g4 in the S and dP products (the same for the
+  // LDS-read and the register operand): groups 1 and 2 swapped. A probe of these 16-byte
+  // row reads on the swizzled rows counted bank conflicts in half of their LDS cycles with
+  // slice g4 and none with this order
+  const int g4k = ((g4 & 1) << 1) | (g4 >> 1);
   const int q_len = (int)p.q_len, kv_len = (int)p.kv_len, bk = p.tab.bk;
   const int i = r * p.tab.bq + w * 16 + col;   // this lane's row (S^T column)
   const bool row_ok = i < q_len;
@@ -650,8 +660,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
     const int64_t base = ((int64_t)bh * q_len + ir) * D;
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
-      qf[t] = __builtin_bit_cast(bf16x8, load16(p.q + base + 32 * t + 8 * g4));
-      gf[t] = __builtin_bit_cast(bf16x8, load16(bp.dout + base + 32 * t + 8 * g4));
+      qf[t] = __builtin_bit_cast(bf16x8, load16(p.q + base + 32 * t + 8 * g4k));
+      gf[t] = __builtin_bit_cast(bf16x8, load16(bp.dout + base + 32 * t + 8 * g4k));
     }
   }
   const ScoreCtx sc = make_score_ctx(p.score, p.scale, hq);
@@ -764,7 +774,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
       auto rd_s = [&](int kn, int t, bf16x8 (&f)[4]) {   // K h0, V h0, K h1, V h1
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int off = L::off(kn + 16 * h + col, 32 * t + 8 * g4);
+          const int off = L::off(kn + 16 * h + col, 32 * t + 8 * g4k);
           f[2 * h] = *reinterpret_cast<const bf16x8*>(ks + off);
           f[2 * h + 1] = *reinterpret_cast<const bf16x8*>(vs + off);
         }
@@ -824,7 +834,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams bp) {
           dp[h] = dp0;
 #pragma unroll
           for (int t = 0; t < KS; ++t) {
-            const int off = L::off(k0 + 16 * h + col, 32 * t + 8 * g4);
+            const int off = L::off(k0 + 16 * h + col, 32 * t + 8 * g4k);
             s[h] = mma_k32(*reinterpret_cast<const bf16x8*>(ks + off), qf[t], s[h]);
             dp[h] = mma_k32(*reinterpret_cast<const bf16x8*>(vs + off), gf[t], dp[h]);
           }
